@@ -1,0 +1,182 @@
+/*
+ * qsmoe.h -- C ABI of the MI355X (gfx950) quantized sparse mixture-of-experts FFN
+ * layer and the dense Q8_0 decode GEMV.
+ *
+ * Sources, cited by page title and section:
+ *   [LILY]  "Optimizing on-device inference for Apple Silicon" (Perplexity blog):
+ *           "Qwen creates three distinct workload shapes" (router scores 256 experts,
+ *           picks eight; a shared expert processes every token), "Dequantize weights
+ *           during matrix multiplication" (4-bit integer codes, one scale and bias per
+ *           group of 64 weights; fp32 accumulation), "Keep expert routing on the GPU"
+ *           (histogram -> prefix scan -> scatter -> block map, no CPU round trip),
+ *           "Match tile size to expert load", "Optimize the single-row weight path",
+ *           "Reduce intermediate and state traffic" (fused expert input projections
+ *           with the gated activation; fused output projection with the routing score
+ *           and the shared-expert result).
+ *   [OMLX]  "oMLX MoE gate/up fusion: qwen35_moe_gate_up implementation analysis"
+ *           (pwwt.cn): "Fusion principle" ([gate; up] concatenated along the output
+ *           axis is bit-identical to separate gate and up), "_can_fuse" (eligibility:
+ *           equal group size, bits, shapes and dtypes).
+ *   [EMBER] "Ember packed Q8 decode" (voidwest.dev): Q8_0 blocks ([fp16 scale][32 x
+ *           int8]) and the packed 16-row tile (eight 64-byte groups + 16 fp16 scales,
+ *           544 bytes); a reusable decode workspace instead of per-layer temporaries.
+ *
+ * General conventions
+ *   - Every tensor pointer is a DEVICE pointer (HBM) unless stated otherwise; every
+ *     call only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *     never synchronizes with the host.
+ *   - The caller owns and frees every buffer.  The library allocates no device memory
+ *     and keeps no state between calls.  Descriptors are read during the call only.
+ *   - All validation runs on the host before the first enqueue; on any error nothing
+ *     is enqueued and the outputs are untouched.  No exception or abort crosses the ABI.
+ *   - Results are bit-deterministic for equal inputs, device and build: there are no
+ *     floating-point atomics and every reduction has a fixed order.
+ *   - Calls on different streams with distinct workspaces and outputs may run
+ *     concurrently.
+ */
+#ifndef QSMOE_H
+#define QSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSMOE_ABI_VERSION 1
+
+typedef int32_t qsmoe_status;
+#define QSMOE_OK               0
+#define QSMOE_ERR_INVALID     -1   /* NULL / misaligned pointer, negative size, bad enum   */
+#define QSMOE_ERR_UNSUPPORTED -2   /* shape or format outside the supported limits         */
+#define QSMOE_ERR_WORKSPACE   -3   /* workspace NULL or smaller than qsmoe_workspace_size  */
+#define QSMOE_ERR_DEVICE      -4   /* a HIP launch failed (hipGetLastError)                */
+
+/* element types */
+#define QSMOE_BF16 0
+#define QSMOE_F16  1
+#define QSMOE_F32  2
+
+/*
+ * A stack of affine-quantized matrices, each [rows][cols], quantized in groups of
+ * 64 consecutive columns of one row ([LILY] "Dequantize weights during matrix
+ * multiplication"):  W[r][c] = scale[r][c/64] * q[r][c] + bias[r][c/64]
+ * with an unsigned integer code q in [0, 2^bits).
+ *   codes   uint8; matrix e, row r starts at byte (e*mat_stride + r) * cols*bits/8.
+ *           4-bit codes: column 2i in the low nibble of byte i, 2i+1 in the high.
+ *   scales  fp16, [..][cols/64]; matrix e, row r at element (e*mat_stride + r)*cols/64
+ *   biases  fp16, same shape and indexing as scales
+ *   mat_stride  rows between consecutive matrices: `rows` for a plain stack, or
+ *           2*inter when gate and up are the two halves of one fused [gate; up]
+ *           stack ([OMLX] "Fusion principle"; then up.codes = gate.codes +
+ *           inter*cols*bits/8 and up.scales/biases = gate.* + inter*cols/64).
+ * All three pointers must be 16-byte aligned and every row's codes start 16-byte
+ * aligned (guaranteed by the shape limits below).
+ */
+typedef struct {
+    const void *codes;
+    const void *scales;
+    const void *biases;
+    int64_t     mat_stride;
+} qsmoe_qmat;
+
+/*
+ * One MoE FFN layer ([LILY] "Qwen creates three distinct workload shapes").
+ *   router_w     [n_experts][hidden] bf16
+ *   router_bias  [n_experts] fp32 added to the logits before selection, or NULL
+ *   gate, up     [n_experts][inter][hidden] stacks;  down [n_experts][hidden][inter]
+ *   has_shared   1: the shared expert (s_gate, s_up [inter][hidden], s_down
+ *                [hidden][inter], one matrix each) processes every token with weight 1
+ *   scale_dtype  QSMOE_F16 (the only supported value)
+ * Limits (else QSMOE_ERR_UNSUPPORTED): group == 64; bits in {4, 8};
+ *   1 <= n_experts <= 256; 1 <= top_k <= min(n_experts, 16);
+ *   hidden % 128 == 0, 128 <= hidden <= 8192; inter % 128 == 0, 128 <= inter <= 2048;
+ *   (top_k + 1) * inter <= 24576 (the decode down kernel keeps every h in LDS).
+ * Every qmat needs mat_stride >= its rows (QSMOE_ERR_INVALID otherwise).
+ */
+typedef struct {
+    int32_t hidden, inter, n_experts, top_k, bits, group;
+    int32_t scale_dtype;
+    const void  *router_w;
+    const float *router_bias;
+    qsmoe_qmat gate, up, down;
+    int32_t    has_shared;
+    qsmoe_qmat s_gate, s_up, s_down;
+} qsmoe_layer_desc;
+
+int          qsmoe_abi_version(void);
+const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL */
+
+/*
+ * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
+ * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
+ * 256-byte aligned; its contents are undefined between calls.  Peak use is at most a
+ * few hundred bytes per routed assignment plus fixed tables; ~320 MiB at T = 4096,
+ * hidden 2048, inter 512, top-8.
+ */
+size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T);
+
+/*
+ * Router only ([LILY] "Qwen creates three distinct workload shapes"): fp32 logits
+ * l[t][e] = sum_c x[t][c] * router_w[e][c] (+ router_bias[e]), the top_k largest per
+ * token (exact ties to the lower expert id), and weights renormalised over the
+ * selection, w_j = exp(l_j - l_max) / sum_{i in selection} exp(l_i - l_max).
+ *   x        [T][hidden] bf16
+ *   topk_idx [T][top_k] int32, ascending expert id within a token (written)
+ *   topk_w   [T][top_k] fp32, aligned with topk_idx (written)
+ *   ws       device workspace of ws_bytes >= qsmoe_workspace_size(d, T)
+ * T == 0 returns QSMOE_OK and enqueues nothing; T > 2^20 is QSMOE_ERR_UNSUPPORTED.
+ */
+qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T,
+                       int32_t *topk_idx, float *topk_w,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole layer: router, top-k, (T >= 2) expert binning, fused [gate; up]
+ * projection + SwiGLU h = silu(g) * u with silu(z) = z / (1 + e^-z), down
+ * projection, and the combine
+ *     y[t] = sum over the selected experts in ascending id of w_j * o_j  +  o_shared,
+ * accumulated in fp32 in that fixed order ([LILY] "Reduce intermediate and state
+ * traffic"; [OMLX] "Fusion principle").
+ *   x        [T][hidden] bf16, |x| < 65504 (activations are consumed as fp16)
+ *   y        [T][hidden], y_dtype QSMOE_BF16 (round-to-nearest-even) or QSMOE_F32
+ *   topk_idx, topk_w  optional outputs as in moe_route (NULL to skip)
+ * Path: T == 1 runs the batch-1 decode kernels (register dequantization on the
+ * vector ALUs, fp32 intermediates); T >= 2 runs the grouped-GEMM path (MFMA on
+ * fp16 operands dequantized in registers, fp32 accumulation, fp16 intermediates).
+ * For a given T the result does not depend on whether gate/up are fused or separate,
+ * nor on the other tokens of the call (tokens are independent), bit for bit.
+ */
+qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t T,
+                               void *y, int32_t y_dtype,
+                               int32_t *topk_idx, float *topk_w,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dense Q8_0 decode GEMV over 16-row packed tiles ([EMBER] packed 16-row tile):
+ *     y[n] = sum_b d[n][b] * sum_{c<32} q[n][32b + c] * x[32b + c]
+ * with fp32 accumulation.
+ *   w_tiles  (N/16)*(K/32) tiles of 544 bytes, panel-major (tile p*(K/32) + b holds
+ *            rows 16p..16p+15, columns 32b..32b+31): eight 64-byte groups, group j =
+ *            rows 0..15 x codes 4j..4j+3 (4 bytes per row, rows in order), then the
+ *            16 fp16 scales in row order.  16-byte aligned.
+ *   x        [K] bf16;  y  [N], y_dtype QSMOE_BF16 or QSMOE_F32
+ * Limits: N % 16 == 0, K % 32 == 0, N >= 16, 32 <= K <= 8192 (else QSMOE_ERR_UNSUPPORTED).
+ */
+qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x,
+                     void *y, int32_t y_dtype, void *stream);
+
+/*
+ * Load-time repacking ([EMBER] packed 16-row tile): row-contiguous Q8_0 blocks
+ * w_rows [N][K/32] x 34 bytes ([fp16 d][32 x int8]) -> w_tiles (layout of q8_gemv).
+ * Pure byte moves, idempotent; w_rows and w_tiles must not overlap.
+ * Limits: N % 16 == 0, K % 32 == 0.
+ */
+qsmoe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSMOE_H */

@@ -1,0 +1,246 @@
+"""Python binding of libqsmoe, the MI355X (gfx950) quantized sparse MoE layer library.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libqsmoe.so`` behind the C ABI declared in ``include/qsmoe.h``.  PyTorch supplies
+device memory and the current stream; outputs and workspaces the caller does not pass
+are allocated here with torch.  The functions carry the names of the C entry points:
+
+    qsmoe_workspace_size, moe_route, moe_layer_forward, q8_gemv, q8_pack_rows16
+
+There is no fallback: if the shared library is missing, loading raises.
+Build it with ``python -m quantized_sparse_moe_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
+
+QSMOE_OK, QSMOE_ERR_INVALID, QSMOE_ERR_UNSUPPORTED, QSMOE_ERR_WORKSPACE, QSMOE_ERR_DEVICE = 0, -1, -2, -3, -4
+QSMOE_BF16, QSMOE_F16, QSMOE_F32 = 0, 1, 2
+
+_lib = None
+
+
+class QsmoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class qsmoe_qmat(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("biases", ctypes.c_void_p), ("mat_stride", ctypes.c_int64)]
+
+
+class qsmoe_layer_desc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("scale_dtype", ctypes.c_int32),
+                ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("gate", qsmoe_qmat), ("up", qsmoe_qmat), ("down", qsmoe_qmat),
+                ("has_shared", ctypes.c_int32),
+                ("s_gate", qsmoe_qmat), ("s_up", qsmoe_qmat), ("s_down", qsmoe_qmat)]
+
+
+EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size", "moe_route",
+           "moe_layer_forward", "q8_gemv", "q8_pack_rows16")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqsmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m quantized_sparse_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.qsmoe_abi_version.restype = ctypes.c_int
+        L.qsmoe_abi_version.argtypes = []
+        L.qsmoe_status_string.restype = ctypes.c_char_p
+        L.qsmoe_status_string.argtypes = [I32]
+        L.qsmoe_workspace_size.restype = SZ
+        L.qsmoe_workspace_size.argtypes = [P, I64]
+        L.moe_route.restype = I32
+        L.moe_route.argtypes = [P, P, I64, P, P, P, SZ, P]
+        L.moe_layer_forward.restype = I32
+        L.moe_layer_forward.argtypes = [P, P, I64, P, I32, P, P, P, SZ, P]
+        L.q8_gemv.restype = I32
+        L.q8_gemv.argtypes = [P, I64, I64, P, P, I32, P]
+        L.q8_pack_rows16.restype = I32
+        L.q8_pack_rows16.argtypes = [P, I64, I64, P, P]
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().qsmoe_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return lib().qsmoe_abi_version()
+
+
+def _check(status: int, where: str) -> None:
+    if status != QSMOE_OK:
+        raise QsmoeError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ---------------------------------------------------------------- layer descriptor
+class LayerDesc:
+    """A ``qsmoe_layer_desc`` plus the device tensors it points into.
+
+    ``gate``, ``up``, ``down`` (and ``s_gate``, ``s_up``, ``s_down`` for the shared
+    expert) are ``(codes, scales, biases, mat_stride, row0)`` tuples of device tensors:
+    matrix e, row r lives at row ``row0 + e*mat_stride + r`` of those tensors.
+    """
+
+    def __init__(self, hidden, inter, n_experts, top_k, bits, router_w, gate, up, down,
+                 router_bias=None, shared=None):
+        self.hidden, self.inter, self.n_experts, self.top_k, self.bits = hidden, inter, n_experts, top_k, bits
+        self._keep = [router_w, router_bias, gate, up, down, shared]
+        d = qsmoe_layer_desc()
+        d.hidden, d.inter, d.n_experts, d.top_k, d.bits, d.group = hidden, inter, n_experts, top_k, bits, 64
+        d.scale_dtype = QSMOE_F16
+        d.router_w = router_w.data_ptr()
+        d.router_bias = None if router_bias is None else router_bias.data_ptr()
+        d.gate, d.up = self._qmat(gate, hidden), self._qmat(up, hidden)
+        d.down = self._qmat(down, inter)
+        d.has_shared = 0 if shared is None else 1
+        if shared is not None:
+            d.s_gate, d.s_up, d.s_down = (self._qmat(shared[0], hidden), self._qmat(shared[1], hidden),
+                                          self._qmat(shared[2], inter))
+        self.desc = d
+
+    def _qmat(self, m, cols: int) -> qsmoe_qmat:
+        codes, scales, biases, stride, row0 = m
+        rb = cols * self.bits // 8
+        ng = cols // 64
+        return qsmoe_qmat(codes.data_ptr() + row0 * rb, scales.data_ptr() + row0 * ng * 2,
+                          biases.data_ptr() + row0 * ng * 2, stride)
+
+    @property
+    def ptr(self) -> int:
+        return ctypes.addressof(self.desc)
+
+    @classmethod
+    def from_host(cls, layer, device="cuda", fused: bool = True) -> "LayerDesc":
+        """Upload a host layer (numpy arrays laid out as ``qsmoe_synth.LayerInputs``).
+
+        ``fused=True`` passes gate and up as the two halves of one [gate; up] stack;
+        ``fused=False`` copies them into two separate stacks.
+        """
+        import numpy as np
+        import torch
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
+
+        I = layer.inter
+
+        def gate_up(qm):
+            c, s, b = dev(qm.codes), dev(qm.scales), dev(qm.biases)
+            if fused:
+                return (c, s, b, 2 * I, 0), (c, s, b, 2 * I, I)
+            g = (c[:, :I].contiguous(), s[:, :I].contiguous(), b[:, :I].contiguous(), I, 0)
+            u = (c[:, I:].contiguous(), s[:, I:].contiguous(), b[:, I:].contiguous(), I, 0)
+            return g, u
+
+        g, u = gate_up(layer.gate_up)
+        dn = (dev(layer.down.codes), dev(layer.down.scales), dev(layer.down.biases), layer.hidden, 0)
+        shared = None
+        if layer.has_shared:
+            sg, su = gate_up(layer.s_gate_up)
+            sd = (dev(layer.s_down.codes), dev(layer.s_down.scales), dev(layer.s_down.biases),
+                  layer.hidden, 0)
+            shared = (sg, su, sd)
+        rb = None if layer.router_bias is None else dev(np.asarray(layer.router_bias, np.float32))
+        return cls(layer.hidden, I, layer.n_experts, layer.top_k, layer.bits, dev(layer.router_w),
+                   g, u, dn, router_bias=rb, shared=shared)
+
+
+# ------------------------------------------------------------------- entry points
+def qsmoe_workspace_size(desc: LayerDesc, T: int) -> int:
+    n = lib().qsmoe_workspace_size(desc.ptr, int(T))
+    if n == ctypes.c_size_t(-1).value:
+        raise QsmoeError(QSMOE_ERR_UNSUPPORTED, "qsmoe_workspace_size")
+    return n
+
+
+def _workspace(desc: LayerDesc, T: int, workspace, device):
+    import torch
+    n = qsmoe_workspace_size(desc, T)
+    if workspace is None:
+        workspace = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def moe_route(desc: LayerDesc, x, topk_idx=None, topk_w=None, workspace=None,
+              stream=None) -> Tuple["object", "object"]:
+    """Router + top-k: returns (topk_idx int32 [T, k], topk_w fp32 [T, k])."""
+    import torch
+    T = x.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, desc.top_k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, desc.top_k), dtype=torch.float32, device=x.device)
+    ws, nbytes = _workspace(desc, T, workspace, x.device)
+    _check(lib().moe_route(desc.ptr, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes,
+                           _stream(stream)), "moe_route")
+    return topk_idx, topk_w
+
+
+def moe_layer_forward(desc: LayerDesc, x, y=None, y_dtype=None, topk_idx=None, topk_w=None,
+                      workspace=None, stream=None):
+    """The whole MoE layer on bf16 ``x`` [T, hidden]; returns ``y`` (fp32 or bf16)."""
+    import torch
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, desc.hidden), dtype=y_dtype or torch.float32, device=x.device)
+    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
+    if code is None:
+        raise QsmoeError(QSMOE_ERR_INVALID, "moe_layer_forward: y must be float32 or bfloat16")
+    ws, nbytes = _workspace(desc, T, workspace, x.device)
+    _check(lib().moe_layer_forward(desc.ptr, _ptr(x), T, _ptr(y), code, _ptr(topk_idx), _ptr(topk_w),
+                                   _ptr(ws), nbytes, _stream(stream)), "moe_layer_forward")
+    return y
+
+
+def q8_gemv(w_tiles, N: int, K: int, x, y=None, y_dtype=None, stream=None):
+    """Dense Q8_0 GEMV over 16-row packed tiles; returns ``y`` [N] (fp32 or bf16)."""
+    import torch
+    if y is None:
+        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=x.device)
+    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
+    if code is None:
+        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv: y must be float32 or bfloat16")
+    _check(lib().q8_gemv(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), code, _stream(stream)), "q8_gemv")
+    return y
+
+
+def q8_pack_rows16(w_rows, N: int, K: int, w_tiles=None, stream=None):
+    """Row-contiguous Q8_0 blocks -> 16-row packed tiles (load-time, on the device)."""
+    import torch
+    if w_tiles is None:
+        w_tiles = torch.empty((N // 16 * (K // 32) * 544,), dtype=torch.uint8, device=w_rows.device)
+    _check(lib().q8_pack_rows16(_ptr(w_rows), N, K, _ptr(w_tiles), _stream(stream)), "q8_pack_rows16")
+    return w_tiles

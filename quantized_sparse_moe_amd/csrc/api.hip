@@ -1,0 +1,256 @@
+// api.hip -- the C ABI of libqsmoe (declared in include/qsmoe.h): host-side validation,
+// workspace carving and the launch sequence on the caller's stream.
+//
+// [LILY] "Keep expert routing on the GPU": a layer call enqueues its whole sequence
+// (router, binning, expert GEMMs, combine) and never waits for the device.
+// [OMLX] "_can_fuse": eligibility is checked up front (equal group size and bits,
+// matching shapes); unlike that patch, an ineligible layer is an error here, never a
+// silent fallback to a second code path.
+// [EMBER]: decode reuses one caller-provided workspace instead of per-layer temporaries.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace qs;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+qsmoe_status check_qmat(const qsmoe_qmat &m, int64_t rows) {
+    if (!m.codes || !m.scales || !m.biases) return QSMOE_ERR_INVALID;
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 2) || !aligned(m.biases, 2)) return QSMOE_ERR_INVALID;
+    if (m.mat_stride < rows) return QSMOE_ERR_INVALID;
+    return QSMOE_OK;
+}
+
+qsmoe_status check_desc(const qsmoe_layer_desc *d) {
+    if (!d) return QSMOE_ERR_INVALID;
+    if (d->group != 64 || (d->bits != 4 && d->bits != 8) || d->scale_dtype != QSMOE_F16)
+        return QSMOE_ERR_UNSUPPORTED;
+    if (d->n_experts < 1 || d->n_experts > 256) return QSMOE_ERR_UNSUPPORTED;
+    if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return QSMOE_ERR_UNSUPPORTED;
+    if (d->hidden < 128 || d->hidden > 8192 || d->hidden % 128) return QSMOE_ERR_UNSUPPORTED;
+    if (d->inter < 128 || d->inter > 2048 || d->inter % 128) return QSMOE_ERR_UNSUPPORTED;
+    if ((int64_t)(d->top_k + 1) * d->inter > 24576) return QSMOE_ERR_UNSUPPORTED;
+    if (!d->router_w || !aligned(d->router_w, 16)) return QSMOE_ERR_INVALID;
+    if (d->router_bias && !aligned(d->router_bias, 4)) return QSMOE_ERR_INVALID;
+    if (d->has_shared != 0 && d->has_shared != 1) return QSMOE_ERR_INVALID;
+    qsmoe_status s;
+    if ((s = check_qmat(d->gate, d->inter)) || (s = check_qmat(d->up, d->inter)) ||
+        (s = check_qmat(d->down, d->hidden)))
+        return s;
+    if (d->has_shared &&
+        ((s = check_qmat(d->s_gate, d->inter)) || (s = check_qmat(d->s_up, d->inter)) ||
+         (s = check_qmat(d->s_down, d->hidden))))
+        return s;
+    return QSMOE_OK;
+}
+
+QMat to_qmat(const qsmoe_qmat &m) {
+    QMat q;
+    q.codes = (const uint8_t *)m.codes;
+    q.scales = (const uint16_t *)m.scales;
+    q.biases = (const uint16_t *)m.biases;
+    q.stride = m.mat_stride;
+    return q;
+}
+
+Layer to_layer(const qsmoe_layer_desc *d) {
+    Layer L;
+    L.H = d->hidden;
+    L.I = d->inter;
+    L.E = d->n_experts;
+    L.K = d->top_k;
+    L.bits = d->bits;
+    L.router_w = (const uint16_t *)d->router_w;
+    L.router_bias = d->router_bias;
+    L.gate = to_qmat(d->gate);
+    L.up = to_qmat(d->up);
+    L.down = to_qmat(d->down);
+    L.has_shared = d->has_shared;
+    if (d->has_shared) {
+        L.s_gate = to_qmat(d->s_gate);
+        L.s_up = to_qmat(d->s_up);
+        L.s_down = to_qmat(d->s_down);
+    } else {
+        L.s_gate = L.s_up = L.s_down = QMat{nullptr, nullptr, nullptr, 0};
+    }
+    return L;
+}
+
+// ---------------------------------------------------------------- workspace layouts
+struct Carver {
+    char *base;
+    size_t off = 0;
+    template <typename T>
+    T *take(size_t count) {
+        T *p = base ? (T *)(base + off) : nullptr;
+        off += up(count * sizeof(T));
+        return p;
+    }
+};
+
+DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
+    Carver c{(char *)ws};
+    DecodeBufs b;
+    b.logits = c.take<float>(d->n_experts);
+    b.h = c.take<float>((size_t)(d->top_k + 1) * d->inter);
+    b.idx = c.take<int32_t>(d->top_k);
+    b.w = c.take<float>(d->top_k);
+    *bytes = c.off;
+    return b;
+}
+
+PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t *bytes) {
+    Carver c{(char *)ws};
+    const int64_t H = d->hidden, I = d->inter, K = d->top_k, E = d->n_experts;
+    const int64_t nblk = (T + ROUTER_TOKENS - 1) / ROUTER_TOKENS;
+    PrefillBufs b;
+    b.x16 = c.take<uint16_t>((size_t)(T * H));
+    b.idx = c.take<int32_t>((size_t)(T * K));
+    b.w = c.take<float>((size_t)(T * K));
+    b.blkcnt = c.take<int32_t>((size_t)(nblk * E));
+    b.blkoff = c.take<int32_t>((size_t)(nblk * E));
+    b.expert_off = c.take<int32_t>((size_t)(2 * E + 1));
+    b.perm = c.take<int32_t>((size_t)(T * K));
+    b.tiles = c.take<Tile>((size_t)prefill_max_tiles(T, (int)K, (int)E));
+    b.ntiles = c.take<int32_t>(2);
+    b.h = c.take<uint16_t>((size_t)((T * K + T) * I));
+    b.slot = c.take<uint16_t>((size_t)(T * K * H));
+    *bytes = c.off;
+    return b;
+}
+
+size_t ws_size(const qsmoe_layer_desc *d, int64_t T) {
+    size_t n = 0;
+    if (T <= 0) return 0;
+    if (T == 1) carve_decode(d, nullptr, &n);
+    else carve_prefill(d, T, nullptr, &n);
+    return n;
+}
+
+qsmoe_status check_ws(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, ALIGN)) return QSMOE_ERR_WORKSPACE;
+    if (ws_bytes < ws_size(d, T)) return QSMOE_ERR_WORKSPACE;
+    return QSMOE_OK;
+}
+
+inline qsmoe_status dev(hipError_t e) { return e == hipSuccess ? QSMOE_OK : QSMOE_ERR_DEVICE; }
+
+// tokens * hidden must stay addressable with the kernels' 32-bit row offsets
+constexpr int64_t MAX_TOKENS = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+int qsmoe_abi_version(void) { return QSMOE_ABI_VERSION; }
+
+const char *qsmoe_status_string(qsmoe_status s) {
+    switch (s) {
+        case QSMOE_OK: return "ok";
+        case QSMOE_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size or enum)";
+        case QSMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case QSMOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case QSMOE_ERR_DEVICE: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T) {
+    if (check_desc(d) != QSMOE_OK) return SIZE_MAX;
+    if (T > MAX_TOKENS) return SIZE_MAX;
+    return ws_size(d, T);
+}
+
+qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int32_t *topk_idx,
+                       float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    qsmoe_status s = check_desc(d);
+    if (s) return s;
+    if (T < 0) return QSMOE_ERR_INVALID;
+    if (T > MAX_TOKENS) return QSMOE_ERR_UNSUPPORTED;
+    if (T == 0) return QSMOE_OK;
+    if (!x || !aligned(x, 16) || !topk_idx || !topk_w || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return QSMOE_ERR_INVALID;
+    if ((s = check_ws(d, T, ws, ws_bytes))) return s;
+    const Layer L = to_layer(d);
+    hipStream_t st = (hipStream_t)stream;
+    if (T == 1) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        hipError_t e = launch_decode_router_shared(L, (const uint16_t *)x, b, false, st);
+        if (e == hipSuccess) e = launch_decode_topk(L, b, topk_idx, topk_w, st);
+        return dev(e);
+    }
+    PrefillBufs b;
+    std::memset(&b, 0, sizeof(b));
+    b.idx = topk_idx;
+    b.w = topk_w;
+    return dev(launch_prefill_router(L, (const uint16_t *)x, T, b, false, nullptr, nullptr, st));
+}
+
+qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t T, void *y,
+                               int32_t y_dtype, int32_t *topk_idx, float *topk_w, void *ws,
+                               size_t ws_bytes, void *stream) {
+    qsmoe_status s = check_desc(d);
+    if (s) return s;
+    if (T < 0) return QSMOE_ERR_INVALID;
+    if (T > MAX_TOKENS) return QSMOE_ERR_UNSUPPORTED;
+    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (T == 0) return QSMOE_OK;
+    if (!x || !aligned(x, 16) || !y || !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2)) return QSMOE_ERR_INVALID;
+    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return QSMOE_ERR_INVALID;
+    if ((s = check_ws(d, T, ws, ws_bytes))) return s;
+    const Layer L = to_layer(d);
+    hipStream_t st = (hipStream_t)stream;
+    const uint16_t *xx = (const uint16_t *)x;
+    hipError_t e;
+    if (T == 1) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        e = launch_decode_router_shared(L, xx, b, true, st);
+        if (e == hipSuccess) e = launch_decode_gate_up(L, xx, b, topk_idx, topk_w, st);
+        if (e == hipSuccess) e = launch_decode_down(L, b, y, y_dtype, st);
+        return dev(e);
+    }
+    size_t n;
+    const PrefillBufs b = carve_prefill(d, T, ws, &n);
+    e = launch_prefill_router(L, xx, T, b, true, topk_idx, topk_w, st);
+    if (e == hipSuccess) e = launch_prefill_binning(L, T, b, st);
+    if (e == hipSuccess) e = launch_prefill_gemms(L, T, b, y, y_dtype, st);
+    return dev(e);
+}
+
+qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
+                     int32_t y_dtype, void *stream) {
+    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
+    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
+        return QSMOE_ERR_UNSUPPORTED;
+    if (!w_tiles || !aligned(w_tiles, 16) || !x || !aligned(x, 16) || !y ||
+        !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
+        return QSMOE_ERR_INVALID;
+    return dev(launch_q8_gemv((const uint8_t *)w_tiles, N, K, (const uint16_t *)x, y, y_dtype,
+                              (hipStream_t)stream));
+}
+
+qsmoe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles, void *stream) {
+    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
+    if (N % 16 || K % 32) return QSMOE_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return QSMOE_OK;
+    if (!w_rows || !w_tiles || !aligned(w_tiles, 16)) return QSMOE_ERR_INVALID;
+    const size_t bytes = (size_t)N * (size_t)(K / 32) * 34;
+    const uintptr_t a = (uintptr_t)w_rows, b = (uintptr_t)w_tiles;
+    if (a < b + bytes && b < a + bytes) return QSMOE_ERR_INVALID;   // overlap
+    return dev(launch_q8_pack((const uint8_t *)w_rows, N, K, (uint8_t *)w_tiles, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// q8.hip -- dense Q8_0 decode GEMV over 16-row packed tiles, and the load-time packer.
+//
+// [EMBER] packed 16-row tile: rows are packed 16 at a time; for each block of 32 input
+// columns, the bytes of the same 4 columns of the 16 rows sit next to each other
+// (eight 64-byte groups), followed by the 16 fp16 scales -- 544 bytes, the size of 16
+// ordinary Q8_0 blocks.  On x86 this lets one VNNI step broadcast 4 activation bytes
+// against a 64-byte weight group.  On gfx950 the same layout makes a wave's load of
+// 4 consecutive groups one contiguous 256-byte read: lane l takes row l % 16 of group
+// l / 16 (and of group l / 16 + 4), so a whole tile is read by two dword loads per lane
+// and every lane keeps accumulating one row.
+//
+// Codes are widened exactly: (q ^ 0x80) is q + 128 as an unsigned byte, which the
+// byte-to-float conversion turns into fp32 in one instruction; the +128 is removed per
+// lane with the staged sum of the 8 activations the lane multiplies.
+#include "common.h"
+#include "internal.h"
+
+namespace qs {
+
+namespace {
+
+constexpr int Q8_THREADS = 512;           // 8 waves share one 16-row panel (split-K)
+constexpr int Q8_WAVES = Q8_THREADS / 64;
+constexpr int TILE = 544;
+
+// byte N of p as fp32 (selected as a single v_cvt_f32_ubyteN)
+template <int N>
+__device__ __forceinline__ float ubyte(uint32_t p) { return (float)((p >> (8 * N)) & 0xffu); }
+
+template <int UNROLL>
+__global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv(const uint8_t *__restrict__ tiles, int64_t K,
+                                                        const uint16_t *__restrict__ x, void *y,
+                                                        int y_dtype) {
+    extern __shared__ float q8s[];
+    const int nb = (int)(K / 32);
+    float *xl = q8s;                      // [nb*4][8]
+    float *x8 = q8s + (int64_t)nb * 32;   // [nb*4]
+    __shared__ float red[Q8_WAVES][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // stage x: slot (b, j) holds x[32b+4j .. +4] and x[32b+16+4j .. +4]
+    for (int sl = tid; sl < nb * 4; sl += Q8_THREADS) {
+        const int b = sl >> 2, j = sl & 3;
+        const uint2 lo = *(const uint2 *)(x + 32 * b + 4 * j);
+        const uint2 hi = *(const uint2 *)(x + 32 * b + 16 + 4 * j);
+        float v[8];
+        v[0] = __uint_as_float(lo.x << 16); v[1] = __uint_as_float(lo.x & 0xffff0000u);
+        v[2] = __uint_as_float(lo.y << 16); v[3] = __uint_as_float(lo.y & 0xffff0000u);
+        v[4] = __uint_as_float(hi.x << 16); v[5] = __uint_as_float(hi.x & 0xffff0000u);
+        v[6] = __uint_as_float(hi.y << 16); v[7] = __uint_as_float(hi.y & 0xffff0000u);
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += v[i];
+        *(f32x4 *)(xl + 8 * sl) = (f32x4){v[0], v[1], v[2], v[3]};
+        *(f32x4 *)(xl + 8 * sl + 4) = (f32x4){v[4], v[5], v[6], v[7]};
+        x8[sl] = s;
+    }
+    __syncthreads();
+
+    const int r = lane & 15, j = lane >> 4;
+    const uint8_t *panel = tiles + (int64_t)blockIdx.x * nb * TILE;
+    float acc = 0.0f;
+    int b = wave;
+    for (; b + (UNROLL - 1) * Q8_WAVES < nb; b += UNROLL * Q8_WAVES) {
+        uint32_t w0[UNROLL], w1[UNROLL];
+        uint16_t dd[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const uint8_t *t = panel + (int64_t)(b + u * Q8_WAVES) * TILE;
+            w0[u] = __builtin_nontemporal_load((const uint32_t *)(t + 64 * j + 4 * r));
+            w1[u] = __builtin_nontemporal_load((const uint32_t *)(t + 64 * (j + 4) + 4 * r));
+            dd[u] = __builtin_nontemporal_load((const uint16_t *)(t + 512 + 2 * r));
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int sl = (b + u * Q8_WAVES) * 4 + j;
+            const f32x4 xa = *(const f32x4 *)(xl + 8 * sl);
+            const f32x4 xb = *(const f32x4 *)(xl + 8 * sl + 4);
+            const uint32_t p0 = w0[u] ^ 0x80808080u, p1 = w1[u] ^ 0x80808080u;
+            float s = 0.0f;
+            s = __builtin_fmaf(ubyte<0>(p0), xa[0], s);
+            s = __builtin_fmaf(ubyte<1>(p0), xa[1], s);
+            s = __builtin_fmaf(ubyte<2>(p0), xa[2], s);
+            s = __builtin_fmaf(ubyte<3>(p0), xa[3], s);
+            s = __builtin_fmaf(ubyte<0>(p1), xb[0], s);
+            s = __builtin_fmaf(ubyte<1>(p1), xb[1], s);
+            s = __builtin_fmaf(ubyte<2>(p1), xb[2], s);
+            s = __builtin_fmaf(ubyte<3>(p1), xb[3], s);
+            acc = __builtin_fmaf(f16_to_f32(dd[u]), s - 128.0f * x8[sl], acc);
+        }
+    }
+    for (; b < nb; b += Q8_WAVES) {
+        const uint8_t *t = panel + (int64_t)b * TILE;
+        const uint32_t p0 = *(const uint32_t *)(t + 64 * j + 4 * r) ^ 0x80808080u;
+        const uint32_t p1 = *(const uint32_t *)(t + 64 * (j + 4) + 4 * r) ^ 0x80808080u;
+        const uint16_t d = *(const uint16_t *)(t + 512 + 2 * r);
+        const int sl = b * 4 + j;
+        const f32x4 xa = *(const f32x4 *)(xl + 8 * sl);
+        const f32x4 xb = *(const f32x4 *)(xl + 8 * sl + 4);
+        float s = 0.0f;
+        s = __builtin_fmaf(ubyte<0>(p0), xa[0], s);
+        s = __builtin_fmaf(ubyte<1>(p0), xa[1], s);
+        s = __builtin_fmaf(ubyte<2>(p0), xa[2], s);
+        s = __builtin_fmaf(ubyte<3>(p0), xa[3], s);
+        s = __builtin_fmaf(ubyte<0>(p1), xb[0], s);
+        s = __builtin_fmaf(ubyte<1>(p1), xb[1], s);
+        s = __builtin_fmaf(ubyte<2>(p1), xb[2], s);
+        s = __builtin_fmaf(ubyte<3>(p1), xb[3], s);
+        acc = __builtin_fmaf(f16_to_f32(d), s - 128.0f * x8[sl], acc);
+    }
+    // lanes r, r+16, r+32, r+48 hold row r of this wave's blocks
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < 16) red[wave][lane] = acc;
+    __syncthreads();
+    if (tid < 16) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < Q8_WAVES; ++w) s += red[w][tid];
+        const int64_t n = (int64_t)blockIdx.x * 16 + tid;
+        if (y_dtype == QSMOE_F32) ((float *)y)[n] = s;
+        else ((uint16_t *)y)[n] = f32_to_bf16(s);
+    }
+}
+
+// one thread per 16-byte chunk of the packed output
+__global__ __launch_bounds__(256) void k_q8_pack(const uint8_t *__restrict__ rows, int64_t N, int64_t K,
+                                                 uint8_t *__restrict__ tiles) {
+    const int64_t nb = K / 32;
+    const int64_t chunks = (N / 16) * nb * 34;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= chunks) return;
+    const int64_t tt = c / 34;
+    const int i = (int)(c % 34);
+    const int64_t p = tt / nb, b = tt % nb;
+    uint8_t out[16];
+    if (i < 32) {
+        const int j = i >> 2, r0 = 4 * (i & 3);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint8_t *blk = rows + ((p * 16 + r0 + rr) * nb + b) * 34;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) out[4 * rr + q] = blk[2 + 4 * j + q];
+        }
+    } else {
+        const int r0 = 8 * (i - 32);
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const uint8_t *blk = rows + ((p * 16 + r0 + rr) * nb + b) * 34;
+            out[2 * rr] = blk[0];
+            out[2 * rr + 1] = blk[1];
+        }
+    }
+    u32x4 v;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        v[q] = (uint32_t)out[4 * q] | ((uint32_t)out[4 * q + 1] << 8) | ((uint32_t)out[4 * q + 2] << 16) |
+               ((uint32_t)out[4 * q + 3] << 24);
+    *(u32x4 *)(tiles + tt * TILE + 16 * i) = v;
+}
+
+}  // namespace
+
+hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint16_t *x, void *y,
+                          int y_dtype, hipStream_t s) {
+    const size_t lds = (size_t)(K / 32) * 32 * 4 + (size_t)(K / 32) * 4 * 4;
+    hipLaunchKernelGGL((k_q8_gemv<4>), dim3((unsigned)(N / 16)), dim3(Q8_THREADS), lds, s, tiles, K, x, y,
+                       y_dtype);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_pack(const uint8_t *rows, int64_t N, int64_t K, uint8_t *tiles, hipStream_t s) {
+    const int64_t chunks = (N / 16) * (K / 32) * 34;
+    hipLaunchKernelGGL(k_q8_pack, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, rows, N, K, tiles);
+    return hipGetLastError();
+}
+
+}  // namespace qs

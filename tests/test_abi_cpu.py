@@ -1,0 +1,166 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every entry point
+the header declares, and rejects invalid calls on the host before any HIP call.
+
+Pointers passed here are fake, never dereferenced: every call below fails validation
+(or is a T = 0 no-op), which the ABI guarantees happens before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_sparse_moe_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsmoe.h")
+FAKE = 0x7F0000000000          # 256-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_library_exports_every_declared_function():
+    L = q.lib()
+    declared = header_functions()
+    assert set(declared) == set(q.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", q.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_abi_version_and_status_strings():
+    assert q.abi_version() == 1
+    for s in (0, -1, -2, -3, -4):
+        assert q.status_string(s) and q.status_string(s) != "unknown status"
+    assert q.status_string(7) == "unknown status"
+
+
+def desc(**kw):
+    d = q.qsmoe_layer_desc()
+    d.hidden, d.inter, d.n_experts, d.top_k, d.bits, d.group = 2048, 512, 256, 8, 4, 64
+    d.scale_dtype = q.QSMOE_F16
+    d.router_w = FAKE
+    d.router_bias = None
+    rows_gu, rows_d = 512, 2048
+    d.gate = q.qsmoe_qmat(FAKE, FAKE, FAKE, 2 * rows_gu)
+    d.up = q.qsmoe_qmat(FAKE + 512 * 1024, FAKE, FAKE, 2 * rows_gu)
+    d.down = q.qsmoe_qmat(FAKE, FAKE, FAKE, rows_d)
+    d.has_shared = 1
+    d.s_gate = q.qsmoe_qmat(FAKE, FAKE, FAKE, 2 * rows_gu)
+    d.s_up = q.qsmoe_qmat(FAKE, FAKE, FAKE, 2 * rows_gu)
+    d.s_down = q.qsmoe_qmat(FAKE, FAKE, FAKE, rows_d)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def fwd(d, T=16, x=FAKE, y=FAKE, y_dtype=q.QSMOE_F32, ws=FAKE, ws_bytes=1 << 40, idx=None, w=None):
+    return q.lib().moe_layer_forward(ctypes.byref(d), x, T, y, y_dtype, idx, w, ws, ws_bytes, None)
+
+
+def route(d, T=16, x=FAKE, ws=FAKE, ws_bytes=1 << 40, idx=FAKE, w=FAKE):
+    return q.lib().moe_route(ctypes.byref(d), x, T, idx, w, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("bits", 3, q.QSMOE_ERR_UNSUPPORTED), ("bits", 2, q.QSMOE_ERR_UNSUPPORTED),
+    ("group", 32, q.QSMOE_ERR_UNSUPPORTED), ("scale_dtype", q.QSMOE_BF16, q.QSMOE_ERR_UNSUPPORTED),
+    ("n_experts", 0, q.QSMOE_ERR_UNSUPPORTED), ("n_experts", 257, q.QSMOE_ERR_UNSUPPORTED),
+    ("top_k", 0, q.QSMOE_ERR_UNSUPPORTED), ("top_k", 17, q.QSMOE_ERR_UNSUPPORTED),
+    ("hidden", 2000, q.QSMOE_ERR_UNSUPPORTED), ("hidden", 64, q.QSMOE_ERR_UNSUPPORTED),
+    ("hidden", 8320, q.QSMOE_ERR_UNSUPPORTED), ("inter", 576, q.QSMOE_ERR_UNSUPPORTED),
+    ("inter", 2176, q.QSMOE_ERR_UNSUPPORTED), ("router_w", None, q.QSMOE_ERR_INVALID),
+    ("router_w", FAKE + 8, q.QSMOE_ERR_INVALID), ("has_shared", 2, q.QSMOE_ERR_INVALID),
+])
+def test_descriptor_validation(field, value, status):
+    d = desc(**{field: value})
+    assert fwd(d) == status
+    assert route(d) == status
+    assert q.lib().qsmoe_workspace_size(ctypes.byref(d), 16) == ctypes.c_size_t(-1).value
+
+
+def test_top_k_above_experts_and_lds_limit():
+    assert fwd(desc(n_experts=4, top_k=8)) == q.QSMOE_ERR_UNSUPPORTED
+    assert fwd(desc(top_k=16, inter=2048)) == q.QSMOE_ERR_UNSUPPORTED     # (k+1)*inter > 24576
+
+
+def test_qmat_validation():
+    d = desc()
+    d.gate = q.qsmoe_qmat(None, FAKE, FAKE, 1024)
+    assert fwd(d) == q.QSMOE_ERR_INVALID
+    d = desc()
+    d.up = q.qsmoe_qmat(FAKE + 4, FAKE, FAKE, 1024)                      # codes misaligned
+    assert fwd(d) == q.QSMOE_ERR_INVALID
+    d = desc()
+    d.down = q.qsmoe_qmat(FAKE, FAKE, FAKE, 100)                         # stride < rows
+    assert fwd(d) == q.QSMOE_ERR_INVALID
+    d = desc()
+    d.s_down = q.qsmoe_qmat(FAKE, None, FAKE, 2048)
+    assert fwd(d) == q.QSMOE_ERR_INVALID
+    d.has_shared = 0                                                     # shared ignored
+    assert fwd(d, T=0) == q.QSMOE_OK
+
+
+def test_call_validation():
+    d = desc()
+    assert fwd(d, T=-1) == q.QSMOE_ERR_INVALID
+    assert fwd(d, T=0) == q.QSMOE_OK                                     # no work, nothing enqueued
+    assert fwd(d, T=0, x=None, y=None, ws=None) == q.QSMOE_OK
+    assert fwd(d, x=None) == q.QSMOE_ERR_INVALID
+    assert fwd(d, x=FAKE + 2) == q.QSMOE_ERR_INVALID
+    assert fwd(d, y=None) == q.QSMOE_ERR_INVALID
+    assert fwd(d, y_dtype=q.QSMOE_F16) == q.QSMOE_ERR_INVALID
+    assert fwd(d, y=FAKE + 2, y_dtype=q.QSMOE_F32) == q.QSMOE_ERR_INVALID
+    assert fwd(d, idx=FAKE + 1) == q.QSMOE_ERR_INVALID
+    assert fwd(d, ws=None) == q.QSMOE_ERR_WORKSPACE
+    assert fwd(d, ws=FAKE + 64) == q.QSMOE_ERR_WORKSPACE
+    need = q.lib().qsmoe_workspace_size(ctypes.byref(d), 16)
+    assert fwd(d, ws_bytes=need - 1) == q.QSMOE_ERR_WORKSPACE
+    assert fwd(d, T=(1 << 20) + 1) == q.QSMOE_ERR_UNSUPPORTED
+    assert route(d, idx=None) == q.QSMOE_ERR_INVALID
+    assert route(d, w=FAKE + 2) == q.QSMOE_ERR_INVALID
+    assert route(d, T=0) == q.QSMOE_OK
+
+
+def test_workspace_sizes():
+    d = desc()
+    f = lambda T: q.lib().qsmoe_workspace_size(ctypes.byref(d), T)
+    assert f(0) == 0 and f(-3) == 0
+    assert 0 < f(1) < 1 << 20                                            # decode: a few KB
+    prev = f(2)
+    for T in (3, 17, 64, 1000, 4096):
+        assert f(T) >= prev
+        prev = f(T)
+    # the grouped path keeps x16, h (routed + shared) and the fp16 slots
+    T, H, I, K = 4096, 2048, 512, 8
+    assert f(T) >= 2 * T * H + 2 * (T * K + T) * I + 2 * T * K * H
+    assert f(T) < 400 * 2 ** 20
+
+
+def test_q8_validation():
+    L = q.lib()
+    assert L.q8_gemv(FAKE, 2048, 2048, FAKE, FAKE, q.QSMOE_F16, None) == q.QSMOE_ERR_INVALID
+    assert L.q8_gemv(FAKE, 2040, 2048, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_gemv(FAKE, 2048, 2050, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_gemv(FAKE, 2048, 8224, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_gemv(FAKE, -16, 2048, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_INVALID
+    assert L.q8_gemv(None, 2048, 2048, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_INVALID
+    assert L.q8_gemv(FAKE + 8, 2048, 2048, FAKE, FAKE, q.QSMOE_F32, None) == q.QSMOE_ERR_INVALID
+    assert L.q8_pack_rows16(FAKE, 2048, 2040, FAKE, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_pack_rows16(FAKE, 0, 2048, FAKE, None) == q.QSMOE_OK
+    assert L.q8_pack_rows16(FAKE, 32, 64, FAKE + 64, None) == q.QSMOE_ERR_INVALID     # overlap
+    assert L.q8_pack_rows16(None, 32, 64, FAKE, None) == q.QSMOE_ERR_INVALID
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(q, "_lib", None)
+    monkeypatch.setattr(q, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        q.lib()

@@ -1,0 +1,211 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Sizes: small cases the oracle finishes in seconds (several tiles plus ragged tails),
+and the full workload sizes in the launch configuration the benchmark times, checked
+on sampled tokens (tokens are independent, so the oracle evaluates just those rows).
+Bit-exact invariants: fused [gate; up] == separate gate and up, repeat calls,
+token permutation and chunking.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qsmoe_synth as syn
+from gpu_util import (check_output, check_routing, sample_tokens, to_dev, y_to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a ROCm device"
+    return t
+
+
+@pytest.fixture(scope="module")
+def qs():
+    import quantized_sparse_moe_amd as q
+    q.lib()
+    return q
+
+
+_LAYERS = {}
+
+
+def layer(name, **over):
+    key = (name, tuple(sorted(over.items())))
+    if key not in _LAYERS:
+        cfg = dict(getattr(syn, name)) if isinstance(name, str) else dict(name)
+        cfg.update(over)
+        _LAYERS.clear()                       # keep one big layer resident at a time
+        _LAYERS[key] = syn.make_layer(**cfg)
+    return _LAYERS[key]
+
+
+def run_layer(torch, qs, L, x_np, fused=True, bf16_out=False, desc=None):
+    desc = desc or qs.LayerDesc.from_host(L, fused=fused)
+    x = to_dev(x_np, torch)
+    T = x_np.shape[0]
+    idx = torch.empty((T, L.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, L.top_k), dtype=torch.float32, device="cuda")
+    y = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16 if bf16_out else torch.float32,
+                             topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    return y, idx.cpu().numpy(), w.cpu().numpy()
+
+
+def oracle_check(L, x_np, y, idx, w, bf16_out, what, rows=None, torch=None):
+    """Compare GPU (y, idx, w) with the oracle on `rows` (default: all tokens)."""
+    rows = np.arange(x_np.shape[0]) if rows is None else rows
+    ol = oracle.OracleLayer(L)
+    xs = x_np[rows]
+    idx_r, w_r, gap = oracle.route(ol, xs)
+    amb = check_routing(idx[rows], w[rows], idx_r, w_r, gap)
+    # evaluate the oracle on the GPU's routing where it is ambiguous, its own elsewhere
+    use_idx = np.where(amb[:, None], idx[rows], idx_r)
+    use_w = np.where(amb[:, None], w[rows].astype(np.float64), w_r)
+    ref = oracle.layer_forward_with_routing(ol, xs, use_idx, use_w)
+    return check_output(y[rows], ref, bf16_out, what), int(amb.sum())
+
+
+# ------------------------------------------------------------------------- routing
+@pytest.mark.parametrize("cfg,T,nsample", [("TINY", 4, None), ("TINY", 200, None), ("DECODE", 1, None),
+                                           ("PREFILL", 4096, 256), ("SKEW", 16384, 256)])
+def test_route_parity(torch, qs, cfg, T, nsample):
+    L = layer(cfg)
+    x_np = syn.make_x(T, L.hidden, seed=11)
+    desc = qs.LayerDesc.from_host(L)
+    idx, w = qs.moe_route(desc, to_dev(x_np, torch))
+    torch.cuda.synchronize()
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    rows = np.arange(T) if nsample is None else sample_tokens(T, nsample, seed=T)
+    idx_r, w_r, gap = oracle.route(oracle.OracleLayer(L), x_np[rows])
+    check_routing(idx[rows], w[rows], idx_r, w_r, gap)
+    assert ((idx >= 0) & (idx < L.n_experts)).all()
+
+
+# -------------------------------------------------------------------- whole layer
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_decode_parity(torch, qs, bf16_out):
+    """T = 1 decode kernels at the decode workload, several tokens one at a time."""
+    L = layer("DECODE")
+    desc = qs.LayerDesc.from_host(L)
+    xs = syn.make_x(6, L.hidden, seed=3)
+    for t in range(xs.shape[0]):
+        y, idx, w = run_layer(torch, qs, L, xs[t:t + 1], bf16_out=bf16_out, desc=desc)
+        oracle_check(L, xs[t:t + 1], y_to_np(y, torch), idx, w, bf16_out, f"decode token {t}")
+
+
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_tiny_grouped_and_decode(torch, qs, bf16_out):
+    """Tiny layer: T = 4 through the grouped path and as 4 separate T = 1 calls."""
+    L = layer("TINY")
+    x_np = syn.make_x(4, L.hidden, seed=0)
+    y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
+    oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, "tiny grouped")
+    for t in range(4):
+        y1, i1, w1 = run_layer(torch, qs, L, x_np[t:t + 1], bf16_out=bf16_out)
+        oracle_check(L, x_np[t:t + 1], y_to_np(y1, torch), i1, w1, bf16_out, f"tiny decode {t}")
+
+
+@pytest.mark.parametrize("cfg,T", [("DECODE", 2), ("DECODE", 40), ("DECODE", 97), ("SKEW", 64)])
+def test_grouped_small_parity(torch, qs, cfg, T):
+    """Grouped path, every token checked: small T spans many tiles and ragged tails."""
+    L = layer(cfg)
+    x_np = syn.make_x(T, L.hidden, seed=T)
+    for bf16_out in (False, True):
+        y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
+        oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} T={T}")
+
+
+@pytest.mark.parametrize("cfg,T", [("PREFILL", 4096), ("SKEW", 16384)])
+def test_full_size_sampled(torch, qs, cfg, T):
+    """Full workload size in the benchmark's launch configuration; sampled tokens vs
+    the oracle, plus a bit-identical repeat."""
+    L = layer(cfg)
+    x_np = syn.make_x(T, L.hidden, seed=0)
+    desc = qs.LayerDesc.from_host(L)
+    y, idx, w = run_layer(torch, qs, L, x_np, desc=desc)
+    y2, idx2, w2 = run_layer(torch, qs, L, x_np, desc=desc)
+    assert torch.equal(y, y2) and (idx == idx2).all() and (w == w2).all()
+    rows = sample_tokens(T, 24, seed=1)
+    oracle_check(L, x_np, y_to_np(y, torch), idx, w, False, f"{cfg} T={T} sampled", rows=rows)
+    # the bins were uneven as the workload intends
+    counts = np.bincount(idx.reshape(-1), minlength=L.n_experts)
+    assert counts.sum() == T * L.top_k
+    if cfg == "SKEW":
+        assert (counts > 10 * counts.mean()).sum() >= 3
+
+
+# ----------------------------------------------------------------- bit invariants
+@pytest.mark.parametrize("cfg,T", [("DECODE", 1), ("DECODE", 40), ("TINY", 4), ("SKEW", 40)])
+def test_fused_equals_separate_bit_exact(torch, qs, cfg, T):
+    """oMLX fusion principle: [gate; up] as one stack == separate gate and up, bit for bit."""
+    L = layer(cfg)
+    x_np = syn.make_x(T, L.hidden, seed=5)
+    ya, ia, wa = run_layer(torch, qs, L, x_np, fused=True)
+    yb, ib, wb = run_layer(torch, qs, L, x_np, fused=False)
+    assert torch.equal(ya, yb)
+    assert (ia == ib).all() and (wa == wb).all()
+
+
+def test_permutation_and_chunking_invariance(torch, qs):
+    """Tokens are independent: permuting them permutes y bit for bit, and splitting the
+    call into chunks gives the same bits (the chunked-prefill property)."""
+    L = layer("DECODE")
+    T = 256
+    x_np = syn.make_x(T, L.hidden, seed=9)
+    desc = qs.LayerDesc.from_host(L)
+    y, idx, w = run_layer(torch, qs, L, x_np, desc=desc)
+    perm = np.random.default_rng(0).permutation(T)
+    yp, ip, wp = run_layer(torch, qs, L, x_np[perm], desc=desc)
+    assert torch.equal(yp, y[torch.from_numpy(perm).cuda()])
+    assert (ip == idx[perm]).all() and (wp == w[perm]).all()
+    parts = [run_layer(torch, qs, L, x_np[a:a + 64], desc=desc)[0] for a in range(0, T, 64)]
+    assert torch.equal(torch.cat(parts), y)
+
+
+def test_zero_tokens_is_a_no_op(torch, qs):
+    L = layer("TINY")
+    desc = qs.LayerDesc.from_host(L)
+    x = torch.zeros((0, L.hidden), dtype=torch.int16, device="cuda")
+    y = torch.full((0, L.hidden), 7.0, device="cuda")
+    qs.moe_layer_forward(desc, x, y=y)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------- edge shapes
+@pytest.mark.parametrize("shape", [
+    dict(hidden=384, inter=384, n_experts=20, top_k=3, bits=4, router_std=0.05),
+    dict(hidden=384, inter=256, n_experts=20, top_k=3, bits=8, router_std=0.05, has_shared=False),
+    dict(hidden=640, inter=128, n_experts=70, top_k=1, bits=4, zipf_s=1.1),
+    dict(hidden=256, inter=128, n_experts=256, top_k=16, bits=8, router_std=0.05),
+    dict(hidden=128, inter=640, n_experts=2, top_k=2, bits=4, router_std=0.05),
+])
+@pytest.mark.parametrize("T", [1, 2, 33])
+def test_edge_shapes(torch, qs, shape, T):
+    L = syn.make_layer(seed=2, **shape)
+    x_np = syn.make_x(T, L.hidden, seed=T + 1)
+    y, idx, w = run_layer(torch, qs, L, x_np)
+    oracle_check(L, x_np, y_to_np(y, torch), idx, w, False, f"{shape} T={T}")
+
+
+# --------------------------------------------------------------------------- Q8_0
+@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288)])
+def test_q8_pack_and_gemv(torch, qs, N, K):
+    rows = syn.make_q8_rows(N, K, seed=N + K)
+    x_np = syn.make_x(1, K, seed=K)[0]
+    tiles = qs.q8_pack_rows16(to_dev(rows.reshape(-1), torch), N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(tiles.cpu().numpy(), oracle.q8_pack_rows16(rows, N, K))
+    ref = oracle.q8_gemv(rows, N, K, x_np)
+    x = to_dev(x_np, torch)
+    y = qs.q8_gemv(tiles, N, K, x)
+    yb = qs.q8_gemv(tiles, N, K, x, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    # fp32 accumulation of K products: bound well inside 1e-4 * RMS at these sizes
+    assert np.max(np.abs(y - ref)) <= 1e-4 * rms
+    check_output(y_to_np(yb, torch), ref, True, f"q8 bf16 {N}x{K}")
