@@ -47,6 +47,9 @@ __device__ __forceinline__ _Float16 f32_to_f16_ftz(float v) {
     return (__builtin_fabsf(v) < 6.103515625e-05f) ? (_Float16)0.0f : (_Float16)v;
 }
 
+// reinterpret a dword as two fp16 (by value: never bit_cast a vector-element lvalue)
+__device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+
 __device__ __forceinline__ uint32_t pack_f16x2(_Float16 lo, _Float16 hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }

@@ -84,8 +84,7 @@ __device__ __forceinline__ float row_dot(const uint8_t *__restrict__ codes,
                 const u32x4 xx = xv[d];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, m[i]),
-                                                 __builtin_bit_cast(f16x2, xx[i]), acc, false);
+                    acc = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc, false);
             }
         } else {
 #pragma unroll
@@ -94,10 +93,8 @@ __device__ __forceinline__ float row_dot(const uint8_t *__restrict__ codes,
                 magic_u8(q[d], m);
                 const u32x4 xx = xv[d >> 1];
                 const int o = 2 * (d & 1);
-                acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, m[0]),
-                                             __builtin_bit_cast(f16x2, xx[o]), acc, false);
-                acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, m[1]),
-                                             __builtin_bit_cast(f16x2, xx[o + 1]), acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc, false);
+                acc = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc, false);
             }
         }
         const int g = (c * CPC) >> 6;

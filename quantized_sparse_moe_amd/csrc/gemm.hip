@@ -65,7 +65,7 @@ __device__ __forceinline__ f16x8 dequant_step(const u32x4 &c0, const u32x4 &c1, 
     const f16x2 k1024 = (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f16x2 q = __builtin_bit_cast(f16x2, m[i]) - k1024;   // exact
+        const f16x2 q = as_h2(m[i]) - k1024;   // exact
         const f16x2 v = __builtin_elementwise_fma(q, sc, bi);       // one rounding
         out[2 * i] = v[0];
         out[2 * i + 1] = v[1];
