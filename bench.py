@@ -133,7 +133,7 @@ def bench_decode(qs, torch, syn, steps, warmup, copies=40):
     descs = _dev_layer_copies(qs, torch, L, copies)
     xs = [torch.from_numpy(syn.make_x(1, L.hidden, seed=100 + l).view(np.int16)).cuda() for l in range(copies)]
     ys = [torch.empty((1, L.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
-    ws = torch.empty(qs.qsmoe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
 
     def step(i):
         l = i % copies
@@ -149,7 +149,7 @@ def bench_prefill(qs, torch, syn, cfg, T, steps, warmup, copies):
     descs = _dev_layer_copies(qs, torch, L, copies)
     x = torch.from_numpy(syn.make_x(T, L.hidden, seed=0).view(np.int16)).cuda()
     y = torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(qs.qsmoe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
 
     def step(i):
         qs.moe_layer_forward(descs[i % copies], x, y=y, workspace=ws)

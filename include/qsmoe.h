@@ -71,8 +71,8 @@ typedef int32_t qsmoe_status;
  *           2*inter when gate and up are the two halves of one fused [gate; up]
  *           stack ([OMLX] "Fusion principle"; then up.codes = gate.codes +
  *           inter*cols*bits/8 and up.scales/biases = gate.* + inter*cols/64).
- * All three pointers must be 16-byte aligned and every row's codes start 16-byte
- * aligned (guaranteed by the shape limits below).
+ * codes must be 16-byte aligned (every row then starts 16-byte aligned, given the
+ * shape limits below); scales and biases 2-byte aligned.
  */
 typedef struct {
     const void *codes;
@@ -111,9 +111,10 @@ const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL
 /*
  * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
  * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
- * 256-byte aligned; its contents are undefined between calls.  Peak use is at most a
- * few hundred bytes per routed assignment plus fixed tables; ~320 MiB at T = 4096,
- * hidden 2048, inter 512, top-8.
+ * 256-byte aligned.  Its first 256 bytes are control words of the T = 1 path: they
+ * must be zero before the first call that uses the workspace (e.g. allocate it
+ * zero-filled) and every call leaves them zero; the rest is scratch whose contents are
+ * undefined between calls.  ~200 MiB at T = 4096, hidden 2048, inter 512, top-8.
  */
 size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T);
 

@@ -101,10 +101,9 @@ struct Carver {
 DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
     Carver c{(char *)ws};
     DecodeBufs b;
+    b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);
     b.logits = c.take<float>(d->n_experts);
     b.h = c.take<float>((size_t)(d->top_k + 1) * d->inter);
-    b.idx = c.take<int32_t>(d->top_k);
-    b.w = c.take<float>(d->top_k);
     *bytes = c.off;
     return b;
 }
@@ -114,6 +113,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     const int64_t H = d->hidden, I = d->inter, K = d->top_k, E = d->n_experts;
     const int64_t nblk = (T + ROUTER_TOKENS - 1) / ROUTER_TOKENS;
     PrefillBufs b;
+    c.take<uint32_t>(WS_CTL_BYTES / 4);              // decode control words stay untouched
     b.x16 = c.take<uint16_t>((size_t)(T * H));
     b.idx = c.take<int32_t>((size_t)(T * K));
     b.w = c.take<float>((size_t)(T * K));
@@ -186,9 +186,7 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
     if (T == 1) {
         size_t n;
         const DecodeBufs b = carve_decode(d, ws, &n);
-        hipError_t e = launch_decode_router_shared(L, (const uint16_t *)x, b, false, st);
-        if (e == hipSuccess) e = launch_decode_topk(L, b, topk_idx, topk_w, st);
-        return dev(e);
+        return dev(launch_decode_route(L, (const uint16_t *)x, b, topk_idx, topk_w, st));
     }
     PrefillBufs b;
     std::memset(&b, 0, sizeof(b));
@@ -216,10 +214,7 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
     if (T == 1) {
         size_t n;
         const DecodeBufs b = carve_decode(d, ws, &n);
-        e = launch_decode_router_shared(L, xx, b, true, st);
-        if (e == hipSuccess) e = launch_decode_gate_up(L, xx, b, topk_idx, topk_w, st);
-        if (e == hipSuccess) e = launch_decode_down(L, b, y, y_dtype, st);
-        return dev(e);
+        return dev(launch_decode_layer(L, xx, b, y, y_dtype, topk_idx, topk_w, st));
     }
     size_t n;
     const PrefillBufs b = carve_prefill(d, T, ws, &n);

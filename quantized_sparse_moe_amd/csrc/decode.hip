@@ -1,25 +1,33 @@
-// decode.hip -- batch-1 (T = 1) MoE layer on the vector ALUs of gfx950.
+// decode.hip -- batch-1 (T = 1) MoE layer: one kernel on the vector ALUs of gfx950.
 //
 // [LILY] "Optimize the single-row weight path": with one activation row there is no
-// weight reuse, so the layer is bound by how fast the active experts' quantized
-// weights stream from HBM.  Each row is read with 16-byte coalesced loads, several
-// lanes cooperate on one row (split-K) and reduce with cross-lane shuffles.
-// [LILY] "Reduce intermediate and state traffic": the two expert input projections
-// are fused with the gated activation (one kernel, [gate; up] pairs), and the output
-// projection is fused with the routing weight and the shared-expert result.
+// weight reuse; the layer is bound by how fast the active experts' quantized weights
+// stream from HBM.  Rows are read with 16-byte coalesced loads, several lanes share a
+// row (split-K) and reduce with cross-lane shuffles.
+// [LILY] "Reduce intermediate and state traffic": the two expert input projections are
+// fused with the gated activation, and the output projection with the routing weight
+// and the shared-expert result; temporaries stay in registers / LDS.
+// [LILY] "Overlap independent GPU work": phases without a data dependency run at the
+// same time, and a phase waits only for the results it consumes.
 //
-// Three launches, in stream order:
-//   1. router logits (fp32) for every expert, and -- independent of routing -- the
-//      shared expert's gate/up + SwiGLU;
-//   2. every workgroup re-derives the top-k from the logits (L2-resident), then the
-//      routed experts' gate/up + SwiGLU;
-//   3. down projections of the k routed experts and the shared expert for each output
-//      row, weighted and summed in a fixed order (ascending expert id, shared last).
+// One launch, four phases.  A workgroup takes a ticket when it starts; the ticket, not
+// blockIdx, picks its phase, so a workgroup only ever waits for workgroups that took
+// earlier tickets and are therefore already running: no deadlock whatever the
+// occupancy.
+//   R  router logits (fp32), one wave per expert                      -> router_done
+//   S  shared expert gate/up + SwiGLU (needs nothing)                 -> h_done
+//   G  routed expert gate/up + SwiGLU: waits for R, takes the top-k   -> h_done
+//   D  down projections of the k routed + shared experts for a block of output rows,
+//      weighted and summed in a fixed order (ascending expert id, shared last): waits
+//      for R, takes the top-k, issues its weight loads, then waits for all of h.
+// Counters live in the first bytes of the caller's workspace: zero before the first
+// call, and the last workgroup to exit puts them back to zero.  Waits are bounded: a
+// wait that exceeds SPIN_LIMIT polls raises an error flag and the kernel still ends.
 //
 // Dequantization happens in registers: codes become fp16 (1024+q) by bit operations
-// and meet fp16 activations in v_dot2_f32_f16 with fp32 accumulation; per group the
-// affine map is applied exactly once:  sum_c (s*q_c + b) x_c = s*A + (b - 1024 s)*X
-// with A = sum_c (1024+q_c) x_c and X = sum_c x_c over the 16-byte chunk.
+// and meet fp16 activations in v_dot2_f32_f16 with fp32 accumulation; per 16-byte chunk
+// the affine map is applied once:  sum_c (s q_c + b) x_c = s A + (b - 1024 s) X  with
+// A = sum_c (1024+q_c) x_c and X = sum_c x_c.
 #include "common.h"
 #include "internal.h"
 
@@ -27,113 +35,14 @@ namespace qs {
 
 namespace {
 
-constexpr int DEC_THREADS = 256;
+constexpr int DT = 256;                 // threads per workgroup
+constexpr int NBUF_G = 8;               // (row, chunk) loads a G/S lane keeps in flight
+constexpr int NBUF_D = 18;              // (expert, chunk) loads a D lane keeps in flight
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
-// Stage an activation vector into LDS: fp16 (|v| < 2^-14 flushed), each group of 8
-// permuted into the code order of BITS, plus the fp32 sum of every 16-byte chunk of
-// codes it will meet (CPC = 128/BITS columns).
-template <int BITS, typename Src>
-__device__ void stage_vec(Src src, int n, uint32_t *xs, float *xsum, float *gsum) {
-    constexpr int CPC = 128 / BITS;
-    constexpr int GPC = CPC / 8;
-    for (int g = threadIdx.x; g < n / 8; g += blockDim.x) {
-        float v[8];
-        src(g, v);
-        _Float16 hv[8];
-        float sum = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            hv[i] = f32_to_f16_ftz(v[i]);
-            sum += (float)hv[i];
-        }
-        u32x4 nat;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nat[i] = pack_f16x2(hv[2 * i], hv[2 * i + 1]);
-        *(u32x4 *)(xs + 4 * g) = perm8<BITS>(nat);
-        gsum[g] = sum;
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < n / CPC; c += blockDim.x) {
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < GPC; ++i) s += gsum[c * GPC + i];
-        xsum[c] = s;
-    }
-    __syncthreads();
-}
-
-// Dot product of one quantized row (ncols columns) with a staged vector; LPR lanes
-// share the row (lane_in_row = lane % LPR), every lane returns the full sum.
-template <int BITS, int LPR>
-__device__ __forceinline__ float row_dot(const uint8_t *__restrict__ codes,
-                                         const uint16_t *__restrict__ sc,
-                                         const uint16_t *__restrict__ bi, int ncols,
-                                         int lane_in_row, const uint32_t *xs, const float *xsum) {
-    constexpr int CPC = 128 / BITS;
-    const int nch = ncols / CPC;
-    float part = 0.0f;
-    for (int c = lane_in_row; c < nch; c += LPR) {
-        const u32x4 q = __builtin_nontemporal_load((const u32x4 *)(codes + 16 * c));
-        const u32x4 *xv = (const u32x4 *)(xs + c * (CPC / 2));
-        float acc = 0.0f;
-        if constexpr (BITS == 4) {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t m[4];
-                magic_u4(q[d], m);
-                const u32x4 xx = xv[d];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc, false);
-            }
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t m[2];
-                magic_u8(q[d], m);
-                const u32x4 xx = xv[d >> 1];
-                const int o = 2 * (d & 1);
-                acc = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc, false);
-                acc = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc, false);
-            }
-        }
-        const int g = (c * CPC) >> 6;
-        const float s = f16_to_f32(sc[g]);
-        const float b = f16_to_f32(bi[g]);
-        part += s * acc + (b - 1024.0f * s) * xsum[c];
-    }
-    return group_sum<LPR>(part);
-}
-
-struct RowPtr {
-    const uint8_t *codes;
-    const uint16_t *sc, *bi;
+struct Ctl {
+    uint32_t ticket, router_done, h_done, exit_cnt, err;
 };
-
-__device__ __forceinline__ RowPtr row_of(const QMat &m, int64_t e, int64_t r, int ncols, int bits) {
-    const int64_t R = e * m.stride + r;
-    RowPtr p;
-    p.codes = m.codes + R * (int64_t)(ncols * bits / 8);
-    p.sc = m.scales + R * (ncols / 64);
-    p.bi = m.biases + R * (ncols / 64);
-    return p;
-}
-
-// gate/up + SwiGLU for `npairs` rows of expert (mg, mu, e), output h[j] for j in
-// [j0, j0 + pairs handled by this block)
-template <int BITS, int LPR>
-__device__ void gate_up_rows(const QMat &mg, const QMat &mu, int64_t e, int H, int I, int j0,
-                             const uint32_t *xs, const float *xsum, float *h) {
-    constexpr int RPW = 64 / LPR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = j0 + wave * RPW + lane / LPR;
-    const int jc = j < I ? j : I - 1;               // keep every lane in the shuffles
-    const RowPtr g = row_of(mg, e, jc, H, BITS);
-    const RowPtr u = row_of(mu, e, jc, H, BITS);
-    const float gv = row_dot<BITS, LPR>(g.codes, g.sc, g.bi, H, lane % LPR, xs, xsum);
-    const float uv = row_dot<BITS, LPR>(u.codes, u.sc, u.bi, H, lane % LPR, xs, xsum);
-    if (j < I && lane % LPR == 0) h[j] = silu(gv) * uv;
-}
 
 struct DecArgs {
     Layer L;
@@ -143,236 +52,432 @@ struct DecArgs {
     float *out_w;
     void *y;
     int y_dtype;
-    int n_router_blocks;
-    int shared;
+    int shared;                 // shared expert present
+    int route_only;             // moe_route: router + publish the top-k only
+    int nR, nS, nG, nD;         // workgroups per phase
+    int lprg, prw, pbg;         // gate/up: lanes per row, pair rounds per wave, pairs per workgroup
+    int lprd, rbd;              // down: lanes per row, output rows per workgroup
 };
 
-template <int BITS, int LPR>
-__global__ __launch_bounds__(DEC_THREADS) void k_router_shared(DecArgs a) {
-    __shared__ uint32_t xs[8192 / 2];
-    __shared__ float xsum[8192 / 16];
-    __shared__ float gsum[8192 / 8];
-    const Layer &L = a.L;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if ((int)blockIdx.x < a.n_router_blocks) {
-        // one wave per expert: fp32 logit over bf16 x and bf16 router weights
-        const int e = blockIdx.x * (DEC_THREADS / 64) + wave;
-        if (e >= L.E) return;
-        const uint16_t *wr = L.router_w + (int64_t)e * L.H;
-        float acc = 0.0f;
-        for (int c = lane; c < L.H / 8; c += 64) {
-            const u32x4 xv = *(const u32x4 *)(a.x + 8 * c);
-            const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc = __builtin_fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), acc);
-                acc = __builtin_fmaf(__uint_as_float(xv[i] & 0xffff0000u),
-                                     __uint_as_float(wv[i] & 0xffff0000u), acc);
-            }
-        }
-        acc = wave_sum(acc);
-        if (lane == 0) a.b.logits[e] = acc + (L.router_bias ? L.router_bias[e] : 0.0f);
-        return;
-    }
-    // shared expert gate/up (no dependence on routing)
-    stage_vec<BITS>([&](int g, float v[8]) {
-        const u32x4 xv = *(const u32x4 *)(a.x + 8 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(xv[i] << 16); v[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u); }
-    }, L.H, xs, xsum, gsum);
-    constexpr int PAIRS = (DEC_THREADS / 64) * (64 / LPR);
-    const int j0 = (blockIdx.x - a.n_router_blocks) * PAIRS;
-    gate_up_rows<BITS, LPR>(L.s_gate, L.s_up, 0, L.H, L.I, j0, xs, xsum, a.b.h + (int64_t)L.K * L.I);
+__device__ __forceinline__ uint32_t ld_acq(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, int LPR>
-__global__ __launch_bounds__(DEC_THREADS) void k_gate_up(DecArgs a) {
-    __shared__ uint32_t xs[8192 / 2];
-    __shared__ float xsum[8192 / 16];
-    __shared__ float gsum[8192 / 8];
-    const Layer &L = a.L;
-    constexpr int PAIRS = (DEC_THREADS / 64) * (64 / LPR);
-    const int bpe = (L.I + PAIRS - 1) / PAIRS;
-    const int slot = blockIdx.x / bpe;
-    const int lane = threadIdx.x & 63;
-    // every wave derives the routing from the L2-resident logits
-    const float *lg = a.b.logits;
-    const TopkOut tk = wave_topk([&](int e) { return lg[e]; }, L.E, L.K);
-    const int e = __shfl(tk.idx, slot, 64);
-    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < L.K) {
-        a.b.idx[lane] = tk.idx;
-        a.b.w[lane] = tk.w;
-        if (a.out_idx) a.out_idx[lane] = tk.idx;
-        if (a.out_w) a.out_w[lane] = tk.w;
+// thread 0 waits until *p >= target (bounded), then the whole workgroup proceeds with
+// acquire semantics
+__device__ void wait_count(Ctl *ctl, const uint32_t *p, uint32_t target) {
+    if (threadIdx.x == 0) {
+        uint32_t n = 0;
+        while (ld_acq(p) < target) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++n > SPIN_LIMIT) {
+                __hip_atomic_fetch_or(&ctl->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
     }
-    stage_vec<BITS>([&](int g, float v[8]) {
-        const u32x4 xv = *(const u32x4 *)(a.x + 8 * g);
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// every thread's prior global stores become visible device-wide, then one increment
+__device__ void signal(uint32_t *p) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
+
+// Top-k of the E <= 256 logits in LDS by rank counting (one thread per expert, exact
+// ties to the lower id), renormalised over the selection; result ascending by id in
+// s_idx / s_w.
+__device__ void block_topk(const float *lg, int E, int K, int *sel_idx, float *sel_val, int *s_idx,
+                           float *s_w) {
+    const int e = threadIdx.x;
+    if (e < K) { sel_idx[e] = 0; sel_val[e] = -__builtin_inff(); }
+    __syncthreads();
+    if (e < E) {
+        const float v = no_nan(lg[e]);
+        int rank = 0;
+        for (int i = 0; i < E; ++i) {
+            const float u = no_nan(lg[i]);
+            rank += (u > v || (u == v && i < e)) ? 1 : 0;
+        }
+        if (rank < K) { sel_idx[rank] = e; sel_val[rank] = v; }
+    }
+    __syncthreads();
+    if (e < K) {
+        const float m = sel_val[0];
+        float z = 0.0f;
+        for (int j = 0; j < K; ++j) z += expf(sel_val[j] - m);
+        const float wv = expf(sel_val[e] - m) / z;
+        const int my = sel_idx[e];
+        int r2 = 0;
+        for (int j = 0; j < K; ++j) r2 += (sel_idx[j] < my) ? 1 : 0;
+        s_idx[r2] = my;
+        s_w[r2] = wv;
+    }
+    __syncthreads();
+}
+
+// Stage activations into LDS as fp16 (|v| < 2^-14 flushed), each group of 8 permuted
+// into the code order of BITS, plus the fp32 sum of every 16-byte code chunk (CPC
+// columns).  One thread per chunk.  `load8(col, v)` fetches 8 consecutive values.
+template <int BITS, typename Load8>
+__device__ void stage_chunks(Load8 load8, int nchunks, uint32_t *xs, float *xsum) {
+    constexpr int CPC = 128 / BITS;
+    for (int c = threadIdx.x; c < nchunks; c += DT) {
+        float sum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { v[2 * i] = __uint_as_float(xv[i] << 16); v[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u); }
-    }, L.H, xs, xsum, gsum);
-    const int j0 = (blockIdx.x - slot * bpe) * PAIRS;
-    gate_up_rows<BITS, LPR>(L.gate, L.up, e, L.H, L.I, j0, xs, xsum, a.b.h + (int64_t)slot * L.I);
+        for (int g = 0; g < CPC / 8; ++g) {
+            float v[8];
+            load8(c * CPC + 8 * g, v);
+            _Float16 hv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                hv[i] = f32_to_f16_ftz(v[i]);
+                sum += (float)hv[i];
+            }
+            u32x4 nat;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) nat[i] = pack_f16x2(hv[2 * i], hv[2 * i + 1]);
+            *(u32x4 *)(xs + (c * CPC + 8 * g) / 2) = perm8<BITS>(nat);
+        }
+        xsum[c] = sum;
+    }
+}
+
+// sum_c (s q_c + b) x_c over one 16-byte chunk of codes
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, float s, float b, float X) {
+    const u32x4 *xv = (const u32x4 *)xs;
+    float acc = 0.0f;
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t m[4];
+            magic_u4(q[d], m);
+            const u32x4 xx = xv[d];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc, false);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t m[2];
+            magic_u8(q[d], m);
+            const u32x4 xx = xv[d >> 1];
+            const int o = 2 * (d & 1);
+            acc = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc, false);
+            acc = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc, false);
+        }
+    }
+    return s * acc + (b - 1024.0f * s) * X;
+}
+
+__device__ __forceinline__ float group_reduce(float v, int width) {
+    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+struct Row {
+    const uint8_t *codes;
+    const uint16_t *sc, *bi;
+};
+
+__device__ __forceinline__ Row row_of(const QMat &m, int64_t e, int64_t r, int ncols, int bits) {
+    const int64_t R = e * m.stride + r;
+    Row p;
+    p.codes = m.codes + R * (int64_t)(ncols * bits / 8);
+    p.sc = m.scales + R * (ncols / 64);
+    p.bi = m.biases + R * (ncols / 64);
+    return p;
+}
+
+// gate/up + SwiGLU for the pairs of one workgroup.  `pre` runs after the first batch of
+// weight loads is issued and before any of them is consumed (x staging, waits).
+template <int BITS, typename Pre>
+__device__ void gate_up_block(const DecArgs &a, const QMat &mg, const QMat &mu, int64_t e, int p0,
+                              float *h, uint32_t *xs, float *xsum, Pre pre) {
+    constexpr int CPC = 128 / BITS;
+    const Layer &L = a.L;
+    const int H = L.H, I = L.I;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lpr = a.lprg, rpw = 64 / lpr, prw = a.prw;
+    const int nch = H / CPC;
+    const int cpl = (nch + lpr - 1) / lpr;
+    const int nitems = 2 * prw * cpl;
+    const int lr = lane % lpr;
+    float part[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[i] = 0.0f;
+    bool first = true;
+    for (int base = 0; base < nitems; base += NBUF_G) {
+        u32x4 q[NBUF_G];
+        uint16_t sv[NBUF_G], bv[NBUF_G];
+#pragma unroll
+        for (int i = 0; i < NBUF_G; ++i) {
+            const int it = base + i;
+            const int r = it / (2 * cpl), row = (it / cpl) & 1, ci = it % cpl;
+            const int j = p0 + (r * 4 + wave) * rpw + lane / lpr;
+            const int c = lr + ci * lpr;
+            q[i] = (u32x4){0u, 0u, 0u, 0u};
+            sv[i] = bv[i] = 0;
+            if (it < nitems && j < I && c < nch) {
+                const Row rp = row_of(row ? mu : mg, e, j, H, BITS);
+                q[i] = __builtin_nontemporal_load((const u32x4 *)(rp.codes + 16 * c));
+                const int g = (c * CPC) >> 6;
+                sv[i] = rp.sc[g];
+                bv[i] = rp.bi[g];
+            }
+        }
+        if (first) { pre(); first = false; }
+#pragma unroll
+        for (int i = 0; i < NBUF_G; ++i) {
+            const int it = base + i;
+            const int r = it / (2 * cpl), row = (it / cpl) & 1, ci = it % cpl;
+            const int c = lr + ci * lpr;
+            if (it < nitems && c < nch) {
+                const float d = chunk_dot<BITS>(q[i], xs + c * (CPC / 2), f16_to_f32(sv[i]), f16_to_f32(bv[i]), xsum[c]);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (k == r * 2 + row) part[k] += d;
+            }
+        }
+    }
+    if (first) pre();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        if (r < prw) {
+            const float g = group_reduce(part[2 * r], lpr);
+            const float u = group_reduce(part[2 * r + 1], lpr);
+            const int j = p0 + (r * 4 + wave) * rpw + lane / lpr;
+            if (lr == 0 && j < I) h[j] = silu(g) * u;
+        }
+    }
 }
 
 template <int BITS>
-__global__ __launch_bounds__(64) void k_topk_only(DecArgs a) {
-    const Layer &L = a.L;
-    const float *lg = a.b.logits;
-    const TopkOut tk = wave_topk([&](int e) { return lg[e]; }, L.E, L.K);
-    const int lane = threadIdx.x & 63;
-    if (lane < L.K) {
-        if (a.out_idx) a.out_idx[lane] = tk.idx;
-        if (a.out_w) a.out_w[lane] = tk.w;
-    }
-}
-
-constexpr int DOWN_THREADS = 128;
-
-template <int BITS, int LPR>
-__global__ __launch_bounds__(DOWN_THREADS) void k_down(DecArgs a, int nvec) {
-    extern __shared__ uint32_t smem[];
-    const Layer &L = a.L;
+__global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
+    __shared__ uint32_t s_ticket;
+    __shared__ float s_logit[256];
+    __shared__ int s_sel_idx[16], s_idx[16];
+    __shared__ float s_sel_val[16], s_w[16];
     constexpr int CPC = 128 / BITS;
-    const int I = L.I;
-    uint32_t *hs = smem;                                    // nvec * I/2 dwords
-    float *hsum = (float *)(hs + (int64_t)nvec * I / 2);    // nvec * I/CPC
-    float *gsum = hsum + nvec * (I / CPC);                  // I/8 scratch
-    for (int v = 0; v < nvec; ++v) {
-        const float *hv = a.b.h + (int64_t)v * I;
-        stage_vec<BITS>([&](int g, float o[8]) {
-            const f32x4 p0 = *(const f32x4 *)(hv + 8 * g);
-            const f32x4 p1 = *(const f32x4 *)(hv + 8 * g + 4);
+    const Layer &L = a.L;
+    Ctl *ctl = (Ctl *)a.b.ctl;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = L.H, I = L.I, E = L.E, K = L.K;
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int t = (int)s_ticket;
+    const int nR = a.nR, nS = a.nS, nG = a.nG, nD = a.nD;
+
+    auto load_x8 = [&](int col, float v[8]) {
+        const u32x4 xv = *(const u32x4 *)(a.x + col);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { o[i] = p0[i]; o[4 + i] = p1[i]; }
-        }, I, hs + (int64_t)v * I / 2, hsum + v * (I / CPC), gsum);
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(xv[i] << 16);
+            v[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u);
+        }
+    };
+    auto topk_from_logits = [&]() {
+        wait_count(ctl, &ctl->router_done, (uint32_t)nR);
+        if (tid < E) s_logit[tid] = a.b.logits[tid];
+        __syncthreads();
+        block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
+    };
+
+    if (t < nR) {
+        // ---------------------------------------------------------------- R: logits
+        const int e = t * 4 + wave;
+        if (e < E) {
+            const uint16_t *wr = L.router_w + (int64_t)e * H;
+            float acc = 0.0f;
+            for (int c = lane; c < H / 8; c += 64) {
+                const u32x4 xv = *(const u32x4 *)(a.x + 8 * c);
+                const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = __builtin_fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), acc);
+                    acc = __builtin_fmaf(__uint_as_float(xv[i] & 0xffff0000u),
+                                         __uint_as_float(wv[i] & 0xffff0000u), acc);
+                }
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) a.b.logits[e] = acc + (L.router_bias ? L.router_bias[e] : 0.0f);
+        }
+        signal(&ctl->router_done);
+    } else if (t < nR + nS) {
+        // ---------------------------------------------- S: shared expert gate/up
+        uint32_t *xs = dsm;
+        float *xsum = (float *)(dsm + H / 2);
+        gate_up_block<BITS>(a, L.s_gate, L.s_up, 0, (t - nR) * a.pbg, a.b.h + (int64_t)K * I, xs, xsum, [&]() {
+            stage_chunks<BITS>(load_x8, H / CPC, xs, xsum);
+            __syncthreads();
+        });
+        signal(&ctl->h_done);
+    } else if (t < nR + nS + nG) {
+        // ---------------------------------------------- G: routed expert gate/up
+        uint32_t *xs = dsm;
+        float *xsum = (float *)(dsm + H / 2);
+        const int g = t - nR - nS;
+        const int bpe = (I + a.pbg - 1) / a.pbg;
+        const int slot = g / bpe;
+        stage_chunks<BITS>(load_x8, H / CPC, xs, xsum);      // independent of routing
+        topk_from_logits();                                  // ends with a barrier
+        const int e = min(max(s_idx[slot], 0), E - 1);
+        gate_up_block<BITS>(a, L.gate, L.up, e, (g % bpe) * a.pbg, a.b.h + (int64_t)slot * I, xs, xsum, []() {});
+        signal(&ctl->h_done);
+    } else if (t < nR + nS + nG + nD) {
+        // ------------------------------------------ D: down + weighted combine
+        const int d = t - nR - nS - nG;
+        topk_from_logits();
+        if (d == 0 && tid < K) {
+            if (a.out_idx) a.out_idx[tid] = s_idx[tid];
+            if (a.out_w) a.out_w[tid] = s_w[tid];
+        }
+        if (!a.route_only) {
+            const int nvec = K + (a.shared ? 1 : 0);
+            const int lpr = a.lprd, rpw = 64 / lpr;
+            const int nch = I / CPC;
+            const int cpl = (nch + lpr - 1) / lpr;
+            const int nitems = nvec * cpl;
+            const int lr = lane % lpr;
+            const int n = d * a.rbd + wave * rpw + lane / lpr;
+            const int nc = n < H ? n : H - 1;
+            uint32_t *hs = dsm;
+            float *hsum = (float *)(dsm + nvec * I / 2);
+            float yv = 0.0f;
+            for (int base = 0; base < nitems; base += NBUF_D) {
+                u32x4 q[NBUF_D];
+                uint16_t sv[NBUF_D], bv[NBUF_D];
+#pragma unroll
+                for (int i = 0; i < NBUF_D; ++i) {
+                    const int it = base + i;
+                    const int v = it / cpl, c = lr + (it % cpl) * lpr;
+                    q[i] = (u32x4){0u, 0u, 0u, 0u};
+                    sv[i] = bv[i] = 0;
+                    if (it < nitems && c < nch) {
+                        const int e = (v < K) ? min(max(s_idx[v], 0), E - 1) : 0;
+                        const Row rp = row_of(v < K ? L.down : L.s_down, e, nc, I, BITS);
+                        q[i] = __builtin_nontemporal_load((const u32x4 *)(rp.codes + 16 * c));
+                        const int g = (c * CPC) >> 6;
+                        sv[i] = rp.sc[g];
+                        bv[i] = rp.bi[g];
+                    }
+                }
+                if (base == 0) {
+                    // all of h: S and G workgroups
+                    wait_count(ctl, &ctl->h_done, (uint32_t)(nS + nG));
+                    const float *hsrc = a.b.h;
+                    stage_chunks<BITS>([&](int col, float v8[8]) {
+                        const f32x4 p0 = *(const f32x4 *)(hsrc + col);
+                        const f32x4 p1 = *(const f32x4 *)(hsrc + col + 4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) { v8[i] = p0[i]; v8[4 + i] = p1[i]; }
+                    }, nvec * nch, hs, hsum);
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int i = 0; i < NBUF_D; ++i) {
+                    const int it = base + i;
+                    const int v = it / cpl, c = lr + (it % cpl) * lpr;
+                    if (it < nitems && c < nch) {
+                        const float p = chunk_dot<BITS>(q[i], hs + (v * I + c * CPC) / 2, f16_to_f32(sv[i]),
+                                                        f16_to_f32(bv[i]), hsum[v * nch + c]);
+                        yv += (v < K ? s_w[v] : 1.0f) * p;      // ascending expert id, shared last
+                    }
+                }
+            }
+            yv = group_reduce(yv, lpr);
+            if (n < H && lr == 0) {
+                if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = yv;
+                else ((uint16_t *)a.y)[n] = f32_to_bf16(yv);
+            }
+        }
     }
-    constexpr int RPW = 64 / LPR;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n = (blockIdx.x * (DOWN_THREADS / 64) + wave) * RPW + lane / LPR;
-    const int nc = n < L.H ? n : L.H - 1;
-    float y = 0.0f;
-    for (int j = 0; j < L.K; ++j) {                         // ascending expert id
-        const int e = a.b.idx[j];
-        const RowPtr r = row_of(L.down, e, nc, I, BITS);
-        const float p = row_dot<BITS, LPR>(r.codes, r.sc, r.bi, I, lane % LPR,
-                                           hs + (int64_t)j * I / 2, hsum + j * (I / CPC));
-        y += a.b.w[j] * p;
-    }
-    if (a.shared) {
-        const RowPtr r = row_of(L.s_down, 0, nc, I, BITS);
-        y += row_dot<BITS, LPR>(r.codes, r.sc, r.bi, I, lane % LPR,
-                                hs + (int64_t)L.K * I / 2, hsum + L.K * (I / CPC));
-    }
-    if (n < L.H && lane % LPR == 0) {
-        if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = y;
-        else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
+    // the last workgroup out resets the counters for the next call
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&ctl->exit_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == gridDim.x - 1) {
+            __hip_atomic_store(&ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl->h_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl->exit_cnt, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 
 // lanes sharing one row: the largest power of two <= min(64, 16-byte chunks per row)
-template <int BITS>
-int lpr_for(int ncols) {
-    const int chunks = ncols * BITS / 128;
+int lanes_per_row(int ncols, int bits) {
+    const int chunks = ncols * bits / 128;
     int l = 64;
     while (l > chunks) l >>= 1;
     return l;
 }
 
-#define QS_DISPATCH_LPR(lpr, ...)                                                           \
-    switch (lpr) {                                                                          \
-        case 64: { constexpr int LPR = 64; __VA_ARGS__; } break;                            \
-        case 32: { constexpr int LPR = 32; __VA_ARGS__; } break;                            \
-        case 16: { constexpr int LPR = 16; __VA_ARGS__; } break;                            \
-        case 8: { constexpr int LPR = 8; __VA_ARGS__; } break;                              \
-        case 4: { constexpr int LPR = 4; __VA_ARGS__; } break;                              \
-        default: { constexpr int LPR = 2; __VA_ARGS__; } break;                             \
-    }
-
-template <int BITS>
-hipError_t router_shared(const DecArgs &a, hipStream_t s) {
-    const int lpr = lpr_for<BITS>(a.L.H);
-    const int nR = (a.L.E + 3) / 4;
-    QS_DISPATCH_LPR(lpr, {
-        constexpr int PAIRS = (DEC_THREADS / 64) * (64 / LPR);
-        const int nS = a.shared ? (a.L.I + PAIRS - 1) / PAIRS : 0;
-        DecArgs b = a;
-        b.n_router_blocks = nR;
-        hipLaunchKernelGGL((k_router_shared<BITS, LPR>), dim3(nR + nS), dim3(DEC_THREADS), 0, s, b);
-    })
-    return hipGetLastError();
-}
-
-template <int BITS>
-hipError_t gate_up(const DecArgs &a, hipStream_t s) {
-    const int lpr = lpr_for<BITS>(a.L.H);
-    QS_DISPATCH_LPR(lpr, {
-        constexpr int PAIRS = (DEC_THREADS / 64) * (64 / LPR);
-        const int bpe = (a.L.I + PAIRS - 1) / PAIRS;
-        hipLaunchKernelGGL((k_gate_up<BITS, LPR>), dim3(bpe * a.L.K), dim3(DEC_THREADS), 0, s, a);
-    })
-    return hipGetLastError();
-}
-
-template <int BITS>
-hipError_t down(const DecArgs &a, hipStream_t s) {
-    const int lpr = lpr_for<BITS>(a.L.I);
-    const int nvec = a.L.K + (a.shared ? 1 : 0);
-    constexpr int CPC = 128 / BITS;
-    const size_t lds = (size_t)nvec * a.L.I * 2 + (size_t)nvec * (a.L.I / CPC) * 4 + (a.L.I / 8) * 4;
-    QS_DISPATCH_LPR(lpr, {
-        constexpr int ROWS = (DOWN_THREADS / 64) * (64 / LPR);
-        const int nb = (a.L.H + ROWS - 1) / ROWS;
-        hipLaunchKernelGGL((k_down<BITS, LPR>), dim3(nb), dim3(DOWN_THREADS), lds, s, a, nvec);
-    })
+hipError_t launch(DecArgs a, bool route_only, hipStream_t s) {
+    const Layer &L = a.L;
+    const int cpc = 128 / L.bits;
+    a.route_only = route_only ? 1 : 0;
+    a.lprg = lanes_per_row(L.H, L.bits);
+    const int cplg = (L.H / cpc + a.lprg - 1) / a.lprg;
+    a.prw = NBUF_G / (2 * cplg);
+    if (a.prw < 1) a.prw = 1;
+    if (a.prw > 4) a.prw = 4;
+    a.pbg = 4 * (64 / a.lprg) * a.prw;
+    a.lprd = lanes_per_row(L.I, L.bits);
+    a.rbd = 4 * (64 / a.lprd);
+    const int bpe = (L.I + a.pbg - 1) / a.pbg;
+    a.nR = (L.E + 3) / 4;
+    a.nS = (!route_only && a.shared) ? bpe : 0;
+    a.nG = route_only ? 0 : L.K * bpe;
+    a.nD = route_only ? 1 : (L.H + a.rbd - 1) / a.rbd;
+    const int nvec = L.K + (a.shared ? 1 : 0);
+    const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 4;
+    const size_t lds_d = (size_t)nvec * L.I * 2 + (size_t)nvec * (L.I / cpc) * 4;
+    const size_t lds = route_only ? 16 : (lds_g > lds_d ? lds_g : lds_d);
+    const int grid = a.nR + a.nS + a.nG + a.nD;
+    if (L.bits == 4)
+        hipLaunchKernelGGL((k_decode<4>), dim3(grid), dim3(DT), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_decode<8>), dim3(grid), dim3(DT), lds, s, a);
     return hipGetLastError();
 }
 
 DecArgs make_args(const Layer &L, const uint16_t *x, const DecodeBufs &b) {
-    DecArgs a;
+    DecArgs a{};
     a.L = L;
     a.x = x;
     a.b = b;
-    a.out_idx = nullptr;
-    a.out_w = nullptr;
-    a.y = nullptr;
     a.y_dtype = QSMOE_F32;
-    a.n_router_blocks = 0;
     a.shared = L.has_shared;
     return a;
 }
 
 }  // namespace
 
-hipError_t launch_decode_router_shared(const Layer &L, const uint16_t *x, const DecodeBufs &b,
-                                       bool shared, hipStream_t s) {
+hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
+                               int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s) {
     DecArgs a = make_args(L, x, b);
-    a.shared = shared && L.has_shared;
-    return L.bits == 4 ? router_shared<4>(a, s) : router_shared<8>(a, s);
-}
-
-hipError_t launch_decode_gate_up(const Layer &L, const uint16_t *x, const DecodeBufs &b,
-                                 int32_t *out_idx, float *out_w, hipStream_t s) {
-    DecArgs a = make_args(L, x, b);
-    a.out_idx = out_idx;
-    a.out_w = out_w;
-    return L.bits == 4 ? gate_up<4>(a, s) : gate_up<8>(a, s);
-}
-
-hipError_t launch_decode_down(const Layer &L, const DecodeBufs &b, void *y, int y_dtype,
-                              hipStream_t s) {
-    DecArgs a = make_args(L, nullptr, b);
     a.y = y;
     a.y_dtype = y_dtype;
-    return L.bits == 4 ? down<4>(a, s) : down<8>(a, s);
-}
-
-hipError_t launch_decode_topk(const Layer &L, const DecodeBufs &b, int32_t *out_idx,
-                              float *out_w, hipStream_t s) {
-    DecArgs a = make_args(L, nullptr, b);
     a.out_idx = out_idx;
     a.out_w = out_w;
-    hipLaunchKernelGGL((k_topk_only<4>), dim3(1), dim3(64), 0, s, a);
-    return hipGetLastError();
+    return launch(a, false, s);
+}
+
+hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBufs &b, int32_t *out_idx,
+                               float *out_w, hipStream_t s) {
+    DecArgs a = make_args(L, x, b);
+    a.shared = 0;
+    a.out_idx = out_idx;
+    a.out_w = out_w;
+    return launch(a, true, s);
 }
 
 }  // namespace qs

@@ -26,21 +26,20 @@ struct Layer {
 };
 
 // -------------------------------------------------------------------- decode T = 1
+// Control words at the start of every workspace (zero before the first call, left zero
+// by every call): tickets and completion counters of the one-launch decode kernel.
+constexpr size_t WS_CTL_BYTES = 256;
+
 struct DecodeBufs {
+    uint32_t *ctl;                 // WS_CTL_BYTES of control words
     float *logits;                 // [E]
     float *h;                      // [(K+1)][I]  (slot K = shared expert)
-    int32_t *idx;                  // [K]
-    float *w;                      // [K]
 };
 
-hipError_t launch_decode_router_shared(const Layer &L, const uint16_t *x, const DecodeBufs &b,
-                                       bool shared, hipStream_t s);
-hipError_t launch_decode_gate_up(const Layer &L, const uint16_t *x, const DecodeBufs &b,
-                                 int32_t *out_idx, float *out_w, hipStream_t s);
-hipError_t launch_decode_down(const Layer &L, const DecodeBufs &b, void *y, int y_dtype,
-                              hipStream_t s);
-hipError_t launch_decode_topk(const Layer &L, const DecodeBufs &b, int32_t *out_idx,
-                              float *out_w, hipStream_t s);
+hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
+                               int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);
+hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBufs &b,
+                               int32_t *out_idx, float *out_w, hipStream_t s);
 
 // ------------------------------------------------------------------- prefill T >= 2
 constexpr int ROUTER_TOKENS = 32;  // tokens per router workgroup (= one binning block)
