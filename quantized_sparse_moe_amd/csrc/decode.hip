@@ -59,16 +59,22 @@ struct DecArgs {
     int lprd, rbd;              // down: lanes per row, output rows per workgroup
 };
 
-__device__ __forceinline__ uint32_t ld_acq(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup data (logits, h) is written and read with device-scope (sc1)
+// stores and loads, which go to the coherence point shared by all XCDs; counters are
+// device-scope atomics.  That avoids whole-L2 write-back / invalidate operations that a
+// release / acquire fence at device scope would issue in every workgroup.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// thread 0 waits until *p >= target (bounded), then the whole workgroup proceeds with
-// acquire semantics
+// thread 0 waits until *p >= target (bounded), then the whole workgroup proceeds
 __device__ void wait_count(Ctl *ctl, const uint32_t *p, uint32_t target) {
     if (threadIdx.x == 0) {
         uint32_t n = 0;
-        while (ld_acq(p) < target) {
+        while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(2);
             if (++n > SPIN_LIMIT) {
                 __hip_atomic_fetch_or(&ctl->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -77,14 +83,13 @@ __device__ void wait_count(Ctl *ctl, const uint32_t *p, uint32_t target) {
         }
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// every thread's prior global stores become visible device-wide, then one increment
+// every wave's device-scope stores are acknowledged, then one increment
 __device__ void signal(uint32_t *p) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
@@ -253,7 +258,7 @@ __device__ void gate_up_block(const DecArgs &a, const QMat &mg, const QMat &mu, 
             const float g = group_reduce(part[2 * r], lpr);
             const float u = group_reduce(part[2 * r + 1], lpr);
             const int j = p0 + (r * 4 + wave) * rpw + lane / lpr;
-            if (lr == 0 && j < I) h[j] = silu(g) * u;
+            if (lr == 0 && j < I) st_dev(&h[j], silu(g) * u);
         }
     }
 }
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
     };
     auto topk_from_logits = [&]() {
         wait_count(ctl, &ctl->router_done, (uint32_t)nR);
-        if (tid < E) s_logit[tid] = a.b.logits[tid];
+        if (tid < E) s_logit[tid] = ld_dev(&a.b.logits[tid]);
         __syncthreads();
         block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
     };
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
                 }
             }
             acc = wave_sum(acc);
-            if (lane == 0) a.b.logits[e] = acc + (L.router_bias ? L.router_bias[e] : 0.0f);
+            if (lane == 0) st_dev(&a.b.logits[e], acc + (L.router_bias ? L.router_bias[e] : 0.0f));
         }
         signal(&ctl->router_done);
     } else if (t < nR + nS) {
@@ -374,10 +379,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
                     wait_count(ctl, &ctl->h_done, (uint32_t)(nS + nG));
                     const float *hsrc = a.b.h;
                     stage_chunks<BITS>([&](int col, float v8[8]) {
-                        const f32x4 p0 = *(const f32x4 *)(hsrc + col);
-                        const f32x4 p1 = *(const f32x4 *)(hsrc + col + 4);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) { v8[i] = p0[i]; v8[4 + i] = p1[i]; }
+                        for (int i = 0; i < 8; ++i) v8[i] = ld_dev(hsrc + col + i);
                     }, nvec * nch, hs, hsum);
                     __syncthreads();
                 }
@@ -402,12 +405,12 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
     // the last workgroup out resets the counters for the next call
     __syncthreads();
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&ctl->exit_cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(&ctl->exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (old == gridDim.x - 1) {
             __hip_atomic_store(&ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ctl->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ctl->h_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctl->exit_cnt, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl->exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

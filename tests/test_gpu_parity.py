@@ -166,6 +166,25 @@ def test_permutation_and_chunking_invariance(torch, qs):
     assert torch.equal(torch.cat(parts), y)
 
 
+def test_decode_repeat_bit_identical(torch, qs):
+    """The one-launch decode kernel hands logits and h between workgroups through the
+    workspace: many back-to-back calls, alternating inputs and two layers sharing one
+    workspace, must reproduce the first results bit for bit (stale data would not)."""
+    L = layer("DECODE")
+    descs = [qs.LayerDesc.from_host(L), qs.LayerDesc.from_host(L, fused=False)]
+    xs = [to_dev(syn.make_x(1, L.hidden, seed=s), torch) for s in (21, 22, 23)]
+    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
+    ref = [qs.moe_layer_forward(descs[0], x, workspace=ws) for x in xs]
+    torch.cuda.synchronize()
+    outs = []
+    for i in range(60):
+        outs.append((i % 3, qs.moe_layer_forward(descs[i % 2], xs[i % 3], workspace=ws)))
+    torch.cuda.synchronize()
+    for j, y in outs:
+        assert torch.equal(y, ref[j])
+    assert (ws[:16].cpu().numpy() == 0).all()          # counters back at zero
+
+
 def test_zero_tokens_is_a_no_op(torch, qs):
     L = layer("TINY")
     desc = qs.LayerDesc.from_host(L)
