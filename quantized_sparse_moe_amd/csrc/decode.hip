@@ -41,7 +41,7 @@ constexpr int NBUF_D = 18;              // (expert, chunk) loads a D lane keeps 
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
 struct Ctl {
-    uint32_t ticket, router_done, h_done, exit_cnt, err;
+    uint32_t ticket, router_done, topk_done, h_done, exit_cnt, err;
 };
 
 struct DecArgs {
@@ -56,7 +56,7 @@ struct DecArgs {
     int route_only;             // moe_route: router + publish the top-k only
     int nR, nS, nG, nD;         // workgroups per phase
     int lprg, prw, pbg;         // gate/up: lanes per row, pair rounds per wave, pairs per workgroup
-    int lprd, rbd;              // down: lanes per row, output rows per workgroup
+    int lprd, prd, rbd;         // down: lanes per row, row rounds per wave, output rows per workgroup
 };
 
 // Cross-workgroup data (logits, h) is written and read with device-scope (sc1)
@@ -67,6 +67,15 @@ __device__ __forceinline__ void st_dev(float *p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_u(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -85,11 +94,14 @@ __device__ void wait_count(Ctl *ctl, const uint32_t *p, uint32_t target) {
     __syncthreads();
 }
 
-// every wave's device-scope stores are acknowledged, then one increment
-__device__ void signal(uint32_t *p) {
+// every wave's device-scope stores are acknowledged, then one increment; returns (to
+// every thread) the counter value before the increment
+__device__ uint32_t signal(uint32_t *p, uint32_t *s_old) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) *s_old = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *s_old;
 }
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
@@ -266,7 +278,7 @@ __device__ void gate_up_block(const DecArgs &a, const QMat &mg, const QMat &mu, 
 template <int BITS>
 __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
-    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_ticket, s_old;
     __shared__ float s_logit[256];
     __shared__ int s_sel_idx[16], s_idx[16];
     __shared__ float s_sel_val[16], s_w[16];
@@ -288,11 +300,14 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             v[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u);
         }
     };
-    auto topk_from_logits = [&]() {
-        wait_count(ctl, &ctl->router_done, (uint32_t)nR);
-        if (tid < E) s_logit[tid] = ld_dev(&a.b.logits[tid]);
+    // the routing, published once by the last router workgroup
+    auto get_topk = [&]() {
+        wait_count(ctl, &ctl->topk_done, 1u);
+        if (tid < K) {
+            s_idx[tid] = min(max((int)ld_dev_u((const uint32_t *)a.b.sel + tid), 0), E - 1);
+            s_w[tid] = ld_dev(a.b.sel + 16 + tid);
+        }
         __syncthreads();
-        block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
     };
 
     if (t < nR) {
@@ -314,7 +329,19 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             acc = wave_sum(acc);
             if (lane == 0) st_dev(&a.b.logits[e], acc + (L.router_bias ? L.router_bias[e] : 0.0f));
         }
-        signal(&ctl->router_done);
+        if (signal(&ctl->router_done, &s_old) == (uint32_t)(nR - 1)) {
+            // last router workgroup: every logit is in; select and publish the top-k
+            if (tid < E) s_logit[tid] = ld_dev(&a.b.logits[tid]);
+            __syncthreads();
+            block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
+            if (tid < K) {
+                st_dev_u((uint32_t *)a.b.sel + tid, (uint32_t)s_idx[tid]);
+                st_dev(a.b.sel + 16 + tid, s_w[tid]);
+                if (a.out_idx) a.out_idx[tid] = s_idx[tid];
+                if (a.out_w) a.out_w[tid] = s_w[tid];
+            }
+            signal(&ctl->topk_done, &s_old);
+        }
     } else if (t < nR + nS) {
         // ---------------------------------------------- S: shared expert gate/up
         uint32_t *xs = dsm;
@@ -323,7 +350,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             stage_chunks<BITS>(load_x8, H / CPC, xs, xsum);
             __syncthreads();
         });
-        signal(&ctl->h_done);
+        signal(&ctl->h_done, &s_old);
     } else if (t < nR + nS + nG) {
         // ---------------------------------------------- G: routed expert gate/up
         uint32_t *xs = dsm;
@@ -332,73 +359,106 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
         const int bpe = (I + a.pbg - 1) / a.pbg;
         const int slot = g / bpe;
         stage_chunks<BITS>(load_x8, H / CPC, xs, xsum);      // independent of routing
-        topk_from_logits();                                  // ends with a barrier
-        const int e = min(max(s_idx[slot], 0), E - 1);
-        gate_up_block<BITS>(a, L.gate, L.up, e, (g % bpe) * a.pbg, a.b.h + (int64_t)slot * I, xs, xsum, []() {});
-        signal(&ctl->h_done);
+        get_topk();                                          // ends with a barrier
+        gate_up_block<BITS>(a, L.gate, L.up, s_idx[slot], (g % bpe) * a.pbg, a.b.h + (int64_t)slot * I, xs,
+                            xsum, []() {});
+        signal(&ctl->h_done, &s_old);
     } else if (t < nR + nS + nG + nD) {
         // ------------------------------------------ D: down + weighted combine
         const int d = t - nR - nS - nG;
-        topk_from_logits();
-        if (d == 0 && tid < K) {
-            if (a.out_idx) a.out_idx[tid] = s_idx[tid];
-            if (a.out_w) a.out_w[tid] = s_w[tid];
-        }
-        if (!a.route_only) {
-            const int nvec = K + (a.shared ? 1 : 0);
-            const int lpr = a.lprd, rpw = 64 / lpr;
-            const int nch = I / CPC;
-            const int cpl = (nch + lpr - 1) / lpr;
-            const int nitems = nvec * cpl;
-            const int lr = lane % lpr;
-            const int n = d * a.rbd + wave * rpw + lane / lpr;
-            const int nc = n < H ? n : H - 1;
-            uint32_t *hs = dsm;
-            float *hsum = (float *)(dsm + nvec * I / 2);
-            float yv = 0.0f;
-            for (int base = 0; base < nitems; base += NBUF_D) {
-                u32x4 q[NBUF_D];
-                uint16_t sv[NBUF_D], bv[NBUF_D];
+        get_topk();
+        const int nvec = K + (a.shared ? 1 : 0);
+        const int lpr = a.lprd, rpw = 64 / lpr, prd = a.prd;
+        const int nch = I / CPC;
+        const int cpl = (nch + lpr - 1) / lpr;
+        const int per_row = nvec * cpl;                       // items per (lane, output row)
+        const int nitems = prd * per_row;
+        const int lr = lane % lpr;
+        uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * I fp16, code order
+        float *hsum = (float *)(dsm + nvec * I / 2);          // nvec * nch chunk sums
+        float yv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int base = 0; base < nitems; base += NBUF_D) {
+            u32x4 q[NBUF_D];
+            uint16_t sv[NBUF_D], bv[NBUF_D];
 #pragma unroll
-                for (int i = 0; i < NBUF_D; ++i) {
-                    const int it = base + i;
-                    const int v = it / cpl, c = lr + (it % cpl) * lpr;
-                    q[i] = (u32x4){0u, 0u, 0u, 0u};
-                    sv[i] = bv[i] = 0;
-                    if (it < nitems && c < nch) {
-                        const int e = (v < K) ? min(max(s_idx[v], 0), E - 1) : 0;
-                        const Row rp = row_of(v < K ? L.down : L.s_down, e, nc, I, BITS);
-                        q[i] = __builtin_nontemporal_load((const u32x4 *)(rp.codes + 16 * c));
-                        const int g = (c * CPC) >> 6;
-                        sv[i] = rp.sc[g];
-                        bv[i] = rp.bi[g];
-                    }
-                }
-                if (base == 0) {
-                    // all of h: S and G workgroups
-                    wait_count(ctl, &ctl->h_done, (uint32_t)(nS + nG));
-                    const float *hsrc = a.b.h;
-                    stage_chunks<BITS>([&](int col, float v8[8]) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) v8[i] = ld_dev(hsrc + col + i);
-                    }, nvec * nch, hs, hsum);
-                    __syncthreads();
-                }
-#pragma unroll
-                for (int i = 0; i < NBUF_D; ++i) {
-                    const int it = base + i;
-                    const int v = it / cpl, c = lr + (it % cpl) * lpr;
-                    if (it < nitems && c < nch) {
-                        const float p = chunk_dot<BITS>(q[i], hs + (v * I + c * CPC) / 2, f16_to_f32(sv[i]),
-                                                        f16_to_f32(bv[i]), hsum[v * nch + c]);
-                        yv += (v < K ? s_w[v] : 1.0f) * p;      // ascending expert id, shared last
-                    }
+            for (int i = 0; i < NBUF_D; ++i) {
+                const int it = base + i;
+                const int r = it / per_row, v = (it % per_row) / cpl, c = lr + (it % cpl) * lpr;
+                const int n = d * a.rbd + (wave * prd + r) * rpw + lane / lpr;
+                q[i] = (u32x4){0u, 0u, 0u, 0u};
+                sv[i] = bv[i] = 0;
+                if (it < nitems && c < nch && n < H) {
+                    const Row rp = row_of(v < K ? L.down : L.s_down, v < K ? s_idx[v] : 0, n, I, BITS);
+                    q[i] = __builtin_nontemporal_load((const u32x4 *)(rp.codes + 16 * c));
+                    const int g = (c * CPC) >> 6;
+                    sv[i] = rp.sc[g];
+                    bv[i] = rp.bi[g];
                 }
             }
-            yv = group_reduce(yv, lpr);
-            if (n < H && lr == 0) {
-                if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = yv;
-                else ((uint16_t *)a.y)[n] = f32_to_bf16(yv);
+            if (base == 0) {
+                // all of h (S and G workgroups), read coalesced: fp16 in code order + sums
+                wait_count(ctl, &ctl->h_done, (uint32_t)(nS + nG));
+                const uint64_t *h2 = (const uint64_t *)a.b.h;
+                for (int p0 = 0; p0 < nvec * I / 2; p0 += 8 * DT) {
+                    uint64_t hv[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int p = p0 + k * DT + tid;
+                        hv[k] = p < nvec * I / 2 ? ld_dev_u64(h2 + p) : 0ull;
+                    }
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int p = p0 + k * DT + tid;
+                        if (p < nvec * I / 2) {
+                            const int i0 = 2 * p;                     // element index (even)
+                            const int gb = i0 & ~7;
+                            hs16[gb + perm_pos<BITS>(i0 & 7)] =
+                                __builtin_bit_cast(uint16_t, f32_to_f16_ftz(__uint_as_float((uint32_t)hv[k])));
+                            hs16[gb + perm_pos<BITS>((i0 + 1) & 7)] =
+                                __builtin_bit_cast(uint16_t, f32_to_f16_ftz(__uint_as_float((uint32_t)(hv[k] >> 32))));
+                        }
+                    }
+                }
+                __syncthreads();
+                for (int cc = tid; cc < nvec * nch; cc += DT) {
+                    const u32x4 *src = (const u32x4 *)(hs16 + cc * CPC);
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int g8 = 0; g8 < CPC / 8; ++g8) {
+                        const u32x4 w4 = src[g8];
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const f16x2 hh = as_h2(w4[k]);
+                            sum += (float)hh[0] + (float)hh[1];
+                        }
+                    }
+                    hsum[cc] = sum;
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int i = 0; i < NBUF_D; ++i) {
+                const int it = base + i;
+                const int r = it / per_row, v = (it % per_row) / cpl, c = lr + (it % cpl) * lpr;
+                if (it < nitems && c < nch) {
+                    const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + v * I + c * CPC),
+                                                    f16_to_f32(sv[i]), f16_to_f32(bv[i]), hsum[v * nch + c]);
+                    const float contrib = (v < K ? s_w[v] : 1.0f) * p;   // ascending expert id, shared last
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (k == r) yv[k] += contrib;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (r < prd) {
+                const float y = group_reduce(yv[r], lpr);
+                const int n = d * a.rbd + (wave * prd + r) * rpw + lane / lpr;
+                if (n < H && lr == 0) {
+                    if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = y;
+                    else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
+                }
             }
         }
     }
@@ -409,6 +469,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
         if (old == gridDim.x - 1) {
             __hip_atomic_store(&ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ctl->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ctl->topk_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ctl->h_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ctl->exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -434,13 +495,17 @@ hipError_t launch(DecArgs a, bool route_only, hipStream_t s) {
     if (a.prw > 4) a.prw = 4;
     a.pbg = 4 * (64 / a.lprg) * a.prw;
     a.lprd = lanes_per_row(L.I, L.bits);
-    a.rbd = 4 * (64 / a.lprd);
+    const int nvec = L.K + (a.shared ? 1 : 0);
+    const int per_row = nvec * ((L.I / cpc + a.lprd - 1) / a.lprd);
+    a.prd = NBUF_D / per_row;
+    if (a.prd < 1) a.prd = 1;
+    if (a.prd > 4) a.prd = 4;
+    a.rbd = 4 * (64 / a.lprd) * a.prd;
     const int bpe = (L.I + a.pbg - 1) / a.pbg;
     a.nR = (L.E + 3) / 4;
     a.nS = (!route_only && a.shared) ? bpe : 0;
     a.nG = route_only ? 0 : L.K * bpe;
-    a.nD = route_only ? 1 : (L.H + a.rbd - 1) / a.rbd;
-    const int nvec = L.K + (a.shared ? 1 : 0);
+    a.nD = route_only ? 0 : (L.H + a.rbd - 1) / a.rbd;
     const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 4;
     const size_t lds_d = (size_t)nvec * L.I * 2 + (size_t)nvec * (L.I / cpc) * 4;
     const size_t lds = route_only ? 16 : (lds_g > lds_d ? lds_g : lds_d);

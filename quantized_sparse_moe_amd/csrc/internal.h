@@ -33,6 +33,7 @@ constexpr size_t WS_CTL_BYTES = 256;
 struct DecodeBufs {
     uint32_t *ctl;                 // WS_CTL_BYTES of control words
     float *logits;                 // [E]
+    float *sel;                    // [32]: top-k expert ids (as int32) [16], weights [16]
     float *h;                      // [(K+1)][I]  (slot K = shared expert)
 };
 
