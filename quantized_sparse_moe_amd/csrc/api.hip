@@ -103,7 +103,6 @@ DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
     DecodeBufs b;
     b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);
     b.logits = c.take<float>(d->n_experts);
-    b.sel = c.take<float>(32);
     b.h = c.take<float>((size_t)(d->top_k + 1) * d->inter);
     *bytes = c.off;
     return b;

@@ -40,9 +40,16 @@ constexpr int NBUF_G = 8;               // (row, chunk) loads a G/S lane keeps i
 constexpr int NBUF_D = 18;              // (expert, chunk) loads a D lane keeps in flight
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
-struct Ctl {
-    uint32_t ticket, router_done, topk_done, h_done, exit_cnt, err;
-};
+// Control words (uint32 offsets into the workspace's control region).  Counters that
+// many workgroups increment sit on lines of their own; the "ready" flags that many
+// workgroups poll are replicated NCOPY times, far apart, each waiting workgroup polling
+// one copy, so no single line carries all the polling traffic.
+constexpr int CTL_TICKET = 0, CTL_EXIT = 1, CTL_ERR = 2;
+constexpr int CTL_ROUTER = 64, CTL_H = 128;
+constexpr int NCOPY = 16;
+constexpr int COPY_BASE = 256, COPY_STRIDE = 1088;          // 4352 bytes between copies
+constexpr int CP_TOPK = 0, CP_H = 1, CP_IDX = 16, CP_W = 32;  // inside one copy
+static_assert(COPY_BASE + NCOPY * COPY_STRIDE <= (int)(WS_CTL_BYTES / 4), "control region");
 
 struct DecArgs {
     Layer L;
@@ -79,14 +86,16 @@ __device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// thread 0 waits until *p >= target (bounded), then the whole workgroup proceeds
-__device__ void wait_count(Ctl *ctl, const uint32_t *p, uint32_t target) {
+// thread 0 waits (bounded, with back-off) until the flag at p is non-zero, then the
+// whole workgroup proceeds
+__device__ void wait_flag(uint32_t *ctl, const uint32_t *p) {
     if (threadIdx.x == 0) {
         uint32_t n = 0;
-        while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(2);
+        while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            if (n < 8) __builtin_amdgcn_s_sleep(1);
+            else __builtin_amdgcn_s_sleep(8);
             if (++n > SPIN_LIMIT) {
-                __hip_atomic_fetch_or(&ctl->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(ctl + CTL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
         }
@@ -284,10 +293,11 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
     __shared__ float s_sel_val[16], s_w[16];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
-    Ctl *ctl = (Ctl *)a.b.ctl;
+    uint32_t *ctl = a.b.ctl;
+    uint32_t *copy = ctl + COPY_BASE + (blockIdx.x % NCOPY) * COPY_STRIDE;   // the copy this WG polls
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K;
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&ctl->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(ctl + CTL_TICKET, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     const int t = (int)s_ticket;
     const int nR = a.nR, nS = a.nS, nG = a.nG, nD = a.nD;
@@ -300,14 +310,20 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             v[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u);
         }
     };
-    // the routing, published once by the last router workgroup
+    // the routing, published once (in every copy) by the last router workgroup
     auto get_topk = [&]() {
-        wait_count(ctl, &ctl->topk_done, 1u);
+        wait_flag(ctl, copy + CP_TOPK);
         if (tid < K) {
-            s_idx[tid] = min(max((int)ld_dev_u((const uint32_t *)a.b.sel + tid), 0), E - 1);
-            s_w[tid] = ld_dev(a.b.sel + 16 + tid);
+            s_idx[tid] = min(max((int)ld_dev_u(copy + CP_IDX + tid), 0), E - 1);
+            s_w[tid] = ld_dev((const float *)(copy + CP_W + tid));
         }
         __syncthreads();
+    };
+    // raise a ready flag in every copy (after this WG's own stores are acknowledged)
+    auto raise = [&](int which) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid < NCOPY) st_dev_u(ctl + COPY_BASE + tid * COPY_STRIDE + which, 1u);
     };
 
     if (t < nR) {
@@ -329,18 +345,22 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             acc = wave_sum(acc);
             if (lane == 0) st_dev(&a.b.logits[e], acc + (L.router_bias ? L.router_bias[e] : 0.0f));
         }
-        if (signal(&ctl->router_done, &s_old) == (uint32_t)(nR - 1)) {
+        if (signal(ctl + CTL_ROUTER, &s_old) == (uint32_t)(nR - 1)) {
             // last router workgroup: every logit is in; select and publish the top-k
             if (tid < E) s_logit[tid] = ld_dev(&a.b.logits[tid]);
             __syncthreads();
             block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
+            for (int i = tid; i < NCOPY * K; i += DT) {
+                uint32_t *cp = ctl + COPY_BASE + (i / K) * COPY_STRIDE;
+                const int j = i % K;
+                st_dev_u(cp + CP_IDX + j, (uint32_t)s_idx[j]);
+                st_dev((float *)(cp + CP_W + j), s_w[j]);
+            }
             if (tid < K) {
-                st_dev_u((uint32_t *)a.b.sel + tid, (uint32_t)s_idx[tid]);
-                st_dev(a.b.sel + 16 + tid, s_w[tid]);
                 if (a.out_idx) a.out_idx[tid] = s_idx[tid];
                 if (a.out_w) a.out_w[tid] = s_w[tid];
             }
-            signal(&ctl->topk_done, &s_old);
+            raise(CP_TOPK);
         }
     } else if (t < nR + nS) {
         // ---------------------------------------------- S: shared expert gate/up
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             stage_chunks<BITS>(load_x8, H / CPC, xs, xsum);
             __syncthreads();
         });
-        signal(&ctl->h_done, &s_old);
+        if (signal(ctl + CTL_H, &s_old) == (uint32_t)(nS + nG - 1)) raise(CP_H);
     } else if (t < nR + nS + nG) {
         // ---------------------------------------------- G: routed expert gate/up
         uint32_t *xs = dsm;
@@ -362,7 +382,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
         get_topk();                                          // ends with a barrier
         gate_up_block<BITS>(a, L.gate, L.up, s_idx[slot], (g % bpe) * a.pbg, a.b.h + (int64_t)slot * I, xs,
                             xsum, []() {});
-        signal(&ctl->h_done, &s_old);
+        if (signal(ctl + CTL_H, &s_old) == (uint32_t)(nS + nG - 1)) raise(CP_H);
     } else if (t < nR + nS + nG + nD) {
         // ------------------------------------------ D: down + weighted combine
         const int d = t - nR - nS - nG;
@@ -397,7 +417,7 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             }
             if (base == 0) {
                 // all of h (S and G workgroups), read coalesced: fp16 in code order + sums
-                wait_count(ctl, &ctl->h_done, (uint32_t)(nS + nG));
+                wait_flag(ctl, copy + CP_H);
                 const uint64_t *h2 = (const uint64_t *)a.b.h;
                 for (int p0 = 0; p0 < nvec * I / 2; p0 += 8 * DT) {
                     uint64_t hv[8];
@@ -462,16 +482,21 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             }
         }
     }
-    // the last workgroup out resets the counters for the next call
+    // the last workgroup out resets counters and flags for the next call
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&ctl->exit_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == gridDim.x - 1) {
-            __hip_atomic_store(&ctl->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctl->router_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctl->topk_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctl->h_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&ctl->exit_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+        s_old = __hip_atomic_fetch_add(ctl + CTL_EXIT, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_old == gridDim.x - 1) {
+        if (tid < NCOPY) {
+            st_dev_u(ctl + COPY_BASE + tid * COPY_STRIDE + CP_TOPK, 0u);
+            st_dev_u(ctl + COPY_BASE + tid * COPY_STRIDE + CP_H, 0u);
+        }
+        if (tid == 0) {
+            st_dev_u(ctl + CTL_TICKET, 0u);
+            st_dev_u(ctl + CTL_ROUTER, 0u);
+            st_dev_u(ctl + CTL_H, 0u);
+            st_dev_u(ctl + CTL_EXIT, 0u);
         }
     }
 }

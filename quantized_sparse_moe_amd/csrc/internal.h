@@ -28,12 +28,11 @@ struct Layer {
 // -------------------------------------------------------------------- decode T = 1
 // Control words at the start of every workspace (zero before the first call, left zero
 // by every call): tickets and completion counters of the one-launch decode kernel.
-constexpr size_t WS_CTL_BYTES = 256;
+constexpr size_t WS_CTL_BYTES = 72 * 1024;
 
 struct DecodeBufs {
     uint32_t *ctl;                 // WS_CTL_BYTES of control words
     float *logits;                 // [E]
-    float *sel;                    // [32]: top-k expert ids (as int32) [16], weights [16]
     float *h;                      // [(K+1)][I]  (slot K = shared expert)
 };
 

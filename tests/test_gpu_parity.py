@@ -182,7 +182,7 @@ def test_decode_repeat_bit_identical(torch, qs):
     torch.cuda.synchronize()
     for j, y in outs:
         assert torch.equal(y, ref[j])
-    assert (ws[:16].cpu().numpy() == 0).all()          # counters back at zero
+    assert (ws[:72 * 1024].cpu().numpy() == 0).all()   # control words back at zero
 
 
 def test_zero_tokens_is_a_no_op(torch, qs):
