@@ -111,7 +111,7 @@ const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL
 /*
  * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
  * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
- * 256-byte aligned.  Its first 72 KiB are control words of the T = 1 path: they must
+ * 256-byte aligned.  Its first 96 KiB are control words of the T = 1 path: they must
  * be zero before the first call that uses the workspace (e.g. allocate it zero-filled)
  * and every call leaves them zero; the rest is scratch whose contents are undefined
  * between calls.  ~200 MiB at T = 4096, hidden 2048, inter 512, top-8.

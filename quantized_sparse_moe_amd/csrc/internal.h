@@ -28,7 +28,7 @@ struct Layer {
 // -------------------------------------------------------------------- decode T = 1
 // Control words at the start of every workspace (zero before the first call, left zero
 // by every call): tickets and completion counters of the one-launch decode kernel.
-constexpr size_t WS_CTL_BYTES = 72 * 1024;
+constexpr size_t WS_CTL_BYTES = 96 * 1024;
 
 struct DecodeBufs {
     uint32_t *ctl;                 // WS_CTL_BYTES of control words

@@ -182,7 +182,11 @@ def test_decode_repeat_bit_identical(torch, qs):
     torch.cuda.synchronize()
     for j, y in outs:
         assert torch.equal(y, ref[j])
-    assert (ws[:72 * 1024].cpu().numpy() == 0).all()   # control words back at zero
+    # counters (ticket, exit, error, router, h) and every copy's ready flags back at zero
+    w32 = ws[:72 * 1024].cpu().numpy().view(np.uint32)
+    assert (w32[[0, 1, 2, 64, 128]] == 0).all()
+    for c in range(16):
+        assert (w32[256 + c * 1088: 256 + c * 1088 + 2] == 0).all()
 
 
 def test_zero_tokens_is_a_no_op(torch, qs):
