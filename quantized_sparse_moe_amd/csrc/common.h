@@ -112,73 +112,83 @@ __device__ __forceinline__ float group_sum(float v) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------------ top-k
-// One wave selects the top_k largest of n_experts (<= 256) fp32 logits read from
-// `logits` (any address space), exact ties to the lower expert id, and renormalises
-// w_j = exp(l_j - l_max) / sum_selected exp(l_i - l_max).  On return lanes j < top_k
-// hold (idx, w) of the j-th selected expert in ASCENDING expert-id order.
+// One wave selects the top_k largest of n_experts (<= 256) fp32 logits read through
+// `load(e)` (NaN ranks as -inf), exact ties going to the lower expert id, and
+// renormalises w_j = exp(l_j - l_max) / sum_selected exp(l_i - l_max).  On return lanes
+// j < top_k hold (idx, w) of the j-th selected expert in ASCENDING expert-id order.
+//
+// The k-th largest value is found by a bitwise search over order-preserving integer
+// keys, each step counting candidates with ballots and popcounts (no cross-lane
+// shuffles, whose latency dominates a butterfly arg-max); ties at the threshold are
+// taken in expert-id order; the selection is compacted through a small LDS slot.
 struct TopkOut {
     int idx;
     float w;
 };
 
-__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+__device__ __forceinline__ uint32_t order_key(float v) {
+    uint32_t u = __float_as_uint(v);
+    if (v != v) u = 0xff800000u;                       // NaN ranks as -inf
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u); // monotone in v; live keys > 0
 }
 
 template <typename LoadFn>
 __device__ __forceinline__ TopkOut wave_topk(LoadFn load, int n_experts, int top_k) {
-    const int lane = threadIdx.x & 63;
-    float v[4];
-    bool live[4];
+    __shared__ int tk_idx[16][16];
+    __shared__ float tk_val[16][16];
+    const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) & 15;
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t key[4];
+    float val[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int e = lane + 64 * i;
-        live[i] = e < n_experts;
-        v[i] = live[i] ? load(e) : 0.0f;
+        const bool live = e < n_experts;
+        val[i] = live ? load(e) : 0.0f;
+        key[i] = live ? order_key(val[i]) : 0u;
     }
-    int my_idx = 0x7fffffff;
-    float my_val = 0.0f;
-    for (int r = 0; r < top_k; ++r) {
-        float bv = 0.0f;
-        int bi = 0x7fffffff;
+    // T = key of the top_k-th largest value
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = T | (1u << b);
+        int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            if (live[i] && (bi == 0x7fffffff || better(v[i], e, bv, bi))) { bv = v[i]; bi = e; }
+        for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
+        if (cnt >= top_k) T = c;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(key[i] > T));
+    const int need = top_k - gt;                       // ties at T to take, lowest ids first
+    int ties_before = 0, base = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint64_t tie = __ballot(key[i] == T);
+        const bool sel = key[i] > T || (key[i] == T && ties_before + __popcll(tie & lt) < need);
+        ties_before += __popcll(tie);
+        const uint64_t sm = __ballot(sel);
+        if (sel) {
+            const int pos = base + __popcll(sm & lt);  // rank by expert id = lane + 64 i
+            tk_idx[wv][pos] = lane + 64 * i;
+            tk_val[wv][pos] = val[i];
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, QS_WAVE);
-            const int oi = __shfl_xor(bi, off, QS_WAVE);
-            if (oi != 0x7fffffff && (bi == 0x7fffffff || better(ov, oi, bv, bi))) { bv = ov; bi = oi; }
-        }
-        // bi is now wave-uniform: retire it from its owner lane
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (bi == lane + 64 * i) live[i] = false;
-        if (lane == r) { my_idx = bi; my_val = bv; }
+        base += __popcll(sm);
     }
-    // renormalised weights over the selection: the first pick holds the maximum
-    const float vmax = __shfl(my_val, 0, QS_WAVE);
-    const float ex = (lane < top_k) ? expf(my_val - vmax) : 0.0f;
-    const float z = wave_sum(ex);
-    const float w = ex / z;
-    // rank by expert id (ids are distinct)
-    int rank = 0;
-    for (int j = 0; j < top_k; ++j) {
-        const int oj = __shfl(my_idx, j, QS_WAVE);
-        rank += (oj < my_idx) ? 1 : 0;
-    }
-    // move (idx, w) of rank j to lane j
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     TopkOut out;
     out.idx = 0;
     out.w = 0.0f;
-    for (int j = 0; j < top_k; ++j) {
-        const int rj = __shfl(rank, j, QS_WAVE);
-        const int ij = __shfl(my_idx, j, QS_WAVE);
-        const float wj = __shfl(w, j, QS_WAVE);
-        if (lane == rj) { out.idx = ij; out.w = wj; }
+    if (lane < top_k) {
+        float m = tk_val[wv][0];
+        for (int j = 1; j < top_k; ++j) m = fmaxf(m, tk_val[wv][j]);
+        float z = 0.0f;
+        for (int j = 0; j < top_k; ++j) z += __expf(tk_val[wv][j] - m);
+        out.idx = tk_idx[wv][lane];
+        out.w = __expf(tk_val[wv][lane] - m) / z;
     }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     return out;
 }
 

@@ -141,45 +141,6 @@ __device__ void reset_controls(uint32_t *ctl) {
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
 
-// Top-k of 256 logits in LDS (unused entries -inf) by rank counting, one thread per
-// expert, exact ties to the lower id; weights renormalised over the selection; result
-// ascending by expert id in s_idx / s_w.
-__device__ void block_topk(const float *lg, int E, int K, int *sel_idx, float *sel_val, int *s_idx,
-                           float *s_w) {
-    const int e = threadIdx.x;
-    if (e < K) { sel_idx[e] = 0; sel_val[e] = -__builtin_inff(); }
-    __syncthreads();
-    if (e < E) {
-        const float v = no_nan(lg[e]);
-        int rank = 0;
-        for (int i4 = 0; i4 < 64; i4 += 4) {
-            f32x4 u[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) u[k] = *(const f32x4 *)(lg + 4 * (i4 + k));
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float w = no_nan(u[k >> 2][k & 3]);
-                const int i = 4 * i4 + k;
-                rank += (w > v || (w == v && i < e)) ? 1 : 0;
-            }
-        }
-        if (rank < K) { sel_idx[rank] = e; sel_val[rank] = v; }
-    }
-    __syncthreads();
-    if (e < K) {
-        const float m = sel_val[0];
-        float z = 0.0f;
-        for (int j = 0; j < K; ++j) z += expf(sel_val[j] - m);
-        const float wv = expf(sel_val[e] - m) / z;
-        const int my = sel_idx[e];
-        int r2 = 0;
-        for (int j = 0; j < K; ++j) r2 += (sel_idx[j] < my) ? 1 : 0;
-        s_idx[r2] = my;
-        s_w[r2] = wv;
-    }
-    __syncthreads();
-}
-
 // x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk fp32 sums
 template <int BITS>
 __device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float *xsum) {
@@ -236,51 +197,54 @@ __device__ __forceinline__ float group_reduce(float v, int width) {
     return v;
 }
 
-// [gate; up] row pair j of matrix stacks (mg, mu), expert e: SwiGLU value in every
-// lane of the row group (lpr lanes share the pair)
+// [gate; up] row pairs j0 and j1 of matrix stacks (mg, mu), expert e: SwiGLU values
+// (in every lane of the row group; lpr lanes share a pair).  All loads of a step --
+// 2 pairs x 2 rows x 2 chunks -- are issued before any is used.
 template <int BITS>
-__device__ float pair_swiglu(const QMat &mg, const QMat &mu, int64_t e, int j, int H, int lpr,
-                             const uint32_t *xs, const float *xsum) {
+__device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int64_t e, int j0, int j1, int H, int lpr,
+                             const uint32_t *xs, const float *xsum, float hv[2]) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
     const int64_t rb = (int64_t)H * BITS / 8;
-    const int64_t Rg = e * mg.stride + j, Ru = e * mu.stride + j;
-    const uint8_t *cg = mg.codes + Rg * rb, *cu = mu.codes + Ru * rb;
-    const uint16_t *sg = mg.scales + Rg * ng, *bg = mg.biases + Rg * ng;
-    const uint16_t *su = mu.scales + Ru * ng, *bu = mu.biases + Ru * ng;
-    float g = 0.0f, u = 0.0f;
-    for (int c0 = lr; c0 < nch; c0 += 2 * lpr) {
-        // two chunks of each row in flight
-        u32x4 qg[2], qu[2];
-        uint32_t s[4], b[4];
+    const uint8_t *cp[4];
+    const uint16_t *sp[4], *bp[4];
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int c = c0 + k * lpr;
-            qg[k] = qu[k] = (u32x4){0u, 0u, 0u, 0u};
-            s[2 * k] = s[2 * k + 1] = b[2 * k] = b[2 * k + 1] = 0;
+    for (int r = 0; r < 4; ++r) {               // r = 2 * pair + (0 gate | 1 up)
+        const QMat &m = (r & 1) ? mu : mg;
+        const int64_t R = e * m.stride + ((r >> 1) ? j1 : j0);
+        cp[r] = m.codes + R * rb;
+        sp[r] = m.scales + R * ng;
+        bp[r] = m.biases + R * ng;
+    }
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c0 = lr; c0 < nch; c0 += 2 * lpr) {
+        u32x4 q[8];
+        uint32_t s[8], b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = i >> 1, c = c0 + (i & 1) * lpr;
+            q[i] = (u32x4){0u, 0u, 0u, 0u};
+            s[i] = b[i] = 0;
             if (c < nch) {
                 const int gi = (c * CPC) >> 6;
-                qg[k] = __builtin_nontemporal_load((const u32x4 *)(cg + 16 * c));
-                qu[k] = __builtin_nontemporal_load((const u32x4 *)(cu + 16 * c));
-                s[2 * k] = sg[gi];
-                b[2 * k] = bg[gi];
-                s[2 * k + 1] = su[gi];
-                b[2 * k + 1] = bu[gi];
+                q[i] = __builtin_nontemporal_load((const u32x4 *)(cp[r] + 16 * c));
+                s[i] = sp[r][gi];
+                b[i] = bp[r][gi];
             }
         }
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int c = c0 + k * lpr;
-            if (c < nch) {
-                g += chunk_dot<BITS>(qg[k], xs + c * (CPC / 2), s[2 * k], b[2 * k], xsum[c]);
-                u += chunk_dot<BITS>(qu[k], xs + c * (CPC / 2), s[2 * k + 1], b[2 * k + 1], xsum[c]);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + (i & 1) * lpr;
+            if (c < nch) acc[i >> 1] += chunk_dot<BITS>(q[i], xs + c * (CPC / 2), s[i], b[i], xsum[c]);
         }
     }
-    g = group_reduce(g, lpr);
-    u = group_reduce(u, lpr);
-    return silu(g) * u;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const float g = group_reduce(acc[2 * p], lpr);
+        const float u = group_reduce(acc[2 * p + 1], lpr);
+        hv[p] = silu(g) * u;
+    }
 }
 
 template <int BITS>
@@ -288,8 +252,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
     __shared__ uint32_t s_flag;
     __shared__ __attribute__((aligned(16))) float s_logit[256];
-    __shared__ int s_sel_idx[16], s_idx[16];
-    __shared__ float s_sel_val[16], s_w[16];
+    __shared__ int s_idx[16];
+    __shared__ float s_w[16];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
     uint32_t *ctl = a.b.ctl;
@@ -343,7 +307,12 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             if (tid < 256)
                 s_logit[tid] = (tid < E) ? __uint_as_float(ld_dev((const uint32_t *)a.b.logits + tid)) : -__builtin_inff();
             __syncthreads();
-            block_topk(s_logit, E, K, s_sel_idx, s_sel_val, s_idx, s_w);
+            if (wave == 0) {
+                // one wave: K rounds of butterfly arg-max over 4 logits per lane
+                const TopkOut tk = wave_topk([&](int e2) { return no_nan(s_logit[e2]); }, E, K);
+                if (lane < K) { s_idx[lane] = min(max(tk.idx, 0), E - 1); s_w[lane] = tk.w; }
+            }
+            __syncthreads();
             for (int i = tid; i < NCOPY * K; i += DT) {
                 uint32_t *cp = ctl + COPY_BASE + (i / K) * COPY_STRIDE;
                 st_dev(cp + CP_IDX + i % K, (uint32_t)s_idx[i % K]);
@@ -362,14 +331,15 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
         // ------------------------------------------- S / G: gate/up + SwiGLU -> h
         uint32_t *xs = dsm;
         float *xsum = (float *)(dsm + H / 2);
-        const int rpw = 64 / a.lprg;                         // pairs per wave
-        const int pb = NW * rpw;                             // pairs per workgroup
+        const int rpw = 64 / a.lprg;                         // row groups per wave
+        const int pb = 2 * NW * rpw;                         // pairs per workgroup (2 per row group)
         const bool sh = b < nR + nS;
         const int m = b - nR;                                // member index among S and G
         const int g = sh ? m : m - nS;
         const int bpe = (I + pb - 1) / pb;                   // workgroups per expert
         const int slot = sh ? K : g / bpe;                   // h row (K = shared)
-        const int j = (sh ? g : g % bpe) * pb + wave * rpw + lane / a.lprg;
+        const int j0 = (sh ? g : g % bpe) * pb + wave * rpw + lane / a.lprg;
+        const int j1 = j0 + NW * rpw;
         stage_x<BITS>(a.x, H, xs, xsum);
         int64_t e = 0;
         if (sh) {
@@ -378,9 +348,14 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             get_topk();                                      // ends with a barrier
             e = s_idx[slot];
         }
-        const float hv = pair_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, j < I ? j : I - 1,
-                                           H, a.lprg, xs, xsum);
-        if (j < I && lane % a.lprg == 0) st_dev((uint32_t *)a.b.h + (int64_t)slot * I + j, __float_as_uint(hv));
+        float hv[2];
+        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, j0 < I ? j0 : I - 1,
+                           j1 < I ? j1 : I - 1, H, a.lprg, xs, xsum, hv);
+        if (lane % a.lprg == 0) {
+            float *hrow = a.b.h + (int64_t)slot * I;
+            if (j0 < I) st_dev((uint32_t *)hrow + j0, __float_as_uint(hv[0]));
+            if (j1 < I) st_dev((uint32_t *)hrow + j1, __float_as_uint(hv[1]));
+        }
         if (signal_all(ctl, K_H, m, nS + nG, &s_flag)) raise_flag(ctl, CP_H);
         return;
     }
@@ -493,7 +468,7 @@ hipError_t launch(DecArgs a, bool route_only, hipStream_t s) {
     const int cpc = 128 / L.bits;
     a.lprg = lanes_per_row(L.H, L.bits);
     a.lprd = lanes_per_row(L.I, L.bits);
-    const int pb = NW * (64 / a.lprg);
+    const int pb = 2 * NW * (64 / a.lprg);
     const int bpe = (L.I + pb - 1) / pb;
     a.nR = (L.E + NW - 1) / NW;
     a.nS = (!route_only && a.shared) ? bpe : 0;
