@@ -111,10 +111,13 @@ const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL
 /*
  * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
  * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
- * 256-byte aligned.  Its first 96 KiB are control words of the T = 1 path: they must
- * be zero before the first call that uses the workspace (e.g. allocate it zero-filled)
- * and every call leaves them zero; the rest is scratch whose contents are undefined
- * between calls.  ~200 MiB at T = 4096, hidden 2048, inter 512, top-8.
+ * 256-byte aligned.  Its first 1 MiB holds the state of the T = 1 path (a call
+ * counter, completion counters, and tagged words the workgroups of one call hand to
+ * each other): it must be zero before the first call that uses the workspace (e.g.
+ * allocate it zero-filled) and then belongs to the library; a caller that writes it
+ * must zero it again before the next call.  The rest is scratch whose contents are
+ * undefined between calls.  Calls that share one workspace must not overlap in time
+ * (issue them on one stream).  ~200 MiB at T = 4096, hidden 2048, inter 512, top-8.
  */
 size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T);
 

@@ -190,7 +190,7 @@ def _workspace(desc: LayerDesc, T: int, workspace, device):
     import torch
     n = qsmoe_workspace_size(desc, T)
     if workspace is None:
-        # zero-filled: the first 256 bytes are control words that must start at zero
+        # zero-filled: the start of the workspace holds decode state that must begin at zero
         workspace = torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 

@@ -102,8 +102,6 @@ DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
     Carver c{(char *)ws};
     DecodeBufs b;
     b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);
-    b.logits = c.take<float>(d->n_experts);
-    b.h = c.take<float>((size_t)(d->top_k + 1) * d->inter);
     *bytes = c.off;
     return b;
 }
@@ -113,7 +111,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     const int64_t H = d->hidden, I = d->inter, K = d->top_k, E = d->n_experts;
     const int64_t nblk = (T + ROUTER_TOKENS - 1) / ROUTER_TOKENS;
     PrefillBufs b;
-    c.take<uint32_t>(WS_CTL_BYTES / 4);              // decode control words stay untouched
+    c.take<uint32_t>(WS_CTL_BYTES / 4);              // decode state stays untouched
     b.x16 = c.take<uint16_t>((size_t)(T * H));
     b.idx = c.take<int32_t>((size_t)(T * K));
     b.w = c.take<float>((size_t)(T * K));

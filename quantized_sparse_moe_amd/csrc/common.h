@@ -24,6 +24,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// global-memory views of addresses held as integers (e.g. read from another lane), so
+// that loads through them are global loads rather than flat ones
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) const uint16_t g_u16;
+
+// a wave-uniform lane's 64-bit value, as a scalar
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 #define QS_MAGIC 0x64006400u       // two fp16 1024.0
 #define QS_WAVE 64
 
@@ -95,19 +107,30 @@ __device__ __forceinline__ int perm_pos(int c) {
 }
 
 // ------------------------------------------------------------------ wave helpers
-__device__ __forceinline__ float wave_sum(float v) {
-    // butterfly in a fixed order: every lane ends with the same, deterministic sum
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, QS_WAVE);
+// Sums over aligned groups of `width` lanes (a power of two, 1..64), the same value in
+// every lane of a group.  Inside a 16-lane row the butterfly runs on DPP lane
+// permutations (a few cycles each, where a generic shuffle goes through the LDS unit);
+// rows are combined through scalar reads of one lane per row, in row order.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float group_sum(float v, int width) {
+    if (width >= 2) v += dpp<0xB1>(v);        // quad_perm [1,0,3,2]: lane ^ 1
+    if (width >= 4) v += dpp<0x4E>(v);        // quad_perm [2,3,0,1]: lane ^ 2
+    if (width >= 8) v += dpp<0x141>(v);       // row_half_mirror: the other quad of the 8
+    if (width >= 16) v += dpp<0x140>(v);      // row_mirror: the other 8 of the row
+    if (width >= 32) {
+        const float r0 = lane_value(v, 0), r1 = lane_value(v, 16), r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+        if (width == 32) v = ((threadIdx.x & 63) < 32) ? r0 + r1 : r2 + r3;
+        else v = (r0 + r1) + (r2 + r3);
+    }
     return v;
 }
-
-template <int WIDTH>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = WIDTH / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, QS_WAVE);
-    return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
@@ -132,29 +155,43 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u); // monotone in v; live keys > 0
 }
 
-template <typename LoadFn>
-__device__ __forceinline__ TopkOut wave_topk(LoadFn load, int n_experts, int top_k) {
+// v[i] = value of expert lane + 64 i (ignored for ids >= n_experts)
+__device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_experts, int top_k) {
     __shared__ int tk_idx[16][16];
-    __shared__ float tk_val[16][16];
+    __shared__ __attribute__((aligned(16))) float tk_val[16][16];
     const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) & 15;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[4];
     float val[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        const bool live = e < n_experts;
-        val[i] = live ? load(e) : 0.0f;
+        const bool live = lane + 64 * i < n_experts;
+        val[i] = live ? v[i] : 0.0f;
         key[i] = live ? order_key(val[i]) : 0u;
     }
-    // T = key of the top_k-th largest value
+    // T = the largest key prefix with at least top_k keys >= T, two bits per step (the
+    // three candidate counts of a step are independent); once exactly top_k keys are
+    // >= T the selection is decided and the remaining bits need not be searched
     uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
-        const uint32_t c = T | (1u << b);
-        int cnt = 0;
+    for (int b = 30; b >= 0; b -= 2) {
+        const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
+        int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(key[i] >= c));
-        if (cnt >= top_k) T = c;
+        for (int i = 0; i < 4; ++i) {
+            n1 += __popcll(__ballot(key[i] >= c1));
+            n2 += __popcll(__ballot(key[i] >= c2));
+            n3 += __popcll(__ballot(key[i] >= c3));
+        }
+        if (n3 >= top_k) {
+            T = c3;
+            if (n3 == top_k) break;
+        } else if (n2 >= top_k) {
+            T = c2;
+            if (n2 == top_k) break;
+        } else if (n1 >= top_k) {
+            T = c1;
+            if (n1 == top_k) break;
+        }
     }
     int gt = 0;
 #pragma unroll
@@ -180,16 +217,30 @@ __device__ __forceinline__ TopkOut wave_topk(LoadFn load, int n_experts, int top
     out.idx = 0;
     out.w = 0.0f;
     if (lane < top_k) {
-        float m = tk_val[wv][0];
-        for (int j = 1; j < top_k; ++j) m = fmaxf(m, tk_val[wv][j]);
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) *(float4 *)(v + j) = *(const float4 *)(&tk_val[wv][j]);
+        float m = v[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) m = (j < top_k) ? fmaxf(m, v[j]) : m;
         float z = 0.0f;
-        for (int j = 0; j < top_k; ++j) z += __expf(tk_val[wv][j] - m);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) z += (j < top_k) ? __expf(v[j] - m) : 0.0f;
         out.idx = tk_idx[wv][lane];
         out.w = __expf(tk_val[wv][lane] - m) / z;
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     return out;
+}
+
+template <typename LoadFn>
+__device__ __forceinline__ TopkOut wave_topk(LoadFn load, int n_experts, int top_k) {
+    const int lane = threadIdx.x & 63;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (lane + 64 * i < n_experts) ? load(lane + 64 * i) : 0.0f;
+    return wave_topk_regs(v, n_experts, top_k);
 }
 
 // XCD-aware remap: consecutive hardware workgroup ids go round-robin to the 8 XCDs;

@@ -48,34 +48,51 @@ namespace {
 constexpr int DT = 512;                     // threads per workgroup (8 waves)
 constexpr int NW = DT / 64;
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
-constexpr int NGRP = 16;                    // group counters per completion count
-constexpr int NCOPY = 16;                   // copies of the ready flags / routing
+constexpr int NGRP = 16;                    // group counters of the completion count
 
-// control region layout, in uint32 units (each counter on a line of its own)
-enum { K_ROUTER = 0, K_H = 1, K_DONE = 2 };
-constexpr int CTL_ERR = 0;
-constexpr int CNT_BASE = 64;                               // + (kind * NGRP + g) * 64
-constexpr int TOP_BASE = CNT_BASE + 3 * NGRP * 64;         // + kind * 64
-constexpr int COPY_BASE = TOP_BASE + 3 * 64;               // + copy * COPY_STRIDE
-constexpr int COPY_STRIDE = 1088;                          // 4352 bytes between copies
-constexpr int CP_TOPK = 0, CP_H = 1, CP_IDX = 16, CP_W = 32;
-static_assert(COPY_BASE + NCOPY * COPY_STRIDE <= (int)(WS_CTL_BYTES / 4), "control region");
+// Decode state at the start of the workspace, in uint32 units.  It must be zero before
+// the first call and is kept by the library between calls.
+constexpr int CTL_ERR = 0;                  // set if a bounded wait ever gave up
+constexpr int CTL_GEN = 64;                 // calls completed; this call's tag is gen + 1
+constexpr int CNT_BASE = 128;               // + g * 64: completion group counters
+constexpr int CNT_TOP = CNT_BASE + NGRP * 64;
+// Hand-off words are written in several copies, 256 bytes off a multiple of the copy
+// size apart, so that the many workgroups polling them spread over memory channels
+// instead of queueing on a few lines.
+constexpr int LOGIT_COPIES = 32;
+constexpr int LOGIT_STRIDE = 2 * 256 + 64;  // per copy: E words of 64 bits, logit bits | tag << 32
+constexpr int LOGIT_BASE = CNT_TOP + 64;
+constexpr int H_COPIES = 8;
+constexpr int H_WORDS_MAX = 24576 / 2;      // (top_k + 1) * inter <= 24576
+constexpr int H_STRIDE = 2 * H_WORDS_MAX + 64;  // per copy: (K+1)*I/2 words, fp16 h[j], h[j+1] | tag << 32
+constexpr int H_BASE = LOGIT_BASE + LOGIT_COPIES * LOGIT_STRIDE;
+constexpr int TOPK_COPIES = 32;
+constexpr int TOPK_STRIDE = 1088;           // per copy: 2 words of 64 bits per selected expert,
+                                            // (id | tag << 32) and (weight bits | tag << 32)
+constexpr int TOPK_BASE = H_BASE + H_COPIES * H_STRIDE;
+constexpr int N_SELECT = 8;                 // selector workgroups of a layer call
+static_assert((TOPK_BASE + TOPK_COPIES * TOPK_STRIDE) * 4 <= (int)WS_CTL_BYTES, "decode state region");
 
 struct DecArgs {
     Layer L;
     const uint16_t *x;
-    DecodeBufs b;
+    uint32_t *ctl;
     int32_t *out_idx;
     float *out_w;
     void *y;
     int y_dtype;
     int shared;
-    int nR, nS, nG, nD;         // workgroups per role
-    int lprg;                   // gate/up: lanes per row (pairs per wave = 64 / lprg)
+    int nR, nP, nS, nG, nD;     // workgroups per role (route only: nP = 1, nS = nG = nD = 0)
+    int route_only;
+    int lprg;                   // gate/up: lanes per row (row groups per wave = 64 / lprg)
     int lprd;                   // down: lanes per row (rows per wave = 64 / lprd)
+    int vs;                     // down: wave groups splitting the vectors of a row block
 };
 
 __device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
@@ -87,10 +104,21 @@ __device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
 __device__ __forceinline__ uint32_t add_dev(uint32_t *p) {
     return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 
-// member `m` of `total` signals completion of its device-scope stores; true (in every
-// thread) for exactly one workgroup: the last of all members
-__device__ bool signal_all(uint32_t *ctl, int kind, int m, int total, uint32_t *s_flag) {
+__device__ void raise_error(uint32_t *ctl) {
+    __hip_atomic_fetch_or(ctl + CTL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// back-off between polls of a word another workgroup has not yet written
+__device__ __forceinline__ void poll_pause(uint32_t n) {
+    if (n < 8) __builtin_amdgcn_s_sleep(1);
+    else __builtin_amdgcn_s_sleep(4);
+}
+
+// member `m` of `total` reports completion; true (in every thread) for exactly one
+// workgroup: the last of all members
+__device__ bool last_to_finish(uint32_t *ctl, int m, int total, uint32_t *s_flag) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -98,45 +126,20 @@ __device__ bool signal_all(uint32_t *ctl, int kind, int m, int total, uint32_t *
         const int gsize = total / NGRP + (g < total % NGRP ? 1 : 0);
         const int ngroups = total < NGRP ? total : NGRP;
         uint32_t last = 0;
-        if (add_dev(ctl + CNT_BASE + (kind * NGRP + g) * 64) == (uint32_t)(gsize - 1))
-            last = add_dev(ctl + TOP_BASE + kind * 64) == (uint32_t)(ngroups - 1);
+        if (add_dev(ctl + CNT_BASE + g * 64) == (uint32_t)(gsize - 1))
+            last = add_dev(ctl + CNT_TOP) == (uint32_t)(ngroups - 1);
         *s_flag = last;
     }
     __syncthreads();
     return *s_flag != 0;
 }
 
-// raise a ready flag in every copy, after this workgroup's stores are acknowledged
-__device__ void raise_flag(uint32_t *ctl, int which) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x < NCOPY) st_dev(ctl + COPY_BASE + threadIdx.x * COPY_STRIDE + which, 1u);
-}
-
-// thread 0 waits (bounded, with back-off) for a non-zero flag; then the workgroup goes on
-__device__ void wait_flag(uint32_t *ctl, const uint32_t *p) {
-    if (threadIdx.x == 0) {
-        uint32_t n = 0;
-        while (ld_dev(p) == 0u) {
-            if (n < 8) __builtin_amdgcn_s_sleep(1);
-            else __builtin_amdgcn_s_sleep(6);
-            if (++n > SPIN_LIMIT) {
-                __hip_atomic_fetch_or(ctl + CTL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
-            }
-        }
-    }
-    __syncthreads();
-}
-
-__device__ void reset_controls(uint32_t *ctl) {
+// the last workgroup of a call: counters back to zero, generation advanced
+__device__ void finish_call(uint32_t *ctl, uint32_t tag) {
     const int t = threadIdx.x;
-    if (t < 3 * NGRP) st_dev(ctl + CNT_BASE + t * 64, 0u);
-    if (t < 3) st_dev(ctl + TOP_BASE + t * 64, 0u);
-    if (t < NCOPY) {
-        st_dev(ctl + COPY_BASE + t * COPY_STRIDE + CP_TOPK, 0u);
-        st_dev(ctl + COPY_BASE + t * COPY_STRIDE + CP_H, 0u);
-    }
+    if (t < NGRP) st_dev(ctl + CNT_BASE + t * 64, 0u);
+    if (t == NGRP) st_dev(ctl + CNT_TOP, 0u);
+    if (t == NGRP + 1) st_dev(ctl + CTL_GEN, tag);
 }
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
@@ -163,11 +166,11 @@ __device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float *xsum) {
     }
 }
 
-// sum_c (s q_c + b) x_c over one 16-byte chunk of codes
+// sum_c (s q_c + b) x_c over one 16-byte chunk of codes (four independent dot chains)
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float X) {
     const u32x4 *xv = (const u32x4 *)xs;
-    float acc = 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (BITS == 4) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -175,7 +178,7 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, u
             magic_u4(q[d], m);
             const u32x4 xx = xv[d];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc, false);
+            for (int i = 0; i < 4; ++i) acc[d] = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc[d], false);
         }
     } else {
 #pragma unroll
@@ -184,149 +187,198 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, u
             magic_u8(q[d], m);
             const u32x4 xx = xv[d >> 1];
             const int o = 2 * (d & 1);
-            acc = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc, false);
-            acc = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc, false);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc[d], false);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc[d], false);
         }
     }
+    const float A = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     const float s = f16_to_f32((uint16_t)s16), b = f16_to_f32((uint16_t)b16);
-    return s * acc + (b - 1024.0f * s) * X;
+    return s * A + (b - 1024.0f * s) * X;
 }
 
-__device__ __forceinline__ float group_reduce(float v, int width) {
-    for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
-// [gate; up] row pairs j0 and j1 of matrix stacks (mg, mu), expert e: SwiGLU values
-// (in every lane of the row group; lpr lanes share a pair).  All loads of a step --
-// 2 pairs x 2 rows x 2 chunks -- are issued before any is used.
+// [gate; up] row pairs j0 and j0 + 1 of expert e in matrix stacks (mg, mu): SwiGLU
+// values (in every lane of the row group; lpr lanes share a pair).  Each step loads one
+// chunk of each of the 4 rows; loads are unconditional (a lane past the row end re-reads
+// the last chunk and discards it) so that all of a step's loads are issued before any
+// wait.  Addresses are a uniform matrix base plus a 32-bit per-lane offset.
 template <int BITS>
-__device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int64_t e, int j0, int j1, int H, int lpr,
+__device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
                              const uint32_t *xs, const float *xsum, float hv[2]) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
-    const int64_t rb = (int64_t)H * BITS / 8;
-    const uint8_t *cp[4];
-    const uint16_t *sp[4], *bp[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {               // r = 2 * pair + (0 gate | 1 up)
-        const QMat &m = (r & 1) ? mu : mg;
-        const int64_t R = e * m.stride + ((r >> 1) ? j1 : j0);
-        cp[r] = m.codes + R * rb;
-        sp[r] = m.scales + R * ng;
-        bp[r] = m.biases + R * ng;
-    }
+    const uint32_t rb = (uint32_t)H * BITS / 8;
+    const int64_t eg = (int64_t)e * mg.stride, eu = (int64_t)e * mu.stride;
+    const uint64_t cg = (uint64_t)(mg.codes + eg * rb), cu = (uint64_t)(mu.codes + eu * rb);
+    const uint64_t sg = (uint64_t)(mg.scales + eg * ng), bg = (uint64_t)(mg.biases + eg * ng);
+    const uint64_t su = (uint64_t)(mu.scales + eu * ng), bu = (uint64_t)(mu.biases + eu * ng);
+    const uint32_t oc0 = (uint32_t)j0 * rb, os0 = (uint32_t)j0 * ng;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c0 = lr; c0 < nch; c0 += 2 * lpr) {
-        u32x4 q[8];
-        uint32_t s[8], b[8];
+    for (int k0 = 0; k0 < nch; k0 += lpr) {
+        const int c = k0 + lr;
+        const bool ok = c < nch;
+        const int cc = ok ? c : nch - 1;
+        const uint32_t oc = oc0 + 16u * cc, os = os0 + ((cc * CPC) >> 6);
+        u32x4 q[4];
+        uint32_t sc[4], bi[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = i >> 1, c = c0 + (i & 1) * lpr;
-            q[i] = (u32x4){0u, 0u, 0u, 0u};
-            s[i] = b[i] = 0;
-            if (c < nch) {
-                const int gi = (c * CPC) >> 6;
-                q[i] = __builtin_nontemporal_load((const u32x4 *)(cp[r] + 16 * c));
-                s[i] = sp[r][gi];
-                b[i] = bp[r][gi];
-            }
+        for (int r = 0; r < 4; ++r) {               // r = 2 * (row j0 + r/2) + (0 gate | 1 up)
+            const uint32_t dc = (r >> 1) ? rb : 0u, ds = (r >> 1) ? (uint32_t)ng : 0u;
+            q[r] = __builtin_nontemporal_load((g_u32x4 *)(((r & 1) ? cu : cg) + oc + dc));
+            sc[r] = *(g_u16 *)(((r & 1) ? su : sg) + 2u * (os + ds));
+            bi[r] = *(g_u16 *)(((r & 1) ? bu : bg) + 2u * (os + ds));
         }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = c0 + (i & 1) * lpr;
-            if (c < nch) acc[i >> 1] += chunk_dot<BITS>(q[i], xs + c * (CPC / 2), s[i], b[i], xsum[c]);
+        for (int r = 0; r < 4; ++r) {
+            const float p = chunk_dot<BITS>(q[r], xs + cc * (CPC / 2), sc[r], bi[r], xsum[cc]);
+            acc[r] += ok ? p : 0.0f;
         }
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const float g = group_reduce(acc[2 * p], lpr);
-        const float u = group_reduce(acc[2 * p + 1], lpr);
+        const float g = group_sum(acc[2 * p], lpr);
+        const float u = group_sum(acc[2 * p + 1], lpr);
         hv[p] = silu(g) * u;
     }
 }
 
+// Selector (one wave): waits (bounded) until every logit of this call is in, polling
+// with two reads in flight, and takes the top-k: lanes j < K return (id, weight) of the
+// j-th selected expert in ascending id.
+__device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t *lg = (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE);
+    const uint64_t none = (uint64_t)tag << 32;
+    uint64_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
+    for (uint32_t n = 0;; ++n) {
+        uint64_t w2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w2[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
+        bool miss = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) miss |= tag_of(w[i]) != tag;
+        if (__ballot(miss) == 0ull) break;
+        if (n > SPIN_LIMIT) {
+            if (lane == 0) raise_error(ctl);
+            break;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = w2[i];
+        poll_pause(n);
+    }
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = no_nan(__uint_as_float((uint32_t)w[i]));
+    TopkOut tk = wave_topk_regs(v, E, K);
+    tk.idx = min(max(tk.idx, 0), E - 1);
+    return tk;
+}
+
+// Consumer: wave 0 waits (bounded) for the published selection, with two reads in
+// flight; the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights.
+__device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int *s_idx, float *s_w) {
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
+        const bool act = lane < 2 * K;
+        const uint64_t none = (uint64_t)tag << 32;
+        uint64_t w = act ? ld_dev64(tp + lane) : none;
+        for (uint32_t n = 0;; ++n) {
+            const uint64_t w2 = act ? ld_dev64(tp + lane) : none;
+            if (__ballot(tag_of(w) != tag) == 0ull) break;
+            if (n > SPIN_LIMIT) {
+                if (lane == 0) raise_error(ctl);
+                break;
+            }
+            w = w2;
+            poll_pause(n);
+        }
+        if (act) {
+            if (lane & 1) s_w[lane >> 1] = __uint_as_float((uint32_t)w);
+            else s_idx[lane >> 1] = min(max((int)(uint32_t)w, 0), E - 1);
+        }
+    }
+    __syncthreads();
+}
+
 template <int BITS>
-__global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
+__global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_decode(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
     __shared__ uint32_t s_flag;
-    __shared__ __attribute__((aligned(16))) float s_logit[256];
     __shared__ int s_idx[16];
     __shared__ float s_w[16];
+    __shared__ float s_part[NW][DT / 64 * 16];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
-    uint32_t *ctl = a.b.ctl;
-    uint32_t *copy = ctl + COPY_BASE + (blockIdx.x % NCOPY) * COPY_STRIDE;    // the copy this WG reads
+    uint32_t *ctl = a.ctl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K;
-    const int nR = a.nR, nS = a.nS, nG = a.nG, nD = a.nD;
+    int nR = a.nR;
+    const int nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
 
-    auto get_topk = [&]() {
-        wait_flag(ctl, copy + CP_TOPK);
-        if (tid < K) {
-            s_idx[tid] = min(max((int)ld_dev(copy + CP_IDX + tid), 0), E - 1);
-            s_w[tid] = __uint_as_float(ld_dev(copy + CP_W + tid));
-        }
-        __syncthreads();
-    };
-
     if (b < nR) {
-        // ---------------------------------------------------------------- R: logits
+        // ------------------------------------------------- R: one router logit per wave
         const int e = b * NW + wave;
-        if (e < E) {
-            const uint16_t *wr = L.router_w + (int64_t)e * H;
-            float acc = 0.0f;
-            for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
-                u32x4 xv[4], wv[4];
+        if (e >= E) return;
+        const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+        const uint16_t *wr = L.router_w + (int64_t)e * H;
+        float acc = 0.0f;
+        for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
+            u32x4 xv[4], wv[4];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int c = c0 + 64 * k;
-                    xv[k] = wv[k] = (u32x4){0u, 0u, 0u, 0u};
-                    if (c < H / 8) {
-                        xv[k] = *(const u32x4 *)(a.x + 8 * c);
-                        wv[k] = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
-                    }
+            for (int k = 0; k < 4; ++k) {
+                const int c = c0 + 64 * k;
+                xv[k] = wv[k] = (u32x4){0u, 0u, 0u, 0u};
+                if (c < H / 8) {
+                    xv[k] = *(const u32x4 *)(a.x + 8 * c);
+                    wv[k] = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
                 }
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc = __builtin_fmaf(__uint_as_float(xv[k][i] << 16), __uint_as_float(wv[k][i] << 16), acc);
-                        acc = __builtin_fmaf(__uint_as_float(xv[k][i] & 0xffff0000u),
-                                             __uint_as_float(wv[k][i] & 0xffff0000u), acc);
-                    }
             }
-            acc = wave_sum(acc);
-            if (lane == 0)
-                st_dev((uint32_t *)a.b.logits + e, __float_as_uint(acc + (L.router_bias ? L.router_bias[e] : 0.0f)));
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = __builtin_fmaf(__uint_as_float(xv[k][i] << 16), __uint_as_float(wv[k][i] << 16), acc);
+                    acc = __builtin_fmaf(__uint_as_float(xv[k][i] & 0xffff0000u),
+                                         __uint_as_float(wv[k][i] & 0xffff0000u), acc);
+                }
         }
-        if (signal_all(ctl, K_ROUTER, b, nR, &s_flag)) {
-            // the last router workgroup: every logit is in; select and publish
-            if (tid < 256)
-                s_logit[tid] = (tid < E) ? __uint_as_float(ld_dev((const uint32_t *)a.b.logits + tid)) : -__builtin_inff();
-            __syncthreads();
-            if (wave == 0) {
-                // one wave: K rounds of butterfly arg-max over 4 logits per lane
-                const TopkOut tk = wave_topk([&](int e2) { return no_nan(s_logit[e2]); }, E, K);
-                if (lane < K) { s_idx[lane] = min(max(tk.idx, 0), E - 1); s_w[lane] = tk.w; }
-            }
-            __syncthreads();
-            for (int i = tid; i < NCOPY * K; i += DT) {
-                uint32_t *cp = ctl + COPY_BASE + (i / K) * COPY_STRIDE;
-                st_dev(cp + CP_IDX + i % K, (uint32_t)s_idx[i % K]);
-                st_dev(cp + CP_W + i % K, __float_as_uint(s_w[i % K]));
-            }
-            if (tid < K) {
-                if (a.out_idx) a.out_idx[tid] = s_idx[tid];
-                if (a.out_w) a.out_w[tid] = s_w[tid];
-            }
-            if (nS + nG + nD == 0) reset_controls(ctl);      // routing only: nobody waits
-            else raise_flag(ctl, CP_TOPK);
+        acc = wave_sum(acc);
+        if (lane < LOGIT_COPIES) {
+            const float lgt = acc + (L.router_bias ? L.router_bias[e] : 0.0f);
+            st_dev64((uint64_t *)(ctl + LOGIT_BASE + lane * LOGIT_STRIDE) + e,
+                     __float_as_uint(lgt) | ((uint64_t)tag << 32));
         }
         return;
     }
+    const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+    if (b < nR + a.nP) {
+        // ------------------------------------------- P: selectors (wave 0 works)
+        if (wave != 0) return;
+        const int sel = b - nR;
+        const TopkOut tk = select_topk(ctl, tag, E, K);
+        if (a.route_only) {
+            if (lane < K) {
+                if (a.out_idx) a.out_idx[lane] = tk.idx;
+                if (a.out_w) a.out_w[lane] = tk.w;
+            }
+            if (lane == 0) st_dev(ctl + CTL_GEN, tag);       // the only reader of this call's logits
+            return;
+        }
+        if (lane < K)
+            for (int c = sel; c < TOPK_COPIES; c += a.nP) {
+                uint64_t *tp = (uint64_t *)(ctl + TOPK_BASE + c * TOPK_STRIDE);
+                st_dev64(tp + 2 * lane, (uint32_t)tk.idx | ((uint64_t)tag << 32));
+                st_dev64(tp + 2 * lane + 1, __float_as_uint(tk.w) | ((uint64_t)tag << 32));
+            }
+        return;
+    }
+    nR += a.nP;                                              // the roles below follow the selectors
     if (b < nR + nS + nG) {
         // ------------------------------------------- S / G: gate/up + SwiGLU -> h
         uint32_t *xs = dsm;
@@ -334,90 +386,119 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
         const int rpw = 64 / a.lprg;                         // row groups per wave
         const int pb = 2 * NW * rpw;                         // pairs per workgroup (2 per row group)
         const bool sh = b < nR + nS;
-        const int m = b - nR;                                // member index among S and G
-        const int g = sh ? m : m - nS;
+        const int g = sh ? b - nR : b - nR - nS;
         const int bpe = (I + pb - 1) / pb;                   // workgroups per expert
         const int slot = sh ? K : g / bpe;                   // h row (K = shared)
-        const int j0 = (sh ? g : g % bpe) * pb + wave * rpw + lane / a.lprg;
-        const int j1 = j0 + NW * rpw;
+        const int j0 = (sh ? g : g % bpe) * pb + 2 * (wave * rpw + lane / a.lprg);
         stage_x<BITS>(a.x, H, xs, xsum);
-        int64_t e = 0;
+        int e = 0;
         if (sh) {
             __syncthreads();
         } else {
-            get_topk();                                      // ends with a barrier
-            e = s_idx[slot];
+            get_topk(ctl, tag, E, K, s_idx, s_w);            // ends with a barrier
+            e = __builtin_amdgcn_readfirstlane(s_idx[slot]);
         }
+        const int jj = j0 < I ? j0 : I - 2;
         float hv[2];
-        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, j0 < I ? j0 : I - 1,
-                           j1 < I ? j1 : I - 1, H, a.lprg, xs, xsum, hv);
-        if (lane % a.lprg == 0) {
-            float *hrow = a.b.h + (int64_t)slot * I;
-            if (j0 < I) st_dev((uint32_t *)hrow + j0, __float_as_uint(hv[0]));
-            if (j1 < I) st_dev((uint32_t *)hrow + j1, __float_as_uint(hv[1]));
+        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, hv);
+        if (j0 < I) {                                        // lanes of the row group write the copies
+            const uint64_t word = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1])) | ((uint64_t)tag << 32);
+            for (int cp = lane % a.lprg; cp < H_COPIES; cp += a.lprg)
+                st_dev64((uint64_t *)(ctl + H_BASE + cp * H_STRIDE) + slot * (I / 2) + j0 / 2, word);
         }
-        if (signal_all(ctl, K_H, m, nS + nG, &s_flag)) raise_flag(ctl, CP_H);
         return;
     }
-    if (b < nR + nS + nG + nD) {
+    {
         // ------------------------------------------ D: down + weighted combine
         const int d = b - nR - nS - nG;
-        get_topk();
+        get_topk(ctl, tag, E, K, s_idx, s_w);
+        if (d == 0 && tid < K) {
+            if (a.out_idx) a.out_idx[tid] = s_idx[tid];
+            if (a.out_w) a.out_w[tid] = s_w[tid];
+        }
         const int nvec = K + (a.shared ? 1 : 0);
         const int lpr = a.lprd, rpw = 64 / lpr;
         const int nch = I / CPC, ng = I / 64;
         const int64_t rb = (int64_t)I * BITS / 8;
         const int lr = lane % lpr;
-        const int n = d * NW * rpw + wave * rpw + lane / lpr;
+        // the waves form a.vs groups; group gv takes vectors [v_lo, v_hi) of the same rows
+        const int wpg = NW / a.vs, gv = wave / wpg, wg = wave % wpg;
+        const int vpg = (nvec + a.vs - 1) / a.vs;
+        const int v_lo = min(gv * vpg, nvec), v_hi = min(v_lo + vpg, nvec);
+        const int rloc = wg * rpw + lane / lpr;               // row within the workgroup
+        const int n = d * wpg * rpw + rloc;
         const int nc = n < H ? n : H - 1;
         uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * I fp16, code order
         float *hsum = (float *)(dsm + nvec * I / 2);          // nvec * nch chunk sums
+        // lane j < nvec holds row 0 of vector j's down matrix (the k routed experts in
+        // ascending id, then the shared one) and its combine weight
+        uint64_t pc = 0, ps = 0, pbi = 0;
+        float wl = 1.0f;
+        if (lane < nvec) {
+            const bool routed = lane < K;
+            const QMat &mm = routed ? L.down : L.s_down;
+            const int64_t R0 = routed ? (int64_t)s_idx[lane] * mm.stride : 0;
+            pc = (uint64_t)(mm.codes + R0 * rb);
+            ps = (uint64_t)(mm.scales + R0 * ng);
+            pbi = (uint64_t)(mm.biases + R0 * ng);
+            if (routed) wl = s_w[lane];
+        }
         float yv = 0.0f;
-        // items (vector v, chunk c = lr + ci*lpr), NB in flight per lane
-        constexpr int NB = 9;
-        int v = 0, ci = 0;
-        for (int base = 0; v < nvec; base += NB) {
+        // items (vector v, chunk lr + k*lpr), NB per step, loaded unconditionally (clamped
+        // to a valid chunk and discarded) so that all of a step's loads are in flight
+        constexpr int NB = 5;
+        const int cpl = (nch + lpr - 1) / lpr;                 // chunks per lane per vector
+        const int nit = (v_hi - v_lo) * cpl;
+        const int vlast = v_hi > v_lo ? v_hi - 1 : v_lo;       // a valid vector to clamp to
+        const uint32_t rowc = (uint32_t)nc * (uint32_t)rb, rows = (uint32_t)nc * ng;
+        int v = v_lo, k = 0;
+        for (int base = 0; base == 0 || base < nit; base += NB) {
             u32x4 q[NB];
             uint32_t sv[NB], bv[NB];
-            int vv[NB], cc[NB];
+            int v2 = v, k2 = k;
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                const int c = lr + ci * lpr;
-                vv[i] = v;
-                cc[i] = c;
-                q[i] = (u32x4){0u, 0u, 0u, 0u};
-                sv[i] = bv[i] = 0;
-                if (v < nvec && c < nch) {
-                    const QMat &mm = v < K ? L.down : L.s_down;
-                    const int64_t R = (int64_t)(v < K ? s_idx[v] : 0) * mm.stride + nc;
-                    q[i] = __builtin_nontemporal_load((const u32x4 *)(mm.codes + R * rb + 16 * c));
-                    const int64_t gi = R * ng + ((c * CPC) >> 6);
-                    sv[i] = mm.scales[gi];
-                    bv[i] = mm.biases[gi];
-                }
-                if (v < nvec && (++ci) * lpr >= nch) { ci = 0; ++v; }
+                const int vi = base + i < nit ? v : min(vlast, nvec - 1);
+                const int c = lr + k * lpr, cc = c < nch ? c : nch - 1;
+                const uint32_t gi = rows + ((cc * CPC) >> 6);
+                q[i] = __builtin_nontemporal_load((g_u32x4 *)(readlane64(pc, vi) + (rowc + 16u * cc)));
+                sv[i] = *(g_u16 *)(readlane64(ps, vi) + 2u * gi);
+                bv[i] = *(g_u16 *)(readlane64(pbi, vi) + 2u * gi);
+                if (++k == cpl) { k = 0; ++v; }
             }
+            __builtin_amdgcn_sched_barrier(0);
             if (base == 0) {
-                // all of h (S and G), read coalesced: fp16 in code order, then chunk sums
-                wait_flag(ctl, copy + CP_H);
-                const uint64_t *h2 = (const uint64_t *)a.b.h;
+                // all of h (S and G) as it arrives: fp16 pairs into LDS in code order
+                const uint64_t *hw = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE);
                 const int npairs = nvec * I / 2;
-                for (int p0 = 0; p0 < npairs; p0 += 4 * DT) {
-                    uint64_t hv[4];
+                for (int p0 = 0; p0 < npairs; p0 += 8 * DT) {
+                    uint64_t w[8];
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int p = p0 + k * DT + tid;
-                        hv[k] = p < npairs ? ld_dev64(h2 + p) : 0ull;
+                    for (int j = 0; j < 8; ++j) {
+                        const int p = p0 + j * DT + tid;
+                        w[j] = p < npairs ? ld_dev64(hw + p) : (uint64_t)tag << 32;
+                    }
+                    for (uint32_t t = 0;; ++t) {
+                        bool miss = false;
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) miss |= tag_of(w[j]) != tag;
+                        if (!miss) break;
+                        if (t > SPIN_LIMIT) {
+                            raise_error(ctl);
+                            break;
+                        }
+                        poll_pause(t);
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            if (tag_of(w[j]) != tag) w[j] = ld_dev64(hw + p0 + j * DT + tid);
                     }
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int p = p0 + k * DT + tid;
+                    for (int j = 0; j < 8; ++j) {
+                        const int p = p0 + j * DT + tid;
                         if (p < npairs) {
                             const int i0 = 2 * p, gb = i0 & ~7;
-                            hs16[gb + perm_pos<BITS>(i0 & 7)] =
-                                __builtin_bit_cast(uint16_t, f32_to_f16_ftz(__uint_as_float((uint32_t)hv[k])));
-                            hs16[gb + perm_pos<BITS>((i0 + 1) & 7)] =
-                                __builtin_bit_cast(uint16_t, f32_to_f16_ftz(__uint_as_float((uint32_t)(hv[k] >> 32))));
+                            hs16[gb + perm_pos<BITS>(i0 & 7)] = (uint16_t)w[j];
+                            hs16[gb + perm_pos<BITS>((i0 + 1) & 7)] = (uint16_t)(w[j] >> 16);
                         }
                     }
                 }
@@ -428,8 +509,8 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
                     for (int g8 = 0; g8 < CPC / 8; ++g8) {
                         const u32x4 w4 = src[g8];
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) {
-                            const f16x2 hh = as_h2(w4[k]);
+                        for (int j = 0; j < 4; ++j) {
+                            const f16x2 hh = as_h2(w4[j]);
                             sum += (float)hh[0] + (float)hh[1];
                         }
                     }
@@ -439,20 +520,42 @@ __global__ __launch_bounds__(DT) void k_decode(DecArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
-                if (vv[i] < nvec && cc[i] < nch) {
-                    const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + vv[i] * I + cc[i] * CPC), sv[i],
-                                                    bv[i], hsum[vv[i] * nch + cc[i]]);
-                    yv += (vv[i] < K ? s_w[vv[i]] : 1.0f) * p;   // experts in ascending id, shared last
-                }
+                const bool live = base + i < nit;
+                const int vi = live ? v2 : min(vlast, nvec - 1);
+                const int c = lr + k2 * lpr, cc = c < nch ? c : nch - 1;
+                const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + vi * I + cc * CPC), sv[i], bv[i],
+                                                hsum[vi * nch + cc]);
+                const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), vi));
+                yv += (live && c < nch) ? wv * p : 0.0f;       // experts in ascending id, shared last
+                if (++k2 == cpl) { k2 = 0; ++v2; }
+                __builtin_amdgcn_sched_barrier(0);             // one item at a time: bounded registers
             }
         }
-        yv = group_reduce(yv, lpr);
-        if (n < H && lr == 0) {
-            if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = yv;
-            else ((uint16_t *)a.y)[n] = f32_to_bf16(yv);
+        yv = group_sum(yv, lpr);
+        // groups' partial sums combined in group order
+        if (lr == 0) s_part[gv][rloc] = yv;
+        __syncthreads();
+        if (gv == 0 && lr == 0 && n < H) {
+            float y = s_part[0][rloc];
+            for (int j = 1; j < a.vs; ++j) y += s_part[j][rloc];
+            if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = y;
+            else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
         }
-        if (signal_all(ctl, K_DONE, d, nD, &s_flag)) reset_controls(ctl);
+        if (last_to_finish(ctl, d, nD, &s_flag)) finish_call(ctl, tag);
     }
+}
+
+int n_compute_units() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+            n = cu;
+        else
+            n = 256;
+    }
+    return n;
 }
 
 // lanes sharing one row: the largest power of two <= min(64, 16-byte chunks per row)
@@ -463,7 +566,7 @@ int lanes_per_row(int ncols, int bits) {
     return l;
 }
 
-hipError_t launch(DecArgs a, bool route_only, hipStream_t s) {
+hipError_t launch(DecArgs a, hipStream_t s) {
     const Layer &L = a.L;
     const int cpc = 128 / L.bits;
     a.lprg = lanes_per_row(L.H, L.bits);
@@ -471,14 +574,36 @@ hipError_t launch(DecArgs a, bool route_only, hipStream_t s) {
     const int pb = 2 * NW * (64 / a.lprg);
     const int bpe = (L.I + pb - 1) / pb;
     a.nR = (L.E + NW - 1) / NW;
-    a.nS = (!route_only && a.shared) ? bpe : 0;
-    a.nG = route_only ? 0 : L.K * bpe;
-    a.nD = route_only ? 0 : (L.H + NW * (64 / a.lprd) - 1) / (NW * (64 / a.lprd));
-    const int nvec = L.K + (a.shared ? 1 : 0);
-    const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 4;
-    const size_t lds_d = (size_t)nvec * L.I * 2 + (size_t)nvec * (L.I / cpc) * 4;
-    const size_t lds = route_only ? 16 : (lds_g > lds_d ? lds_g : lds_d);
-    const int grid = a.nR + a.nS + a.nG + a.nD;
+    size_t lds = 16;
+    a.vs = 1;
+    if (a.route_only) {
+        a.nP = 1;
+        a.nS = a.nG = a.nD = 0;
+    } else {
+        a.nP = N_SELECT;                               // reduced below to what the consumers need
+        a.nS = a.shared ? bpe : 0;
+        a.nG = L.K * bpe;
+        const int nvec = L.K + (a.shared ? 1 : 0);
+        // split the vectors of a row block over more waves while the grid stays within
+        // what the device holds at once (two workgroups per CU)
+        const int resident = 2 * n_compute_units();
+        a.vs = 1;
+        while (a.vs < 4 && 2 * a.vs <= nvec) {
+            const int rows = NW / (2 * a.vs) * (64 / a.lprd);
+            if (a.nR + a.nP + a.nS + a.nG + (L.H + rows - 1) / rows > resident) break;
+            a.vs *= 2;
+        }
+        const int rows = NW / a.vs * (64 / a.lprd);
+        a.nD = (L.H + rows - 1) / rows;
+        // consumer b reads copy b % TOPK_COPIES, written by selector b % nP: with nP a power
+        // of two no larger than the (contiguous) G and D range, every selector is read, so
+        // every selector has started before the call can complete
+        while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
+        const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 4;
+        const size_t lds_d = (size_t)nvec * L.I * 2 + (size_t)nvec * (L.I / cpc) * 4;
+        lds = lds_g > lds_d ? lds_g : lds_d;
+    }
+    const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
     if (L.bits == 4)
         hipLaunchKernelGGL((k_decode<4>), dim3(grid), dim3(DT), lds, s, a);
     else
@@ -490,7 +615,7 @@ DecArgs make_args(const Layer &L, const uint16_t *x, const DecodeBufs &b) {
     DecArgs a{};
     a.L = L;
     a.x = x;
-    a.b = b;
+    a.ctl = b.ctl;
     a.y_dtype = QSMOE_F32;
     a.shared = L.has_shared;
     return a;
@@ -505,16 +630,17 @@ hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBu
     a.y_dtype = y_dtype;
     a.out_idx = out_idx;
     a.out_w = out_w;
-    return launch(a, false, s);
+    return launch(a, s);
 }
 
 hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBufs &b, int32_t *out_idx,
                                float *out_w, hipStream_t s) {
     DecArgs a = make_args(L, x, b);
     a.shared = 0;
+    a.route_only = 1;
     a.out_idx = out_idx;
     a.out_w = out_w;
-    return launch(a, true, s);
+    return launch(a, s);
 }
 
 }  // namespace qs

@@ -26,14 +26,13 @@ struct Layer {
 };
 
 // -------------------------------------------------------------------- decode T = 1
-// Control words at the start of every workspace (zero before the first call, left zero
-// by every call): tickets and completion counters of the one-launch decode kernel.
-constexpr size_t WS_CTL_BYTES = 96 * 1024;
+// Decode state at the start of every workspace: zero before the first call, then kept
+// by the library between calls (call generation, completion counters, and the tagged
+// logit and h words the workgroups of one call hand to each other).
+constexpr size_t WS_CTL_BYTES = 1024 * 1024;
 
 struct DecodeBufs {
-    uint32_t *ctl;                 // WS_CTL_BYTES of control words
-    float *logits;                 // [E]
-    float *h;                      // [(K+1)][I]  (slot K = shared expert)
+    uint32_t *ctl;                 // WS_CTL_BYTES of decode state
 };
 
 hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
