@@ -12,7 +12,7 @@ Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256
 Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
 HIP graph; HIP events on the replay stream bracket the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,...]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,copy]
 """
 from __future__ import annotations
 
@@ -27,6 +27,14 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 GROUP = 64
+
+# HBM traffic of one decode-kernel launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (KiB per dispatch, median over the timed launches), each scaled by what the same
+# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  A
+# figure holds only for the kernel sources it was measured on, identified by their
+# sha256; once they change the traffic is reported as null until measured again.
+DECODE_SOURCES = ("csrc/decode.hip", "csrc/common.h", "csrc/internal.h")
+DECODE_TRAFFIC = {"sources_sha256": "32fac9acbc53d63d1586e6484af3dd66cf013411ad13d58ffafb42c6f83e131a", "bytes": 18510014}
 
 
 # ----------------------------------------------------------- algorithmic accounting
@@ -53,6 +61,16 @@ def decode_layer_bytes(H: int, I: int, E: int, K: int, bits: int, shared: bool =
 def layer_flops(T: int, H: int, I: int, E: int, K: int, shared: bool = True) -> int:
     """2*T*E*H (router) + 2 * 3*H*I per (token, expert) over the k routed + shared."""
     return 2 * T * E * H + 2 * T * (K + (1 if shared else 0)) * 3 * H * I
+
+
+def decode_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_sparse_moe_amd")
+    for f in DECODE_SOURCES:
+        with open(os.path.join(pkg, f), "rb") as fh:
+            h.update(fh.read())
+    return DECODE_TRAFFIC["bytes"] if h.hexdigest() == DECODE_TRAFFIC["sources_sha256"] else None
 
 
 # ------------------------------------------------------------------------- helpers
@@ -180,6 +198,15 @@ def bench_q8(qs, torch, syn, steps, warmup, layers=16):
     return ms, nbytes
 
 
+def bench_copy(torch, steps, nbytes=1 << 30):
+    """Plain device-to-device copy of `nbytes` (torch's copy kernel): the calibration
+    workload for the HBM byte counters (it must read and write exactly `nbytes`)."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    ms = _graph_time(torch, lambda i: b.copy_(a), steps, 2)
+    return ms, nbytes
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,7 +239,7 @@ def main(argv=None):
                          "global_batch": 1, "seq_len": 1}
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                           "frac": gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
                            "kernel": "decode layer (router+shared gate/up, routed gate/up, down+combine)",
                            "bytes_per_launch": nbytes}
     if "prefill" in only:
@@ -237,6 +264,9 @@ def main(argv=None):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["q8"] = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
                      "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": nbytes}
+    if "copy" in only:
+        ms, nbytes = bench_copy(torch, 8)
+        out["copy"] = {"bytes_each_way": nbytes, "ms": ms, "GB_per_s": 2 * nbytes / (ms * 1e-3) / 1e9}
     if not args.no_cpu and Ld is not None:
         out["cpu_baseline"] = cpu_baseline_decode(Ld, 96)
     print(json.dumps(out), flush=True)
