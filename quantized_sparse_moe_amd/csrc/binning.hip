@@ -46,37 +46,49 @@ __global__ __launch_bounds__(256) void k_colscan(const int32_t *__restrict__ blk
     if (lane == 63) counts[e] = incl;
 }
 
-// Expert offsets (exclusive scan over experts) and the block map.
+// Expert offsets (exclusive scan over experts) and the block map.  Tiles are listed
+// full ones first (in expert order), then every expert's partial last tile, then the
+// shared expert's tiles, so that the grouped GEMM meets the heavy tiles first.
 __global__ __launch_bounds__(256) void k_tiles(const int32_t *__restrict__ counts,
                                                int32_t *__restrict__ expert_off,
                                                Tile *__restrict__ tiles, int32_t *__restrict__ ntiles,
                                                int E, int64_t T, int K, int shared) {
-    __shared__ int wsum[2][4];
+    __shared__ int wsum[3][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = tid < E ? counts[tid] : 0;
-    const int nt = (n + GEMM_BM - 1) / GEMM_BM;
-    int in = n, it = nt;
+    const int nf = n / GEMM_BM, np = (n % GEMM_BM) ? 1 : 0;
+    int in = n, itf = nf, itp = np;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const int o1 = __shfl_up(in, off, 64), o2 = __shfl_up(it, off, 64);
-        if (lane >= off) { in += o1; it += o2; }
+        const int o1 = __shfl_up(in, off, 64), o2 = __shfl_up(itf, off, 64), o3 = __shfl_up(itp, off, 64);
+        if (lane >= off) { in += o1; itf += o2; itp += o3; }
     }
-    if (lane == 63) { wsum[0][wave] = in; wsum[1][wave] = it; }
+    if (lane == 63) { wsum[0][wave] = in; wsum[1][wave] = itf; wsum[2][wave] = itp; }
     __syncthreads();
-    int bn = 0, bt = 0;
-    for (int w = 0; w < wave; ++w) { bn += wsum[0][w]; bt += wsum[1][w]; }
-    const int off = bn + in - n, toff = bt + it - nt;
+    int bn = 0, bf = 0, bp = 0;
+    for (int w = 0; w < wave; ++w) { bn += wsum[0][w]; bf += wsum[1][w]; bp += wsum[2][w]; }
+    const int nfull = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
+    const int npart = wsum[2][0] + wsum[2][1] + wsum[2][2] + wsum[2][3];
+    const int off = bn + in - n, foff = bf + itf - nf, poff = nfull + bp + itp - np;
     if (tid < E) expert_off[tid] = off;
     if (tid == E - 1) expert_off[E] = off + n;
-    for (int m = 0; m < nt; ++m) {
+    for (int m = 0; m < nf; ++m) {
         Tile t;
         t.expert = tid;
         t.row0 = off + m * GEMM_BM;
-        t.nrows = min(GEMM_BM, n - m * GEMM_BM);
+        t.nrows = GEMM_BM;
         t.pad = 0;
-        tiles[toff + m] = t;
+        tiles[foff + m] = t;
     }
-    const int routed = wsum[1][0] + wsum[1][1] + wsum[1][2] + wsum[1][3];
+    if (np) {
+        Tile t;
+        t.expert = tid;
+        t.row0 = off + nf * GEMM_BM;
+        t.nrows = n - nf * GEMM_BM;
+        t.pad = 0;
+        tiles[poff] = t;
+    }
+    const int routed = nfull + npart;
     const int nsh = shared ? (int)((T + GEMM_BM - 1) / GEMM_BM) : 0;
     for (int m = tid; m < nsh; m += 256) {
         Tile t;

@@ -1,29 +1,41 @@
 // gemm.hip -- grouped expert GEMMs of the prefill path on MFMA (gfx950).
 //
 // [LILY] "Dequantize weights during matrix multiplication": the quantized weights are
-// never expanded in memory; each workgroup dequantizes the small weight tile it is
-// about to multiply, straight into MFMA operand registers, with fp32 accumulation.
+// never expanded in memory; each workgroup dequantizes the weight tile it is about to
+// multiply, straight into MFMA operand registers, with fp32 accumulation.
 // [LILY] "Keep expert routing on the GPU" / "Match tile size to expert load": work is
-// enumerated as (expert row block, column block) items from the device-side block map.
-// [OMLX] "Fusion principle": gate and up rows of one expert are handled by the same
-// wave, so SwiGLU is formed in registers and only h leaves the kernel.
+// enumerated as (expert row block, column block) items from the device-side block map;
+// a partial row block skips its empty 16-row MFMA subtiles.
+// [OMLX] "Fusion principle": gate row j and up row j of one expert are handled by the
+// same wave, so SwiGLU is formed in registers and only h leaves the kernel.
 //
-// Operands: activations fp16 (x copy from the router, h from the gate/up kernel), with
-// each group of 8 columns permuted into the code order (see common.h); weights fp16
-// w = fma(s, q, b) with q recovered exactly from the codes by the 1024-magic; MFMA
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  (fp16 rather than bf16 operands:
-// at these sizes weights rounded to bf16 leave ~2e-2 x RMS of error in the layer
-// output, fp16 ~2e-3; the matrix rate is the same.)
+// Tile: 128 activation rows x 256 weight rows, K step 64 (one quantization group), four
+// waves, each owning 64 weight rows (four 16-row MFMA subtiles) against all 128 rows
+// (eight subtiles): 32 v_mfma_f32_16x16x32_f16 per 32-wide K slice.
 //
-// Workgroup = 4 waves, tile = GEMM_BM rows x (4 waves x 64 weight rows).  Lane l of a
-// wave owns weight row (l % 16) of each 16-row subtile and columns [32c, 32c+32) of each
-// 128-column K step (c = l / 16); the MFMA K slots of lane group c are those columns in
-// code order, which the LDS activation tile mirrors.
+// Data movement: every operand of a K step -- the activation rows (fp16), the weight
+// codes, scales and biases -- goes global -> LDS by direct-to-LDS loads
+// (global_load_lds), which take no registers and no ALU.  A ring of stages keeps two K
+// steps in flight (one for 8-bit codes, whose stages are larger) while the current
+// one is multiplied; each wave waits only for its own loads (vmcnt) and one barrier
+// per step publishes the stage to the whole workgroup.  The position of each 16-byte
+// chunk in LDS is XOR-swizzled by row so that the MFMA operand reads are free of bank
+// conflicts (direct-to-LDS loads place lane l at byte 16 l, so the swizzle is chosen
+// by which global chunk each lane fetches).
+//
+// Operands: activations fp16 (x copy from the router, h from the gate/up pass) with
+// each group of 8 columns permuted into the order the packed codes unpack in (see
+// common.h); weights fp16 w = fma(s, q, b) with q recovered exactly from the codes by
+// the 1024-magic.  (fp16 rather than bf16 operands: at these sizes weights rounded to
+// bf16 leave ~2e-2 x RMS of error in the layer output, fp16 ~2e-3; the matrix rate is
+// the same.)
 //
 // Modes: 0 = [gate; up] + SwiGLU -> h (routed rows gathered through perm, shared rows
 // direct); 1 = routed down projection -> slot[t, j] = w_tj * o (fp16); 2 = shared down
 // projection whose epilogue adds the k slots of the token in ascending expert order and
-// writes y: a deterministic, atomic-free combine.
+// then the shared result, and writes y: a deterministic, atomic-free combine.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -31,10 +43,23 @@ namespace qs {
 
 namespace {
 
-constexpr int MT = GEMM_MT;
-constexpr int BM = GEMM_BM;
-constexpr int KT = 128;              // K step
-constexpr int APITCH = KT + 8;       // fp16 per LDS row (272 bytes)
+constexpr int BM = GEMM_BM;          // activation rows per tile
+constexpr int MT = BM / 16;          // 16-row subtiles
+constexpr int BN = 256;              // weight rows per workgroup
+constexpr int BK = 64;               // K step
+constexpr int NT = 256;              // threads (4 waves)
+
+template <int BITS>
+struct Cfg {
+    static constexpr int A_BYTES = BM * BK * 2;               // fp16 rows, 128 B each
+    static constexpr int B_BYTES = BN * BK * BITS / 8;        // codes, 32 or 64 B per row
+    static constexpr int S_BYTES = BN * 4;                    // one dword per row (fp16 in the low half)
+    static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
+    static constexpr int NSTAGE = BITS == 4 ? 3 : 2;
+    static constexpr int B_DMA = B_BYTES / 1024 / 4;          // per wave and stage
+    static constexpr int DMA = 4 + B_DMA + 2;                 // A, codes, scales, biases
+    static constexpr int LDS = NSTAGE * STAGE;
+};
 
 struct GemmArgs {
     Layer L;
@@ -51,22 +76,38 @@ struct GemmArgs {
     int nb;                          // column blocks per tile
 };
 
+typedef __attribute__((address_space(3))) void lds_t;
+
+__device__ __forceinline__ void dma16(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma2(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 2, 0, 0);   // lands zero-extended in a dword
+}
+// this wave's direct-to-LDS loads: all but the most recent N have landed
+template <int N>
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// the workgroup's LDS reads issued so far are complete and every wave has arrived
+__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// order this wave's own LDS writes before its later LDS reads (no cross-wave effect)
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// 8 codes of one lane and K slice as MFMA operand: w = fma(q, s, b), q exact
 template <int BITS>
-__device__ __forceinline__ f16x8 dequant_step(const u32x4 &c0, const u32x4 &c1, int s, f16x2 sc, f16x2 bi) {
+__device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f16x2 bi) {
     uint32_t m[4];
     if constexpr (BITS == 4) {
-        magic_u4(c0[s], m);
+        magic_u4(w0, m);
     } else {
-        const u32x4 &c = (s < 2) ? c0 : c1;
-        magic_u8(c[(2 * s) & 3], m);
-        magic_u8(c[(2 * s + 1) & 3], m + 2);
+        magic_u8(w0, m);
+        magic_u8(w1, m + 2);
     }
-    f16x8 out;
     const f16x2 k1024 = (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
+    f16x8 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const f16x2 q = as_h2(m[i]) - k1024;   // exact
-        const f16x2 v = __builtin_elementwise_fma(q, sc, bi);       // one rounding
+        const f16x2 q = as_h2(m[i]) - k1024;
+        const f16x2 v = __builtin_elementwise_fma(q, sc, bi);
         out[2 * i] = v[0];
         out[2 * i + 1] = v[1];
     }
@@ -74,68 +115,109 @@ __device__ __forceinline__ f16x8 dequant_step(const u32x4 &c0, const u32x4 &c1, 
 }
 
 template <int BITS, int MODE>
-__global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * APITCH];
+__global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
+    using C = Cfg<BITS>;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
     const Layer &L = a.L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    const int ti = lid / a.nb, nbi = lid % a.nb;
-    int tcount, tbase;
-    if (MODE == 0) { tbase = 0; tcount = a.ntiles[1]; }
-    else if (MODE == 1) { tbase = 0; tcount = a.ntiles[0]; }
-    else { tbase = a.ntiles[0]; tcount = a.ntiles[1] - a.ntiles[0]; }
-    if (ti >= tcount) return;
-    const Tile tile = a.tiles[tbase + ti];
+
+    // ---- which tile and column block: the nb column blocks of a tile (which share its
+    // activation rows) run on one XCD; consecutive tiles go round the XCDs in list order
+    const int xcd = blockIdx.x & 7, bslot = blockIdx.x >> 3;
+    const int ti = (bslot / a.nb) * 8 + xcd, nbi = bslot % a.nb;
+    const int nrt = a.ntiles[0], nsh = a.ntiles[1] - nrt;
+    int tix;
+    if (MODE == 0) {
+        if (ti >= nrt + nsh) return;
+        tix = ti < nsh ? nrt + ti : ti - nsh;          // shared (full) tiles first
+    } else if (MODE == 1) {
+        if (ti >= nrt) return;
+        tix = ti;
+    } else {
+        if (ti >= nsh) return;
+        tix = nrt + ti;
+    }
+    const Tile tile = a.tiles[tix];
     const int E = L.E, K = L.K, H = L.H, I = L.I;
     const bool shared = tile.expert == E;
     const int64_t e = shared ? 0 : tile.expert;
     const int Kdim = (MODE == 0) ? H : I;
+    const int nk = Kdim / BK;
     const int64_t TK = a.T * K;
+    const int nrows = tile.nrows;
+    const int msub = (nrows + 15) >> 4;
 
-    // ---- weight rows of this lane (4 subtiles)
-    const int n16 = lane & 15, cgrp = lane >> 4;
-    const int row_bytes = Kdim * BITS / 8;
-    int wrow[4];
-    bool wvalid[4];
-    const uint8_t *wcodes[4];
-    const uint16_t *wsc[4], *wbi[4];
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-        QMat m;
+    // ---- weight row of workgroup row slot rs (0..255)
+    auto wrow = [&](int rs, QMat &m) -> int {
         if (MODE == 0) {
-            wrow[sub] = nbi * 128 + wave * 32 + (sub & 1) * 16 + n16;
-            wvalid[sub] = true;                               // I % 128 == 0
-            m = (sub < 2) ? (shared ? L.s_gate : L.gate) : (shared ? L.s_up : L.up);
-        } else {
-            const int col = nbi * 256 + wave * 64 + sub * 16 + n16;
-            wvalid[sub] = col < H;
-            wrow[sub] = wvalid[sub] ? col : H - 1;
-            m = shared ? L.s_down : L.down;
+            const int j = (rs >> 4) & 3;
+            m = (j < 2) ? (shared ? L.s_gate : L.gate) : (shared ? L.s_up : L.up);
+            return nbi * 128 + (rs >> 6) * 32 + (j & 1) * 16 + (rs & 15);
         }
-        const int64_t R = e * m.stride + wrow[sub];
-        wcodes[sub] = m.codes + R * row_bytes;
-        wsc[sub] = m.scales + R * (Kdim / 64);
-        wbi[sub] = m.biases + R * (Kdim / 64);
-    }
+        m = shared ? L.s_down : L.down;
+        const int col = nbi * BN + rs;
+        return col < H ? col : H - 1;
+    };
+    const int row_bytes = Kdim * BITS / 8;
+    const int ngrp = Kdim / 64;
 
-    // ---- activation rows staged by this thread: rows tid/16 + 16 i, chunk tid % 16
-    const int arow0 = tid >> 4, achunk = tid & 15;
-    int64_t asrc[MT];
+    // ---- per-lane sources of the direct-to-LDS loads
+    const uint16_t *asrc[4];
+    {
+        const int ach = (lane & 7) ^ (lane >> 3);      // swizzled chunk this lane fetches
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int r = arow0 + 16 * i;
-        int64_t src = -1;
-        if (r < tile.nrows) {
+        for (int i = 0; i < 4; ++i) {
+            int r = 32 * wave + 8 * i + (lane >> 3);
+            r = r < nrows ? r : nrows - 1;             // rows past the tile repeat a valid one
+            int64_t src;
             if (MODE == 0) {
                 const int64_t t = shared ? (tile.row0 - TK + r) : (a.perm[tile.row0 + r] / K);
                 src = t * H;
+                asrc[i] = a.x16 + src + 8 * ach;
             } else {
                 src = (int64_t)(tile.row0 + r) * I;
+                asrc[i] = a.h + src + 8 * ach;
             }
         }
-        asrc[i] = src;
     }
-    const uint16_t *abase = (MODE == 0) ? a.x16 : a.h;
+    const uint8_t *bsrc[C::B_DMA];
+#pragma unroll
+    for (int d = 0; d < C::B_DMA; ++d) {
+        QMat m;
+        if constexpr (BITS == 4) {
+            const int rs = 64 * wave + 32 * d + (lane >> 1);
+            const int hsel = (lane & 1) ^ ((rs >> 2) & 1);
+            const int r = wrow(rs, m);
+            bsrc[d] = m.codes + (e * m.stride + r) * row_bytes + 16 * hsel;
+        } else {
+            const int rs = 64 * wave + 16 * d + (lane >> 2);
+            const int q = (lane & 3) ^ ((rs >> 1) & 3);
+            const int r = wrow(rs, m);
+            bsrc[d] = m.codes + (e * m.stride + r) * row_bytes + 16 * q;
+        }
+    }
+    const uint16_t *ssrc, *bisrc;
+    {
+        QMat m;
+        const int r = wrow(64 * wave + lane, m);
+        ssrc = m.scales + (e * m.stride + r) * ngrp;
+        bisrc = m.biases + (e * m.stride + r) * ngrp;
+    }
+
+    auto issue = [&](int k) {
+        uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(asrc[i] + k * BK, st + (32 * wave + 8 * i) * 128);
+        uint8_t *bst = st + C::A_BYTES;
+#pragma unroll
+        for (int d = 0; d < C::B_DMA; ++d) {
+            if constexpr (BITS == 4) dma16(bsrc[d] + k * 32, bst + (64 * wave + 32 * d) * 32);
+            else dma16(bsrc[d] + k * 64, bst + (64 * wave + 16 * d) * 64);
+        }
+        uint8_t *sst = bst + C::B_BYTES;
+        dma2(ssrc + k, sst + 64 * wave * 4);
+        dma2(bisrc + k, sst + C::S_BYTES + 64 * wave * 4);
+    };
 
     f32x4 acc[MT][4];
 #pragma unroll
@@ -143,102 +225,165 @@ __global__ __launch_bounds__(256, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[i][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    for (int kt = 0; kt < Kdim; kt += KT) {
-        // weight codes, scales and biases of this K step (issued first: longest latency)
-        u32x4 c0[4], c1[4];
-        f16x2 sc[4], bi[4];
-        const int kc = kt + 32 * cgrp;
+    const int n16 = lane & 15, cg = lane >> 4;
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub) {
-            const uint8_t *p = wcodes[sub] + kc * BITS / 8;
-            c0[sub] = __builtin_nontemporal_load((const u32x4 *)p);
-            if (BITS == 8) c1[sub] = __builtin_nontemporal_load((const u32x4 *)(p + 16));
-            else c1[sub] = c0[sub];
-            const uint16_t s16 = wsc[sub][kc >> 6], b16 = wbi[sub][kc >> 6];
-            const _Float16 sv = __builtin_bit_cast(_Float16, s16), bv = __builtin_bit_cast(_Float16, b16);
-            sc[sub] = (f16x2){sv, sv};
-            bi[sub] = (f16x2){bv, bv};
-        }
-        // activation tile -> LDS
+    for (int p = 0; p < C::NSTAGE - 1; ++p)
+        if (p < nk) issue(p);
+
+    // the K loop; FULL: all eight row subtiles live (no per-subtile branches, so every
+    // operand read of a K slice is issued ahead of its MFMAs)
+    auto kloop = [&](auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        for (int k = 0; k < nk; ++k) {
+            // stage k has landed once at most the later stages' loads are outstanding
+            if (C::NSTAGE == 3 && k + 1 < nk) wait_dma<C::DMA>();
+            else wait_dma<0>();
+            block_sync();             // stage k visible; stage k-1 fully consumed
+            if (k + C::NSTAGE - 1 < nk) issue(k + C::NSTAGE - 1);
+
+            const uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
+            const uint8_t *bst = st + C::A_BYTES;
+            const uint32_t *sst = (const uint32_t *)(bst + C::B_BYTES);
+            uint32_t cw[4][4];
+            f16x2 sc[4], bi[4];
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-            if (asrc[i] >= 0) v = *(const u32x4 *)(abase + asrc[i] + kt + achunk * 8);
-            *(u32x4 *)(As + (arow0 + 16 * i) * APITCH + achunk * 8) = v;
-        }
-        __syncthreads();
+            for (int j = 0; j < 4; ++j) {
+                const int rs = 64 * wave + 16 * j + n16;
+                if constexpr (BITS == 4) {
+                    const int hsel = (cg >> 1) ^ ((rs >> 2) & 1);
+                    const uint32_t *p = (const uint32_t *)(bst + rs * 32 + hsel * 16 + (cg & 1) * 8);
+                    cw[j][0] = p[0];
+                    cw[j][1] = p[1];
+                } else {
+                    const int q = cg ^ ((rs >> 1) & 3);
+                    const u32x4 v = *(const u32x4 *)(bst + rs * 64 + q * 16);
+                    cw[j][0] = v[0];
+                    cw[j][1] = v[1];
+                    cw[j][2] = v[2];
+                    cw[j][3] = v[3];
+                }
+                const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sst[rs]);
+                const _Float16 b = __builtin_bit_cast(_Float16, (uint16_t)sst[BN + rs]);
+                sc[j] = (f16x2){s, s};
+                bi[j] = (f16x2){b, b};
+            }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            f16x8 B[4];
+            for (int s = 0; s < 2; ++s) {
+                const int pos = (2 * cg + s) ^ (n16 & 7);
+                f16x8 A[MT];
 #pragma unroll
-            for (int sub = 0; sub < 4; ++sub) B[sub] = dequant_step<BITS>(c0[sub], c1[sub], s, sc[sub], bi[sub]);
+                for (int i = 0; i < MT; ++i)
+                    if (FULL || i < msub) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
+                f16x8 B[4];
 #pragma unroll
-            for (int i = 0; i < MT; ++i) {
-                const f16x8 A = *(const f16x8 *)(As + (i * 16 + n16) * APITCH + 32 * cgrp + 8 * s);
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BITS == 4) B[j] = dequant8<4>(cw[j][s], 0u, sc[j], bi[j]);
+                    else B[j] = dequant8<8>(cw[j][2 * s], cw[j][2 * s + 1], sc[j], bi[j]);
+                }
 #pragma unroll
-                for (int sub = 0; sub < 4; ++sub)
-                    acc[i][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B[sub], acc[i][sub], 0, 0, 0);
+                for (int i = 0; i < MT; ++i)
+                    if (FULL || i < msub)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], B[j], acc[i][j], 0, 0, 0);
             }
         }
-        __syncthreads();
-    }
+    };
+    if (msub == MT) kloop(std::true_type{});
+    else kloop(std::false_type{});
+    block_sync();                     // the ring is free: epilogues stage through it
 
-    // ---- epilogues.  acc[i][sub][r]: row i*16 + 4*cgrp + r, weight row wrow[sub]
+    // ---- epilogues.  acc[i][j][r]: tile row i*16 + 4*cg + r, weight row slot 64*wave + 16*j + n16
     if (MODE == 0) {
-        uint16_t *hout = a.h;
+        constexpr int HP = 40;                                   // fp16 per staged row
+        uint16_t *hs = (uint16_t *)(smem + wave * (BM * HP * 2));
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int i = 0; i < MT; ++i) {
+            if (i < msub) {
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-                const int hcol = wrow[sub];
-                const int pcol = (hcol & ~7) | perm_pos<BITS>(hcol & 7);
+                for (int j = 0; j < 2; ++j) {
+                    const int col = j * 16 + n16;
+                    const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = i * 16 + 4 * cgrp + r;
-                    if (row < tile.nrows) {
-                        const float hv = silu(acc[i][sub][r]) * acc[i][sub + 2][r];
-                        hout[(int64_t)(tile.row0 + row) * I + pcol] =
-                            __builtin_bit_cast(uint16_t, f32_to_f16_ftz(hv));
+                    for (int r = 0; r < 4; ++r) {
+                        const float hv = silu(acc[i][j][r]) * acc[i][j + 2][r];
+                        hs[(i * 16 + 4 * cg + r) * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(hv));
                     }
                 }
             }
-    } else if (MODE == 1) {
+        }
+        wave_lds_sync();
+        const int chunk = lane & 3;
+        uint16_t *hout = a.h + (int64_t)tile.row0 * I + nbi * 128 + wave * 32 + chunk * 8;
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+        for (int q = 0; q < BM / 16; ++q) {
+            const int row = (lane >> 2) + 16 * q;
+            if (row < nrows) *(u32x4 *)(hout + (int64_t)row * I) = *(const u32x4 *)(hs + row * HP + chunk * 8);
+        }
+        return;
+    }
+
+    // MODE 1 / 2: 32 rows at a time through a per-wave fp32 staging area
+    const int colbase = nbi * BN + wave * 64;
+    if (colbase >= H) return;                                    // columns past H (H % 256 == 128)
+    constexpr int FP = 68;                                       // floats per staged row
+    float *fs = (float *)(smem + wave * (32 * FP * 4));
+    const int chunk = lane & 7;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = i * 16 + 4 * cgrp + r;
-                if (row < tile.nrows) {
+    for (int hp = 0; hp < MT / 2; ++hp) {
+        if (32 * hp >= nrows) break;
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fs[(ii * 16 + 4 * cg + r) * FP + j * 16 + n16] = acc[2 * hp + ii][j][r];
+        wave_lds_sync();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rr = (lane >> 3) + 8 * q, row = 32 * hp + rr;
+            if (row < nrows) {
+                const f32x4 v0 = *(const f32x4 *)(fs + rr * FP + chunk * 8);
+                const f32x4 v1 = *(const f32x4 *)(fs + rr * FP + chunk * 8 + 4);
+                float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const int col = colbase + chunk * 8;
+                if (MODE == 1) {
                     const int64_t p = a.perm[tile.row0 + row];
                     const float wv = a.w[p];
+                    u32x4 o;
 #pragma unroll
-                    for (int sub = 0; sub < 4; ++sub)
-                        if (wvalid[sub])
-                            a.slot[p * H + wrow[sub]] =
-                                __builtin_bit_cast(uint16_t, (_Float16)(acc[i][sub][r] * wv));
-                }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < MT; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = i * 16 + 4 * cgrp + r;
-                if (row < tile.nrows) {
+                    for (int c = 0; c < 4; ++c)
+                        o[c] = pack_f16x2((_Float16)(v[2 * c] * wv), (_Float16)(v[2 * c + 1] * wv));
+                    *(u32x4 *)(a.slot + p * H + col) = o;
+                } else {
                     const int64_t t = tile.row0 - TK + row;
+                    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    for (int j = 0; j < K; ++j) {                // ascending expert id
+                        const u32x4 sv = *(const u32x4 *)(a.slot + (t * K + j) * H + col);
 #pragma unroll
-                    for (int sub = 0; sub < 4; ++sub)
-                        if (wvalid[sub]) {
-                            const int col = wrow[sub];
-                            float sum = 0.0f;
-                            for (int j = 0; j < K; ++j)             // ascending expert id
-                                sum += f16_to_f32(a.slot[(t * K + j) * H + col]);
-                            sum += acc[i][sub][r];                    // shared expert last
-                            if (a.y_dtype == QSMOE_F32) ((float *)a.y)[t * H + col] = sum;
-                            else ((uint16_t *)a.y)[t * H + col] = f32_to_bf16(sum);
+                        for (int c = 0; c < 4; ++c) {
+                            const f16x2 h2 = as_h2(sv[c]);
+                            sum[2 * c] += (float)h2[0];
+                            sum[2 * c + 1] += (float)h2[1];
                         }
+                    }
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) sum[c] += v[c];  // shared expert last
+                    if (a.y_dtype == QSMOE_F32) {
+                        float *yp = (float *)a.y + t * H + col;
+                        *(f32x4 *)yp = (f32x4){sum[0], sum[1], sum[2], sum[3]};
+                        *(f32x4 *)(yp + 4) = (f32x4){sum[4], sum[5], sum[6], sum[7]};
+                    } else {
+                        u32x4 o;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            o[c] = (uint32_t)f32_to_bf16(sum[2 * c]) | ((uint32_t)f32_to_bf16(sum[2 * c + 1]) << 16);
+                        *(u32x4 *)((uint16_t *)a.y + t * H + col) = o;
+                    }
                 }
             }
+        }
+        wave_lds_sync();
     }
 }
 
@@ -254,7 +399,11 @@ __global__ __launch_bounds__(256) void k_combine_routed(const uint16_t *__restri
     else ((uint16_t *)y)[i] = f32_to_bf16(sum);
 }
 
-inline int round8(int64_t n) { return (int)(((n + 7) / 8) * 8); }
+// workgroups for `tiles` tiles of nb column blocks: a multiple of 8 * nb (see k_gemm)
+inline unsigned grid_for(int64_t tiles, int nb) {
+    const int64_t per = 8 * (int64_t)nb;
+    return (unsigned)(((tiles + 7) / 8) * per);
+}
 
 template <int BITS>
 hipError_t gemms(GemmArgs a, hipStream_t s) {
@@ -263,12 +412,12 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
     const int64_t maxs = L.has_shared ? (a.T + GEMM_BM - 1) / GEMM_BM : 0;
     // [gate; up] + SwiGLU over routed and shared tiles
     a.nb = L.I / 128;
-    hipLaunchKernelGGL((k_gemm<BITS, 0>), dim3(round8((maxr + maxs) * a.nb)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<BITS, 0>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
     // routed down -> slots
-    a.nb = (L.H + 255) / 256;
-    hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(round8(maxr * a.nb)), dim3(256), 0, s, a);
+    a.nb = (L.H + BN - 1) / BN;
+    hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr, a.nb)), dim3(NT), 0, s, a);
     if (L.has_shared) {
-        hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(round8(maxs * a.nb)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(grid_for(maxs, a.nb)), dim3(NT), 0, s, a);
     } else {
         const int64_t n = a.T * L.H;
         hipLaunchKernelGGL(k_combine_routed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,

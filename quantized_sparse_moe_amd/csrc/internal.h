@@ -41,8 +41,8 @@ hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBu
                                int32_t *out_idx, float *out_w, hipStream_t s);
 
 // ------------------------------------------------------------------- prefill T >= 2
-constexpr int ROUTER_TOKENS = 32;  // tokens per router workgroup (= one binning block)
-constexpr int GEMM_MT = 4;         // 16-row MFMA subtiles per GEMM tile
+constexpr int ROUTER_TOKENS = 16;  // tokens per router workgroup (= one binning block)
+constexpr int GEMM_MT = 8;         // 16-row MFMA subtiles per GEMM tile
 constexpr int GEMM_BM = 16 * GEMM_MT;
 
 struct Tile {                      // one row block of one expert bin
@@ -60,7 +60,7 @@ struct PrefillBufs {
     int32_t *blkoff;               // [nblk][E]  first position of that block's rows in the expert bin
     int32_t *expert_off;           // [E+1]
     int32_t *perm;                 // [T*K]      position -> t*K + j
-    Tile *tiles;                   // [max_tiles]
+    Tile *tiles;                   // [max_tiles] routed full, routed partial, then shared tiles
     int32_t *ntiles;               // [2] routed tiles, routed + shared tiles
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
     uint16_t *slot;                // [T*K][H] fp16: w_j * o_j

@@ -2,12 +2,12 @@
 //
 // [LILY] "Qwen creates three distinct workload shapes": a router scores 256 experts and
 // picks eight per token.  [LILY] "Keep expert routing on the GPU": after the choice a
-// histogram counts the assignments of every expert; here each 32-token workgroup writes
+// histogram counts the assignments of every expert; here each 16-token workgroup writes
 // the counts of its block, which the binning pass turns into offsets.
 //
 // Logits are a dense [T x H] x [H x E] contraction: bf16 activations against bf16
 // router weights on MFMA (v_mfma_f32_16x16x32_bf16, exact products, fp32 accumulation).
-// A workgroup owns 32 tokens and all experts (each wave 64 of them), so the top-k of a
+// A workgroup owns 16 tokens and all experts (each wave 64 of them), so the top-k of a
 // token is taken straight from LDS.  The same pass writes an fp16 copy of x with each
 // group of 8 columns permuted into the code order used by the expert GEMMs.
 #include "common.h"
@@ -17,9 +17,10 @@ namespace qs {
 
 namespace {
 
-constexpr int RT = ROUTER_TOKENS;   // tokens per workgroup
-constexpr int RKT = 256;            // K tile (columns of x staged per step)
-constexpr int RPITCH = RKT + 8;     // bf16 elements per LDS row (breaks bank alignment)
+constexpr int RT = ROUTER_TOKENS;   // tokens per workgroup (one 16-row MFMA subtile)
+constexpr int RKC = 1024;           // columns of x staged per chunk
+constexpr int RPITCH = RKC + 8;     // bf16 elements per LDS row (breaks bank alignment)
+constexpr int RU = 4;               // 32-column K slices whose weight loads are in flight together
 
 struct RouterArgs {
     Layer L;
@@ -33,6 +34,10 @@ struct RouterArgs {
     float *out_w;
 };
 
+// One workgroup = RT tokens x all experts; wave w owns experts 64w .. 64w+63.  x is
+// staged a chunk of RKC columns at a time with every load of the chunk in flight at
+// once (the fp16 copy for the expert GEMMs is written from the same registers); router
+// weights stream from L2 straight into MFMA operands, RU K slices per batch of loads.
 template <int BITS>
 __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xa[RT * RPITCH];
@@ -42,67 +47,78 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * RT;
     const int H = L.H, E = L.E;
+    const int n16 = lane & 15, cg = lane >> 4;
 
-    f32x4 acc[2][4];
+    f32x4 acc[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int n = 0; n < 4; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const uint16_t *wrow[4];
+    bool wlive[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 4; ++n) {
+        const int e = wave * 64 + n * 16 + n16;
+        wlive[n] = e < E;
+        wrow[n] = L.router_w + (int64_t)(wlive[n] ? e : 0) * H + 8 * cg;
+    }
 
-    for (int kt = 0; kt < H; kt += RKT) {
-        const int kw = (H - kt) < RKT ? (H - kt) : RKT;     // H % 128 == 0
-        for (int q = tid; q < RT * (RKT / 8); q += 256) {
-            const int r = q / (RKT / 8), cc = q % (RKT / 8);
+    for (int kc = 0; kc < H; kc += RKC) {
+        const int kw = (H - kc) < RKC ? (H - kc) : RKC;          // multiple of 128
+        // stage: RT rows x kw columns, 16 bytes per item, all loads first
+        constexpr int PER = RT * RKC / 8 / 256;                    // items per thread (8)
+        u32x4 v[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int q = tid + 256 * i, r = q / (RKC / 8), cc = q % (RKC / 8);
             const int64_t t = t0 + r;
-            u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-            if (t < a.T && cc * 8 < kw) {
-                v = *(const u32x4 *)(a.x + t * H + kt + cc * 8);
-                if (a.x16) {
-                    u32x4 h;
+            v[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (t < a.T && cc * 8 < kw) v[i] = *(const u32x4 *)(a.x + t * H + kc + cc * 8);
+        }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        h[i] = pack_f16x2(f32_to_f16_ftz(__uint_as_float(v[i] << 16)),
-                                          f32_to_f16_ftz(__uint_as_float(v[i] & 0xffff0000u)));
-                    *(u32x4 *)(a.x16 + t * H + kt + cc * 8) = perm8<BITS>(h);
-                }
+        for (int i = 0; i < PER; ++i) {
+            const int q = tid + 256 * i, r = q / (RKC / 8), cc = q % (RKC / 8);
+            const int64_t t = t0 + r;
+            *(u32x4 *)(xa + r * RPITCH + cc * 8) = v[i];
+            if (a.x16 && t < a.T && cc * 8 < kw) {
+                u32x4 h;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    h[c] = pack_f16x2(f32_to_f16_ftz(__uint_as_float(v[i][c] << 16)),
+                                      f32_to_f16_ftz(__uint_as_float(v[i][c] & 0xffff0000u)));
+                *(u32x4 *)(a.x16 + t * H + kc + cc * 8) = perm8<BITS>(h);
             }
-            *(u32x4 *)(xa + r * RPITCH + cc * 8) = v;
         }
         __syncthreads();
-        for (int s = 0; s < kw / 32; ++s) {
-            bf16x8 A[2];
+        for (int s0 = 0; s0 < kw / 32; s0 += RU) {
+            bf16x8 B[RU][4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                A[i] = *(const bf16x8 *)(xa + (i * 16 + (lane & 15)) * RPITCH + s * 32 + 8 * (lane >> 4));
+            for (int u = 0; u < RU; ++u)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int e = wave * 64 + n * 16 + (lane & 15);
-                bf16x8 B;
-                if (e < E)
-                    B = *(const bf16x8 *)(L.router_w + (int64_t)e * H + kt + s * 32 + 8 * (lane >> 4));
-                else
-                    B = (bf16x8){};
+                for (int n = 0; n < 4; ++n) {
+                    const int col = kc + (s0 + u) * 32;
+                    B[u][n] = (s0 + u < kw / 32) ? *(const bf16x8 *)(wrow[n] + col) : (bf16x8){};
+                }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[i], B, acc[i][n], 0, 0, 0);
+            for (int u = 0; u < RU; ++u) {
+                if (s0 + u < kw / 32) {
+                    const bf16x8 A = *(const bf16x8 *)(xa + n16 * RPITCH + (s0 + u) * 32 + 8 * cg);
+#pragma unroll
+                    for (int n = 0; n < 4; ++n)
+                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlive[n] ? B[u][n] : (bf16x8){}, acc[n], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
     }
-    // logits -> LDS (+ bias)
+    // logits -> LDS (+ bias).  acc[n][r]: token 4*cg + r, expert 64*wave + 16*n + n16
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int n = 0; n < 4; ++n) {
+        const int e = wave * 64 + n * 16 + n16;
+        const float bias = (e < E && L.router_bias) ? L.router_bias[e] : 0.0f;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int e = wave * 64 + n * 16 + (lane & 15);
-            const float bias = (e < E && L.router_bias) ? L.router_bias[e] : 0.0f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = i * 16 + 4 * (lane >> 4) + r;
-                if (e < E) lg[row * 257 + e] = acc[i][n][r] + bias;
-            }
-        }
-    for (int e = tid; e < 256; e += 256) hist[e] = 0;
+        for (int r = 0; r < 4; ++r)
+            if (e < E) lg[(4 * cg + r) * 257 + e] = acc[n][r] + bias;
+    }
+    hist[tid] = 0;
     __syncthreads();
     for (int r = wave; r < RT; r += 4) {
         const int64_t t = t0 + r;
