@@ -92,26 +92,47 @@ __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0
 // order this wave's own LDS writes before its later LDS reads (no cross-wave effect)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// 8 codes of one lane and K slice as MFMA operand: w = fma(q, s, b), q exact
+// (x & m) | c in one VALU op (the masks and the magic live in registers)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+    return r;
+}
+
+// 8 codes of one lane and K slice as MFMA operand: w = fma(q, s, b), q exact, in the
+// order [0,4,1,5,2,6,3,7] (4-bit) or [0,2,1,3,4,6,5,7] (8-bit) of the 8 columns.
+// 4-bit: the high nibble of each byte is taken in place (value 16 q, exact in fp16
+// next to the 1024 magic) and paired with s/16, which is exact, so that only one
+// shift is needed per 8 codes; the product (16 q)(s / 16) equals q s exactly, so the
+// result is the same single rounding of q s + b.
+struct DqConst {
+    uint32_t lo, hi, magic;
+};
 template <int BITS>
-__device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f16x2 bi) {
+__device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f16x2 sc16, f16x2 bi,
+                                          const DqConst &k) {
     uint32_t m[4];
     if constexpr (BITS == 4) {
-        magic_u4(w0, m);
+        const uint32_t w8 = w0 >> 8;
+        m[0] = and_or(w0, k.lo, k.magic);
+        m[1] = and_or(w0, k.hi, k.magic);
+        m[2] = and_or(w8, k.lo, k.magic);
+        m[3] = and_or(w8, k.hi, k.magic);
     } else {
-        magic_u8(w0, m);
-        magic_u8(w1, m + 2);
+        m[0] = and_or(w0, k.lo, k.magic);
+        m[1] = and_or(w0 >> 8, k.lo, k.magic);
+        m[2] = and_or(w1, k.lo, k.magic);
+        m[3] = and_or(w1 >> 8, k.lo, k.magic);
     }
     const f16x2 k1024 = (f16x2){(_Float16)1024.0f, (_Float16)1024.0f};
-    f16x8 out;
+    u32x4 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const f16x2 q = as_h2(m[i]) - k1024;
-        const f16x2 v = __builtin_elementwise_fma(q, sc, bi);
-        out[2 * i] = v[0];
-        out[2 * i + 1] = v[1];
+        const f16x2 sv = (BITS == 4 && (i & 1)) ? sc16 : sc;
+        out[i] = __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q, sv, bi));
     }
-    return out;
+    return __builtin_bit_cast(f16x8, out);
 }
 
 template <int BITS, int MODE>
@@ -148,7 +169,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     const int msub = (nrows + 15) >> 4;
 
     // ---- weight row of workgroup row slot rs (0..255)
-    auto wrow = [&](int rs, QMat &m) -> int {
+    auto wrow = [&](int rs, QMat &m) __attribute__((always_inline)) -> int {
         if (MODE == 0) {
             const int j = (rs >> 4) & 3;
             m = (j < 2) ? (shared ? L.s_gate : L.gate) : (shared ? L.s_up : L.up);
@@ -204,7 +225,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         bisrc = m.biases + (e * m.stride + r) * ngrp;
     }
 
-    auto issue = [&](int k) {
+    auto issue = [&](int k) __attribute__((always_inline)) {
         uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16(asrc[i] + k * BK, st + (32 * wave + 8 * i) * 128);
@@ -226,47 +247,75 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         for (int n = 0; n < 4; ++n) acc[i][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     const int n16 = lane & 15, cg = lane >> 4;
-#pragma unroll
-    for (int p = 0; p < C::NSTAGE - 1; ++p)
-        if (p < nk) issue(p);
+    constexpr int CW = BITS == 4 ? 2 : 4;           // code dwords per lane and subtile per K step
 
-    // the K loop; FULL: all eight row subtiles live (no per-subtile branches, so every
-    // operand read of a K slice is issued ahead of its MFMAs)
-    auto kloop = [&](auto full) {
+    // wait until stage `k` has landed: `newer` stages were issued after it
+    auto wait_stage = [&](int newer) __attribute__((always_inline)) {
+        if (newer >= 2) wait_dma<2 * C::DMA>();
+        else if (newer == 1) wait_dma<C::DMA>();
+        else wait_dma<0>();
+    };
+    // operands of K step k from the LDS ring: per weight subtile j, the code dwords of
+    // K slice s of this lane, and the scale and bias
+    auto load_codes = [&](int k, int s, uint32_t (&cw)[4][CW / 2]) __attribute__((always_inline)) {
+        const uint8_t *bst = smem + (k % C::NSTAGE) * C::STAGE + C::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rs = 64 * wave + 16 * j + n16;
+            if constexpr (BITS == 4) {
+                const int hsel = (cg >> 1) ^ ((rs >> 2) & 1);
+                cw[j][0] = *(const uint32_t *)(bst + rs * 32 + hsel * 16 + (cg & 1) * 8 + 4 * s);
+            } else {
+                const int q = cg ^ ((rs >> 1) & 3);
+                const uint32_t *p = (const uint32_t *)(bst + rs * 64 + q * 16 + 8 * s);
+                cw[j][0] = p[0];
+                cw[j][1] = p[1];
+            }
+        }
+    };
+    auto load_sb = [&](int k, f16x2 (&sc)[4], f16x2 (&sc16)[4], f16x2 (&bi)[4]) __attribute__((always_inline)) {
+        const uint32_t *sst = (const uint32_t *)(smem + (k % C::NSTAGE) * C::STAGE + C::A_BYTES + C::B_BYTES);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rs = 64 * wave + 16 * j + n16;
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sst[rs]);
+            const _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)sst[BN + rs]);
+            sc[j] = (f16x2){sv, sv};
+            const _Float16 sv16 = sv * (_Float16)0.0625f;        // exact: scales are normal numbers
+            sc16[j] = (f16x2){sv16, sv16};
+            bi[j] = (f16x2){bv, bv};
+        }
+    };
+    uint32_t cw[4][CW / 2];
+    f16x2 sc[4], sc16[4], bi[4];
+    DqConst dk;
+    dk.lo = BITS == 4 ? 0x000F000Fu : 0x00FF00FFu;
+    dk.hi = 0x00F000F0u;
+    dk.magic = QS_MAGIC;
+    auto deq = [&](const uint32_t (&cw)[4][CW / 2], f16x8 (&B)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (BITS == 4) B[j] = dequant8<4>(cw[j][0], 0u, sc[j], sc16[j], bi[j], dk);
+            else B[j] = dequant8<8>(cw[j][0], cw[j][1], sc[j], sc16[j], bi[j], dk);
+        }
+    };
+
+
+    // The K loop: per 64-wide step, one barrier (stage k visible, stage k-1 consumed),
+    // the refill of stage k-1's buffer with stage k+NSTAGE-1, then two MFMA blocks
+    // (32-wide slices), each on a weight slice dequantized just before it.  FULL: all
+    // eight row subtiles live (no per-subtile branches, so every fragment read of a
+    // block is issued ahead of its MFMAs).
+    auto kloop = [&](auto full) __attribute__((always_inline)) {
         constexpr bool FULL = decltype(full)::value;
         for (int k = 0; k < nk; ++k) {
             // stage k has landed once at most the later stages' loads are outstanding
-            if (C::NSTAGE == 3 && k + 1 < nk) wait_dma<C::DMA>();
-            else wait_dma<0>();
-            block_sync();             // stage k visible; stage k-1 fully consumed
+            const int issued = k + C::NSTAGE - 1 < nk ? C::NSTAGE - 2 : nk - 1 - k;
+            wait_stage(issued < 0 ? 0 : issued);
+            block_sync();
             if (k + C::NSTAGE - 1 < nk) issue(k + C::NSTAGE - 1);
-
             const uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
-            const uint8_t *bst = st + C::A_BYTES;
-            const uint32_t *sst = (const uint32_t *)(bst + C::B_BYTES);
-            uint32_t cw[4][4];
-            f16x2 sc[4], bi[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rs = 64 * wave + 16 * j + n16;
-                if constexpr (BITS == 4) {
-                    const int hsel = (cg >> 1) ^ ((rs >> 2) & 1);
-                    const uint32_t *p = (const uint32_t *)(bst + rs * 32 + hsel * 16 + (cg & 1) * 8);
-                    cw[j][0] = p[0];
-                    cw[j][1] = p[1];
-                } else {
-                    const int q = cg ^ ((rs >> 1) & 3);
-                    const u32x4 v = *(const u32x4 *)(bst + rs * 64 + q * 16);
-                    cw[j][0] = v[0];
-                    cw[j][1] = v[1];
-                    cw[j][2] = v[2];
-                    cw[j][3] = v[3];
-                }
-                const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)sst[rs]);
-                const _Float16 b = __builtin_bit_cast(_Float16, (uint16_t)sst[BN + rs]);
-                sc[j] = (f16x2){s, s};
-                bi[j] = (f16x2){b, b};
-            }
+            load_sb(k, sc, sc16, bi);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int pos = (2 * cg + s) ^ (n16 & 7);
@@ -274,12 +323,9 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
                     if (FULL || i < msub) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
+                load_codes(k, s, cw);
                 f16x8 B[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (BITS == 4) B[j] = dequant8<4>(cw[j][s], 0u, sc[j], bi[j]);
-                    else B[j] = dequant8<8>(cw[j][2 * s], cw[j][2 * s + 1], sc[j], bi[j]);
-                }
+                deq(cw, B);
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
                     if (FULL || i < msub)
@@ -289,8 +335,23 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
             }
         }
     };
+    // MODE 1: the (token, slot) position and routing weight of tile row `tid` (tid < 128)
+    // are fetched now, their latency hidden by the K loop, and parked in LDS after it
+    __shared__ int s_pos[BM];
+    __shared__ float s_w[BM];
+    int my_pos = 0;
+    float my_w = 0.0f;
+    if (MODE == 1 && tid < BM) my_pos = a.perm[tile.row0 + (tid < nrows ? tid : nrows - 1)];
+#pragma unroll
+    for (int p = 0; p < C::NSTAGE - 1; ++p)
+        if (p < nk) issue(p);
+    if (MODE == 1 && tid < BM) my_w = a.w[my_pos];
     if (msub == MT) kloop(std::true_type{});
     else kloop(std::false_type{});
+    if (MODE == 1 && tid < BM) {
+        s_pos[tid] = my_pos;
+        s_w[tid] = my_w;
+    }
     block_sync();                     // the ring is free: epilogues stage through it
 
     // ---- epilogues.  acc[i][j][r]: tile row i*16 + 4*cg + r, weight row slot 64*wave + 16*j + n16
@@ -306,7 +367,8 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
                     const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float hv = silu(acc[i][j][r]) * acc[i][j + 2][r];
+                        const float g = acc[i][j][r];
+                        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[i][j + 2][r];
                         hs[(i * 16 + 4 * cg + r) * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(hv));
                     }
                 }
@@ -323,12 +385,13 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         return;
     }
 
-    // MODE 1 / 2: 32 rows at a time through a per-wave fp32 staging area
+    // MODE 1 / 2: 32 rows at a time through a per-wave fp32 staging area; lane l then
+    // owns row 32*hp + (l % 32) and 32 of the wave's 64 columns
     const int colbase = nbi * BN + wave * 64;
     if (colbase >= H) return;                                    // columns past H (H % 256 == 128)
     constexpr int FP = 68;                                       // floats per staged row
     float *fs = (float *)(smem + wave * (32 * FP * 4));
-    const int chunk = lane & 7;
+    const int er = lane & 31, ecol = colbase + 32 * (lane >> 5);
 #pragma unroll
     for (int hp = 0; hp < MT / 2; ++hp) {
         if (32 * hp >= nrows) break;
@@ -339,46 +402,54 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) fs[(ii * 16 + 4 * cg + r) * FP + j * 16 + n16] = acc[2 * hp + ii][j][r];
         wave_lds_sync();
+        const int row = 32 * hp + er;
+        if (row < nrows) {
+            const float *src = fs + er * FP + 32 * (lane >> 5);
+            if (MODE == 1) {
+                const int64_t p = s_pos[row];
+                const float wv = s_w[row];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rr = (lane >> 3) + 8 * q, row = 32 * hp + rr;
-            if (row < nrows) {
-                const f32x4 v0 = *(const f32x4 *)(fs + rr * FP + chunk * 8);
-                const f32x4 v1 = *(const f32x4 *)(fs + rr * FP + chunk * 8 + 4);
-                float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                const int col = colbase + chunk * 8;
-                if (MODE == 1) {
-                    const int64_t p = a.perm[tile.row0 + row];
-                    const float wv = a.w[p];
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
                     u32x4 o;
+                    o[0] = pack_f16x2((_Float16)(v0[0] * wv), (_Float16)(v0[1] * wv));
+                    o[1] = pack_f16x2((_Float16)(v0[2] * wv), (_Float16)(v0[3] * wv));
+                    o[2] = pack_f16x2((_Float16)(v1[0] * wv), (_Float16)(v1[1] * wv));
+                    o[3] = pack_f16x2((_Float16)(v1[2] * wv), (_Float16)(v1[3] * wv));
+                    *(u32x4 *)(a.slot + p * H + ecol + 8 * c) = o;
+                }
+            } else {
+                const int64_t t = tile.row0 - TK + row;
+                const uint16_t *sp = a.slot + t * K * H + ecol;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        o[c] = pack_f16x2((_Float16)(v[2 * c] * wv), (_Float16)(v[2 * c + 1] * wv));
-                    *(u32x4 *)(a.slot + p * H + col) = o;
-                } else {
-                    const int64_t t = tile.row0 - TK + row;
+                for (int c = 0; c < 4; ++c) {
+                    u32x4 sv[16];                                // the token's k slot rows (k <= 16)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (j < K) sv[j] = *(const u32x4 *)(sp + (int64_t)j * H + 8 * c);
                     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                    for (int j = 0; j < K; ++j) {                // ascending expert id
-                        const u32x4 sv = *(const u32x4 *)(a.slot + (t * K + j) * H + col);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const f16x2 h2 = as_h2(sv[c]);
-                            sum[2 * c] += (float)h2[0];
-                            sum[2 * c + 1] += (float)h2[1];
-                        }
-                    }
+                    for (int j = 0; j < 16; ++j)                 // ascending expert id
+                        if (j < K)
 #pragma unroll
-                    for (int c = 0; c < 8; ++c) sum[c] += v[c];  // shared expert last
+                            for (int q = 0; q < 4; ++q) {
+                                const f16x2 h2 = as_h2(sv[j][q]);
+                                sum[2 * q] += (float)h2[0];
+                                sum[2 * q + 1] += (float)h2[1];
+                            }
+                    const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
+                    sum[0] += v0[0]; sum[1] += v0[1]; sum[2] += v0[2]; sum[3] += v0[3];    // shared expert last
+                    sum[4] += v1[0]; sum[5] += v1[1]; sum[6] += v1[2]; sum[7] += v1[3];
                     if (a.y_dtype == QSMOE_F32) {
-                        float *yp = (float *)a.y + t * H + col;
+                        float *yp = (float *)a.y + t * H + ecol + 8 * c;
                         *(f32x4 *)yp = (f32x4){sum[0], sum[1], sum[2], sum[3]};
                         *(f32x4 *)(yp + 4) = (f32x4){sum[4], sum[5], sum[6], sum[7]};
                     } else {
                         u32x4 o;
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            o[c] = (uint32_t)f32_to_bf16(sum[2 * c]) | ((uint32_t)f32_to_bf16(sum[2 * c + 1]) << 16);
-                        *(u32x4 *)((uint16_t *)a.y + t * H + col) = o;
+                        for (int q = 0; q < 4; ++q)
+                            o[q] = (uint32_t)f32_to_bf16(sum[2 * q]) | ((uint32_t)f32_to_bf16(sum[2 * q + 1]) << 16);
+                        *(u32x4 *)((uint16_t *)a.y + t * H + ecol + 8 * c) = o;
                     }
                 }
             }
