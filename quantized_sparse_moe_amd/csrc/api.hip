@@ -122,7 +122,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     b.tiles = c.take<Tile>((size_t)prefill_max_tiles(T, (int)K, (int)E));
     b.ntiles = c.take<int32_t>(2);
     b.h = c.take<uint16_t>((size_t)((T * K + T) * I));
-    b.slot = c.take<uint16_t>((size_t)(T * K * H));
+    b.slot = c.take<uint16_t>((size_t)((T * K + T) * H));
     *bytes = c.off;
     return b;
 }

@@ -31,9 +31,10 @@
 // the same.)
 //
 // Modes: 0 = [gate; up] + SwiGLU -> h (routed rows gathered through perm, shared rows
-// direct); 1 = routed down projection -> slot[t, j] = w_tj * o (fp16); 2 = shared down
-// projection whose epilogue adds the k slots of the token in ascending expert order and
-// then the shared result, and writes y: a deterministic, atomic-free combine.
+// direct); 1 = routed down projection -> slot row t*k + j = w_tj * o (fp16); 2 = shared
+// down projection -> slot row T*k + t.  k_combine then adds each token's k slot rows in
+// ascending expert order and its shared row, in fp32, and writes y: a deterministic,
+// atomic-free combine.
 #include <type_traits>
 
 #include "common.h"
@@ -70,7 +71,7 @@ struct GemmArgs {
     const Tile *tiles;
     const int32_t *ntiles;
     const float *w;                  // [T*K]
-    uint16_t *slot;                  // [T*K][H]
+    uint16_t *slot;                  // [T*K + T][H]
     void *y;
     int y_dtype;
     int nb;                          // column blocks per tile
@@ -405,69 +406,62 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         const int row = 32 * hp + er;
         if (row < nrows) {
             const float *src = fs + er * FP + 32 * (lane >> 5);
-            if (MODE == 1) {
-                const int64_t p = s_pos[row];
-                const float wv = s_w[row];
+            // routed rows: the (token, slot) row with its routing weight; shared rows:
+            // row T*K + t with weight 1
+            const int64_t p = MODE == 1 ? (int64_t)s_pos[row] : (int64_t)tile.row0 + row;
+            const float wv = MODE == 1 ? s_w[row] : 1.0f;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
-                    u32x4 o;
-                    o[0] = pack_f16x2((_Float16)(v0[0] * wv), (_Float16)(v0[1] * wv));
-                    o[1] = pack_f16x2((_Float16)(v0[2] * wv), (_Float16)(v0[3] * wv));
-                    o[2] = pack_f16x2((_Float16)(v1[0] * wv), (_Float16)(v1[1] * wv));
-                    o[3] = pack_f16x2((_Float16)(v1[2] * wv), (_Float16)(v1[3] * wv));
-                    *(u32x4 *)(a.slot + p * H + ecol + 8 * c) = o;
-                }
-            } else {
-                const int64_t t = tile.row0 - TK + row;
-                const uint16_t *sp = a.slot + t * K * H + ecol;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    u32x4 sv[16];                                // the token's k slot rows (k <= 16)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (j < K) sv[j] = *(const u32x4 *)(sp + (int64_t)j * H + 8 * c);
-                    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)                 // ascending expert id
-                        if (j < K)
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const f16x2 h2 = as_h2(sv[j][q]);
-                                sum[2 * q] += (float)h2[0];
-                                sum[2 * q + 1] += (float)h2[1];
-                            }
-                    const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
-                    sum[0] += v0[0]; sum[1] += v0[1]; sum[2] += v0[2]; sum[3] += v0[3];    // shared expert last
-                    sum[4] += v1[0]; sum[5] += v1[1]; sum[6] += v1[2]; sum[7] += v1[3];
-                    if (a.y_dtype == QSMOE_F32) {
-                        float *yp = (float *)a.y + t * H + ecol + 8 * c;
-                        *(f32x4 *)yp = (f32x4){sum[0], sum[1], sum[2], sum[3]};
-                        *(f32x4 *)(yp + 4) = (f32x4){sum[4], sum[5], sum[6], sum[7]};
-                    } else {
-                        u32x4 o;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            o[q] = (uint32_t)f32_to_bf16(sum[2 * q]) | ((uint32_t)f32_to_bf16(sum[2 * q + 1]) << 16);
-                        *(u32x4 *)((uint16_t *)a.y + t * H + ecol + 8 * c) = o;
-                    }
-                }
+            for (int c = 0; c < 4; ++c) {
+                const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
+                u32x4 o;
+                o[0] = pack_f16x2((_Float16)(v0[0] * wv), (_Float16)(v0[1] * wv));
+                o[1] = pack_f16x2((_Float16)(v0[2] * wv), (_Float16)(v0[3] * wv));
+                o[2] = pack_f16x2((_Float16)(v1[0] * wv), (_Float16)(v1[1] * wv));
+                o[3] = pack_f16x2((_Float16)(v1[2] * wv), (_Float16)(v1[3] * wv));
+                *(u32x4 *)(a.slot + p * H + ecol + 8 * c) = o;
             }
         }
         wave_lds_sync();
     }
 }
 
-// routed-only layers (no shared expert): y = sum of the k slots, fixed order
-__global__ __launch_bounds__(256) void k_combine_routed(const uint16_t *__restrict__ slot, void *y,
-                                                        int y_dtype, int64_t T, int K, int H) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * H) return;
-    const int64_t t = i / H, col = i % H;
-    float sum = 0.0f;
-    for (int j = 0; j < K; ++j) sum += f16_to_f32(slot[(t * K + j) * H + col]);
-    if (y_dtype == QSMOE_F32) ((float *)y)[i] = sum;
-    else ((uint16_t *)y)[i] = f32_to_bf16(sum);
+// The combine: y[t] = sum of the token's k slot rows in ascending expert id, then its
+// shared-expert row, in fp32; one thread per 8 columns of a token (16-byte loads).
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ slot, void *y, int y_dtype,
+                                                 int64_t T, int K, int H, int shared) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (token, 8-column chunk)
+    const int cpr = H / 8;
+    if (i >= T * cpr) return;
+    const int64_t t = i / cpr;
+    const int col = (int)(i % cpr) * 8;
+    u32x4 v[17];
+#pragma unroll
+    for (int j = 0; j < 17; ++j)
+        if (j < K || (j == K && shared)) {
+            const int64_t row = j < K ? t * K + j : T * K + t;
+            v[j] = *(const u32x4 *)(slot + row * H + col);
+        }
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 17; ++j)
+        if (j < K || (j == K && shared))
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f16x2 h2 = as_h2(v[j][q]);
+                sum[2 * q] += (float)h2[0];
+                sum[2 * q + 1] += (float)h2[1];
+            }
+    if (y_dtype == QSMOE_F32) {
+        float *yp = (float *)y + t * H + col;
+        *(f32x4 *)yp = (f32x4){sum[0], sum[1], sum[2], sum[3]};
+        *(f32x4 *)(yp + 4) = (f32x4){sum[4], sum[5], sum[6], sum[7]};
+    } else {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = (uint32_t)f32_to_bf16(sum[2 * q]) | ((uint32_t)f32_to_bf16(sum[2 * q + 1]) << 16);
+        *(u32x4 *)((uint16_t *)y + t * H + col) = o;
+    }
 }
 
 // workgroups for `tiles` tiles of nb column blocks: a multiple of 8 * nb (see k_gemm)
@@ -487,13 +481,11 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
     // routed down -> slots
     a.nb = (L.H + BN - 1) / BN;
     hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr, a.nb)), dim3(NT), 0, s, a);
-    if (L.has_shared) {
-        hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(grid_for(maxs, a.nb)), dim3(NT), 0, s, a);
-    } else {
-        const int64_t n = a.T * L.H;
-        hipLaunchKernelGGL(k_combine_routed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                           a.slot, a.y, a.y_dtype, a.T, L.K, L.H);
-    }
+    // shared down -> its own slot rows
+    if (L.has_shared) hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(grid_for(maxs, a.nb)), dim3(NT), 0, s, a);
+    const int64_t n = a.T * (L.H / 8);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.slot, a.y, a.y_dtype,
+                       a.T, L.K, L.H, L.has_shared);
     return hipGetLastError();
 }
 

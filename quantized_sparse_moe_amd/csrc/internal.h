@@ -63,7 +63,7 @@ struct PrefillBufs {
     Tile *tiles;                   // [max_tiles] routed full, routed partial, then shared tiles
     int32_t *ntiles;               // [2] routed tiles, routed + shared tiles
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
-    uint16_t *slot;                // [T*K][H] fp16: w_j * o_j
+    uint16_t *slot;                // [T*K + T][H] fp16: w_j * o_j per (token, slot), then shared o
 };
 
 int64_t prefill_max_routed_tiles(int64_t T, int K, int E);

@@ -20,7 +20,7 @@ namespace {
 constexpr int RT = ROUTER_TOKENS;   // tokens per workgroup (one 16-row MFMA subtile)
 constexpr int RKC = 1024;           // columns of x staged per chunk
 constexpr int RPITCH = RKC + 8;     // bf16 elements per LDS row (breaks bank alignment)
-constexpr int RU = 4;               // 32-column K slices whose weight loads are in flight together
+constexpr int RU = 2;               // 32-column K slices per batch of router-weight loads
 
 struct RouterArgs {
     Layer L;
@@ -88,23 +88,32 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
             }
         }
         __syncthreads();
-        for (int s0 = 0; s0 < kw / 32; s0 += RU) {
-            bf16x8 B[RU][4];
+        // router-weight fragments of RU K slices per batch; the next batch's loads are in
+        // flight while the current one is multiplied (kw / 32 is a multiple of RU)
+        auto load_b = [&](int s0, bf16x8 (&B)[RU][4]) {
 #pragma unroll
             for (int u = 0; u < RU; ++u)
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    const int col = kc + (s0 + u) * 32;
-                    B[u][n] = (s0 + u < kw / 32) ? *(const bf16x8 *)(wrow[n] + col) : (bf16x8){};
-                }
+                for (int n = 0; n < 4; ++n) B[u][n] = *(const bf16x8 *)(wrow[n] + kc + (s0 + u) * 32);
+        };
+        auto mma = [&](int s0, const bf16x8 (&B)[RU][4]) {
 #pragma unroll
             for (int u = 0; u < RU; ++u) {
-                if (s0 + u < kw / 32) {
-                    const bf16x8 A = *(const bf16x8 *)(xa + n16 * RPITCH + (s0 + u) * 32 + 8 * cg);
+                const bf16x8 A = *(const bf16x8 *)(xa + n16 * RPITCH + (s0 + u) * 32 + 8 * cg);
 #pragma unroll
-                    for (int n = 0; n < 4; ++n)
-                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlive[n] ? B[u][n] : (bf16x8){}, acc[n], 0, 0, 0);
-                }
+                for (int n = 0; n < 4; ++n)
+                    acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, wlive[n] ? B[u][n] : (bf16x8){}, acc[n], 0, 0, 0);
+            }
+        };
+        bf16x8 B0[RU][4], B1[RU][4];
+        const int nsub = kw / 32;
+        load_b(0, B0);
+        for (int s0 = 0; s0 < nsub; s0 += 2 * RU) {
+            if (s0 + RU < nsub) load_b(s0 + RU, B1);
+            mma(s0, B0);
+            if (s0 + RU < nsub) {
+                if (s0 + 2 * RU < nsub) load_b(s0 + 2 * RU, B0);
+                mma(s0 + RU, B1);
             }
         }
         __syncthreads();

@@ -138,9 +138,9 @@ def test_workspace_sizes():
     for T in (3, 17, 64, 1000, 4096):
         assert f(T) >= prev
         prev = f(T)
-    # the grouped path keeps x16, h (routed + shared) and the fp16 slots
+    # the grouped path keeps x16, h (routed + shared) and the fp16 slots (routed + shared)
     T, H, I, K = 4096, 2048, 512, 8
-    assert f(T) >= 2 * T * H + 2 * (T * K + T) * I + 2 * T * K * H
+    assert f(T) >= 2 * T * H + 2 * (T * K + T) * I + 2 * (T * K + T) * H
     assert f(T) < 400 * 2 ** 20
 
 
