@@ -113,6 +113,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     PrefillBufs b;
     c.take<uint32_t>(WS_CTL_BYTES / 4);              // decode state stays untouched
     b.x16 = c.take<uint16_t>((size_t)(T * H));
+    b.logits = c.take<float>((size_t)(T * E));
     b.idx = c.take<int32_t>((size_t)(T * K));
     b.w = c.take<float>((size_t)(T * K));
     b.blkcnt = c.take<int32_t>((size_t)(nblk * E));
@@ -186,8 +187,8 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_route(L, (const uint16_t *)x, b, topk_idx, topk_w, st));
     }
-    PrefillBufs b;
-    std::memset(&b, 0, sizeof(b));
+    size_t n;
+    PrefillBufs b = carve_prefill(d, T, ws, &n);
     b.idx = topk_idx;
     b.w = topk_w;
     return dev(launch_prefill_router(L, (const uint16_t *)x, T, b, false, nullptr, nullptr, st));

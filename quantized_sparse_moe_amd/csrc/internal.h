@@ -54,6 +54,7 @@ struct Tile {                      // one row block of one expert bin
 
 struct PrefillBufs {
     uint16_t *x16;                 // [T][H] fp16, columns permuted per 8-group (code order)
+    float *logits;                 // [T][E] router logits
     int32_t *idx;                  // [T][K]
     float *w;                      // [T][K]
     int32_t *blkcnt;               // [nblk][E]  assignments per (32-token block, expert)
