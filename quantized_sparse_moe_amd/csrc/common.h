@@ -132,6 +132,21 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 }
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// maximum over the wave, returned uniform (in a scalar register)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));                     // every lane: its row's maximum
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------------ top-k
@@ -140,10 +155,10 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // renormalises w_j = exp(l_j - l_max) / sum_selected exp(l_i - l_max).  On return lanes
 // j < top_k hold (idx, w) of the j-th selected expert in ASCENDING expert-id order.
 //
-// The k-th largest value is found by a bitwise search over order-preserving integer
-// keys, each step counting candidates with ballots and popcounts (no cross-lane
-// shuffles, whose latency dominates a butterfly arg-max); ties at the threshold are
-// taken in expert-id order; the selection is compacted through a small LDS slot.
+// The k-th largest value is found on order-preserving integer keys by at most top_k
+// rounds of "take the largest remaining key, count and remove all of its copies" (a
+// DPP wave maximum, then ballots); ties at that threshold are taken in expert-id
+// order; the selection is compacted through a small LDS slot.
 struct TopkOut {
     int idx;
     float w;
@@ -169,28 +184,26 @@ __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_exp
         val[i] = live ? v[i] : 0.0f;
         key[i] = live ? order_key(val[i]) : 0u;
     }
-    // T = the largest key prefix with at least top_k keys >= T, two bits per step (the
-    // three candidate counts of a step are independent); once exactly top_k keys are
-    // >= T the selection is decided and the remaining bits need not be searched
+    // T = the top_k-th largest key, counting repeats: each round takes the largest key
+    // left, counts its copies and removes them (dead entries are 0, below every key)
     uint32_t T = 0;
-    for (int b = 30; b >= 0; b -= 2) {
-        const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
-        int n1 = 0, n2 = 0, n3 = 0;
+    {
+        uint32_t w[4] = {key[0], key[1], key[2], key[3]};
+        int left = top_k;
+        for (int r = 0; r < top_k; ++r) {
+            const uint32_t m = wave_max_u32(max(max(w[0], w[1]), max(w[2], w[3])));
+            int c = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            n1 += __popcll(__ballot(key[i] >= c1));
-            n2 += __popcll(__ballot(key[i] >= c2));
-            n3 += __popcll(__ballot(key[i] >= c3));
-        }
-        if (n3 >= top_k) {
-            T = c3;
-            if (n3 == top_k) break;
-        } else if (n2 >= top_k) {
-            T = c2;
-            if (n2 == top_k) break;
-        } else if (n1 >= top_k) {
-            T = c1;
-            if (n1 == top_k) break;
+            for (int i = 0; i < 4; ++i) {
+                const bool eq = w[i] == m;
+                c += __popcll(__ballot(eq));
+                w[i] = eq ? 0u : w[i];
+            }
+            left -= c;
+            if (left <= 0 || m == 0u) {
+                T = m;
+                break;
+            }
         }
     }
     int gt = 0;

@@ -127,11 +127,21 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     const int E = a.E, K = a.K;
     hist[tid] = 0;
     __syncthreads();
-    for (int r = wave; r < TK_TOKENS; r += 4) {
-        const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + r;
+    // the logits of this wave's tokens are all loaded before the first selection
+    constexpr int TPW = TK_TOKENS / 4;
+    float v[TPW][4];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+        const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[q][i] = (t < a.T && lane + 64 * i < E) ? a.logits[t * E + lane + 64 * i] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+        const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
         if (t >= a.T) break;
-        const float *row = a.logits + t * E;
-        const TopkOut tk = wave_topk([&](int e) { return row[e]; }, E, K);
+        const TopkOut tk = wave_topk_regs(v[q], E, K);
         if (lane < K) {
             a.idx[t * K + lane] = tk.idx;
             a.w[t * K + lane] = tk.w;

@@ -6,12 +6,14 @@ on sampled tokens (tokens are independent, so the oracle evaluates just those ro
 Bit-exact invariants: fused [gate; up] == separate gate and up, repeat calls,
 token permutation and chunking.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
 import oracle
 import qsmoe_synth as syn
-from gpu_util import (check_output, check_routing, sample_tokens, to_dev, y_to_np)
+from gpu_util import (TAU, W_TOL, check_output, check_routing, sample_tokens, to_dev, y_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +85,46 @@ def test_route_parity(torch, qs, cfg, T, nsample):
     idx_r, w_r, gap = oracle.route(oracle.OracleLayer(L), x_np[rows])
     check_routing(idx[rows], w[rows], idx_r, w_r, gap)
     assert ((idx >= 0) & (idx < L.n_experts)).all()
+
+
+@pytest.mark.parametrize("cfg,k", [("TINY", 3), ("DECODE", 7)])
+def test_route_exact_ties(torch, qs, cfg, k):
+    """Router rows duplicated in pairs give exactly equal logits on both sides; with an
+    odd k the last selected pair is split and its lower id must be taken.  x = 0 makes
+    every logit 0: the k lowest ids, each with weight 1/k.  Decode (T = 1) and prefill
+    routers both."""
+    base = layer(cfg)
+    rw = base.router_w.copy()
+    rw[1::2] = rw[0::2]
+    L = dataclasses.replace(base, top_k=k, router_w=rw, router_bias=None)
+    desc = qs.LayerDesc.from_host(L)
+    ol = oracle.OracleLayer(L)
+    x_np = syn.make_x(64, L.hidden, seed=5)
+    lg = oracle.router_logits(ol, x_np)                       # fp64, pairs exactly equal
+    assert (lg[:, 1::2] == lg[:, 0::2]).all()
+    idx_r, w_r, _ = oracle.route(ol, x_np)
+    # unambiguous tokens: the split pair is at least TAU away from the pairs beside it
+    pv = -np.sort(-lg[:, 0::2], axis=1)
+    m = (k + 1) // 2
+    ok = (pv[:, m - 2] - pv[:, m - 1] >= TAU) & (pv[:, m - 1] - pv[:, m] >= TAU)
+    assert ok.sum() >= 48
+    assert (idx_r % 2 == 0).sum(axis=1).tolist() == [m] * len(x_np)   # oracle: lower id of the split pair
+    zero = np.zeros((1, L.hidden), np.uint16)
+    for T in (1, 64):
+        rows = range(0, 64, 8) if T == 1 else [slice(0, 64)]
+        for r in rows:
+            xs = x_np[r] if T == 64 else x_np[r:r + 1]
+            idx, w = qs.moe_route(desc, to_dev(xs, torch))
+            torch.cuda.synchronize()
+            sel = np.arange(64)[r] if T == 64 else np.array([r])
+            good = ok[sel]
+            assert (idx.cpu().numpy()[good] == idx_r[sel][good]).all(), f"T={T} rows {r}"
+            assert np.abs(w.cpu().numpy()[good] - w_r[sel][good]).max() <= W_TOL
+        xz = np.repeat(zero, T, axis=0)
+        idx, w = qs.moe_route(desc, to_dev(xz, torch))
+        torch.cuda.synchronize()
+        assert (idx.cpu().numpy() == np.arange(k)[None, :]).all(), f"x = 0, T={T}"
+        assert np.abs(w.cpu().numpy() - 1.0 / k).max() <= 1e-7
 
 
 # -------------------------------------------------------------------- whole layer
