@@ -244,20 +244,18 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
     }
 }
 
-// Selector (one wave): waits (bounded) until every logit of this call is in, polling
-// with two reads in flight, and takes the top-k: lanes j < K return (id, weight) of the
-// j-th selected expert in ascending id.
+// Selector (one wave): waits (bounded) until every logit of this call is in and takes
+// the top-k: lanes j < K return (id, weight) of the j-th selected expert in ascending
+// id.  One poll is in flight at a time: a read still in flight when the data is found
+// would have to be waited for before its registers are reused, a full extra round trip.
 __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
     const int lane = threadIdx.x & 63;
     const uint64_t *lg = (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE);
     const uint64_t none = (uint64_t)tag << 32;
     uint64_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
     for (uint32_t n = 0;; ++n) {
-        uint64_t w2[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w2[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
+        for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
         bool miss = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) miss |= tag_of(w[i]) != tag;
@@ -266,8 +264,6 @@ __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
             if (lane == 0) raise_error(ctl);
             break;
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = w2[i];
         poll_pause(n);
     }
     float v[4];
@@ -278,23 +274,22 @@ __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
     return tk;
 }
 
-// Consumer: wave 0 waits (bounded) for the published selection, with two reads in
-// flight; the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights.
+// Consumer: wave 0 waits (bounded) for the published selection, one poll in flight;
+// the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights.
 __device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int *s_idx, float *s_w) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
         const bool act = lane < 2 * K;
         const uint64_t none = (uint64_t)tag << 32;
-        uint64_t w = act ? ld_dev64(tp + lane) : none;
+        uint64_t w;
         for (uint32_t n = 0;; ++n) {
-            const uint64_t w2 = act ? ld_dev64(tp + lane) : none;
+            w = act ? ld_dev64(tp + lane) : none;
             if (__ballot(tag_of(w) != tag) == 0ull) break;
             if (n > SPIN_LIMIT) {
                 if (lane == 0) raise_error(ctl);
                 break;
             }
-            w = w2;
             poll_pause(n);
         }
         if (act) {
