@@ -156,9 +156,10 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // j < top_k hold (idx, w) of the j-th selected expert in ASCENDING expert-id order.
 //
 // The k-th largest value is found on order-preserving integer keys by at most top_k
-// rounds of "take the largest remaining key, count and remove all of its copies" (a
-// DPP wave maximum, then ballots); ties at that threshold are taken in expert-id
-// order; the selection is compacted through a small LDS slot.
+// rounds over per-lane sorted lists (a DPP wave maximum of the lanes' heads, then one
+// ballot); ties at that threshold are taken in expert-id order; the normaliser is a
+// wave sum; only the compaction into id order goes through a small LDS slot.  Every
+// step is a dependent chain of one wave, so the instruction count is the latency.
 struct TopkOut {
     int idx;
     float w;
@@ -173,7 +174,7 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // v[i] = value of expert lane + 64 i (ignored for ids >= n_experts)
 __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_experts, int top_k) {
     __shared__ int tk_idx[16][16];
-    __shared__ __attribute__((aligned(16))) float tk_val[16][16];
+    __shared__ float tk_w[16][16];
     const int lane = threadIdx.x & 63, wv = (threadIdx.x >> 6) & 15;
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t key[4];
@@ -184,64 +185,70 @@ __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_exp
         val[i] = live ? v[i] : 0.0f;
         key[i] = live ? order_key(val[i]) : 0u;
     }
-    // T = the top_k-th largest key, counting repeats: each round takes the largest key
-    // left, counts its copies and removes them (dead entries are 0, below every key)
-    uint32_t T = 0;
-    {
-        uint32_t w[4] = {key[0], key[1], key[2], key[3]};
-        int left = top_k;
-        for (int r = 0; r < top_k; ++r) {
-            const uint32_t m = wave_max_u32(max(max(w[0], w[1]), max(w[2], w[3])));
-            int c = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool eq = w[i] == m;
-                c += __popcll(__ballot(eq));
-                w[i] = eq ? 0u : w[i];
-            }
-            left -= c;
-            if (left <= 0 || m == 0u) {
-                T = m;
-                break;
-            }
+    // T = the top_k-th largest key, counting repeats.  Each lane sorts its four keys;
+    // a round takes the wave maximum of the lanes' heads, and every lane whose head
+    // equals it pops one entry, until top_k entries have been popped.
+    uint32_t q0 = max(key[0], key[1]), q1 = min(key[0], key[1]);
+    uint32_t q2 = max(key[2], key[3]), q3 = min(key[2], key[3]);
+    const uint32_t h0 = max(q0, q2), l0 = min(q0, q2), h1 = max(q1, q3), l1 = min(q1, q3);
+    q0 = h0;
+    q1 = max(l0, h1);
+    q2 = min(l0, h1);
+    q3 = l1;
+    uint32_t T = 0, top = 0;
+    int left = top_k;
+    for (int r = 0; r < top_k; ++r) {
+        const uint32_t m = wave_max_u32(q0);
+        if (r == 0) top = m;
+        const bool pop = q0 == m;
+        left -= __popcll(__ballot(pop));
+        if (left <= 0 || m == 0u) {
+            T = m;
+            break;
+        }
+        if (pop) {
+            q0 = q1;
+            q1 = q2;
+            q2 = q3;
+            q3 = 0u;
         }
     }
+    // selection: keys above T, then ties at T in expert-id order (id = lane + 64 i)
     int gt = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(key[i] > T));
-    const int need = top_k - gt;                       // ties at T to take, lowest ids first
-    int ties_before = 0, base = 0;
+    const int need = top_k - gt;
+    int ties_before = 0, base = 0, pos[4];
+    bool sel[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint64_t tie = __ballot(key[i] == T);
-        const bool sel = key[i] > T || (key[i] == T && ties_before + __popcll(tie & lt) < need);
+        sel[i] = key[i] > T || (key[i] == T && ties_before + __popcll(tie & lt) < need);
         ties_before += __popcll(tie);
-        const uint64_t sm = __ballot(sel);
-        if (sel) {
-            const int pos = base + __popcll(sm & lt);  // rank by expert id = lane + 64 i
-            tk_idx[wv][pos] = lane + 64 * i;
-            tk_val[wv][pos] = val[i];
-        }
+        const uint64_t sm = __ballot(sel[i]);
+        pos[i] = base + __popcll(sm & lt);             // rank by expert id
         base += __popcll(sm);
     }
+    // renormalised weights: exp(l - l_max) over the selection, l_max = the key `top`
+    const float vmax = __uint_as_float((top & 0x80000000u) ? (top & 0x7fffffffu) : ~top);
+    float e[4], part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        e[i] = sel[i] ? __expf(val[i] - vmax) : 0.0f;
+        part += e[i];
+    }
+    const float z = wave_sum(part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (sel[i]) {
+            tk_idx[wv][pos[i]] = lane + 64 * i;
+            tk_w[wv][pos[i]] = e[i] / z;
+        }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     TopkOut out;
-    out.idx = 0;
-    out.w = 0.0f;
-    if (lane < top_k) {
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; j += 4) *(float4 *)(v + j) = *(const float4 *)(&tk_val[wv][j]);
-        float m = v[0];
-#pragma unroll
-        for (int j = 1; j < 16; ++j) m = (j < top_k) ? fmaxf(m, v[j]) : m;
-        float z = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) z += (j < top_k) ? __expf(v[j] - m) : 0.0f;
-        out.idx = tk_idx[wv][lane];
-        out.w = __expf(tk_val[wv][lane] - m) / z;
-    }
+    out.idx = lane < top_k ? tk_idx[wv][lane] : 0;
+    out.w = lane < top_k ? tk_w[wv][lane] : 0.0f;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     return out;

@@ -11,9 +11,10 @@
 // same time, and a phase waits only for the results it consumes.
 //
 // One launch (a dependent launch costs ~1.5 us on this part, as much as streaming
-// 12 MB), four roles chosen by workgroup index:
-//   R  router logits (fp32), one wave per expert; the last R workgroup to finish takes
-//      the top-k and publishes it
+// 12 MB), five roles chosen by workgroup index:
+//   R  router logits (fp32), one wave per expert
+//   P  selectors: one wave each waits for all logits, takes the top-k and publishes it
+//      (several selectors write disjoint sets of copies)
 //   S  shared expert gate/up + SwiGLU (needs nothing)
 //   G  routed expert gate/up + SwiGLU, one [gate; up] row pair per row group (waits
 //      for the top-k)
@@ -25,7 +26,11 @@
 // a bound is ever exceeded) so the kernel always ends.
 //
 // Hand-offs between workgroups use device-scope (sc1) stores/loads and device-scope
-// atomics, which are coherent across the XCDs without L2 write-back/invalidate.
+// atomics, which are coherent across the XCDs without L2 write-back/invalidate.  Every
+// hand-off word carries the call's tag in its upper half, so a reader knows a word is
+// current without any ordering between words; a producer gathers its words in LDS and
+// writes each run with whole 16-byte stores (a line assembled from many small writes
+// of different waves becomes visible far later).
 // Completion is counted in two levels (NGRP group counters, then one top counter) so
 // that no single line absorbs one atomic per workgroup; "ready" flags are replicated
 // NCOPY times so that no single line absorbs all the polling.  The last D workgroup
@@ -94,6 +99,11 @@ __device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
 }
 __device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes (two tagged words) written through to device scope in one store: hand-off
+// lines are written whole by one instruction, not merged from many small writes
+__device__ __forceinline__ void st_dev128(void *p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -318,36 +328,48 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
     if (b < nR) {
         // ------------------------------------------------- R: one router logit per wave
+        // the workgroup's NW logits are gathered in LDS, then written to every copy in
+        // 16-byte pieces (one 64-byte run per copy)
+        __shared__ float s_lg[NW];
         const int e = b * NW + wave;
-        if (e >= E) return;
         const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
-        const uint16_t *wr = L.router_w + (int64_t)e * H;
         float acc = 0.0f;
-        for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
-            u32x4 xv[4], wv[4];
+        if (e < E) {
+            const uint16_t *wr = L.router_w + (int64_t)e * H;
+            for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
+                u32x4 xv[4], wv[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int c = c0 + 64 * k;
-                xv[k] = wv[k] = (u32x4){0u, 0u, 0u, 0u};
-                if (c < H / 8) {
-                    xv[k] = *(const u32x4 *)(a.x + 8 * c);
-                    wv[k] = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
+                for (int k = 0; k < 4; ++k) {
+                    const int c = c0 + 64 * k;
+                    xv[k] = wv[k] = (u32x4){0u, 0u, 0u, 0u};
+                    if (c < H / 8) {
+                        xv[k] = *(const u32x4 *)(a.x + 8 * c);
+                        wv[k] = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
+                    }
                 }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc = __builtin_fmaf(__uint_as_float(xv[k][i] << 16), __uint_as_float(wv[k][i] << 16), acc);
+                        acc = __builtin_fmaf(__uint_as_float(xv[k][i] & 0xffff0000u),
+                                             __uint_as_float(wv[k][i] & 0xffff0000u), acc);
+                    }
             }
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc = __builtin_fmaf(__uint_as_float(xv[k][i] << 16), __uint_as_float(wv[k][i] << 16), acc);
-                    acc = __builtin_fmaf(__uint_as_float(xv[k][i] & 0xffff0000u),
-                                         __uint_as_float(wv[k][i] & 0xffff0000u), acc);
-                }
+            acc = wave_sum(acc) + (L.router_bias ? L.router_bias[e] : 0.0f);
         }
-        acc = wave_sum(acc);
-        if (lane < LOGIT_COPIES) {
-            const float lgt = acc + (L.router_bias ? L.router_bias[e] : 0.0f);
-            st_dev64((uint64_t *)(ctl + LOGIT_BASE + lane * LOGIT_STRIDE) + e,
-                     __float_as_uint(lgt) | ((uint64_t)tag << 32));
+        if (lane == 0) s_lg[wave] = acc;
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int PIECES = NW / 2;                   // 16-byte pieces per copy
+            for (int t = lane; t < LOGIT_COPIES * PIECES; t += 64) {
+                const int c = t / PIECES, q = t % PIECES, e0 = b * NW + 2 * q;
+                uint32_t *dst = ctl + LOGIT_BASE + c * LOGIT_STRIDE + 2 * e0;
+                if (e0 + 1 < E)
+                    st_dev128(dst, (u32x4){__float_as_uint(s_lg[2 * q]), tag, __float_as_uint(s_lg[2 * q + 1]), tag});
+                else if (e0 < E)
+                    st_dev64((uint64_t *)dst, __float_as_uint(s_lg[2 * q]) | ((uint64_t)tag << 32));
+            }
         }
         return;
     }
@@ -366,11 +388,9 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             return;
         }
         if (lane < K)
-            for (int c = sel; c < TOPK_COPIES; c += a.nP) {
-                uint64_t *tp = (uint64_t *)(ctl + TOPK_BASE + c * TOPK_STRIDE);
-                st_dev64(tp + 2 * lane, (uint32_t)tk.idx | ((uint64_t)tag << 32));
-                st_dev64(tp + 2 * lane + 1, __float_as_uint(tk.w) | ((uint64_t)tag << 32));
-            }
+            for (int c = sel; c < TOPK_COPIES; c += a.nP)
+                st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * lane,
+                          (u32x4){(uint32_t)tk.idx, tag, __float_as_uint(tk.w), tag});
         return;
     }
     nR += a.nP;                                              // the roles below follow the selectors
@@ -396,10 +416,22 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int jj = j0 < I ? j0 : I - 2;
         float hv[2];
         pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, hv);
-        if (j0 < I) {                                        // lanes of the row group write the copies
-            const uint64_t word = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1])) | ((uint64_t)tag << 32);
-            for (int cp = lane % a.lprg; cp < H_COPIES; cp += a.lprg)
-                st_dev64((uint64_t *)(ctl + H_BASE + cp * H_STRIDE) + slot * (I / 2) + j0 / 2, word);
+        // the workgroup's pb / 2 words (one per row group, consecutive in j) are gathered
+        // in LDS and written to every copy in 16-byte pieces
+        __shared__ uint32_t s_hw[NW * 64];
+        const int wi = wave * rpw + lane / a.lprg;           // word within the workgroup
+        if (lane % a.lprg == 0) s_hw[wi] = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1]));
+        __syncthreads();
+        const int jb = j0 - 2 * wi;                          // first j of the workgroup
+        const int nw = min(pb, I - jb) / 2;                  // valid words
+        const int pieces = (nw + 1) / 2;
+        for (int t = tid; t < H_COPIES * pieces; t += DT) {
+            const int cp = t / pieces, q = t % pieces;
+            uint32_t *dst = ctl + H_BASE + cp * H_STRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
+            if (2 * q + 1 < nw)
+                st_dev128(dst, (u32x4){s_hw[2 * q], tag, s_hw[2 * q + 1], tag});
+            else
+                st_dev64((uint64_t *)dst, s_hw[2 * q] | ((uint64_t)tag << 32));
         }
         return;
     }
