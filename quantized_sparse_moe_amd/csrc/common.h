@@ -136,6 +136,18 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
+// maximum over the wave in every lane, without leaving the vector unit: DPP within each
+// 16-lane row, then the gfx950 half- and row-swaps across rows
+__device__ __forceinline__ uint32_t wave_max_bcast(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    const auto h = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    v = max(h[0], h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return max(r[0], r[1]);
+}
 // maximum over the wave, returned uniform (in a scalar register)
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = max(v, dpp_u32<0xB1>(v));
@@ -185,49 +197,81 @@ __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_exp
         val[i] = live ? v[i] : 0.0f;
         key[i] = live ? order_key(val[i]) : 0u;
     }
-    // T = the top_k-th largest key, counting repeats.  Each lane sorts its four keys;
-    // a round takes the wave maximum of the lanes' heads, and every lane whose head
-    // equals it pops one entry, until top_k entries have been popped.
+    // T = the top_k-th largest key, counting repeats.  Each lane sorts its four keys.
+    // Fast path: top_k rounds, each popping the wave maximum of the lanes' heads; if
+    // exactly top_k keys are >= the last maximum, it is T (no repeats were involved).
     uint32_t q0 = max(key[0], key[1]), q1 = min(key[0], key[1]);
     uint32_t q2 = max(key[2], key[3]), q3 = min(key[2], key[3]);
-    const uint32_t h0 = max(q0, q2), l0 = min(q0, q2), h1 = max(q1, q3), l1 = min(q1, q3);
-    q0 = h0;
-    q1 = max(l0, h1);
-    q2 = min(l0, h1);
-    q3 = l1;
-    uint32_t T = 0, top = 0;
-    int left = top_k;
-    for (int r = 0; r < top_k; ++r) {
-        const uint32_t m = wave_max_u32(q0);
-        if (r == 0) top = m;
-        const bool pop = q0 == m;
-        left -= __popcll(__ballot(pop));
-        if (left <= 0 || m == 0u) {
-            T = m;
-            break;
-        }
-        if (pop) {
-            q0 = q1;
-            q1 = q2;
-            q2 = q3;
-            q3 = 0u;
-        }
+    {
+        const uint32_t h0 = max(q0, q2), l0 = min(q0, q2), h1 = max(q1, q3), l1 = min(q1, q3);
+        q0 = h0;
+        q1 = max(l0, h1);
+        q2 = min(l0, h1);
+        q3 = l1;
     }
-    // selection: keys above T, then ties at T in expert-id order (id = lane + 64 i)
-    int gt = 0;
+    const uint32_t s0 = q0, s1 = q1, s2 = q2, s3 = q3;
+    const uint32_t top = wave_max_bcast(q0);
+    uint32_t T = top;
+    for (int r = 0;;) {
+        const bool pop = q0 == T;
+        q0 = pop ? q1 : q0;
+        q1 = pop ? q2 : q1;
+        q2 = pop ? q3 : q2;
+        q3 = pop ? 0u : q3;
+        if (++r == top_k) break;
+        T = wave_max_bcast(q0);
+    }
+    int ge = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(key[i] > T));
-    const int need = top_k - gt;
-    int ties_before = 0, base = 0, pos[4];
+    for (int i = 0; i < 4; ++i) ge += __popcll(__ballot(key[i] >= T));
     bool sel[4];
+    int pos[4];
+    if (ge == top_k) {
+        int base = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint64_t tie = __ballot(key[i] == T);
-        sel[i] = key[i] > T || (key[i] == T && ties_before + __popcll(tie & lt) < need);
-        ties_before += __popcll(tie);
-        const uint64_t sm = __ballot(sel[i]);
-        pos[i] = base + __popcll(sm & lt);             // rank by expert id
-        base += __popcll(sm);
+        for (int i = 0; i < 4; ++i) {
+            sel[i] = key[i] >= T;
+            const uint64_t sm = __ballot(sel[i]);
+            pos[i] = base + __popcll(sm & lt);         // rank by expert id = lane + 64 i
+            base += __popcll(sm);
+        }
+    } else {
+        // repeated keys: rounds that pop every copy of the maximum and count them
+        q0 = s0;
+        q1 = s1;
+        q2 = s2;
+        q3 = s3;
+        int left = top_k;
+        for (int r = 0; r < top_k; ++r) {
+            const uint32_t m = wave_max_u32(q0);
+            const bool pop = q0 == m;
+            left -= __popcll(__ballot(pop));
+            if (left <= 0 || m == 0u) {
+                T = m;
+                break;
+            }
+            if (pop) {
+                q0 = q1;
+                q1 = q2;
+                q2 = q3;
+                q3 = 0u;
+            }
+        }
+        // keys above T, then ties at T in expert-id order
+        int gt = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gt += __popcll(__ballot(key[i] > T));
+        const int need = top_k - gt;
+        int ties_before = 0, base = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t tie = __ballot(key[i] == T);
+            sel[i] = key[i] > T || (key[i] == T && ties_before + __popcll(tie & lt) < need);
+            ties_before += __popcll(tie);
+            const uint64_t sm = __ballot(sel[i]);
+            pos[i] = base + __popcll(sm & lt);
+            base += __popcll(sm);
+        }
     }
     // renormalised weights: exp(l - l_max) over the selection, l_max = the key `top`
     const float vmax = __uint_as_float((top & 0x80000000u) ? (top & 0x7fffffffu) : ~top);
