@@ -31,10 +31,11 @@
 // current without any ordering between words; a producer gathers its words in LDS and
 // writes each run with whole 16-byte stores (a line assembled from many small writes
 // of different waves becomes visible far later).
-// Completion is counted in two levels (NGRP group counters, then one top counter) so
-// that no single line absorbs one atomic per workgroup; "ready" flags are replicated
-// NCOPY times so that no single line absorbs all the polling.  The last D workgroup
-// puts every control word back to zero for the next call.
+// The D workgroups count themselves in, in two levels (NGRP group counters, then one top
+// counter, so that no single line absorbs one atomic per workgroup), as soon as they
+// hold all of h: by then every workgroup of the call has read the generation.  The last
+// to arrive puts the counters back to zero and advances the generation.  Hand-off words
+// are replicated so that no single line absorbs all the polling.
 //
 // Dequantization in registers: codes become fp16 (1024+q) by bit operations and meet
 // fp16 activations in v_dot2_f32_f16 with fp32 accumulation; per 16-byte chunk of codes
@@ -105,6 +106,17 @@ __device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
 __device__ __forceinline__ void st_dev128(void *p, u32x4 v) {
     asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
+// 32 bytes (four tagged words) read at device scope with two 16-byte loads, waited for
+// here (the compiler does not track loads issued from inline assembly)
+__device__ __forceinline__ void ld_dev256(const void *p, u32x4 &a, u32x4 &b) {
+    asm volatile(
+        "global_load_dwordx4 %0, %2, off sc1\n\t"
+        "global_load_dwordx4 %1, %2, off offset:16 sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(a), "=&v"(b)
+        : "v"(p)
+        : "memory");
+}
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -124,24 +136,6 @@ __device__ void raise_error(uint32_t *ctl) {
 __device__ __forceinline__ void poll_pause(uint32_t n) {
     if (n < 8) __builtin_amdgcn_s_sleep(1);
     else __builtin_amdgcn_s_sleep(4);
-}
-
-// member `m` of `total` reports completion; true (in every thread) for exactly one
-// workgroup: the last of all members
-__device__ bool last_to_finish(uint32_t *ctl, int m, int total, uint32_t *s_flag) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int g = m % NGRP;
-        const int gsize = total / NGRP + (g < total % NGRP ? 1 : 0);
-        const int ngroups = total < NGRP ? total : NGRP;
-        uint32_t last = 0;
-        if (add_dev(ctl + CNT_BASE + g * 64) == (uint32_t)(gsize - 1))
-            last = add_dev(ctl + CNT_TOP) == (uint32_t)(ngroups - 1);
-        *s_flag = last;
-    }
-    __syncthreads();
-    return *s_flag != 0;
 }
 
 // the last workgroup of a call: counters back to zero, generation advanced
@@ -471,6 +465,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             if (routed) wl = s_w[lane];
         }
         float yv = 0.0f;
+        uint32_t arrived = 0;
         // items (vector v, chunk lr + k*lpr), NB per step, loaded unconditionally (clamped
         // to a valid chunk and discarded) so that all of a step's loads are in flight
         constexpr int NB = 5;
@@ -495,55 +490,40 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             }
             __builtin_amdgcn_sched_barrier(0);
             if (base == 0) {
-                // all of h (S and G) as it arrives: fp16 pairs into LDS in code order
+                // all of h (S and G) as it arrives.  Thread t takes groups of 8
+                // consecutive values (4 words): fp16 into LDS in code order with one
+                // 16-byte write, and the chunk sums by a DPP sum over the chunk's groups
                 const uint64_t *hw = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE);
-                const int npairs = nvec * I / 2;
-                for (int p0 = 0; p0 < npairs; p0 += 8 * DT) {
-                    uint64_t w[8];
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int p = p0 + j * DT + tid;
-                        w[j] = p < npairs ? ld_dev64(hw + p) : (uint64_t)tag << 32;
-                    }
+                const int ngrp = nvec * I / 8;
+                for (int g0 = 0; g0 < ngrp; g0 += DT) {
+                    const int g = g0 + tid;
+                    const bool live = g < ngrp;
+                    const int gg = live ? g : ngrp - 1;
+                    u32x4 w0, w1;                                // words (value pair, tag) x 4
                     for (uint32_t t = 0;; ++t) {
-                        bool miss = false;
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) miss |= tag_of(w[j]) != tag;
-                        if (!miss) break;
+                        ld_dev256(hw + 4 * gg, w0, w1);
+                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
                         if (t > SPIN_LIMIT) {
                             raise_error(ctl);
                             break;
                         }
                         poll_pause(t);
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            if (tag_of(w[j]) != tag) w[j] = ld_dev64(hw + p0 + j * DT + tid);
                     }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int p = p0 + j * DT + tid;
-                        if (p < npairs) {
-                            const int i0 = 2 * p, gb = i0 & ~7;
-                            hs16[gb + perm_pos<BITS>(i0 & 7)] = (uint16_t)w[j];
-                            hs16[gb + perm_pos<BITS>((i0 + 1) & 7)] = (uint16_t)(w[j] >> 16);
-                        }
-                    }
-                }
-                __syncthreads();
-                for (int c2 = tid; c2 < nvec * nch; c2 += DT) {
-                    const u32x4 *src = (const u32x4 *)(hs16 + c2 * CPC);
+                    const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
                     float sum = 0.0f;
-                    for (int g8 = 0; g8 < CPC / 8; ++g8) {
-                        const u32x4 w4 = src[g8];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const f16x2 hh = as_h2(w4[j]);
-                            sum += (float)hh[0] + (float)hh[1];
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const f16x2 hh = as_h2(nat[j]);
+                        sum += (float)hh[0] + (float)hh[1];
                     }
-                    hsum[c2] = sum;
+                    if (live) *(u32x4 *)(hs16 + 8 * g) = perm8<BITS>(nat);
+                    sum = group_sum(sum, CPC / 8);               // groups of a chunk are adjacent lanes
+                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = sum;
                 }
                 __syncthreads();
+                // this workgroup has all it reads of the call's state: count it in now
+                // (the reply is needed only at the end)
+                if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
             }
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
@@ -568,7 +548,18 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = y;
             else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
         }
-        if (last_to_finish(ctl, d, nD, &s_flag)) finish_call(ctl, tag);
+        // the last of the D workgroups to have arrived (every other workgroup of the call
+        // has read the generation before any D workgroup could arrive) resets the state
+        if (tid == 0) {
+            const int g = d % NGRP;
+            const int gsize = nD / NGRP + (g < nD % NGRP ? 1 : 0);
+            const int ngroups = nD < NGRP ? nD : NGRP;
+            uint32_t last = 0;
+            if (arrived == (uint32_t)(gsize - 1)) last = add_dev(ctl + CNT_TOP) == (uint32_t)(ngroups - 1);
+            s_flag = last;
+        }
+        __syncthreads();
+        if (s_flag) finish_call(ctl, tag);
     }
 }
 
