@@ -67,17 +67,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(_Float16 lo, _Float16 hi) {
 }
 
 // ---------------------------------------------------------------- code unpacking
-// 8 four-bit codes -> 4 dwords of fp16 pairs (1024+q), order [0,4],[1,5],[2,6],[3,7]
-__device__ __forceinline__ void magic_u4(uint32_t w, uint32_t o[4]) {
-    o[0] = (w & 0x000F000Fu) | QS_MAGIC;
-    o[1] = ((w >> 4) & 0x000F000Fu) | QS_MAGIC;
-    o[2] = ((w >> 8) & 0x000F000Fu) | QS_MAGIC;
-    o[3] = ((w >> 12) & 0x000F000Fu) | QS_MAGIC;
-}
-// 4 eight-bit codes -> 2 dwords of fp16 pairs (1024+q), order [0,2],[1,3]
-__device__ __forceinline__ void magic_u8(uint32_t w, uint32_t o[2]) {
-    o[0] = (w & 0x00FF00FFu) | QS_MAGIC;
-    o[1] = ((w >> 8) & 0x00FF00FFu) | QS_MAGIC;
+// (x & m) | c in one VALU op (the masks and the magic live in registers)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
+    return r;
 }
 
 // permute 8 consecutive fp16 activations (as 4 dwords of natural-order pairs) into

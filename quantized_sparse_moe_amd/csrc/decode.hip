@@ -148,12 +148,13 @@ __device__ void finish_call(uint32_t *ctl, uint32_t tag) {
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
 
-// x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk fp32 sums
+// x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk fp32 sums of
+// the even and of the odd columns
 template <int BITS>
-__device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float *xsum) {
+__device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float2 *xsum) {
     constexpr int CPC = 128 / BITS;
     for (int c = threadIdx.x; c < H / CPC; c += DT) {
-        float sum = 0.0f;
+        float se = 0.0f, so = 0.0f;
         for (int g = 0; g < CPC / 8; ++g) {
             const u32x4 v = *(const u32x4 *)(x + c * CPC + 8 * g);
             u32x4 nat;
@@ -161,45 +162,55 @@ __device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float *xsum) {
             for (int i = 0; i < 4; ++i) {
                 const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[i] << 16));
                 const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[i] & 0xffff0000u));
-                sum += (float)lo + (float)hi;
+                se += (float)lo;
+                so += (float)hi;
                 nat[i] = pack_f16x2(lo, hi);
             }
             *(u32x4 *)(xs + (c * CPC + 8 * g) / 2) = perm8<BITS>(nat);
         }
-        xsum[c] = sum;
+        xsum[c] = make_float2(se, so);
     }
 }
 
-// sum_c (s q_c + b) x_c over one 16-byte chunk of codes (four independent dot chains)
+// sum_c (s q_c + b) x_c over one 16-byte chunk of codes; X = (sum of x over the even
+// columns, over the odd columns).  4-bit: the low nibble of each byte (even columns)
+// becomes 1024 + q, the high nibble (odd columns) is taken in place as 1024 + 16 q, both
+// exact in fp16, so one shift serves 8 codes:
+//   sum (s q + b) x = s A_e + (s / 16) A_o + (b - 1024 s) X_e + (b - 64 s) X_o
+// with A_e, A_o the dot products of the magic values with x.  8-bit: 1024 + q for all.
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float X) {
+__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 X) {
     const u32x4 *xv = (const u32x4 *)xs;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t magic = QS_MAGIC;
+    const float s = f16_to_f32((uint16_t)s16), b = f16_to_f32((uint16_t)b16);
     if constexpr (BITS == 4) {
+        const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+        float ae[2] = {0.0f, 0.0f}, ao[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            uint32_t m[4];
-            magic_u4(q[d], m);
+            const uint32_t w8 = q[d] >> 8;
             const u32x4 xx = xv[d];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[d] = __builtin_amdgcn_fdot2(as_h2(m[i]), as_h2(xx[i]), acc[d], false);
+            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[0]), ae[d & 1], false);
+            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], hi, magic)), as_h2(xx[1]), ao[d & 1], false);
+            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, lo, magic)), as_h2(xx[2]), ae[d & 1], false);
+            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, hi, magic)), as_h2(xx[3]), ao[d & 1], false);
         }
+        const float Ae = ae[0] + ae[1], Ao = ao[0] + ao[1];
+        return s * Ae + (s * 0.0625f) * Ao + (b - 1024.0f * s) * X.x + (b - 64.0f * s) * X.y;
     } else {
+        const uint32_t lo = 0x00FF00FFu;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            uint32_t m[2];
-            magic_u8(q[d], m);
             const u32x4 xx = xv[d >> 1];
             const int o = 2 * (d & 1);
-            acc[d] = __builtin_amdgcn_fdot2(as_h2(m[0]), as_h2(xx[o]), acc[d], false);
-            acc[d] = __builtin_amdgcn_fdot2(as_h2(m[1]), as_h2(xx[o + 1]), acc[d], false);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[o]), acc[d], false);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d] >> 8, lo, magic)), as_h2(xx[o + 1]), acc[d], false);
         }
+        const float A = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return s * A + (b - 1024.0f * s) * (X.x + X.y);
     }
-    const float A = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    const float s = f16_to_f32((uint16_t)s16), b = f16_to_f32((uint16_t)b16);
-    return s * A + (b - 1024.0f * s) * X;
 }
-
 
 // [gate; up] row pairs j0 and j0 + 1 of expert e in matrix stacks (mg, mu): SwiGLU
 // values (in every lane of the row group; lpr lanes share a pair).  Each step loads one
@@ -208,7 +219,7 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, u
 // wait.  Addresses are a uniform matrix base plus a 32-bit per-lane offset.
 template <int BITS>
 __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
-                             const uint32_t *xs, const float *xsum, float hv[2]) {
+                             const uint32_t *xs, const float2 *xsum, float hv[2]) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
@@ -391,7 +402,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     if (b < nR + nS + nG) {
         // ------------------------------------------- S / G: gate/up + SwiGLU -> h
         uint32_t *xs = dsm;
-        float *xsum = (float *)(dsm + H / 2);
+        float2 *xsum = (float2 *)(dsm + H / 2);
         const int rpw = 64 / a.lprg;                         // row groups per wave
         const int pb = 2 * NW * rpw;                         // pairs per workgroup (2 per row group)
         const bool sh = b < nR + nS;
@@ -449,8 +460,11 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int rloc = wg * rpw + lane / lpr;               // row within the workgroup
         const int n = d * wpg * rpw + rloc;
         const int nc = n < H ? n : H - 1;
-        uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * I fp16, code order
-        float *hsum = (float *)(dsm + nvec * I / 2);          // nvec * nch chunk sums
+        // h in LDS: fp16 in code order, each chunk padded to CPITCH so that the 16 lanes
+        // of a row, reading 16 different chunks, meet distinct banks
+        constexpr int CPITCH = CPC + 8;
+        uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * nch chunks
+        float2 *hsum = (float2 *)(dsm + nvec * nch * CPITCH / 2);   // chunk sums (even, odd columns)
         // lane j < nvec holds row 0 of vector j's down matrix (the k routed experts in
         // ascending id, then the shared one) and its combine weight
         uint64_t pc = 0, ps = 0, pbi = 0;
@@ -510,15 +524,17 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                         poll_pause(t);
                     }
                     const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
-                    float sum = 0.0f;
+                    float se = 0.0f, so = 0.0f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const f16x2 hh = as_h2(nat[j]);
-                        sum += (float)hh[0] + (float)hh[1];
+                        se += (float)hh[0];
+                        so += (float)hh[1];
                     }
-                    if (live) *(u32x4 *)(hs16 + 8 * g) = perm8<BITS>(nat);
-                    sum = group_sum(sum, CPC / 8);               // groups of a chunk are adjacent lanes
-                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = sum;
+                    if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
+                    se = group_sum(se, CPC / 8);                 // groups of a chunk are adjacent lanes
+                    so = group_sum(so, CPC / 8);
+                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
                 }
                 __syncthreads();
                 // this workgroup has all it reads of the call's state: count it in now
@@ -530,7 +546,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 const bool live = base + i < nit;
                 const int vi = live ? v2 : min(vlast, nvec - 1);
                 const int c = lr + k2 * lpr, cc = c < nch ? c : nch - 1;
-                const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + vi * I + cc * CPC), sv[i], bv[i],
+                const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + (vi * nch + cc) * CPITCH), sv[i], bv[i],
                                                 hsum[vi * nch + cc]);
                 const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), vi));
                 yv += (live && c < nch) ? wv * p : 0.0f;       // experts in ascending id, shared last
@@ -617,8 +633,8 @@ hipError_t launch(DecArgs a, hipStream_t s) {
         // of two no larger than the (contiguous) G and D range, every selector is read, so
         // every selector has started before the call can complete
         while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
-        const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 4;
-        const size_t lds_d = (size_t)nvec * L.I * 2 + (size_t)nvec * (L.I / cpc) * 4;
+        const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 8;
+        const size_t lds_d = (size_t)nvec * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nvec * (L.I / cpc) * 8;
         lds = lds_g > lds_d ? lds_g : lds_d;
     }
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;

@@ -93,13 +93,6 @@ __device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0
 // order this wave's own LDS writes before its later LDS reads (no cross-wave effect)
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-// (x & m) | c in one VALU op (the masks and the magic live in registers)
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(m), "v"(c));
-    return r;
-}
-
 // 8 codes of one lane and K slice as MFMA operand: w = fma(q, s, b), q exact, in the
 // order [0,4,1,5,2,6,3,7] (4-bit) or [0,2,1,3,4,6,5,7] (8-bit) of the 8 columns.
 // 4-bit: the high nibble of each byte is taken in place (value 16 q, exact in fp16
