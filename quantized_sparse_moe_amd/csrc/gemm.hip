@@ -9,9 +9,14 @@
 // [OMLX] "Fusion principle": gate row j and up row j of one expert are handled by the
 // same wave, so SwiGLU is formed in registers and only h leaves the kernel.
 //
-// Tile: 128 activation rows x 256 weight rows, K step 64 (one quantization group), four
-// waves, each owning 64 weight rows (four 16-row MFMA subtiles) against all 128 rows
-// (eight subtiles): 32 v_mfma_f32_16x16x32_f16 per 32-wide K slice.
+// Tile: 160 activation rows x 256 weight rows, K step 64 (one quantization group), four
+// waves, each owning 64 weight rows (four 16-row MFMA subtiles) against all 160 rows
+// (ten subtiles): 40 v_mfma_f32_16x16x32_f16 per 32-wide K slice.  160 rows take an
+// expert's whole bin in one tile at the mean load of the prefill workload (128 rows per
+// expert, uneven), where 128-row tiles left a sliver tile behind half of the experts that
+// costs a full pass of dequantization for a few rows.  Every tile runs all ten subtiles
+// (rows past the tile repeat a valid row and are discarded): per-subtile branches cost
+// more than the idle MFMAs.
 //
 // Data movement: every operand of a K step -- the activation rows (fp16), the weight
 // codes, scales and biases -- goes global -> LDS by direct-to-LDS loads
@@ -35,8 +40,6 @@
 // down projection -> slot row T*k + t.  k_combine then adds each token's k slot rows in
 // ascending expert order and its shared row, in fp32, and writes y: a deterministic,
 // atomic-free combine.
-#include <type_traits>
-
 #include "common.h"
 #include "internal.h"
 
@@ -56,9 +59,10 @@ struct Cfg {
     static constexpr int B_BYTES = BN * BK * BITS / 8;        // codes, 32 or 64 B per row
     static constexpr int S_BYTES = BN * 4;                    // one dword per row (fp16 in the low half)
     static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
-    static constexpr int NSTAGE = BITS == 4 ? 3 : 2;
+    static constexpr int NSTAGE = 2;                          // two workgroups per CU fit
     static constexpr int B_DMA = B_BYTES / 1024 / 4;          // per wave and stage
-    static constexpr int DMA = 4 + B_DMA + 2;                 // A, codes, scales, biases
+    static constexpr int A_DMA = MT / 2;                      // 8-row pieces per wave and stage
+    static constexpr int DMA = A_DMA + B_DMA + 2;             // A, codes, scales, biases
     static constexpr int LDS = NSTAGE * STAGE;
 };
 
@@ -177,12 +181,12 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     const int ngrp = Kdim / 64;
 
     // ---- per-lane sources of the direct-to-LDS loads
-    const uint16_t *asrc[4];
+    const uint16_t *asrc[C::A_DMA];
     {
         const int ach = (lane & 7) ^ (lane >> 3);      // swizzled chunk this lane fetches
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int r = 32 * wave + 8 * i + (lane >> 3);
+        for (int i = 0; i < C::A_DMA; ++i) {
+            int r = 8 * C::A_DMA * wave + 8 * i + (lane >> 3);
             r = r < nrows ? r : nrows - 1;             // rows past the tile repeat a valid one
             int64_t src;
             if (MODE == 0) {
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     auto issue = [&](int k) __attribute__((always_inline)) {
         uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma16(asrc[i] + k * BK, st + (32 * wave + 8 * i) * 128);
+        for (int i = 0; i < C::A_DMA; ++i) dma16(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
         uint8_t *bst = st + C::A_BYTES;
 #pragma unroll
         for (int d = 0; d < C::B_DMA; ++d) {
@@ -297,11 +301,9 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
 
     // The K loop: per 64-wide step, one barrier (stage k visible, stage k-1 consumed),
     // the refill of stage k-1's buffer with stage k+NSTAGE-1, then two MFMA blocks
-    // (32-wide slices), each on a weight slice dequantized just before it.  FULL: all
-    // eight row subtiles live (no per-subtile branches, so every fragment read of a
-    // block is issued ahead of its MFMAs).
-    auto kloop = [&](auto full) __attribute__((always_inline)) {
-        constexpr bool FULL = decltype(full)::value;
+    // (32-wide slices), each on a weight slice dequantized just before it.  All ten row
+    // subtiles run, so every fragment read of a block is issued ahead of its MFMAs.
+    auto kloop = [&]() __attribute__((always_inline)) {
         for (int k = 0; k < nk; ++k) {
             // stage k has landed once at most the later stages' loads are outstanding
             const int issued = k + C::NSTAGE - 1 < nk ? C::NSTAGE - 2 : nk - 1 - k;
@@ -315,21 +317,19 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
                 const int pos = (2 * cg + s) ^ (n16 & 7);
                 f16x8 A[MT];
 #pragma unroll
-                for (int i = 0; i < MT; ++i)
-                    if (FULL || i < msub) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
+                for (int i = 0; i < MT; ++i) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
                 load_codes(k, s, cw);
                 f16x8 B[4];
                 deq(cw, B);
 #pragma unroll
                 for (int i = 0; i < MT; ++i)
-                    if (FULL || i < msub)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], B[j], acc[i][j], 0, 0, 0);
             }
         }
     };
-    // MODE 1: the (token, slot) position and routing weight of tile row `tid` (tid < 128)
+    // MODE 1: the (token, slot) position and routing weight of tile row `tid` (tid < BM)
     // are fetched now, their latency hidden by the K loop, and parked in LDS after it
     __shared__ int s_pos[BM];
     __shared__ float s_w[BM];
@@ -340,8 +340,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     for (int p = 0; p < C::NSTAGE - 1; ++p)
         if (p < nk) issue(p);
     if (MODE == 1 && tid < BM) my_w = a.w[my_pos];
-    if (msub == MT) kloop(std::true_type{});
-    else kloop(std::false_type{});
+    kloop();
     if (MODE == 1 && tid < BM) {
         s_pos[tid] = my_pos;
         s_w[tid] = my_w;

@@ -42,7 +42,7 @@ hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBu
 
 // ------------------------------------------------------------------- prefill T >= 2
 constexpr int ROUTER_TOKENS = 16;  // tokens per router workgroup (= one binning block)
-constexpr int GEMM_MT = 8;         // 16-row MFMA subtiles per GEMM tile
+constexpr int GEMM_MT = 10;        // 16-row MFMA subtiles per GEMM tile (even)
 constexpr int GEMM_BM = 16 * GEMM_MT;
 
 struct Tile {                      // one row block of one expert bin
