@@ -167,7 +167,9 @@ def bench_prefill(qs, torch, syn, cfg, T, steps, warmup, copies):
     descs = _dev_layer_copies(qs, torch, L, copies)
     x = torch.from_numpy(syn.make_x(T, L.hidden, seed=0).view(np.int16)).cuda()
     y = torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda")
-    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
+    # a workspace for the whole T, so that the call runs unchunked (one pass over the
+    # expert weights); with the default size a long prompt runs in 4096-token chunks
+    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T, chunk=T), dtype=torch.uint8, device="cuda")
 
     def step(i):
         qs.moe_layer_forward(descs[i % copies], x, y=y, workspace=ws)

@@ -117,9 +117,26 @@ const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL
  * allocate it zero-filled) and then belongs to the library; a caller that writes it
  * must zero it again before the next call.  The rest is scratch whose contents are
  * undefined between calls.  Calls that share one workspace must not overlap in time
- * (issue them on one stream).  ~200 MiB at T = 4096, hidden 2048, inter 512, top-8.
+ * (issue them on one stream).  T >= 2 is processed in chunks inside one call
+ * ([LILY] "Reduce intermediate and state traffic": bounded intermediate buffers): this
+ * size is for chunks of QSMOE_PREFILL_CHUNK tokens, so it stops growing there (~200 MiB
+ * for any T >= 4096 at hidden 2048, inter 512, top-8).
  */
 size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T);
+
+/* Default tokens per prefill chunk (T >= 2). */
+#define QSMOE_PREFILL_CHUNK 4096
+
+/*
+ * Bytes of workspace for T tokens run in chunks of `chunk` tokens (0: the default
+ * QSMOE_PREFILL_CHUNK; chunk >= T: unchunked).  moe_route / moe_layer_forward take the
+ * largest chunk whose buffers fit in the ws_bytes they are given (at least the default),
+ * so a caller that can spare the memory avoids re-reading the expert weights once per
+ * chunk.  Chunking changes no result: every token is computed by the same kernels
+ * whatever chunk it falls in, bit for bit.  SIZE_MAX for an invalid descriptor, T or
+ * chunk < 0.
+ */
+size_t qsmoe_workspace_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk);
 
 /*
  * Router only ([LILY] "Qwen creates three distinct workload shapes"): fp32 logits

@@ -47,7 +47,8 @@ class qsmoe_layer_desc(ctypes.Structure):
                 ("s_gate", qsmoe_qmat), ("s_up", qsmoe_qmat), ("s_down", qsmoe_qmat)]
 
 
-EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size", "moe_route",
+EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size",
+           "qsmoe_workspace_size_chunked", "moe_route",
            "moe_layer_forward", "q8_gemv", "q8_pack_rows16")
 
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.qsmoe_status_string.argtypes = [I32]
         L.qsmoe_workspace_size.restype = SZ
         L.qsmoe_workspace_size.argtypes = [P, I64]
+        L.qsmoe_workspace_size_chunked.restype = SZ
+        L.qsmoe_workspace_size_chunked.argtypes = [P, I64, I64]
         L.moe_route.restype = I32
         L.moe_route.argtypes = [P, P, I64, P, P, P, SZ, P]
         L.moe_layer_forward.restype = I32
@@ -179,8 +182,17 @@ class LayerDesc:
 
 
 # ------------------------------------------------------------------- entry points
-def qsmoe_workspace_size(desc: LayerDesc, T: int) -> int:
-    n = lib().qsmoe_workspace_size(desc.ptr, int(T))
+# tokens per prefill chunk inside one call (QSMOE_PREFILL_CHUNK in include/qsmoe.h)
+PREFILL_CHUNK = 4096
+
+
+def qsmoe_workspace_size(desc: LayerDesc, T: int, chunk: Optional[int] = None) -> int:
+    """Workspace bytes for T tokens; `chunk` (tokens per prefill chunk, T for none) as in
+    qsmoe_workspace_size_chunked, default QSMOE_PREFILL_CHUNK."""
+    if chunk is None:
+        n = lib().qsmoe_workspace_size(desc.ptr, int(T))
+    else:
+        n = lib().qsmoe_workspace_size_chunked(desc.ptr, int(T), int(chunk))
     if n == ctypes.c_size_t(-1).value:
         raise QsmoeError(QSMOE_ERR_UNSUPPORTED, "qsmoe_workspace_size")
     return n

@@ -128,12 +128,28 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     return b;
 }
 
-size_t ws_size(const qsmoe_layer_desc *d, int64_t T) {
+// T >= 2 runs in chunks, one after another on the stream, each through the whole
+// prefill sequence in the same workspace: chunks of `chunk` tokens need this much
+size_t ws_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk) {
     size_t n = 0;
     if (T <= 0) return 0;
     if (T == 1) carve_decode(d, nullptr, &n);
-    else carve_prefill(d, T, nullptr, &n);
+    else carve_prefill(d, T < chunk ? T : chunk, nullptr, &n);
     return n;
+}
+size_t ws_size(const qsmoe_layer_desc *d, int64_t T) { return ws_size_chunked(d, T, QSMOE_PREFILL_CHUNK); }
+
+// the largest chunk (at least min(T, QSMOE_PREFILL_CHUNK)) whose buffers fit in ws_bytes
+int64_t pick_chunk(const qsmoe_layer_desc *d, int64_t T, size_t ws_bytes) {
+    int64_t lo = T < QSMOE_PREFILL_CHUNK ? T : QSMOE_PREFILL_CHUNK;
+    if (ws_size_chunked(d, T, T) <= ws_bytes) return T;
+    int64_t hi = T;                                   // lo fits, hi does not
+    while (hi - lo > 1) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (ws_size_chunked(d, T, mid) <= ws_bytes) lo = mid;
+        else hi = mid;
+    }
+    return lo;
 }
 
 qsmoe_status check_ws(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t ws_bytes) {
@@ -170,6 +186,13 @@ size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T) {
     return ws_size(d, T);
 }
 
+size_t qsmoe_workspace_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk) {
+    if (check_desc(d) != QSMOE_OK) return SIZE_MAX;
+    if (T > MAX_TOKENS || chunk < 0) return SIZE_MAX;
+    if (chunk == 0) chunk = QSMOE_PREFILL_CHUNK;
+    return ws_size_chunked(d, T, chunk < 2 ? 2 : chunk);
+}
+
 qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int32_t *topk_idx,
                        float *topk_w, void *ws, size_t ws_bytes, void *stream) {
     qsmoe_status s = check_desc(d);
@@ -188,10 +211,16 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
         return dev(launch_decode_route(L, (const uint16_t *)x, b, topk_idx, topk_w, st));
     }
     size_t n;
-    PrefillBufs b = carve_prefill(d, T, ws, &n);
-    b.idx = topk_idx;
-    b.w = topk_w;
-    return dev(launch_prefill_router(L, (const uint16_t *)x, T, b, false, nullptr, nullptr, st));
+    const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
+    PrefillBufs b = carve_prefill(d, C, ws, &n);
+    for (int64_t t0 = 0; t0 < T; t0 += C) {
+        const int64_t Tc = T - t0 < C ? T - t0 : C;
+        b.idx = topk_idx + t0 * K;
+        b.w = topk_w + t0 * K;
+        const hipError_t e = launch_prefill_router(L, (const uint16_t *)x + t0 * H, Tc, b, false, nullptr, nullptr, st);
+        if (e != hipSuccess) return QSMOE_ERR_DEVICE;
+    }
+    return QSMOE_OK;
 }
 
 qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t T, void *y,
@@ -215,12 +244,22 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_layer(L, xx, b, y, y_dtype, topk_idx, topk_w, st));
     }
+    // chunks of the prefill sequence: every token goes through the same kernels whatever
+    // the chunk it falls in, so the result is bit-identical to one unchunked pass
     size_t n;
-    const PrefillBufs b = carve_prefill(d, T, ws, &n);
-    e = launch_prefill_router(L, xx, T, b, true, topk_idx, topk_w, st);
-    if (e == hipSuccess) e = launch_prefill_binning(L, T, b, st);
-    if (e == hipSuccess) e = launch_prefill_gemms(L, T, b, y, y_dtype, st);
-    return dev(e);
+    const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
+    const PrefillBufs b = carve_prefill(d, C, ws, &n);
+    const size_t ysz = y_dtype == QSMOE_F32 ? 4 : 2;
+    for (int64_t t0 = 0; t0 < T; t0 += C) {
+        const int64_t Tc = T - t0 < C ? T - t0 : C;
+        void *yc = (char *)y + (size_t)(t0 * H) * ysz;
+        e = launch_prefill_router(L, xx + t0 * H, Tc, b, true, topk_idx ? topk_idx + t0 * K : nullptr,
+                                  topk_w ? topk_w + t0 * K : nullptr, st);
+        if (e == hipSuccess) e = launch_prefill_binning(L, Tc, b, st);
+        if (e == hipSuccess) e = launch_prefill_gemms(L, Tc, b, yc, y_dtype, st);
+        if (e != hipSuccess) return QSMOE_ERR_DEVICE;
+    }
+    return QSMOE_OK;
 }
 
 qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,

@@ -142,6 +142,19 @@ def test_workspace_sizes():
     T, H, I, K = 4096, 2048, 512, 8
     assert f(T) >= 2 * T * H + 2 * (T * K + T) * I + 2 * (T * K + T) * H
     assert f(T) < 400 * 2 ** 20
+    # longer prompts run in chunks of QSMOE_PREFILL_CHUNK tokens: the size stops there
+    assert q.PREFILL_CHUNK == 4096
+    assert f(4095) < f(4096) == f(4097) == f(16384) == f(1 << 20)
+    g = lambda T, c: q.lib().qsmoe_workspace_size_chunked(ctypes.byref(d), T, c)
+    assert g(16384, 0) == f(16384) and g(1, 16384) == f(1) and g(100, 4096) == f(100)
+    assert g(16384, 16384) > g(16384, 8192) > g(16384, 4096) == f(16384)
+    assert g(16384, -1) == ctypes.c_size_t(-1).value
+
+
+def test_prefill_chunk_matches_header():
+    import re
+    hdr = open(os.path.join(ROOT, "include", "qsmoe.h")).read()
+    assert int(re.search(r"#define QSMOE_PREFILL_CHUNK (\d+)", hdr).group(1)) == q.PREFILL_CHUNK
 
 
 def test_q8_validation():

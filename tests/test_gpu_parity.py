@@ -208,6 +208,34 @@ def test_permutation_and_chunking_invariance(torch, qs):
     assert torch.equal(torch.cat(parts), y)
 
 
+def test_chunked_prefill_bit_identical(torch, qs):
+    """T = 2 * chunk + 100 tokens: with the default workspace one call runs three chunks;
+    with a workspace for the whole T it runs unchunked; with one for 5000 tokens it runs
+    5000 + 3292.  Outputs and routing must be identical bit for bit, and sampled tokens
+    (both sides of each chunk boundary) must match the oracle."""
+    L = layer("PREFILL")
+    desc = qs.LayerDesc.from_host(L)
+    C = qs.PREFILL_CHUNK
+    T = 2 * C + 100
+    x_np = syn.make_x(T, L.hidden, seed=17)
+    x = to_dev(x_np, torch)
+    outs = []
+    for chunk in (None, T, 5000):
+        ws = torch.zeros(qs.qsmoe_workspace_size(desc, T, chunk), dtype=torch.uint8, device="cuda")
+        idx = torch.empty((T, L.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, L.top_k), dtype=torch.float32, device="cuda")
+        y = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16, topk_idx=idx, topk_w=w, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((y, idx.cpu().numpy(), w.cpu().numpy()))
+        del ws
+    for y, idx, w in outs[1:]:
+        assert torch.equal(y, outs[0][0])
+        assert (idx == outs[0][1]).all() and (w == outs[0][2]).all()
+    y, idx, w = outs[0]
+    rows = np.array([0, C - 1, C, 2 * C - 1, 2 * C, T - 1])
+    oracle_check(L, x_np, y_to_np(y, torch), idx, w, True, "chunked prefill", rows=rows)
+
+
 def test_decode_repeat_bit_identical(torch, qs):
     """The one-launch decode kernel hands logits and h between workgroups through the
     workspace: many back-to-back calls, alternating inputs and two layers sharing one
