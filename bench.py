@@ -6,13 +6,14 @@ batch of synthetic input already resident in HBM.  The headline line reports the
 batch-1 decode workload (hidden 2048, 256 experts top-8 + 1 shared, expert inter 512,
 4-bit affine group-64 weights, T = 1): tokens/s, with the layer's algorithmic weight
 bytes over HBM peak as the roofline.  Extra keys report the prefill (T = 4096), the
-skewed long prefill (T = 16384, 8-bit, Zipf router bias) and the dense Q8_0 GEMV.
+skewed long prefill (T = 16384, 8-bit, Zipf router bias), the dense Q8_0 GEMV and
+(--only smallT) the decode layer at T = 1, 2, 4, 8.
 
 Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256 MB
 Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
 HIP graph; HIP events on the replay stream bracket the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,smallT,copy]
 """
 from __future__ import annotations
 
@@ -162,6 +163,39 @@ def bench_decode(qs, torch, syn, steps, warmup, copies=40):
     return L, ms, nbytes
 
 
+def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 8), copies=40):
+    """Small batches of the decode layer (the verification / batched-decode shape): per T,
+    the time per call and the bytes a call must read -- router weights, each expert that
+    any of the T tokens selects (once), the shared expert, x and y -- per token."""
+    L = syn.make_layer(**syn.DECODE)
+    descs = _dev_layer_copies(qs, torch, L, copies)
+    eb = expert_bytes(L.hidden, L.inter, L.bits)
+    res = []
+    for T in Ts:
+        xs = [torch.from_numpy(syn.make_x(T, L.hidden, seed=1000 * T + l).view(np.int16)).cuda()
+              for l in range(copies)]
+        ys = [torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+        ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
+        union = []
+        for l in range(copies):
+            idx, _ = qs.moe_route(descs[l], xs[l], workspace=ws)
+            union.append(len(np.unique(idx.cpu().numpy())))
+        torch.cuda.synchronize()
+
+        def step(i):
+            l = i % copies
+            qs.moe_layer_forward(descs[l], xs[l], y=ys[l], workspace=ws)
+
+        ms = _graph_time(torch, step, steps, warmup)
+        experts = float(np.mean(union))
+        nbytes = L.n_experts * L.hidden * 2 + (experts + 1) * eb + 2 * T * L.hidden * 2
+        res.append({"T": T, "us_per_call": ms * 1e3, "tokens_per_s": T / (ms * 1e-3),
+                    "experts_read": experts, "bytes_per_token": nbytes / T,
+                    "GB_per_s": nbytes / (ms * 1e-3) / 1e9})
+        del ws
+    return res
+
+
 def bench_prefill(qs, torch, syn, cfg, T, steps, warmup, copies):
     L = syn.make_layer(**cfg)
     descs = _dev_layer_copies(qs, torch, L, copies)
@@ -260,6 +294,8 @@ def main(argv=None):
         tf = flops / (ms * 1e-3) / 1e12
         out["skew"] = {"tokens_per_s": syn.SKEW_T / (ms * 1e-3), "ms_per_step": ms, "T": syn.SKEW_T,
                        "steps": steps, "tflops": tf, "frac_mfma": tf / MFMA_F16_PEAK_TFS}
+    if "smallT" in only:
+        out["small_t"] = bench_small_t(qs, torch, syn, max(40, args.steps // 10), args.warmup)
     if "q8" in only:
         steps = max(16, args.steps // 4)
         ms, nbytes = bench_q8(qs, torch, syn, steps, args.warmup)
