@@ -35,7 +35,7 @@ GROUP = 64
 # figure holds only for the kernel sources it was measured on, identified by their
 # sha256; once they change the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/common.h", "csrc/internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "6b801e576120c46043e362a964cc9f81a41ad4388d60992ec5baa1d66e0e1911", "bytes": 18508354}
+DECODE_TRAFFIC = {"sources_sha256": "e5036e8073e8b40b44842dfaf72352e6edad2c1b8726112594f7f970fc0ddcf2", "bytes": 17888317}
 
 
 # ----------------------------------------------------------- algorithmic accounting
