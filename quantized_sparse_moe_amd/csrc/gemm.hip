@@ -20,7 +20,10 @@
 //
 // Data movement: every operand of a K step -- the activation rows (fp16), the weight
 // codes, scales and biases -- goes global -> LDS by direct-to-LDS loads
-// (global_load_lds), which take no registers and no ALU.  A ring of stages keeps two K
+// (global_load_lds), which take no registers and no ALU.  Scales and biases come 8 groups
+// (16 bytes) per row at a time every 8 K steps (4-bit; 2 groups for 8-bit, whose larger
+// code stages leave less LDS): a per-step 2-byte load per row costs the address unit as
+// much as a 16-byte one, and cost 17 % of the layer time.  A ring of stages keeps two K
 // steps in flight (one for 8-bit codes, whose stages are larger) while the current
 // one is multiplied; each wave waits only for its own loads (vmcnt) and one barrier
 // per step publishes the stage to the whole workgroup.  The position of each 16-byte
@@ -57,14 +60,17 @@ template <int BITS>
 struct Cfg {
     static constexpr int A_BYTES = BM * BK * 2;               // fp16 rows, 128 B each
     static constexpr int B_BYTES = BN * BK * BITS / 8;        // codes, 32 or 64 B per row
-    static constexpr int S_BYTES = BN * 4;                    // one dword per row (fp16 in the low half)
-    static constexpr int STAGE = A_BYTES + B_BYTES + 2 * S_BYTES;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int NSTAGE = 2;                          // two workgroups per CU fit
+    // scales and biases: a ring of two windows of up to WMAX groups per row (16 or 4 bytes)
+    static constexpr int WMAX = BITS == 4 ? 8 : 2;
+    static constexpr int S_BYTES = BN * (WMAX == 8 ? 16 : 4); // one window of scales (or biases)
     static constexpr int B_DMA = B_BYTES / 1024 / 4;          // per wave and stage
     static constexpr int A_DMA = MT / 2;                      // 8-row pieces per wave and stage
     static constexpr int DMA = A_DMA + B_DMA + 2;             // A, codes, scales, biases
-    static constexpr int LDS = NSTAGE * STAGE;
+    static constexpr int LDS = NSTAGE * STAGE + 4 * S_BYTES;
 };
+static_assert(Cfg<4>::NSTAGE == 2 && Cfg<8>::NSTAGE == 2, "every stage wait is a full drain (vmcnt 0)");
 
 struct GemmArgs {
     Layer L;
@@ -79,12 +85,16 @@ struct GemmArgs {
     void *y;
     int y_dtype;
     int nb;                          // column blocks per tile
+    int wlog;                        // log2 of the scale / bias window (groups per row per load)
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
 
 __device__ __forceinline__ void dma16(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 4, 0, 0);
 }
 __device__ __forceinline__ void dma2(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 2, 0, 0);   // lands zero-extended in a dword
@@ -233,9 +243,22 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
             if constexpr (BITS == 4) dma16(bsrc[d] + k * 32, bst + (64 * wave + 32 * d) * 32);
             else dma16(bsrc[d] + k * 64, bst + (64 * wave + 16 * d) * 64);
         }
-        uint8_t *sst = bst + C::B_BYTES;
-        dma2(ssrc + k, sst + 64 * wave * 4);
-        dma2(bisrc + k, sst + C::S_BYTES + 64 * wave * 4);
+        // scales and biases: W = 2^wlog groups of each row every W K steps, into a ring of
+        // two windows (one 2-byte read per lane costs the address unit as much as a 16-byte
+        // one, so the wider and rarer the better)
+        if ((k & ((1 << a.wlog) - 1)) == 0) {
+            uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES;
+            if (C::WMAX == 8 && a.wlog == 3) {                    // 16 bytes per row
+                dma16(ssrc + k, sw + 64 * wave * 16);
+                dma16(bisrc + k, sw + C::S_BYTES + 64 * wave * 16);
+            } else if (a.wlog == 1) {                             // 4 bytes per row
+                dma4(ssrc + k, sw + 64 * wave * 4);
+                dma4(bisrc + k, sw + C::S_BYTES + 64 * wave * 4);
+            } else {                                              // 2 bytes in a 4-byte slot
+                dma2(ssrc + k, sw + 64 * wave * 4);
+                dma2(bisrc + k, sw + C::S_BYTES + 64 * wave * 4);
+            }
+        }
     };
 
     f32x4 acc[MT][4];
@@ -272,12 +295,16 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         }
     };
     auto load_sb = [&](int k, f16x2 (&sc)[4], f16x2 (&sc16)[4], f16x2 (&bi)[4]) __attribute__((always_inline)) {
-        const uint32_t *sst = (const uint32_t *)(smem + (k % C::NSTAGE) * C::STAGE + C::A_BYTES + C::B_BYTES);
+        // row rs, group k % W of the window: 16 (W = 8) or 4 bytes per row, 2 bytes per
+        // group (W = 1: the low half of the dword a 2-byte load fills)
+        const int pitch = a.wlog == 3 ? 16 : 4;
+        const uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES +
+                            2 * (k & ((1 << a.wlog) - 1));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rs = 64 * wave + 16 * j + n16;
-            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sst[rs]);
-            const _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)sst[BN + rs]);
+            const _Float16 sv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + rs * pitch));
+            const _Float16 bv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + C::S_BYTES + rs * pitch));
             sc[j] = (f16x2){sv, sv};
             const _Float16 sv16 = sv * (_Float16)0.0625f;        // exact: scales are normal numbers
             sc16[j] = (f16x2){sv16, sv16};
@@ -462,16 +489,40 @@ inline unsigned grid_for(int64_t tiles, int nb) {
     return (unsigned)(((tiles + 7) / 8) * per);
 }
 
+// log2 of the widest scale / bias window (at most wmax groups) for matrices with `cols`
+// columns: every row's run of W groups must be a multiple of W and 2W-byte aligned
+int window_log(const QMat *const *ms, int n, int cols, int wmax) {
+    const int ngrp = cols / 64;
+    for (int w = wmax; w > 1; w >>= 1) {
+        bool ok = ngrp % w == 0;
+        for (int i = 0; i < n; ++i)
+            ok = ok && (uintptr_t)ms[i]->scales % (2 * w) == 0 && (uintptr_t)ms[i]->biases % (2 * w) == 0;
+        if (ok) return w == 8 ? 3 : w == 4 ? 2 : 1;
+    }
+    return 0;
+}
+
 template <int BITS>
 hipError_t gemms(GemmArgs a, hipStream_t s) {
+    using C = Cfg<BITS>;
     const Layer &L = a.L;
     const int64_t maxr = prefill_max_routed_tiles(a.T, L.K, L.E);
     const int64_t maxs = L.has_shared ? (a.T + GEMM_BM - 1) / GEMM_BM : 0;
     // [gate; up] + SwiGLU over routed and shared tiles
     a.nb = L.I / 128;
+    {
+        const QMat *ms[4] = {&L.gate, &L.up, &L.s_gate, &L.s_up};
+        a.wlog = window_log(ms, L.has_shared ? 4 : 2, L.H, C::WMAX);
+        if (a.wlog == 2) a.wlog = 1;                       // windows of 8, 2 or 1 groups
+    }
     hipLaunchKernelGGL((k_gemm<BITS, 0>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
     // routed down -> slots
     a.nb = (L.H + BN - 1) / BN;
+    {
+        const QMat *ms[2] = {&L.down, &L.s_down};
+        a.wlog = window_log(ms, L.has_shared ? 2 : 1, L.I, C::WMAX);
+        if (a.wlog == 2) a.wlog = 1;
+    }
     hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr, a.nb)), dim3(NT), 0, s, a);
     // shared down -> its own slot rows
     if (L.has_shared) hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(grid_for(maxs, a.nb)), dim3(NT), 0, s, a);
