@@ -236,6 +236,46 @@ def test_chunked_prefill_bit_identical(torch, qs):
     oracle_check(L, x_np, y_to_np(y, torch), idx, w, True, "chunked prefill", rows=rows)
 
 
+def _shifted_desc(torch, qs, base, shift):
+    """The layer of `base` with every scale and bias array copied to an address `shift`
+    fp16 elements past an allocation (2-byte or 4-byte aligned instead of 256-byte)."""
+    made = {}
+
+    def moved(t):
+        if t.data_ptr() not in made:
+            buf = torch.empty(t.numel() + shift, dtype=t.dtype, device=t.device)
+            view = buf[shift:]
+            view.copy_(t.reshape(-1))
+            made[t.data_ptr()] = (buf, view.view(t.shape))
+        return made[t.data_ptr()][1]
+
+    def qm(m):
+        codes, scales, biases, stride, row0 = m
+        return (codes, moved(scales), moved(biases), stride, row0)
+
+    rw, rb, g, u, d, sh = base._keep
+    shared = None if sh is None else tuple(qm(m) for m in sh)
+    desc = qs.LayerDesc(base.hidden, base.inter, base.n_experts, base.top_k, base.bits, rw, qm(g), qm(u), qm(d),
+                        router_bias=rb, shared=shared)
+    desc._made = made
+    return desc
+
+
+@pytest.mark.parametrize("cfg", ["PREFILL", "SKEW"])
+def test_scale_staging_paths_bit_identical(torch, qs, cfg):
+    """The grouped GEMM stages scales and biases 8, 2 or 1 groups per row at a time
+    depending on their alignment; every path must give the same bits (T = 64 and T = 1)."""
+    L = layer(cfg)
+    base = qs.LayerDesc.from_host(L)
+    x_np = syn.make_x(64, L.hidden, seed=29)
+    ref = [run_layer(torch, qs, L, x_np[:T], desc=base)[0] for T in (64, 1)]
+    for shift in (1, 2):                      # 2-byte and 4-byte aligned scales / biases
+        desc = _shifted_desc(torch, qs, base, shift)
+        for T, r in zip((64, 1), ref):
+            y = run_layer(torch, qs, L, x_np[:T], desc=desc)[0]
+            assert torch.equal(y, r), (cfg, shift, T)
+
+
 def test_decode_repeat_bit_identical(torch, qs):
     """The one-launch decode kernel hands logits and h between workgroups through the
     workspace: many back-to-back calls, alternating inputs and two layers sharing one
