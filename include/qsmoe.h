@@ -163,9 +163,11 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T,
  *   x        [T][hidden] bf16, |x| < 65504 (activations are consumed as fp16)
  *   y        [T][hidden], y_dtype QSMOE_BF16 (round-to-nearest-even) or QSMOE_F32
  *   topk_idx, topk_w  optional outputs as in moe_route (NULL to skip)
- * Path: T == 1 runs the batch-1 decode kernels (register dequantization on the
- * vector ALUs, fp32 intermediates); T >= 2 runs the grouped-GEMM path (MFMA on
- * fp16 operands dequantized in registers, fp32 accumulation, fp16 intermediates).
+ * Path: T == 1 runs the batch-1 decode kernel (register dequantization on the vector
+ * ALUs, fp32 intermediates); T = 2 .. 4 the same kernel design over all tokens at once,
+ * each expert any token selected read once (when (top_k + 1) * inter * T <= 49216);
+ * larger T runs the grouped-GEMM path (MFMA on fp16 operands dequantized in registers,
+ * fp32 accumulation, fp16 intermediates).
  * For a given T the result does not depend on whether gate/up are fused or separate,
  * nor on the other tokens of the call (tokens are independent), bit for bit.
  */

@@ -210,6 +210,11 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_route(L, (const uint16_t *)x, b, topk_idx, topk_w, st));
     }
+    if (decode_small_eligible(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        return dev(launch_decode_small_route(L, (const uint16_t *)x, T, b, topk_idx, topk_w, st));
+    }
     size_t n;
     const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
     PrefillBufs b = carve_prefill(d, C, ws, &n);
@@ -243,6 +248,11 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
         size_t n;
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_layer(L, xx, b, y, y_dtype, topk_idx, topk_w, st));
+    }
+    if (decode_small_eligible(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        return dev(launch_decode_small_layer(L, xx, T, b, y, y_dtype, topk_idx, topk_w, st));
     }
     // chunks of the prefill sequence: every token goes through the same kernels whatever
     // the chunk it falls in, so the result is bit-identical to one unchunked pass

@@ -263,9 +263,8 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
 // the top-k: lanes j < K return (id, weight) of the j-th selected expert in ascending
 // id.  One poll is in flight at a time: a read still in flight when the data is found
 // would have to be waited for before its registers are reused, a full extra round trip.
-__device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
+__device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t tag, int E, int K) {
     const int lane = threadIdx.x & 63;
-    const uint64_t *lg = (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE);
     const uint64_t none = (uint64_t)tag << 32;
     uint64_t w[4];
     for (uint32_t n = 0;; ++n) {
@@ -287,6 +286,10 @@ __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
     TopkOut tk = wave_topk_regs(v, E, K);
     tk.idx = min(max(tk.idx, 0), E - 1);
     return tk;
+}
+__device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
+    return select_topk_from(ctl, (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE),
+                            tag, E, K);
 }
 
 // Consumer: wave 0 waits (bounded) for the published selection, one poll in flight;
@@ -592,6 +595,426 @@ int n_compute_units() {
     return n;
 }
 
+// ------------------------------------------------------------------ small batches
+// [LILY] "Optimize the single-row weight path" at T = 2 .. SM_TMAX tokens (batched or
+// verification decode): the T = 1 structure with every role covering all T tokens.  The
+// routed experts are the union U of the tokens' selections: each touched expert's
+// weights are read once (G: gate/up rows for the tokens that chose it; D: down rows for
+// all of them).  The hand-off regions of the T = 1 path are reused with other strides
+// (every word carries the call's tag, so the two paths cannot mistake each other's words).
+constexpr int SM_TMAX = 4;
+constexpr int SM_LCOPIES = 8;
+constexpr int SM_TE = 256;                                  // logit words per token and copy
+constexpr int SM_LSTRIDE = 2 * SM_TMAX * SM_TE + 64;        // u32 per logits copy
+static_assert(SM_LCOPIES * SM_LSTRIDE <= LOGIT_COPIES * LOGIT_STRIDE, "small-T logits region");
+constexpr int SM_HCOPIES = 2;
+constexpr int SM_HSTRIDE = H_COPIES * H_STRIDE / SM_HCOPIES;   // u32 per h copy
+constexpr int SM_HWORDS = SM_HSTRIDE / 2 - 32;                 // h words per copy
+static_assert(2 * SM_TMAX * 16 <= TOPK_STRIDE / 2, "small-T selection region");
+
+struct SmallArgs {
+    Layer L;
+    const uint16_t *x;          // [T][H]
+    uint32_t *ctl;
+    int32_t *out_idx;           // [T][K] or null
+    float *out_w;
+    void *y;                    // [T][H]
+    int y_dtype;
+    int T, shared;
+    int nR, nP, nS, nG, nD;     // route only: nP = 1, nS = nG = nD = 0
+    int route_only;
+    int lprg, lprd;
+};
+
+// wave 0 waits for the published selection of all tokens (entry l = t K + j: id word,
+// weight word); the workgroup then has s_si / s_sw, the union U in ascending id (s_ul,
+// s_nu) and, per union slot and token, the token's position of that expert (s_jt, -1 if
+// the token did not choose it)
+struct SmallSel {
+    int si[SM_TMAX * 16];
+    float sw[SM_TMAX * 16];
+    uint32_t ub[8];
+    int ul[SM_TMAX * 16];
+    int jt[SM_TMAX * 16][SM_TMAX];
+    int nu;
+};
+__device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, SmallSel &S) {
+    const int tid = threadIdx.x, n = T * K;
+    if (tid < 8) S.ub[tid] = 0u;
+    if (tid < SM_TMAX * 16 * SM_TMAX) (&S.jt[0][0])[tid] = -1;
+    if (tid < 64) {
+        const int lane = tid;
+        const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
+        const bool act = lane < n;
+        const uint64_t none = (uint64_t)tag << 32;
+        uint64_t w0, w1;
+        for (uint32_t it = 0;; ++it) {
+            w0 = act ? ld_dev64(tp + 2 * lane) : none;
+            w1 = act ? ld_dev64(tp + 2 * lane + 1) : none;
+            if (__ballot(tag_of(w0) != tag || tag_of(w1) != tag) == 0ull) break;
+            if (it > SPIN_LIMIT) {
+                if (lane == 0) raise_error(ctl);
+                break;
+            }
+            poll_pause(it);
+        }
+        if (act) {
+            S.si[lane] = min(max((int)(uint32_t)w0, 0), E - 1);
+            S.sw[lane] = __uint_as_float((uint32_t)w1);
+        }
+    }
+    __syncthreads();
+    if (tid < n) atomicOr(&S.ub[S.si[tid] >> 5], 1u << (S.si[tid] & 31));
+    __syncthreads();
+    auto rank = [&](int e) {                                 // union slot of expert e
+        int r = __popc(S.ub[e >> 5] & ((1u << (e & 31)) - 1u));
+        for (int w = 0; w < (e >> 5); ++w) r += __popc(S.ub[w]);
+        return r;
+    };
+    if (tid < 256 && ((S.ub[tid >> 5] >> (tid & 31)) & 1u)) S.ul[rank(tid)] = tid;
+    if (tid < n) S.jt[rank(S.si[tid])][tid / K] = tid % K;
+    if (tid == 0) {
+        int c = 0;
+        for (int w = 0; w < 8; ++w) c += __popc(S.ub[w]);
+        S.nu = c;
+    }
+    __syncthreads();
+}
+
+// gate/up row pairs j0, j0 + 1 of expert e for the tokens in `tmask` (x of token t at
+// xs + t * xstride, chunk sums at xsum + t * nch): SwiGLU values per token.  The weights
+// are loaded once and meet every token's activations.
+template <int BITS>
+__device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
+                                    const uint32_t *xs, int xstride, const float2 *xsum, int tmask,
+                                    float hv[SM_TMAX][2]) {
+    constexpr int CPC = 128 / BITS;
+    const int lr = (threadIdx.x & 63) % lpr;
+    const int nch = H / CPC, ng = H / 64;
+    const uint32_t rb = (uint32_t)H * BITS / 8;
+    const int64_t eg = (int64_t)e * mg.stride, eu = (int64_t)e * mu.stride;
+    const uint64_t cg = (uint64_t)(mg.codes + eg * rb), cu = (uint64_t)(mu.codes + eu * rb);
+    const uint64_t sg = (uint64_t)(mg.scales + eg * ng), bg = (uint64_t)(mg.biases + eg * ng);
+    const uint64_t su = (uint64_t)(mu.scales + eu * ng), bu = (uint64_t)(mu.biases + eu * ng);
+    const uint32_t oc0 = (uint32_t)j0 * rb, os0 = (uint32_t)j0 * ng;
+    float acc[SM_TMAX][4];
+#pragma unroll
+    for (int t = 0; t < SM_TMAX; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
+    for (int k0 = 0; k0 < nch; k0 += lpr) {
+        const int c = k0 + lr;
+        const bool ok = c < nch;
+        const int cc = ok ? c : nch - 1;
+        const uint32_t oc = oc0 + 16u * cc, os = os0 + ((cc * CPC) >> 6);
+        u32x4 q[4];
+        uint32_t sc[4], bi[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t dc = (r >> 1) ? rb : 0u, ds = (r >> 1) ? (uint32_t)ng : 0u;
+            q[r] = __builtin_nontemporal_load((g_u32x4 *)(((r & 1) ? cu : cg) + oc + dc));
+            sc[r] = *(g_u16 *)(((r & 1) ? su : sg) + 2u * (os + ds));
+            bi[r] = *(g_u16 *)(((r & 1) ? bu : bg) + 2u * (os + ds));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < SM_TMAX; ++t) {
+            if (!((tmask >> t) & 1)) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = chunk_dot<BITS>(q[r], xs + t * xstride + cc * (CPC / 2), sc[r], bi[r],
+                                                xsum[t * nch + cc]);
+                acc[t][r] += ok ? p : 0.0f;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < SM_TMAX; ++t)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const float g = group_sum(acc[t][2 * p], lpr);
+            const float u = group_sum(acc[t][2 * p + 1], lpr);
+            hv[t][p] = silu(g) * u;
+        }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_small(SmallArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
+    __shared__ SmallSel S;
+    __shared__ uint32_t s_flag;
+    __shared__ float s_lg[SM_TMAX][NW];
+    __shared__ uint32_t s_hw[SM_TMAX][NW * 64];
+    __shared__ float s_part[2][SM_TMAX][128];
+    constexpr int CPC = 128 / BITS;
+    const Layer &L = a.L;
+    uint32_t *ctl = a.ctl;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int H = L.H, I = L.I, E = L.E, K = L.K, T = a.T;
+    const int nR = a.nR, nP = a.nP, nS = a.nS, nG = a.nG, nD = a.nD;
+    const int b = blockIdx.x;
+    const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+
+    if (b < nR) {
+        // -------------------------------------------- R: one expert per wave, all tokens
+        const int e = b * NW + wave;
+        float acc[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e < E) {
+            const uint16_t *wr = L.router_w + (int64_t)e * H;
+            for (int c = lane; c < H / 8; c += 64) {
+                const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
+#pragma unroll
+                for (int t = 0; t < SM_TMAX; ++t) {
+                    if (t >= T) break;
+                    const u32x4 xv = *(const u32x4 *)(a.x + (int64_t)t * H + 8 * c);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        acc[t] = __builtin_fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), acc[t]);
+                        acc[t] = __builtin_fmaf(__uint_as_float(xv[i] & 0xffff0000u),
+                                                __uint_as_float(wv[i] & 0xffff0000u), acc[t]);
+                    }
+                }
+            }
+        }
+        const float bias = (e < E && L.router_bias) ? L.router_bias[e] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < SM_TMAX; ++t) {
+            const float v = wave_sum(acc[t]) + bias;
+            if (lane == 0) s_lg[t][wave] = v;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            constexpr int PIECES = NW / 2;
+            for (int i = lane; i < SM_LCOPIES * SM_TMAX * PIECES; i += 64) {
+                const int c = i / (SM_TMAX * PIECES), t = (i / PIECES) % SM_TMAX, q = i % PIECES;
+                const int e0 = b * NW + 2 * q;
+                if (t >= T) continue;
+                uint32_t *dst = ctl + LOGIT_BASE + c * SM_LSTRIDE + 2 * (t * SM_TE + e0);
+                if (e0 + 1 < E)
+                    st_dev128(dst, (u32x4){__float_as_uint(s_lg[t][2 * q]), tag, __float_as_uint(s_lg[t][2 * q + 1]), tag});
+                else if (e0 < E)
+                    st_dev64((uint64_t *)dst, __float_as_uint(s_lg[t][2 * q]) | ((uint64_t)tag << 32));
+            }
+        }
+        return;
+    }
+    if (b < nR + nP) {
+        // ----------------------------- P: selectors, wave t takes token t's top-k
+        const int sel = b - nR;
+        if (wave < T) {
+            const uint64_t *lg = (const uint64_t *)(ctl + LOGIT_BASE + (sel % SM_LCOPIES) * SM_LSTRIDE) + wave * SM_TE;
+            const TopkOut tk = select_topk_from(ctl, lg, tag, E, K);
+            if (lane < K) {
+                S.si[wave * K + lane] = tk.idx;
+                S.sw[wave * K + lane] = tk.w;
+            }
+        }
+        __syncthreads();
+        if (a.route_only) {
+            if (tid < T * K) {
+                if (a.out_idx) a.out_idx[tid] = S.si[tid];
+                if (a.out_w) a.out_w[tid] = S.sw[tid];
+            }
+            if (tid == 0) st_dev(ctl + CTL_GEN, tag);          // the only reader of the logits
+            return;
+        }
+        if (tid < T * K)
+            for (int c = sel; c < TOPK_COPIES; c += nP)
+                st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * tid,
+                          (u32x4){(uint32_t)S.si[tid], tag, __float_as_uint(S.sw[tid]), tag});
+        return;
+    }
+    const int nRP = nR + nP;
+    if (b < nRP + nS + nG) {
+        // ------------------------------ S / G: gate/up + SwiGLU for all tokens -> h
+        uint32_t *xs = dsm;                                  // [T][H / 2] fp16 pairs, code order
+        float2 *xsum = (float2 *)(dsm + SM_TMAX * H / 2);     // [T][H / CPC]
+        const int rpw = 64 / a.lprg;
+        const int pb = 2 * NW * rpw;                         // h values per item
+        const int bpe = (I + pb - 1) / pb;
+        const bool sh = b < nRP + nS;
+        const int g = sh ? b - nRP : b - nRP - nS;
+        for (int t = 0; t < T; ++t)
+            stage_x<BITS>(a.x + (int64_t)t * H, H, xs + t * (H / 2), xsum + t * (H / CPC));
+        int nitems = 1;
+        if (!sh) {
+            small_get_sel(ctl, tag, E, K, T, S);             // ends with a barrier
+            nitems = (S.nu * bpe - g + nG - 1) / nG;         // items g, g + nG, ... < |U| bpe
+        } else {
+            __syncthreads();
+        }
+        const int wi = wave * rpw + lane / a.lprg;           // word (row pair) within the item
+        for (int m = 0; m < nitems; ++m) {
+            const int item = sh ? g : g + m * nG;
+            const int u = sh ? 0 : item / bpe, rbk = item % bpe;
+            const int e = sh ? 0 : S.ul[u];
+            int tmask = 0;
+            for (int t = 0; t < T; ++t) tmask |= (sh || S.jt[u][t] >= 0) ? (1 << t) : 0;
+            const int j0 = rbk * pb + 2 * wi;
+            const int jj = j0 < I ? j0 : I - 2;
+            float hv[SM_TMAX][2];
+            pairs_swiglu_tokens<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, H / 2,
+                                      xsum, tmask, hv);
+            if (lane % a.lprg == 0)
+                for (int t = 0; t < T; ++t)
+                    s_hw[t][wi] = pack_f16x2(f32_to_f16_ftz(hv[t][0]), f32_to_f16_ftz(hv[t][1]));
+            __syncthreads();
+            const int jb = rbk * pb;
+            const int nw = min(pb, I - jb) / 2;
+            const int pieces = (nw + 1) / 2;
+            for (int i = tid; i < SM_HCOPIES * T * pieces; i += DT) {
+                const int cp = i / (T * pieces), t = (i / pieces) % T, q = i % pieces;
+                if (!((tmask >> t) & 1)) continue;
+                const int slot = t * (K + 1) + (sh ? K : S.jt[u][t]);
+                uint32_t *dst = ctl + H_BASE + cp * SM_HSTRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
+                if (2 * q + 1 < nw)
+                    st_dev128(dst, (u32x4){s_hw[t][2 * q], tag, s_hw[t][2 * q + 1], tag});
+                else
+                    st_dev64((uint64_t *)dst, s_hw[t][2 * q] | ((uint64_t)tag << 32));
+            }
+            __syncthreads();                                 // s_hw is reused by the next item
+        }
+        return;
+    }
+    {
+        // --------------------- D: down + weighted combine for all tokens, rows of a block
+        // four row groups of 64 / lprd rows; wave w takes row group w % 4 and the union
+        // slots of parity w / 4 (the shared expert is slot |U|)
+        const int d = b - nRP - nS - nG;
+        small_get_sel(ctl, tag, E, K, T, S);
+        if (d == 0 && tid < T * K) {
+            if (a.out_idx) a.out_idx[tid] = S.si[tid];
+            if (a.out_w) a.out_w[tid] = S.sw[tid];
+        }
+        const int nu = S.nu, nslot = T * (K + 1);
+        const int nv = nu + (a.shared ? 1 : 0);              // union slots incl. the shared one
+        const int lpr = a.lprd, rpw = 64 / lpr;
+        const int nch = I / CPC, ng = I / 64;
+        const uint32_t rb = (uint32_t)I * BITS / 8;
+        const int lr = lane % lpr, rr = lane / lpr;
+        const int rg = wave & 3, par = wave >> 2;
+        const int rloc = rg * rpw + rr;
+        const int n = d * 4 * rpw + rloc;
+        const int nc = n < H ? n : H - 1;
+        const int cpl = (nch + lpr - 1) / lpr;
+        const int nvp = (nv - par + 1) / 2;                  // union slots of this parity
+        const int nit = nvp * cpl;
+        constexpr int CPITCH = CPC + 8;
+        uint16_t *hs16 = (uint16_t *)dsm;                     // [nslot][nch] chunks, padded
+        float2 *hsum = (float2 *)(dsm + nslot * nch * CPITCH / 2);
+        uint32_t arrived = 0;
+        // item it: union slot v = par + 2 (it / cpl), chunk lr + lpr (it % cpl)
+        auto mat_of = [&](int v, const QMat *&m, int64_t &row0) {
+            const bool routed = v < nu;
+            m = routed ? &L.down : &L.s_down;
+            row0 = routed ? (int64_t)S.ul[v] * L.down.stride : 0;
+        };
+        constexpr int NB = 4;
+        float yv[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int base = 0; base == 0 || base < nit; base += NB) {
+            u32x4 q[NB];
+            uint32_t sv[NB], bv[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int it = min(base + i, max(nit - 1, 0));
+                const int v = min(par + 2 * (it / cpl), nv - 1);
+                const int c = lr + lpr * (it % cpl), cc = c < nch ? c : nch - 1;
+                const QMat *m;
+                int64_t row0;
+                mat_of(v, m, row0);
+                const int64_t row = row0 + nc;
+                q[i] = __builtin_nontemporal_load((g_u32x4 *)(m->codes + row * rb + 16 * cc));
+                const int64_t gi = row * ng + ((cc * CPC) >> 6);
+                sv[i] = *(g_u16 *)(m->scales + gi);
+                bv[i] = *(g_u16 *)(m->biases + gi);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (base == 0) {
+                // all of h: groups of 8 values, 16-byte device loads, fp16 into LDS in code
+                // order, chunk sums by a DPP sum over the chunk's groups
+                const uint32_t *hw = ctl + H_BASE + (d % SM_HCOPIES) * SM_HSTRIDE;
+                const int ngrp = nslot * I / 8;
+                for (int g0 = 0; g0 < ngrp; g0 += DT) {
+                    const int g = g0 + tid;
+                    const bool live = g < ngrp;
+                    const int gg = live ? g : ngrp - 1;
+                    const int j = (gg / (I / 8)) % (K + 1);
+                    // slots nobody writes (a token's shared slot without a shared expert)
+                    const bool used = j < K || a.shared;
+                    u32x4 w0 = {0u, tag, 0u, tag}, w1 = {0u, tag, 0u, tag};
+                    for (uint32_t it = 0; used; ++it) {
+                        ld_dev256(hw + 8 * gg, w0, w1);
+                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
+                        if (it > SPIN_LIMIT) {
+                            raise_error(ctl);
+                            break;
+                        }
+                        poll_pause(it);
+                    }
+                    const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                    float se = 0.0f, so = 0.0f;
+#pragma unroll
+                    for (int jx = 0; jx < 4; ++jx) {
+                        const f16x2 hh = as_h2(nat[jx]);
+                        se += (float)hh[0];
+                        so += (float)hh[1];
+                    }
+                    if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
+                    se = group_sum(se, CPC / 8);
+                    so = group_sum(so, CPC / 8);
+                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
+                }
+                __syncthreads();
+                if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const int it = base + i;
+                const bool live = it < nit;
+                const int v = min(par + 2 * (min(it, max(nit - 1, 0)) / cpl), nv - 1);
+                const int c = lr + lpr * (it % cpl), cc = c < nch ? c : nch - 1;
+#pragma unroll
+                for (int t = 0; t < SM_TMAX; ++t) {
+                    if (t >= T) break;
+                    const int j = v < nu ? S.jt[v][t] : K;
+                    if (!live || j < 0) continue;                // uniform: the token did not choose it
+                    const float w = v < nu ? S.sw[t * K + j] : 1.0f;
+                    const int ch = (t * (K + 1) + j) * nch + cc;
+                    const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + ch * CPITCH), sv[i], bv[i], hsum[ch]);
+                    yv[t] += c < nch ? w * p : 0.0f;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < SM_TMAX; ++t) {
+            if (t >= T) break;
+            const float s = group_sum(yv[t], lpr);
+            if (lr == 0) s_part[par][t][rloc] = s;
+        }
+        __syncthreads();
+        for (int i = tid; i < T * 4 * rpw; i += DT) {
+            const int t = i / (4 * rpw), r = i % (4 * rpw);
+            const int nn = d * 4 * rpw + r;
+            if (nn < H) {
+                const float yy = s_part[0][t][r] + s_part[1][t][r];
+                if (a.y_dtype == QSMOE_F32) ((float *)a.y)[(int64_t)t * H + nn] = yy;
+                else ((uint16_t *)a.y)[(int64_t)t * H + nn] = f32_to_bf16(yy);
+            }
+        }
+        if (tid == 0) {
+            const int g = d % NGRP;
+            const int gsize = nD / NGRP + (g < nD % NGRP ? 1 : 0);
+            const int ngroups = nD < NGRP ? nD : NGRP;
+            uint32_t last = 0;
+            if (arrived == (uint32_t)(gsize - 1)) last = add_dev(ctl + CNT_TOP) == (uint32_t)(ngroups - 1);
+            s_flag = last;
+        }
+        __syncthreads();
+        if (s_flag) finish_call(ctl, tag);
+    }
+}
+
 // lanes sharing one row: the largest power of two <= min(64, 16-byte chunks per row)
 int lanes_per_row(int ncols, int bits) {
     const int chunks = ncols * bits / 128;
@@ -645,6 +1068,49 @@ hipError_t launch(DecArgs a, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_small(SmallArgs a, hipStream_t s) {
+    const Layer &L = a.L;
+    const int cpc = 128 / L.bits;
+    a.lprg = lanes_per_row(L.H, L.bits);
+    a.lprd = lanes_per_row(L.I, L.bits);
+    const int pb = 2 * NW * (64 / a.lprg);
+    const int bpe = (L.I + pb - 1) / pb;
+    a.nR = (L.E + NW - 1) / NW;
+    size_t lds = 16;
+    if (a.route_only) {
+        a.nP = 1;
+        a.nS = a.nG = a.nD = 0;
+    } else {
+        a.nS = a.shared ? bpe : 0;
+        a.nG = L.K * bpe;                              // every G workgroup gets at least one item
+        const int rows = 4 * (64 / a.lprd);
+        a.nD = (L.H + rows - 1) / rows;
+        a.nP = N_SELECT;
+        while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
+        const int nslot = a.T * (L.K + 1);
+        const size_t lds_g = (size_t)SM_TMAX * L.H * 2 + (size_t)SM_TMAX * (L.H / cpc) * 8;
+        const size_t lds_d = (size_t)nslot * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nslot * (L.I / cpc) * 8;
+        lds = lds_g > lds_d ? lds_g : lds_d;
+    }
+    const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
+    if (L.bits == 4)
+        hipLaunchKernelGGL((k_decode_small<4>), dim3(grid), dim3(DT), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_decode_small<8>), dim3(grid), dim3(DT), lds, s, a);
+    return hipGetLastError();
+}
+
+SmallArgs make_small_args(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b) {
+    SmallArgs a{};
+    a.L = L;
+    a.x = x;
+    a.ctl = b.ctl;
+    a.T = (int)T;
+    a.y_dtype = QSMOE_F32;
+    a.shared = L.has_shared;
+    return a;
+}
+
 DecArgs make_args(const Layer &L, const uint16_t *x, const DecodeBufs &b) {
     DecArgs a{};
     a.L = L;
@@ -665,6 +1131,30 @@ hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBu
     a.out_idx = out_idx;
     a.out_w = out_w;
     return launch(a, s);
+}
+
+bool decode_small_eligible(const Layer &L, int64_t T) {
+    return T >= 2 && T <= SM_TMAX && T * (L.K + 1) * L.I / 2 <= SM_HWORDS && L.E <= SM_TE;
+}
+
+hipError_t launch_decode_small_layer(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b, void *y,
+                                     int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s) {
+    SmallArgs a = make_small_args(L, x, T, b);
+    a.y = y;
+    a.y_dtype = y_dtype;
+    a.out_idx = out_idx;
+    a.out_w = out_w;
+    return launch_small(a, s);
+}
+
+hipError_t launch_decode_small_route(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b,
+                                     int32_t *out_idx, float *out_w, hipStream_t s) {
+    SmallArgs a = make_small_args(L, x, T, b);
+    a.shared = 0;
+    a.route_only = 1;
+    a.out_idx = out_idx;
+    a.out_w = out_w;
+    return launch_small(a, s);
 }
 
 hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBufs &b, int32_t *out_idx,

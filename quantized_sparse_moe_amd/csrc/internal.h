@@ -37,6 +37,12 @@ struct DecodeBufs {
 
 hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
                                int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);
+// T = 2 .. 4 tokens in one launch, the routed experts read once for all of them
+bool decode_small_eligible(const Layer &L, int64_t T);
+hipError_t launch_decode_small_layer(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b, void *y,
+                                     int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);
+hipError_t launch_decode_small_route(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b,
+                                     int32_t *out_idx, float *out_w, hipStream_t s);
 hipError_t launch_decode_route(const Layer &L, const uint16_t *x, const DecodeBufs &b,
                                int32_t *out_idx, float *out_w, hipStream_t s);
 

@@ -141,7 +141,7 @@ def test_decode_parity(torch, qs, bf16_out):
 
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_tiny_grouped_and_decode(torch, qs, bf16_out):
-    """Tiny layer: T = 4 through the grouped path and as 4 separate T = 1 calls."""
+    """Tiny layer: T = 4 in one small-batch call and as 4 separate T = 1 calls."""
     L = layer("TINY")
     x_np = syn.make_x(4, L.hidden, seed=0)
     y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
