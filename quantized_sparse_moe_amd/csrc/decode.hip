@@ -681,13 +681,44 @@ __device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, 
     __syncthreads();
 }
 
-// gate/up row pairs j0, j0 + 1 of expert e for the tokens in `tmask` (x of token t at
-// xs + t * xstride, chunk sums at xsum + t * nch): SwiGLU values per token.  The weights
-// are loaded once and meet every token's activations.
+// x of T tokens (bf16, [T][H]) -> LDS fp16 in code order + chunk sums, one (token,
+// chunk) per thread
 template <int BITS>
-__device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
-                                    const uint32_t *xs, int xstride, const float2 *xsum, int tmask,
-                                    float hv[SM_TMAX][2]) {
+__device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs, float2 *xsum) {
+    constexpr int CPC = 128 / BITS;
+    const int nch = H / CPC;
+    for (int i = threadIdx.x; i < T * nch; i += DT) {
+        const int t = i / nch, c = i % nch;
+        const uint16_t *xc = x + (int64_t)t * H + c * CPC;
+        uint32_t *xd = xs + t * (H / 2) + c * (CPC / 2);
+        float se = 0.0f, so = 0.0f;
+        for (int g = 0; g < CPC / 8; ++g) {
+            const u32x4 v = *(const u32x4 *)(xc + 8 * g);
+            u32x4 nat;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[k] << 16));
+                const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[k] & 0xffff0000u));
+                se += (float)lo;
+                so += (float)hi;
+                nat[k] = pack_f16x2(lo, hi);
+            }
+            *(u32x4 *)(xd + 4 * g) = perm8<BITS>(nat);
+        }
+        xsum[t * nch + c] = make_float2(se, so);
+    }
+}
+
+// one chunk step of gate/up row pairs j0, j0 + 1 of expert e: per lane, the 16-byte
+// code chunk and the scale and bias of each of the 4 rows (gate j0, up j0, gate j0+1,
+// up j0+1); loaded ahead of their use so that several items' loads overlap
+struct PairW {
+    u32x4 q[4];
+    uint32_t sc[4], bi[4];
+};
+template <int BITS>
+__device__ __forceinline__ void load_pairs(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, int k0,
+                                           PairW &w) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
@@ -696,7 +727,27 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
     const uint64_t cg = (uint64_t)(mg.codes + eg * rb), cu = (uint64_t)(mu.codes + eu * rb);
     const uint64_t sg = (uint64_t)(mg.scales + eg * ng), bg = (uint64_t)(mg.biases + eg * ng);
     const uint64_t su = (uint64_t)(mu.scales + eu * ng), bu = (uint64_t)(mu.biases + eu * ng);
-    const uint32_t oc0 = (uint32_t)j0 * rb, os0 = (uint32_t)j0 * ng;
+    const int c = k0 + lr, cc = c < nch ? c : nch - 1;
+    const uint32_t oc = (uint32_t)j0 * rb + 16u * cc, os = (uint32_t)j0 * ng + ((cc * CPC) >> 6);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t dc = (r >> 1) ? rb : 0u, ds = (r >> 1) ? (uint32_t)ng : 0u;
+        w.q[r] = __builtin_nontemporal_load((g_u32x4 *)(((r & 1) ? cu : cg) + oc + dc));
+        w.sc[r] = *(g_u16 *)(((r & 1) ? su : sg) + 2u * (os + ds));
+        w.bi[r] = *(g_u16 *)(((r & 1) ? bu : bg) + 2u * (os + ds));
+    }
+}
+
+// gate/up row pairs j0, j0 + 1 of expert e for the tokens in `tmask` (x of token t at
+// xs + t * xstride, chunk sums at xsum + t * nch): SwiGLU values per token.  The weights
+// are loaded once and meet every token's activations.
+template <int BITS>
+__device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, const PairW &w0,
+                                    const uint32_t *xs, int xstride, const float2 *xsum, int T, int tmask,
+                                    float hv[SM_TMAX][2]) {
+    constexpr int CPC = 128 / BITS;
+    const int lr = (threadIdx.x & 63) % lpr;
+    const int nch = H / CPC;
     float acc[SM_TMAX][4];
 #pragma unroll
     for (int t = 0; t < SM_TMAX; ++t)
@@ -706,36 +757,31 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
         const int c = k0 + lr;
         const bool ok = c < nch;
         const int cc = ok ? c : nch - 1;
-        const uint32_t oc = oc0 + 16u * cc, os = os0 + ((cc * CPC) >> 6);
-        u32x4 q[4];
-        uint32_t sc[4], bi[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t dc = (r >> 1) ? rb : 0u, ds = (r >> 1) ? (uint32_t)ng : 0u;
-            q[r] = __builtin_nontemporal_load((g_u32x4 *)(((r & 1) ? cu : cg) + oc + dc));
-            sc[r] = *(g_u16 *)(((r & 1) ? su : sg) + 2u * (os + ds));
-            bi[r] = *(g_u16 *)(((r & 1) ? bu : bg) + 2u * (os + ds));
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        PairW w;
+        if (k0 == 0) w = w0;
+        else load_pairs<BITS>(mg, mu, e, j0, H, lpr, k0, w);
 #pragma unroll
         for (int t = 0; t < SM_TMAX; ++t) {
-            if (!((tmask >> t) & 1)) continue;
+            if (t >= T || !((tmask >> t) & 1)) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = chunk_dot<BITS>(q[r], xs + t * xstride + cc * (CPC / 2), sc[r], bi[r],
+                const float p = chunk_dot<BITS>(w.q[r], xs + t * xstride + cc * (CPC / 2), w.sc[r], w.bi[r],
                                                 xsum[t * nch + cc]);
                 acc[t][r] += ok ? p : 0.0f;
             }
         }
     }
 #pragma unroll
-    for (int t = 0; t < SM_TMAX; ++t)
+    for (int t = 0; t < SM_TMAX; ++t) {
+        hv[t][0] = hv[t][1] = 0.0f;
+        if (t >= T || !((tmask >> t) & 1)) continue;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const float g = group_sum(acc[t][2 * p], lpr);
             const float u = group_sum(acc[t][2 * p + 1], lpr);
             hv[t][p] = silu(g) * u;
         }
+    }
 }
 
 template <int BITS>
@@ -757,21 +803,35 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
 
     if (b < nR) {
         // -------------------------------------------- R: one expert per wave, all tokens
+        // (x of all tokens staged raw in LDS; the router row is read once per wave)
+        uint16_t *xr = (uint16_t *)dsm;
+        for (int i = tid; i < T * H / 8; i += DT) *(u32x4 *)(xr + 8 * i) = *(const u32x4 *)(a.x + 8 * (int64_t)i);
+        __syncthreads();
         const int e = b * NW + wave;
         float acc[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (e < E) {
             const uint16_t *wr = L.router_w + (int64_t)e * H;
-            for (int c = lane; c < H / 8; c += 64) {
-                const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c));
+            for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
+                u32x4 wv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int c = c0 + 64 * k;
+                    wv[k] = c < H / 8 ? __builtin_nontemporal_load((const u32x4 *)(wr + 8 * c)) : (u32x4){0u, 0u, 0u, 0u};
+                }
 #pragma unroll
                 for (int t = 0; t < SM_TMAX; ++t) {
                     if (t >= T) break;
-                    const u32x4 xv = *(const u32x4 *)(a.x + (int64_t)t * H + 8 * c);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[t] = __builtin_fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[i] << 16), acc[t]);
-                        acc[t] = __builtin_fmaf(__uint_as_float(xv[i] & 0xffff0000u),
-                                                __uint_as_float(wv[i] & 0xffff0000u), acc[t]);
+                    for (int k = 0; k < 4; ++k) {
+                        const int c = c0 + 64 * k;
+                        if (c >= H / 8) break;
+                        const u32x4 xv = *(const u32x4 *)(xr + t * H + 8 * c);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[t] = __builtin_fmaf(__uint_as_float(xv[i] << 16), __uint_as_float(wv[k][i] << 16), acc[t]);
+                            acc[t] = __builtin_fmaf(__uint_as_float(xv[i] & 0xffff0000u),
+                                                    __uint_as_float(wv[k][i] & 0xffff0000u), acc[t]);
+                        }
                     }
                 }
             }
@@ -834,8 +894,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int bpe = (I + pb - 1) / pb;
         const bool sh = b < nRP + nS;
         const int g = sh ? b - nRP : b - nRP - nS;
-        for (int t = 0; t < T; ++t)
-            stage_x<BITS>(a.x + (int64_t)t * H, H, xs + t * (H / 2), xsum + t * (H / CPC));
+        stage_x_tokens<BITS>(a.x, T, H, xs, xsum);
         int nitems = 1;
         if (!sh) {
             small_get_sel(ctl, tag, E, K, T, S);             // ends with a barrier
@@ -844,17 +903,34 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             __syncthreads();
         }
         const int wi = wave * rpw + lane / a.lprg;           // word (row pair) within the item
-        for (int m = 0; m < nitems; ++m) {
+        const QMat &mg = sh ? L.s_gate : L.gate, &mu = sh ? L.s_up : L.up;
+        auto item_at = [&](int m, int &u, int &rbk, int &e, int &jj) {
             const int item = sh ? g : g + m * nG;
-            const int u = sh ? 0 : item / bpe, rbk = item % bpe;
-            const int e = sh ? 0 : S.ul[u];
+            u = sh ? 0 : item / bpe;
+            rbk = item % bpe;
+            e = sh ? 0 : S.ul[u];
+            const int j0 = rbk * pb + 2 * wi;
+            jj = j0 < I ? j0 : I - 2;
+        };
+        PairW wnext;
+        {
+            int u, rbk, e, jj;
+            item_at(0, u, rbk, e, jj);
+            load_pairs<BITS>(mg, mu, e, jj, H, a.lprg, 0, wnext);
+        }
+        for (int m = 0; m < nitems; ++m) {
+            int u, rbk, e, jj;
+            item_at(m, u, rbk, e, jj);
+            const PairW wcur = wnext;
+            if (m + 1 < nitems) {                            // the next item's weights, ahead
+                int u2, rbk2, e2, jj2;
+                item_at(m + 1, u2, rbk2, e2, jj2);
+                load_pairs<BITS>(mg, mu, e2, jj2, H, a.lprg, 0, wnext);
+            }
             int tmask = 0;
             for (int t = 0; t < T; ++t) tmask |= (sh || S.jt[u][t] >= 0) ? (1 << t) : 0;
-            const int j0 = rbk * pb + 2 * wi;
-            const int jj = j0 < I ? j0 : I - 2;
             float hv[SM_TMAX][2];
-            pairs_swiglu_tokens<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, H / 2,
-                                      xsum, tmask, hv);
+            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, H / 2, xsum, T, tmask, hv);
             if (lane % a.lprg == 0)
                 for (int t = 0; t < T; ++t)
                     s_hw[t][wi] = pack_f16x2(f32_to_f16_ftz(hv[t][0]), f32_to_f16_ftz(hv[t][1]));
@@ -909,11 +985,15 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             m = routed ? &L.down : &L.s_down;
             row0 = routed ? (int64_t)S.ul[v] * L.down.stride : 0;
         };
+        // NB items per batch, two batches in flight: the next batch's loads are issued
+        // before the current one is multiplied; loads are unconditional (clamped to a
+        // valid item and discarded)
         constexpr int NB = 4;
-        float yv[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int base = 0; base == 0 || base < nit; base += NB) {
+        struct DW {
             u32x4 q[NB];
             uint32_t sv[NB], bv[NB];
+        };
+        auto dload = [&](int base, DW &w) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int it = min(base + i, max(nit - 1, 0));
@@ -923,50 +1003,14 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 int64_t row0;
                 mat_of(v, m, row0);
                 const int64_t row = row0 + nc;
-                q[i] = __builtin_nontemporal_load((g_u32x4 *)(m->codes + row * rb + 16 * cc));
+                w.q[i] = __builtin_nontemporal_load((g_u32x4 *)(m->codes + row * rb + 16 * cc));
                 const int64_t gi = row * ng + ((cc * CPC) >> 6);
-                sv[i] = *(g_u16 *)(m->scales + gi);
-                bv[i] = *(g_u16 *)(m->biases + gi);
+                w.sv[i] = *(g_u16 *)(m->scales + gi);
+                w.bv[i] = *(g_u16 *)(m->biases + gi);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            if (base == 0) {
-                // all of h: groups of 8 values, 16-byte device loads, fp16 into LDS in code
-                // order, chunk sums by a DPP sum over the chunk's groups
-                const uint32_t *hw = ctl + H_BASE + (d % SM_HCOPIES) * SM_HSTRIDE;
-                const int ngrp = nslot * I / 8;
-                for (int g0 = 0; g0 < ngrp; g0 += DT) {
-                    const int g = g0 + tid;
-                    const bool live = g < ngrp;
-                    const int gg = live ? g : ngrp - 1;
-                    const int j = (gg / (I / 8)) % (K + 1);
-                    // slots nobody writes (a token's shared slot without a shared expert)
-                    const bool used = j < K || a.shared;
-                    u32x4 w0 = {0u, tag, 0u, tag}, w1 = {0u, tag, 0u, tag};
-                    for (uint32_t it = 0; used; ++it) {
-                        ld_dev256(hw + 8 * gg, w0, w1);
-                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
-                        if (it > SPIN_LIMIT) {
-                            raise_error(ctl);
-                            break;
-                        }
-                        poll_pause(it);
-                    }
-                    const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
-                    float se = 0.0f, so = 0.0f;
-#pragma unroll
-                    for (int jx = 0; jx < 4; ++jx) {
-                        const f16x2 hh = as_h2(nat[jx]);
-                        se += (float)hh[0];
-                        so += (float)hh[1];
-                    }
-                    if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
-                    se = group_sum(se, CPC / 8);
-                    so = group_sum(so, CPC / 8);
-                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
-                }
-                __syncthreads();
-                if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
-            }
+        };
+        float yv[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
+        auto dcompute = [&](int base, const DW &w) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int it = base + i;
@@ -978,12 +1022,63 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     if (t >= T) break;
                     const int j = v < nu ? S.jt[v][t] : K;
                     if (!live || j < 0) continue;                // uniform: the token did not choose it
-                    const float w = v < nu ? S.sw[t * K + j] : 1.0f;
+                    const float wt = v < nu ? S.sw[t * K + j] : 1.0f;
                     const int ch = (t * (K + 1) + j) * nch + cc;
-                    const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + ch * CPITCH), sv[i], bv[i], hsum[ch]);
-                    yv[t] += c < nch ? w * p : 0.0f;
+                    const float p = chunk_dot<BITS>(w.q[i], (const uint32_t *)(hs16 + ch * CPITCH), w.sv[i], w.bv[i],
+                                                    hsum[ch]);
+                    yv[t] += c < nch ? wt * p : 0.0f;
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        DW wa, wb;
+        dload(0, wa);
+        if (NB < nit) dload(NB, wb);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            // all of h: groups of 8 values, 16-byte device loads, fp16 into LDS in code
+            // order, chunk sums by a DPP sum over the chunk's groups
+            const uint32_t *hw = ctl + H_BASE + (d % SM_HCOPIES) * SM_HSTRIDE;
+            const int ngrp = nslot * I / 8;
+            for (int g0 = 0; g0 < ngrp; g0 += DT) {
+                const int g = g0 + tid;
+                const bool live = g < ngrp;
+                const int gg = live ? g : ngrp - 1;
+                const int j = (gg / (I / 8)) % (K + 1);
+                // slots nobody writes (a token's shared slot without a shared expert)
+                const bool used = j < K || a.shared;
+                u32x4 w0 = {0u, tag, 0u, tag}, w1 = {0u, tag, 0u, tag};
+                for (uint32_t it = 0; used; ++it) {
+                    ld_dev256(hw + 8 * gg, w0, w1);
+                    if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
+                    if (it > SPIN_LIMIT) {
+                        raise_error(ctl);
+                        break;
+                    }
+                    poll_pause(it);
+                }
+                const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                float se = 0.0f, so = 0.0f;
+#pragma unroll
+                for (int jx = 0; jx < 4; ++jx) {
+                    const f16x2 hh = as_h2(nat[jx]);
+                    se += (float)hh[0];
+                    so += (float)hh[1];
+                }
+                if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
+                se = group_sum(se, CPC / 8);
+                so = group_sum(so, CPC / 8);
+                if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
+            }
+            __syncthreads();
+            if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
+        }
+        for (int base = 0; base < nit; base += 2 * NB) {
+            dcompute(base, wa);
+            if (base + 2 * NB < nit) dload(base + 2 * NB, wa);
+            if (base + NB < nit) {
+                dcompute(base + NB, wb);
+                if (base + 3 * NB < nit) dload(base + 3 * NB, wb);
             }
         }
 #pragma unroll
@@ -1092,6 +1187,8 @@ hipError_t launch_small(SmallArgs a, hipStream_t s) {
         const size_t lds_d = (size_t)nslot * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nslot * (L.I / cpc) * 8;
         lds = lds_g > lds_d ? lds_g : lds_d;
     }
+    const size_t lds_r = (size_t)a.T * L.H * 2;        // R: x of all tokens, raw
+    if (lds < lds_r) lds = lds_r;
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
     if (L.bits == 4)
         hipLaunchKernelGGL((k_decode_small<4>), dim3(grid), dim3(DT), lds, s, a);
