@@ -610,6 +610,7 @@ static_assert(SM_LCOPIES * SM_LSTRIDE <= LOGIT_COPIES * LOGIT_STRIDE, "small-T l
 constexpr int SM_HCOPIES = 2;
 constexpr int SM_HSTRIDE = H_COPIES * H_STRIDE / SM_HCOPIES;   // u32 per h copy
 constexpr int SM_HWORDS = SM_HSTRIDE / 2 - 32;                 // h words per copy
+constexpr size_t SMALL_LDS_MAX = 76 * 1024;                    // dynamic LDS of a small-batch call
 static_assert(2 * SM_TMAX * 16 <= TOPK_STRIDE / 2, "small-T selection region");
 
 struct SmallArgs {
@@ -681,16 +682,22 @@ __device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, 
     __syncthreads();
 }
 
-// x of T tokens (bf16, [T][H]) -> LDS fp16 in code order + chunk sums, one (token,
-// chunk) per thread
+// u32 per staged x chunk of the small-batch path: the chunk, then its even / odd column
+// sums in a 16-byte pad, so that the 16-byte LDS reads of consecutive lanes (consecutive
+// chunks) fall in distinct banks
 template <int BITS>
-__device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs, float2 *xsum) {
-    constexpr int CPC = 128 / BITS;
+constexpr int small_xpitch() { return 64 / BITS + 4; }
+
+// x of T tokens (bf16, [T][H]) -> LDS fp16 in code order (chunk c of token t at
+// xs + (t nch + c) * pitch, its column sums right after it), one (token, chunk) per thread
+template <int BITS>
+__device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs) {
+    constexpr int CPC = 128 / BITS, XP = small_xpitch<BITS>();
     const int nch = H / CPC;
     for (int i = threadIdx.x; i < T * nch; i += DT) {
         const int t = i / nch, c = i % nch;
         const uint16_t *xc = x + (int64_t)t * H + c * CPC;
-        uint32_t *xd = xs + t * (H / 2) + c * (CPC / 2);
+        uint32_t *xd = xs + i * XP;
         float se = 0.0f, so = 0.0f;
         for (int g = 0; g < CPC / 8; ++g) {
             const u32x4 v = *(const u32x4 *)(xc + 8 * g);
@@ -705,7 +712,7 @@ __device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs, fl
             }
             *(u32x4 *)(xd + 4 * g) = perm8<BITS>(nat);
         }
-        xsum[t * nch + c] = make_float2(se, so);
+        *(float2 *)(xd + CPC / 2) = make_float2(se, so);
     }
 }
 
@@ -738,48 +745,198 @@ __device__ __forceinline__ void load_pairs(const QMat &mg, const QMat &mu, int e
     }
 }
 
-// gate/up row pairs j0, j0 + 1 of expert e for the tokens in `tmask` (x of token t at
-// xs + t * xstride, chunk sums at xsum + t * nch): SwiGLU values per token.  The weights
-// are loaded once and meet every token's activations.
+// the same loads as load_pairs, direct to LDS (no registers held while they are in
+// flight): row r's chunk of lane l lands at wb + 1024 r + 16 l, its scale and bias
+// (zero-extended to a dword) at wb + 4096 + 256 r + 4 l and wb + 5120 + 256 r + 4 l
+constexpr int PAIR_DMA_BYTES = 6144;                        // per wave
+typedef __attribute__((address_space(3))) void lds_void;
 template <int BITS>
-__device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, const PairW &w0,
-                                    const uint32_t *xs, int xstride, const float2 *xsum, int T, int tmask,
-                                    float hv[SM_TMAX][2]) {
+__device__ __forceinline__ void load_pairs_dma(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
+                                               uint8_t *wb) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
+    const int nch = H / CPC, ng = H / 64;
+    const uint32_t rb = (uint32_t)H * BITS / 8;
+    const int64_t eg = (int64_t)e * mg.stride, eu = (int64_t)e * mu.stride;
+    const uint64_t cg = (uint64_t)(mg.codes + eg * rb), cu = (uint64_t)(mu.codes + eu * rb);
+    const uint64_t sg = (uint64_t)(mg.scales + eg * ng), bg = (uint64_t)(mg.biases + eg * ng);
+    const uint64_t su = (uint64_t)(mu.scales + eu * ng), bu = (uint64_t)(mu.biases + eu * ng);
+    const int cc = lr < nch ? lr : nch - 1;
+    const uint32_t oc = (uint32_t)j0 * rb + 16u * cc, os = (uint32_t)j0 * ng + ((cc * CPC) >> 6);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t dc = (r >> 1) ? rb : 0u, ds = (r >> 1) ? (uint32_t)ng : 0u;
+        __builtin_amdgcn_global_load_lds((const void *)(((r & 1) ? cu : cg) + oc + dc), (lds_void *)(wb + 1024 * r),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(((r & 1) ? su : sg) + 2u * (os + ds)),
+                                         (lds_void *)(wb + 4096 + 256 * r), 2, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(((r & 1) ? bu : bg) + 2u * (os + ds)),
+                                         (lds_void *)(wb + 5120 + 256 * r), 2, 0, 0);
+    }
+}
+__device__ __forceinline__ void read_pairs(const uint8_t *wb, PairW &w) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        w.q[r] = *(const u32x4 *)(wb + 1024 * r + 16 * lane);
+        w.sc[r] = *(const uint32_t *)(wb + 4096 + 256 * r + 4 * lane);
+        w.bi[r] = *(const uint32_t *)(wb + 5120 + 256 * r + 4 * lane);
+    }
+}
+
+// Sums of 16 values over the 64 lanes of a wave in one transposing butterfly: each step
+// halves the values a lane holds, a lane keeping one half and taking its partner's copy
+// of that half (gfx950 half- and row-swaps across rows, DPP mirrors inside a row), so the
+// wave spends 35 instructions where 16 separate reductions would spend ~180.  On return
+// every lane holds the sum of value (lane >> 2).
+__device__ __forceinline__ float wave_sum16(float (&v)[SM_TMAX * 4]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                            // lanes ^ 32: value i or i + 8
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                            // lanes ^ 16: value i or i + 4
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {                            // row mirror (bit 3 differs)
+        const float keep = b3 ? v[i + 2] : v[i], send = b3 ? v[i] : v[i + 2];
+        v[i] = keep + dpp<0x140>(send);
+    }
+    {                                                        // half-row mirror (bit 2 differs)
+        const float keep = b2 ? v[1] : v[0], send = b2 ? v[0] : v[1];
+        v[0] = keep + dpp<0x141>(send);
+    }
+    v[0] += dpp<0xB1>(v[0]);                                 // lanes ^ 1, lanes ^ 2
+    v[0] += dpp<0x4E>(v[0]);
+    return v[0];
+}
+
+// gate/up row pairs j0, j0 + 1 of expert e for the tokens in `tmask` (x chunks and chunk
+// sums as stage_x_tokens leaves them): the SwiGLU words (fp16 h[j0], h[j0 + 1]) of token t
+// go to hq[t * wpi + wi].  The codes of a gate/up row pair are unpacked once and meet every
+// token's activations; when one row spans the wave (lpr = 64) the 16 partial sums of the
+// lane are reduced together.
+template <int BITS>
+__device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, const PairW &w0,
+                                    const uint32_t *xs, int T, int tmask, uint32_t *hq, int wpi,
+                                    int wi) {
+    constexpr int CPC = 128 / BITS, XP = small_xpitch<BITS>();
+    const int lane = threadIdx.x & 63;
+    const int lr = lane % lpr;
     const int nch = H / CPC;
-    float acc[SM_TMAX][4];
+    float acc[SM_TMAX * 4];                                 // value 4 t + r: token t, row r
 #pragma unroll
-    for (int t = 0; t < SM_TMAX; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = 0.0f;
-    for (int k0 = 0; k0 < nch; k0 += lpr) {
+    for (int i = 0; i < SM_TMAX * 4; ++i) acc[i] = 0.0f;
+    // one K step: the lane's chunk of each of the 4 rows, against every token
+    auto kstep = [&](const PairW &w, int k0) __attribute__((always_inline)) {
         const int c = k0 + lr;
         const bool ok = c < nch;
         const int cc = ok ? c : nch - 1;
-        PairW w;
-        if (k0 == 0) w = w0;
-        else load_pairs<BITS>(mg, mu, e, j0, H, lpr, k0, w);
-#pragma unroll
-        for (int t = 0; t < SM_TMAX; ++t) {
-            if (t >= T || !((tmask >> t) & 1)) continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = chunk_dot<BITS>(w.q[r], xs + t * xstride + cc * (CPC / 2), w.sc[r], w.bi[r],
-                                                xsum[t * nch + cc]);
-                acc[t][r] += ok ? p : 0.0f;
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < SM_TMAX; ++t) {
-        hv[t][0] = hv[t][1] = 0.0f;
-        if (t >= T || !((tmask >> t) & 1)) continue;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const float g = group_sum(acc[t][2 * p], lpr);
-            const float u = group_sum(acc[t][2 * p + 1], lpr);
-            hv[t][p] = silu(g) * u;
+            // gate row 2p and up row 2p + 1 against every token: the codes are unpacked
+            // once (all of the chunk), each token's x chunk is read in one go (one wait
+            // per token), and each token keeps even / odd column sums (4-bit, as
+            // chunk_dot) or two partial sums (8-bit) per row
+            const u32x4 &qg = w.q[2 * p], &qu = w.q[2 * p + 1];
+            constexpr int NJ = BITS == 4 ? 4 : 2;          // 16-byte x reads per chunk
+            uint32_t dg[NJ][4], du[NJ][4];                   // fp16 words meeting x word i of read j
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                if constexpr (BITS == 4) {
+                    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+                    const uint32_t g8 = qg[j] >> 8, u8 = qu[j] >> 8;
+                    dg[j][0] = and_or(qg[j], lo, QS_MAGIC);
+                    dg[j][1] = and_or(qg[j], hi, QS_MAGIC);
+                    dg[j][2] = and_or(g8, lo, QS_MAGIC);
+                    dg[j][3] = and_or(g8, hi, QS_MAGIC);
+                    du[j][0] = and_or(qu[j], lo, QS_MAGIC);
+                    du[j][1] = and_or(qu[j], hi, QS_MAGIC);
+                    du[j][2] = and_or(u8, lo, QS_MAGIC);
+                    du[j][3] = and_or(u8, hi, QS_MAGIC);
+                } else {
+                    const uint32_t lo = 0x00FF00FFu;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        dg[j][2 * h] = and_or(qg[2 * j + h], lo, QS_MAGIC);
+                        dg[j][2 * h + 1] = and_or(qg[2 * j + h] >> 8, lo, QS_MAGIC);
+                        du[j][2 * h] = and_or(qu[2 * j + h], lo, QS_MAGIC);
+                        du[j][2 * h + 1] = and_or(qu[2 * j + h] >> 8, lo, QS_MAGIC);
+                    }
+                }
+            }
+            float ag[SM_TMAX][2], au[SM_TMAX][2];
+#pragma unroll
+            for (int t = 0; t < SM_TMAX; ++t) {
+                ag[t][0] = ag[t][1] = au[t][0] = au[t][1] = 0.0f;
+                if (t >= T || !((tmask >> t) & 1)) continue;
+                u32x4 xx[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) xx[j] = *(const u32x4 *)(xs + (t * nch + cc) * XP + 4 * j);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // 4-bit: words 0, 2 are even columns, 1, 3 odd (high nibbles as 16 q)
+                        const int o = BITS == 4 ? (i & 1) : (i >> 1);
+                        ag[t][o] = __builtin_amdgcn_fdot2(as_h2(dg[j][i]), as_h2(xx[j][i]), ag[t][o], false);
+                        au[t][o] = __builtin_amdgcn_fdot2(as_h2(du[j][i]), as_h2(xx[j][i]), au[t][o], false);
+                    }
+            }
+            const float sg = f16_to_f32((uint16_t)w.sc[2 * p]), bg = f16_to_f32((uint16_t)w.bi[2 * p]);
+            const float su = f16_to_f32((uint16_t)w.sc[2 * p + 1]), bu = f16_to_f32((uint16_t)w.bi[2 * p + 1]);
+#pragma unroll
+            for (int t = 0; t < SM_TMAX; ++t) {
+                if (t >= T || !((tmask >> t) & 1)) continue;
+                const u32x4 xp = *(const u32x4 *)(xs + (t * nch + cc) * XP + CPC / 2);   // the sums' pad
+                const float2 X = make_float2(__uint_as_float(xp[0]), __uint_as_float(xp[1]));
+                float pg, pu;
+                if constexpr (BITS == 4) {
+                    pg = sg * ag[t][0] + (sg * 0.0625f) * ag[t][1] + (bg - 1024.0f * sg) * X.x + (bg - 64.0f * sg) * X.y;
+                    pu = su * au[t][0] + (su * 0.0625f) * au[t][1] + (bu - 1024.0f * su) * X.x + (bu - 64.0f * su) * X.y;
+                } else {
+                    pg = sg * (ag[t][0] + ag[t][1]) + (bg - 1024.0f * sg) * (X.x + X.y);
+                    pu = su * (au[t][0] + au[t][1]) + (bu - 1024.0f * su) * (X.x + X.y);
+                }
+                acc[4 * t + 2 * p] += ok ? pg : 0.0f;
+                acc[4 * t + 2 * p + 1] += ok ? pu : 0.0f;
+            }
+        }
+    };
+    // the first step's weights are in registers already; only later steps (rows longer
+    // than lpr chunks) load here, so that the compiler's wait for them is the only wait
+    kstep(w0, 0);
+    for (int k0 = lpr; k0 < nch; k0 += lpr) {
+        PairW w;
+        load_pairs<BITS>(mg, mu, e, j0, H, lpr, k0, w);
+        kstep(w, k0);
+    }
+    if (lpr == 64) {
+        // value 4 t + r ends in lanes 16 t + 4 r .. + 3: gate (r = 0, 2) meets up (r + 1)
+        // four lanes up, and the pair's second h value sits eight lanes up
+        const float v = wave_sum16(acc);
+        const float h = silu(v) * dpp<0x104>(v);
+        const float h1 = dpp<0x108>(h);
+        const int t = lane >> 4;
+        if ((lane & 15) == 0 && t < T)
+            hq[t * wpi + wi] = pack_f16x2(f32_to_f16_ftz(h), f32_to_f16_ftz(h1));
+    } else {
+#pragma unroll
+        for (int t = 0; t < SM_TMAX; ++t) {
+            if (t >= T) continue;
+            float hv[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const float g = group_sum(acc[4 * t + 2 * p], lpr);
+                const float u = group_sum(acc[4 * t + 2 * p + 1], lpr);
+                hv[p] = silu(g) * u;
+            }
+            if (lr == 0) hq[t * wpi + wi] = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1]));
         }
     }
 }
@@ -790,8 +947,6 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     __shared__ SmallSel S;
     __shared__ uint32_t s_flag;
     __shared__ float s_lg[SM_TMAX][NW];
-    __shared__ uint32_t s_hw[SM_TMAX][NW * 64];
-    __shared__ float s_part[2][SM_TMAX][128];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
     uint32_t *ctl = a.ctl;
@@ -887,14 +1042,15 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     const int nRP = nR + nP;
     if (b < nRP + nS + nG) {
         // ------------------------------ S / G: gate/up + SwiGLU for all tokens -> h
-        uint32_t *xs = dsm;                                  // [T][H / 2] fp16 pairs, code order
-        float2 *xsum = (float2 *)(dsm + SM_TMAX * H / 2);     // [T][H / CPC]
+        constexpr int XP = small_xpitch<BITS>();
+        uint8_t *wb = (uint8_t *)dsm + wave * PAIR_DMA_BYTES;   // this wave's next-item weights
+        uint32_t *xs = dsm + NW * PAIR_DMA_BYTES / 4;        // [T][H / CPC] chunks + sums, code order
         const int rpw = 64 / a.lprg;
         const int pb = 2 * NW * rpw;                         // h values per item
         const int bpe = (I + pb - 1) / pb;
         const bool sh = b < nRP + nS;
         const int g = sh ? b - nRP : b - nRP - nS;
-        stage_x_tokens<BITS>(a.x, T, H, xs, xsum);
+        stage_x_tokens<BITS>(a.x, T, H, xs);
         int nitems = 1;
         if (!sh) {
             small_get_sel(ctl, tag, E, K, T, S);             // ends with a barrier
@@ -908,47 +1064,56 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const int item = sh ? g : g + m * nG;
             u = sh ? 0 : item / bpe;
             rbk = item % bpe;
-            e = sh ? 0 : S.ul[u];
+            e = sh ? 0 : __builtin_amdgcn_readfirstlane(S.ul[u]);   // uniform: scalar bases
             const int j0 = rbk * pb + 2 * wi;
             jj = j0 < I ? j0 : I - 2;
         };
-        PairW wnext;
         {
             int u, rbk, e, jj;
             item_at(0, u, rbk, e, jj);
-            load_pairs<BITS>(mg, mu, e, jj, H, a.lprg, 0, wnext);
+            load_pairs_dma<BITS>(mg, mu, e, jj, H, a.lprg, wb);
         }
+        // the waves run through the items on their own (no barrier between items); each
+        // wave's next item streams into its LDS slot while the current one is computed
+        // from registers; the h words of all items collect in LDS and are stored once at
+        // the end
+        const int wpi = pb / 2;                              // h words per item and token
+        uint32_t *hq = xs + SM_TMAX * (H / CPC) * XP;        // [item][T][wpi]
         for (int m = 0; m < nitems; ++m) {
             int u, rbk, e, jj;
             item_at(m, u, rbk, e, jj);
-            const PairW wcur = wnext;
-            if (m + 1 < nitems) {                            // the next item's weights, ahead
+            PairW wcur;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's slot has landed
+            read_pairs(wb, wcur);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // and is read before it is refilled
+            if (m + 1 < nitems) {
                 int u2, rbk2, e2, jj2;
                 item_at(m + 1, u2, rbk2, e2, jj2);
-                load_pairs<BITS>(mg, mu, e2, jj2, H, a.lprg, 0, wnext);
+                load_pairs_dma<BITS>(mg, mu, e2, jj2, H, a.lprg, wb);
             }
             int tmask = 0;
             for (int t = 0; t < T; ++t) tmask |= (sh || S.jt[u][t] >= 0) ? (1 << t) : 0;
-            float hv[SM_TMAX][2];
-            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, H / 2, xsum, T, tmask, hv);
-            if (lane % a.lprg == 0)
-                for (int t = 0; t < T; ++t)
-                    s_hw[t][wi] = pack_f16x2(f32_to_f16_ftz(hv[t][0]), f32_to_f16_ftz(hv[t][1]));
-            __syncthreads();
+            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, T, tmask, hq + m * T * wpi, wpi, wi);
+        }
+        __syncthreads();
+        const int pieces = (wpi + 1) / 2;
+        const int per_copy = nitems * T * pieces;
+        for (int i = tid; i < SM_HCOPIES * per_copy; i += DT) {
+            const int cp = i / per_copy, r = i % per_copy;
+            const int m = r / (T * pieces), t = (r / pieces) % T, q = r % pieces;
+            int u, rbk, e, jj;
+            item_at(m, u, rbk, e, jj);
+            if (!sh && S.jt[u][t] < 0) continue;             // the token did not choose the expert
             const int jb = rbk * pb;
             const int nw = min(pb, I - jb) / 2;
-            const int pieces = (nw + 1) / 2;
-            for (int i = tid; i < SM_HCOPIES * T * pieces; i += DT) {
-                const int cp = i / (T * pieces), t = (i / pieces) % T, q = i % pieces;
-                if (!((tmask >> t) & 1)) continue;
-                const int slot = t * (K + 1) + (sh ? K : S.jt[u][t]);
-                uint32_t *dst = ctl + H_BASE + cp * SM_HSTRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
-                if (2 * q + 1 < nw)
-                    st_dev128(dst, (u32x4){s_hw[t][2 * q], tag, s_hw[t][2 * q + 1], tag});
-                else
-                    st_dev64((uint64_t *)dst, s_hw[t][2 * q] | ((uint64_t)tag << 32));
-            }
-            __syncthreads();                                 // s_hw is reused by the next item
+            if (2 * q >= nw) continue;
+            const int slot = t * (K + 1) + (sh ? K : S.jt[u][t]);
+            const uint32_t *src = hq + (m * T + t) * wpi + 2 * q;
+            uint32_t *dst = ctl + H_BASE + cp * SM_HSTRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
+            if (2 * q + 1 < nw)
+                st_dev128(dst, (u32x4){src[0], tag, src[1], tag});
+            else
+                st_dev64((uint64_t *)dst, src[0] | ((uint64_t)tag << 32));
         }
         return;
     }
@@ -962,7 +1127,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             if (a.out_idx) a.out_idx[tid] = S.si[tid];
             if (a.out_w) a.out_w[tid] = S.sw[tid];
         }
-        const int nu = S.nu, nslot = T * (K + 1);
+        const int nu = __builtin_amdgcn_readfirstlane(S.nu), nslot = T * (K + 1);
         const int nv = nu + (a.shared ? 1 : 0);              // union slots incl. the shared one
         const int lpr = a.lprd, rpw = 64 / lpr;
         const int nch = I / CPC, ng = I / 64;
@@ -978,12 +1143,23 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         constexpr int CPITCH = CPC + 8;
         uint16_t *hs16 = (uint16_t *)dsm;                     // [nslot][nch] chunks, padded
         float2 *hsum = (float2 *)(dsm + nslot * nch * CPITCH / 2);
+        float *s_part = (float *)(hsum + nslot * nch);        // [2][T][4 rpw]: the two parities' sums
         uint32_t arrived = 0;
-        // item it: union slot v = par + 2 (it / cpl), chunk lr + lpr (it % cpl)
-        auto mat_of = [&](int v, const QMat *&m, int64_t &row0) {
+        // item it: union slot v = par + 2 (it / cpl), chunk lr + lpr (it % cpl).  Lane j < |U|
+        // holds row 0 of routed slot j's down matrix; a slot's bases are read from its lane
+        // as scalars (the shared slot's are the layer's)
+        uint64_t pc = 0, ps = 0, pbi = 0;
+        if (lane < nu) {
+            const int64_t r0 = (int64_t)S.ul[lane] * L.down.stride;
+            pc = (uint64_t)(L.down.codes + r0 * rb);
+            ps = (uint64_t)(L.down.scales + r0 * ng);
+            pbi = (uint64_t)(L.down.biases + r0 * ng);
+        }
+        auto slot_base = [&](int v, uint64_t &bc, uint64_t &bs, uint64_t &bb) __attribute__((always_inline)) {
             const bool routed = v < nu;
-            m = routed ? &L.down : &L.s_down;
-            row0 = routed ? (int64_t)S.ul[v] * L.down.stride : 0;
+            bc = routed ? readlane64(pc, v) : (uint64_t)L.s_down.codes;
+            bs = routed ? readlane64(ps, v) : (uint64_t)L.s_down.scales;
+            bb = routed ? readlane64(pbi, v) : (uint64_t)L.s_down.biases;
         };
         // NB items per batch, two batches in flight: the next batch's loads are issued
         // before the current one is multiplied; loads are unconditional (clamped to a
@@ -999,14 +1175,12 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 const int it = min(base + i, max(nit - 1, 0));
                 const int v = min(par + 2 * (it / cpl), nv - 1);
                 const int c = lr + lpr * (it % cpl), cc = c < nch ? c : nch - 1;
-                const QMat *m;
-                int64_t row0;
-                mat_of(v, m, row0);
-                const int64_t row = row0 + nc;
-                w.q[i] = __builtin_nontemporal_load((g_u32x4 *)(m->codes + row * rb + 16 * cc));
-                const int64_t gi = row * ng + ((cc * CPC) >> 6);
-                w.sv[i] = *(g_u16 *)(m->scales + gi);
-                w.bv[i] = *(g_u16 *)(m->biases + gi);
+                uint64_t bc, bs, bb;
+                slot_base(v, bc, bs, bb);
+                w.q[i] = __builtin_nontemporal_load((g_u32x4 *)(bc + (uint32_t)nc * rb + 16u * cc));
+                const uint32_t gi = (uint32_t)nc * ng + ((cc * CPC) >> 6);
+                w.sv[i] = *(g_u16 *)(bs + 2u * gi);
+                w.bv[i] = *(g_u16 *)(bb + 2u * gi);
             }
         };
         float yv[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1085,14 +1259,14 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         for (int t = 0; t < SM_TMAX; ++t) {
             if (t >= T) break;
             const float s = group_sum(yv[t], lpr);
-            if (lr == 0) s_part[par][t][rloc] = s;
+            if (lr == 0) s_part[(par * SM_TMAX + t) * 4 * rpw + rloc] = s;
         }
         __syncthreads();
         for (int i = tid; i < T * 4 * rpw; i += DT) {
             const int t = i / (4 * rpw), r = i % (4 * rpw);
             const int nn = d * 4 * rpw + r;
             if (nn < H) {
-                const float yy = s_part[0][t][r] + s_part[1][t][r];
+                const float yy = s_part[t * 4 * rpw + r] + s_part[(SM_TMAX + t) * 4 * rpw + r];
                 if (a.y_dtype == QSMOE_F32) ((float *)a.y)[(int64_t)t * H + nn] = yy;
                 else ((uint16_t *)a.y)[(int64_t)t * H + nn] = f32_to_bf16(yy);
             }
@@ -1163,15 +1337,32 @@ hipError_t launch(DecArgs a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// dynamic LDS of a small-batch call: the largest of the roles' needs
+//   S / G: per wave a slot for the next item's weights (direct-to-LDS), the tokens' x
+//          chunks with their column sums, the h words of up to SM_TMAX items (a G
+//          workgroup has at most T: |U| <= T K items of blocks over nG = K bpe workgroups)
+//   D:     h of every slot as padded fp16 chunks with chunk sums, the two parities' sums
+//   R:     x of all tokens, raw
+size_t small_lds_bytes(const Layer &L, int T) {
+    const int cpc = 128 / L.bits;
+    const int pb = 2 * NW * (64 / lanes_per_row(L.H, L.bits));
+    const int rows = 4 * (64 / lanes_per_row(L.I, L.bits));
+    const size_t nslot = (size_t)T * (L.K + 1);
+    const size_t g = (size_t)NW * PAIR_DMA_BYTES + (size_t)SM_TMAX * (L.H / cpc) * (cpc / 2 + 4) * 4 +
+                     (size_t)SM_TMAX * SM_TMAX * (pb / 2) * 4;
+    const size_t d = nslot * (L.I / cpc) * (cpc + 8) * 2 + nslot * (L.I / cpc) * 8 + (size_t)2 * SM_TMAX * rows * 4;
+    const size_t r = (size_t)T * L.H * 2;
+    return std::max(std::max(g, d), r);
+}
+
 hipError_t launch_small(SmallArgs a, hipStream_t s) {
     const Layer &L = a.L;
-    const int cpc = 128 / L.bits;
     a.lprg = lanes_per_row(L.H, L.bits);
     a.lprd = lanes_per_row(L.I, L.bits);
     const int pb = 2 * NW * (64 / a.lprg);
     const int bpe = (L.I + pb - 1) / pb;
     a.nR = (L.E + NW - 1) / NW;
-    size_t lds = 16;
+    size_t lds = (size_t)a.T * L.H * 2;                // R: x of all tokens, raw
     if (a.route_only) {
         a.nP = 1;
         a.nS = a.nG = a.nD = 0;
@@ -1182,13 +1373,8 @@ hipError_t launch_small(SmallArgs a, hipStream_t s) {
         a.nD = (L.H + rows - 1) / rows;
         a.nP = N_SELECT;
         while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
-        const int nslot = a.T * (L.K + 1);
-        const size_t lds_g = (size_t)SM_TMAX * L.H * 2 + (size_t)SM_TMAX * (L.H / cpc) * 8;
-        const size_t lds_d = (size_t)nslot * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nslot * (L.I / cpc) * 8;
-        lds = lds_g > lds_d ? lds_g : lds_d;
+        lds = small_lds_bytes(L, a.T);
     }
-    const size_t lds_r = (size_t)a.T * L.H * 2;        // R: x of all tokens, raw
-    if (lds < lds_r) lds = lds_r;
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
     if (L.bits == 4)
         hipLaunchKernelGGL((k_decode_small<4>), dim3(grid), dim3(DT), lds, s, a);
@@ -1230,8 +1416,11 @@ hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBu
     return launch(a, s);
 }
 
+// (LDS bound: two workgroups per CU keep the whole grid resident on these shapes; larger
+// ones take the grouped path)
 bool decode_small_eligible(const Layer &L, int64_t T) {
-    return T >= 2 && T <= SM_TMAX && T * (L.K + 1) * L.I / 2 <= SM_HWORDS && L.E <= SM_TE;
+    return T >= 2 && T <= SM_TMAX && T * (L.K + 1) * L.I / 2 <= SM_HWORDS && L.E <= SM_TE &&
+           small_lds_bytes(L, (int)T) <= SMALL_LDS_MAX;
 }
 
 hipError_t launch_decode_small_layer(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b, void *y,

@@ -161,6 +161,24 @@ def test_grouped_small_parity(torch, qs, cfg, T):
         oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} T={T}")
 
 
+@pytest.mark.parametrize("cfg,T", [("DECODE", 2), ("DECODE", 3), ("DECODE", 4),
+                                   ("SKEW", 2), ("SKEW", 3), ("SKEW", 4)])
+def test_small_batch_decode_parity(torch, qs, cfg, T):
+    """Small-batch decode (T = 2..4 in one launch, 4- and 8-bit codes at hidden 2048):
+    every token vs the oracle in both output types; then T copies of one token, which
+    share all their experts (the union is k experts) and must give T identical rows."""
+    L = layer(cfg)
+    x_np = syn.make_x(T, L.hidden, seed=100 + T)
+    for bf16_out in (False, True):
+        y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
+        oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} small T={T}")
+    xd = np.repeat(x_np[:1], T, axis=0)
+    y, idx, w = run_layer(torch, qs, L, xd)
+    oracle_check(L, xd, y_to_np(y, torch), idx, w, False, f"{cfg} small T={T} repeated token")
+    for t in range(1, T):
+        assert torch.equal(y[t], y[0]) and (idx[t] == idx[0]).all() and (w[t] == w[0]).all()
+
+
 @pytest.mark.parametrize("cfg,T", [("PREFILL", 4096), ("SKEW", 16384)])
 def test_full_size_sampled(torch, qs, cfg, T):
     """Full workload size in the benchmark's launch configuration; sampled tokens vs
