@@ -1,0 +1,179 @@
+// decode_state.h -- what the one-launch decode kernels (T = 1: decode.hip; T = 2..4:
+// decode_small.hip) share: the workgroup shape, the layout of the decode state at the
+// start of the workspace (generation, completion counters, tagged hand-off words), the
+// device-scope hand-off primitives, the in-register dequantising dot product and the
+// selector.
+//
+// Hand-offs between workgroups use device-scope (sc1) stores/loads and device-scope
+// atomics, which are coherent across the XCDs without L2 write-back/invalidate.  Every
+// hand-off word carries the call's tag in its upper half, so a reader knows a word is
+// current without any ordering between words.
+#pragma once
+#include "common.h"
+#include "internal.h"
+
+namespace qs {
+
+namespace {
+
+constexpr int DT = 512;                     // threads per workgroup (8 waves)
+constexpr int NW = DT / 64;
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
+constexpr int NGRP = 16;                    // group counters of the completion count
+
+// Decode state at the start of the workspace, in uint32 units.  It must be zero before
+// the first call and is kept by the library between calls.
+constexpr int CTL_ERR = 0;                  // set if a bounded wait ever gave up
+constexpr int CTL_GEN = 64;                 // calls completed; this call's tag is gen + 1
+constexpr int CNT_BASE = 128;               // + g * 64: completion group counters
+constexpr int CNT_TOP = CNT_BASE + NGRP * 64;
+// Hand-off words are written in several copies, 256 bytes off a multiple of the copy
+// size apart, so that the many workgroups polling them spread over memory channels
+// instead of queueing on a few lines.
+constexpr int LOGIT_COPIES = 32;
+constexpr int LOGIT_STRIDE = 2 * 256 + 64;  // per copy: E words of 64 bits, logit bits | tag << 32
+constexpr int LOGIT_BASE = CNT_TOP + 64;
+constexpr int H_COPIES = 8;
+constexpr int H_WORDS_MAX = 24576 / 2;      // (top_k + 1) * inter <= 24576
+constexpr int H_STRIDE = 2 * H_WORDS_MAX + 64;  // per copy: (K+1)*I/2 words, fp16 h[j], h[j+1] | tag << 32
+constexpr int H_BASE = LOGIT_BASE + LOGIT_COPIES * LOGIT_STRIDE;
+constexpr int TOPK_COPIES = 32;
+constexpr int TOPK_STRIDE = 1088;           // per copy: 2 words of 64 bits per selected expert,
+                                            // (id | tag << 32) and (weight bits | tag << 32)
+constexpr int TOPK_BASE = H_BASE + H_COPIES * H_STRIDE;
+constexpr int N_SELECT = 8;                 // selector workgroups of a layer call
+static_assert((TOPK_BASE + TOPK_COPIES * TOPK_STRIDE) * 4 <= (int)WS_CTL_BYTES, "decode state region");
+
+
+__device__ __forceinline__ void st_dev(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes (two tagged words) written through to device scope in one store: hand-off
+// lines are written whole by one instruction, not merged from many small writes
+__device__ __forceinline__ void st_dev128(void *p, u32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+// 32 bytes (four tagged words) read at device scope with two 16-byte loads, waited for
+// here (the compiler does not track loads issued from inline assembly)
+__device__ __forceinline__ void ld_dev256(const void *p, u32x4 &a, u32x4 &b) {
+    asm volatile(
+        "global_load_dwordx4 %0, %2, off sc1\n\t"
+        "global_load_dwordx4 %1, %2, off offset:16 sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(a), "=&v"(b)
+        : "v"(p)
+        : "memory");
+}
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev(uint32_t *p) {
+    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
+
+__device__ void raise_error(uint32_t *ctl) {
+    __hip_atomic_fetch_or(ctl + CTL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// back-off between polls of a word another workgroup has not yet written
+__device__ __forceinline__ void poll_pause(uint32_t n) {
+    if (n < 8) __builtin_amdgcn_s_sleep(1);
+    else __builtin_amdgcn_s_sleep(4);
+}
+
+// the last workgroup of a call: counters back to zero, generation advanced
+__device__ void finish_call(uint32_t *ctl, uint32_t tag) {
+    const int t = threadIdx.x;
+    if (t < NGRP) st_dev(ctl + CNT_BASE + t * 64, 0u);
+    if (t == NGRP) st_dev(ctl + CNT_TOP, 0u);
+    if (t == NGRP + 1) st_dev(ctl + CTL_GEN, tag);
+}
+
+__device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
+
+// sum_c (s q_c + b) x_c over one 16-byte chunk of codes; X = (sum of x over the even
+// columns, over the odd columns).  4-bit: the low nibble of each byte (even columns)
+// becomes 1024 + q, the high nibble (odd columns) is taken in place as 1024 + 16 q, both
+// exact in fp16, so one shift serves 8 codes:
+//   sum (s q + b) x = s A_e + (s / 16) A_o + (b - 1024 s) X_e + (b - 64 s) X_o
+// with A_e, A_o the dot products of the magic values with x.  8-bit: 1024 + q for all.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 X) {
+    const u32x4 *xv = (const u32x4 *)xs;
+    const uint32_t magic = QS_MAGIC;
+    const float s = f16_to_f32((uint16_t)s16), b = f16_to_f32((uint16_t)b16);
+    if constexpr (BITS == 4) {
+        const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
+        float ae[2] = {0.0f, 0.0f}, ao[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t w8 = q[d] >> 8;
+            const u32x4 xx = xv[d];
+            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[0]), ae[d & 1], false);
+            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], hi, magic)), as_h2(xx[1]), ao[d & 1], false);
+            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, lo, magic)), as_h2(xx[2]), ae[d & 1], false);
+            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, hi, magic)), as_h2(xx[3]), ao[d & 1], false);
+        }
+        const float Ae = ae[0] + ae[1], Ao = ao[0] + ao[1];
+        return s * Ae + (s * 0.0625f) * Ao + (b - 1024.0f * s) * X.x + (b - 64.0f * s) * X.y;
+    } else {
+        const uint32_t lo = 0x00FF00FFu;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const u32x4 xx = xv[d >> 1];
+            const int o = 2 * (d & 1);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[o]), acc[d], false);
+            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d] >> 8, lo, magic)), as_h2(xx[o + 1]), acc[d], false);
+        }
+        const float A = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        return s * A + (b - 1024.0f * s) * (X.x + X.y);
+    }
+}
+
+// Selector (one wave): waits (bounded) until every logit of this call is in and takes
+// the top-k: lanes j < K return (id, weight) of the j-th selected expert in ascending
+// id.  One poll is in flight at a time: a read still in flight when the data is found
+// would have to be waited for before its registers are reused, a full extra round trip.
+__device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t tag, int E, int K) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t none = (uint64_t)tag << 32;
+    uint64_t w[4];
+    for (uint32_t n = 0;; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
+        bool miss = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) miss |= tag_of(w[i]) != tag;
+        if (__ballot(miss) == 0ull) break;
+        if (n > SPIN_LIMIT) {
+            if (lane == 0) raise_error(ctl);
+            break;
+        }
+        poll_pause(n);
+    }
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = no_nan(__uint_as_float((uint32_t)w[i]));
+    TopkOut tk = wave_topk_regs(v, E, K);
+    tk.idx = min(max(tk.idx, 0), E - 1);
+    return tk;
+}
+// lanes sharing one row: the largest power of two <= min(64, 16-byte chunks per row)
+int lanes_per_row(int ncols, int bits) {
+    const int chunks = ncols * bits / 128;
+    int l = 64;
+    while (l > chunks) l >>= 1;
+    return l;
+}
+
+}  // namespace
+
+}  // namespace qs
