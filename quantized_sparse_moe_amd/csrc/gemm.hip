@@ -39,8 +39,9 @@
 // the same.)
 //
 // Modes: 0 = [gate; up] + SwiGLU -> h (routed rows gathered through perm, shared rows
-// direct); 1 = routed down projection -> slot row t*k + j = w_tj * o (fp16); 2 = shared
-// down projection -> slot row T*k + t.  k_combine then adds each token's k slot rows in
+// direct); 1 = down projection: routed tiles -> slot row t*k + j = w_tj * o (fp16),
+// shared tiles -> slot row T*k + t, in one launch (the shared tiles, full ones, first, so
+// the ragged routed tiles fill the last round).  k_combine then adds each token's k slot rows in
 // ascending expert order and its shared row, in fp32, and writes y: a deterministic,
 // atomic-free combine.
 #include "common.h"
@@ -156,16 +157,8 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     const int ti = (bslot / a.nb) * 8 + xcd, nbi = bslot % a.nb;
     const int nrt = a.ntiles[0], nsh = a.ntiles[1] - nrt;
     int tix;
-    if (MODE == 0) {
-        if (ti >= nrt + nsh) return;
-        tix = ti < nsh ? nrt + ti : ti - nsh;          // shared (full) tiles first
-    } else if (MODE == 1) {
-        if (ti >= nrt) return;
-        tix = ti;
-    } else {
-        if (ti >= nsh) return;
-        tix = nrt + ti;
-    }
+    if (ti >= nrt + nsh) return;
+    tix = ti < nsh ? nrt + ti : ti - nsh;              // shared (full) tiles first
     const Tile tile = a.tiles[tix];
     const int E = L.E, K = L.K, H = L.H, I = L.I;
     const bool shared = tile.expert == E;
@@ -362,13 +355,14 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     __shared__ float s_w[BM];
     int my_pos = 0;
     float my_w = 0.0f;
-    if (MODE == 1 && tid < BM) my_pos = a.perm[tile.row0 + (tid < nrows ? tid : nrows - 1)];
+    const bool routed_down = MODE == 1 && !shared;
+    if (routed_down && tid < BM) my_pos = a.perm[tile.row0 + (tid < nrows ? tid : nrows - 1)];
 #pragma unroll
     for (int p = 0; p < C::NSTAGE - 1; ++p)
         if (p < nk) issue(p);
-    if (MODE == 1 && tid < BM) my_w = a.w[my_pos];
+    if (routed_down && tid < BM) my_w = a.w[my_pos];
     kloop();
-    if (MODE == 1 && tid < BM) {
+    if (routed_down && tid < BM) {
         s_pos[tid] = my_pos;
         s_w[tid] = my_w;
     }
@@ -405,7 +399,7 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         return;
     }
 
-    // MODE 1 / 2: 32 rows at a time through a per-wave fp32 staging area; lane l then
+    // MODE 1: 32 rows at a time through a per-wave fp32 staging area; lane l then
     // owns row 32*hp + (l % 32) and 32 of the wave's 64 columns
     const int colbase = nbi * BN + wave * 64;
     if (colbase >= H) return;                                    // columns past H (H % 256 == 128)
@@ -427,8 +421,8 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
             const float *src = fs + er * FP + 32 * (lane >> 5);
             // routed rows: the (token, slot) row with its routing weight; shared rows:
             // row T*K + t with weight 1
-            const int64_t p = MODE == 1 ? (int64_t)s_pos[row] : (int64_t)tile.row0 + row;
-            const float wv = MODE == 1 ? s_w[row] : 1.0f;
+            const int64_t p = routed_down ? (int64_t)s_pos[row] : (int64_t)tile.row0 + row;
+            const float wv = routed_down ? s_w[row] : 1.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
@@ -516,16 +510,14 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
         if (a.wlog == 2) a.wlog = 1;                       // windows of 8, 2 or 1 groups
     }
     hipLaunchKernelGGL((k_gemm<BITS, 0>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
-    // routed down -> slots
+    // routed down -> weighted slot rows, shared down -> its own slot rows, one launch
     a.nb = (L.H + BN - 1) / BN;
     {
         const QMat *ms[2] = {&L.down, &L.s_down};
         a.wlog = window_log(ms, L.has_shared ? 2 : 1, L.I, C::WMAX);
         if (a.wlog == 2) a.wlog = 1;
     }
-    hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr, a.nb)), dim3(NT), 0, s, a);
-    // shared down -> its own slot rows
-    if (L.has_shared) hipLaunchKernelGGL((k_gemm<BITS, 2>), dim3(grid_for(maxs, a.nb)), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
     const int64_t n = a.T * (L.H / 8);
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.slot, a.y, a.y_dtype,
                        a.T, L.K, L.H, L.has_shared);

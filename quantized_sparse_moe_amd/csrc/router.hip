@@ -8,9 +8,9 @@
 // Logits are a dense [T x H] x [H x E] contraction: bf16 activations against bf16
 // router weights on MFMA (v_mfma_f32_16x16x32_bf16, exact products, fp32 accumulation),
 // tiled 64 tokens x 64 experts per workgroup with both operands staged in LDS, so each
-// router row is read once per 64 tokens.  The workgroups of expert block 0 also write
-// the fp16 copy of x, each group of 8 columns permuted into the code order used by the
-// expert GEMMs.  The top-k pass then gives one wave to each token.
+// router row is read once per 64 tokens.  The workgroups of a token block also write
+// the fp16 copy of x (taking K chunks in turn), each group of 8 columns permuted into
+// the code order used by the expert GEMMs.  The top-k pass then gives one wave to each token.
 #include "common.h"
 #include "internal.h"
 
@@ -35,7 +35,7 @@ struct LogitArgs {
 };
 
 template <int BITS>
-__global__ __launch_bounds__(256) void k_logits(LogitArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_logits(LogitArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xa[LT * LPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t wa[LE * LPITCH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -43,7 +43,6 @@ __global__ __launch_bounds__(256) void k_logits(LogitArgs a) {
     const int64_t t0 = (int64_t)blockIdx.x * LT;
     const int e0 = blockIdx.y * LE;
     const int H = a.H, E = a.E;
-    const bool write_x16 = a.x16 && blockIdx.y == 0;
     // staging: thread tid moves chunk (tid % 16) of rows tid / 16 + 16 i (i < 4) of both tiles
     const int sr = tid >> 4, sc = (tid & 15) * 8;
     int64_t xrow[4];
@@ -65,15 +64,18 @@ __global__ __launch_bounds__(256) void k_logits(LogitArgs a) {
     f32x4 acc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    u32x4 xv[4], wv[4];
-    load(0, xv, wv);
-    for (int kc = 0; kc < H; kc += LK) {
+    // chunk kc: registers -> LDS (and the fp16 copy of x), then 4 x 4 MFMAs; two chunks
+    // are in flight in registers while one is multiplied (one workgroup per CU at the
+    // prefill sizes, so the loads' latency is hidden by this workgroup alone)
+    auto step = [&](int kc, const u32x4 (&xv)[4], const u32x4 (&wv)[4]) __attribute__((always_inline)) {
+        // the expert blocks of a token block take turns writing the fp16 copy of x
+        const bool write_x16 = a.x16 && (int)((kc / LK) % gridDim.y) == (int)blockIdx.y;
         __syncthreads();                                 // the previous chunk is consumed
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             *(u32x4 *)(xa + (sr + 16 * i) * LPITCH + sc) = xv[i];
             *(u32x4 *)(wa + (sr + 16 * i) * LPITCH + sc) = wv[i];
-            if (write_x16 && xrow[i] >= 0) {
+            if (write_x16 && xrow[i] >= 0) {                // this chunk's share of the fp16 copy
                 u32x4 h;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -83,7 +85,8 @@ __global__ __launch_bounds__(256) void k_logits(LogitArgs a) {
             }
         }
         __syncthreads();
-        if (kc + LK < H) load(kc + LK, xv, wv);         // next chunk in flight meanwhile
+    };
+    auto mult = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < LK / 32; ++s) {
             const bf16x8 A = *(const bf16x8 *)(xa + (wave * 16 + n16) * LPITCH + s * 32 + 8 * cg);
@@ -92,6 +95,19 @@ __global__ __launch_bounds__(256) void k_logits(LogitArgs a) {
                 const bf16x8 B = *(const bf16x8 *)(wa + (n * 16 + n16) * LPITCH + s * 32 + 8 * cg);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[n], 0, 0, 0);
             }
+        }
+    };
+    u32x4 xv0[4], wv0[4], xv1[4], wv1[4];
+    load(0, xv0, wv0);
+    if (LK < H) load(LK, xv1, wv1);
+    for (int kc = 0; kc < H; kc += 2 * LK) {
+        step(kc, xv0, wv0);
+        if (kc + 2 * LK < H) load(kc + 2 * LK, xv0, wv0);
+        mult();
+        if (kc + LK < H) {
+            step(kc + LK, xv1, wv1);
+            if (kc + 3 * LK < H) load(kc + 3 * LK, xv1, wv1);
+            mult();
         }
     }
     // acc[n][r]: token 16 * wave + 4 * cg + r, expert e0 + 16 * n + n16
