@@ -111,7 +111,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     const int64_t H = d->hidden, I = d->inter, K = d->top_k, E = d->n_experts;
     const int64_t nblk = (T + ROUTER_TOKENS - 1) / ROUTER_TOKENS;
     PrefillBufs b;
-    c.take<uint32_t>(WS_CTL_BYTES / 4);              // decode state stays untouched
+    b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);      // decode state stays untouched (but word 0)
     b.x16 = c.take<uint16_t>((size_t)(T * H));
     b.logits = c.take<float>((size_t)(T * E));
     b.idx = c.take<int32_t>((size_t)(T * K));
@@ -122,6 +122,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     b.perm = c.take<int32_t>((size_t)(T * K));
     b.tiles = c.take<Tile>((size_t)prefill_max_tiles(T, (int)K, (int)E));
     b.ntiles = c.take<int32_t>(2);
+    b.tile_done = c.take<int32_t>((size_t)prefill_max_tiles(T, (int)K, (int)E));
     b.h = c.take<uint16_t>((size_t)((T * K + T) * I));
     b.slot = c.take<uint16_t>((size_t)((T * K + T) * H));
     *bytes = c.off;

@@ -52,7 +52,9 @@ __global__ __launch_bounds__(256) void k_colscan(const int32_t *__restrict__ blk
 __global__ __launch_bounds__(256) void k_tiles(const int32_t *__restrict__ counts,
                                                int32_t *__restrict__ expert_off,
                                                Tile *__restrict__ tiles, int32_t *__restrict__ ntiles,
+                                               int32_t *__restrict__ tile_done, int max_tiles,
                                                int E, int64_t T, int K, int shared) {
+    for (int i = threadIdx.x; i < max_tiles; i += 256) tile_done[i] = 0;   // the GEMMs' tile counters
     __shared__ int wsum[3][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = tid < E ? counts[tid] : 0;
@@ -161,8 +163,8 @@ hipError_t launch_prefill_binning(const Layer &L, int64_t T, const PrefillBufs &
     int32_t *counts = b.expert_off + (L.E + 1);        // E ints after expert_off
     hipLaunchKernelGGL(k_colscan, dim3((L.E + 3) / 4), dim3(256), 0, s, b.blkcnt, b.blkoff, counts,
                        nblk, L.E);
-    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(256), 0, s, counts, b.expert_off, b.tiles, b.ntiles,
-                       L.E, T, L.K, L.has_shared);
+    hipLaunchKernelGGL(k_tiles, dim3(1), dim3(256), 0, s, counts, b.expert_off, b.tiles, b.ntiles, b.tile_done,
+                       (int)prefill_max_tiles(T, L.K, L.E), L.E, T, L.K, L.has_shared);
     hipLaunchKernelGGL(k_scatter, dim3(nblk), dim3(256), 0, s, b.idx, b.blkoff, b.expert_off, b.perm,
                        T, L.K, L.E);
     return hipGetLastError();

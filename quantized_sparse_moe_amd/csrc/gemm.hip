@@ -87,12 +87,20 @@ struct GemmArgs {
     int y_dtype;
     int nb;                          // column blocks per tile
     int wlog;                        // log2 of the scale / bias window (groups per row per load)
+    int32_t *tile_done;              // [tiles] gate/up column blocks finished (zeroed by binning)
+    int nb_gateup;                   // down pass: the gate/up column blocks a tile waits for
+    uint32_t *err;                   // bounded-wait error flag
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
 
 __device__ __forceinline__ void dma16(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 16, 0, 0);
+}
+// the same at device scope (sc1): data another XCD wrote in this launch, not a stale
+// line of this XCD's L2
+__device__ __forceinline__ void dma16_dev(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 16, 0, 16);
 }
 __device__ __forceinline__ void dma4(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_t *)l, 4, 0, 0);
@@ -145,15 +153,14 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f1
 }
 
 template <int BITS, int MODE>
-__global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint8_t *smem) {
     using C = Cfg<BITS>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
     const Layer &L = a.L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---- which tile and column block: the nb column blocks of a tile (which share its
     // activation rows) run on one XCD; consecutive tiles go round the XCDs in list order
-    const int xcd = blockIdx.x & 7, bslot = blockIdx.x >> 3;
+    const int xcd = bid & 7, bslot = bid >> 3;
     const int ti = (bslot / a.nb) * 8 + xcd, nbi = bslot % a.nb;
     const int nrt = a.ntiles[0], nsh = a.ntiles[1] - nrt;
     int tix;
@@ -229,7 +236,10 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     auto issue = [&](int k) __attribute__((always_inline)) {
         uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < C::A_DMA; ++i) dma16(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
+        for (int i = 0; i < C::A_DMA; ++i) {
+            if (MODE == 1) dma16_dev(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
+            else dma16(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
+        }
         uint8_t *bst = st + C::A_BYTES;
 #pragma unroll
         for (int d = 0; d < C::B_DMA; ++d) {
@@ -357,6 +367,23 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
     float my_w = 0.0f;
     const bool routed_down = MODE == 1 && !shared;
     if (routed_down && tid < BM) my_pos = a.perm[tile.row0 + (tid < nrows ? tid : nrows - 1)];
+    if (MODE == 1) {
+        // this tile's h rows are complete once all gate/up column blocks of the tile have
+        // counted themselves in; they run earlier in the grid (lower workgroup index,
+        // dispatched first), so the wait ends; it is bounded regardless
+        if (tid == 0) {
+            for (uint32_t it = 0;
+                 __hip_atomic_load(a.tile_done + tix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.nb_gateup;
+                 ++it) {
+                if (it > (1u << 24)) {
+                    __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        __syncthreads();
+    }
 #pragma unroll
     for (int p = 0; p < C::NSTAGE - 1; ++p)
         if (p < nk) issue(p);
@@ -391,11 +418,19 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         wave_lds_sync();
         const int chunk = lane & 3;
         uint16_t *hout = a.h + (int64_t)tile.row0 * I + nbi * 128 + wave * 32 + chunk * 8;
+        // h goes out at device scope (sc1, written through), and once every wave's stores
+        // have completed the workgroup counts itself in for the tile's down pass
 #pragma unroll
         for (int q = 0; q < BM / 16; ++q) {
             const int row = (lane >> 2) + 16 * q;
-            if (row < nrows) *(u32x4 *)(hout + (int64_t)row * I) = *(const u32x4 *)(hs + row * HP + chunk * 8);
+            if (row < nrows) {
+                const u32x4 v = *(const u32x4 *)(hs + row * HP + chunk * 8);
+                asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(hout + (int64_t)row * I), "v"(v) : "memory");
+            }
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -436,6 +471,16 @@ __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a) {
         }
         wave_lds_sync();
     }
+}
+
+// gate/up (workgroups [0, g0)) and down (the rest) in one launch: a down workgroup waits
+// only for the gate/up column blocks of its own tile, so down tiles fill the slots the
+// last, partial round of gate/up tiles leaves free
+template <int BITS>
+__global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a0, GemmArgs a1, int g0) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<BITS>::LDS];
+    if ((int)blockIdx.x < g0) gemm_body<BITS, 0>(a0, (int)blockIdx.x, smem);
+    else gemm_body<BITS, 1>(a1, (int)blockIdx.x - g0, smem);
 }
 
 // The combine: y[t] = sum of the token's k slot rows in ascending expert id, then its
@@ -503,21 +548,24 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
     const int64_t maxr = prefill_max_routed_tiles(a.T, L.K, L.E);
     const int64_t maxs = L.has_shared ? (a.T + GEMM_BM - 1) / GEMM_BM : 0;
     // [gate; up] + SwiGLU over routed and shared tiles
-    a.nb = L.I / 128;
+    GemmArgs a0 = a;
+    a0.nb = L.I / 128;
     {
         const QMat *ms[4] = {&L.gate, &L.up, &L.s_gate, &L.s_up};
-        a.wlog = window_log(ms, L.has_shared ? 4 : 2, L.H, C::WMAX);
-        if (a.wlog == 2) a.wlog = 1;                       // windows of 8, 2 or 1 groups
+        a0.wlog = window_log(ms, L.has_shared ? 4 : 2, L.H, C::WMAX);
+        if (a0.wlog == 2) a0.wlog = 1;                     // windows of 8, 2 or 1 groups
     }
-    hipLaunchKernelGGL((k_gemm<BITS, 0>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
-    // routed down -> weighted slot rows, shared down -> its own slot rows, one launch
-    a.nb = (L.H + BN - 1) / BN;
+    // down: routed tiles -> weighted slot rows, shared tiles -> their own slot rows
+    GemmArgs a1 = a;
+    a1.nb = (L.H + BN - 1) / BN;
+    a1.nb_gateup = a0.nb;
     {
         const QMat *ms[2] = {&L.down, &L.s_down};
-        a.wlog = window_log(ms, L.has_shared ? 2 : 1, L.I, C::WMAX);
-        if (a.wlog == 2) a.wlog = 1;
+        a1.wlog = window_log(ms, L.has_shared ? 2 : 1, L.I, C::WMAX);
+        if (a1.wlog == 2) a1.wlog = 1;
     }
-    hipLaunchKernelGGL((k_gemm<BITS, 1>), dim3(grid_for(maxr + maxs, a.nb)), dim3(NT), 0, s, a);
+    const unsigned g0 = grid_for(maxr + maxs, a0.nb), g1 = grid_for(maxr + maxs, a1.nb);
+    hipLaunchKernelGGL((k_gemm<BITS>), dim3(g0 + g1), dim3(NT), 0, s, a0, a1, (int)g0);
     const int64_t n = a.T * (L.H / 8);
     hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.slot, a.y, a.y_dtype,
                        a.T, L.K, L.H, L.has_shared);
@@ -538,6 +586,9 @@ hipError_t launch_prefill_gemms(const Layer &L, int64_t T, const PrefillBufs &b,
     a.ntiles = b.ntiles;
     a.w = b.w;
     a.slot = b.slot;
+    a.tile_done = b.tile_done;
+    a.err = b.ctl;
+    a.nb_gateup = 0;
     a.y = y;
     a.y_dtype = y_dtype;
     a.nb = 1;

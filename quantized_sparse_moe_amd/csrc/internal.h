@@ -69,6 +69,8 @@ struct PrefillBufs {
     int32_t *perm;                 // [T*K]      position -> t*K + j
     Tile *tiles;                   // [max_tiles] routed full, routed partial, then shared tiles
     int32_t *ntiles;               // [2] routed tiles, routed + shared tiles
+    int32_t *tile_done;            // [max_tiles] gate/up column blocks finished per tile
+    uint32_t *ctl;                 // the workspace's state region (word 0: bounded-wait error flag)
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
     uint16_t *slot;                // [T*K + T][H] fp16: w_j * o_j per (token, slot), then shared o
 };
