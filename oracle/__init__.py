@@ -68,11 +68,13 @@ def lib():
         L.orc_q8_unpack_rows16.argtypes = [P, I64, I64, P]
         L.orc_q8_quantize_row.argtypes = [P, I64, P]
         L.orc_q8_dequantize_row.argtypes = [P, I64, P]
+        L.orc_q8_quantize_x.argtypes = [P, I64, P, P]
+        L.orc_q8_gemv_q8x.argtypes = [P, I64, I64, P, P, P]
         L.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_dequant_matrix", "orc_router_logits", "orc_route", "orc_layer_forward",
                   "orc_layer_forward_with_routing", "orc_expert_mlp", "orc_q8_gemv",
                   "orc_q8_pack_rows16", "orc_q8_unpack_rows16", "orc_q8_quantize_row",
-                  "orc_q8_dequantize_row"):
+                  "orc_q8_dequantize_row", "orc_q8_quantize_x", "orc_q8_gemv_q8x"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -235,6 +237,26 @@ def q8_dequantize_row(blocks: np.ndarray, K: int) -> np.ndarray:
     out = np.empty((K,), dtype=np.float64)
     lib().orc_q8_dequantize_row(blocks.ctypes.data, K, out.ctypes.data)
     return out
+
+
+def q8_quantize_x(x_bf16: np.ndarray):
+    """Activation quantization (bf16 bits [K] -> int8 codes [K], fp16 scale bits [K/32])."""
+    x = np.ascontiguousarray(x_bf16).view(np.uint16)
+    K = x.shape[0]
+    q = np.empty((K,), dtype=np.int8)
+    d = np.empty((K // 32,), dtype=np.uint16)
+    lib().orc_q8_quantize_x(x.ctypes.data, K, q.ctypes.data, d.ctypes.data)
+    return q, d
+
+
+def q8_gemv_q8x(rows: np.ndarray, N: int, K: int, xq: np.ndarray, xd: np.ndarray) -> np.ndarray:
+    """GEMV over row-contiguous Q8_0 blocks with a quantized activation (fp64 result)."""
+    rows = np.ascontiguousarray(rows, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    xd = np.ascontiguousarray(xd, dtype=np.uint16)
+    y = np.empty((N,), dtype=np.float64)
+    lib().orc_q8_gemv_q8x(rows.ctypes.data, N, K, xq.ctypes.data, xd.ctypes.data, y.ctypes.data)
+    return y
 
 
 def f16_to_double(h: int) -> float:

@@ -361,6 +361,50 @@ void orc_q8_dequantize_row(const uint8_t *blocks, int64_t K, double *v)
     }
 }
 
+/* Activation quantization shared by the projections that read one vector ([EMBER]:
+ * Q/K/V, and gate/up, read one quantized copy of their input).  Each block of 32 values
+ * becomes a Q8_0 block: d = max|x| / 127 in binary32, stored as binary16; q = x / d in
+ * binary32 (the unrounded d), rounded half away from zero (roundf), clamped to
+ * [-127, 127]; an all-zero block has d = 0 and q = 0.  The codes are an integer
+ * decision, taken in binary32 on both sides. */
+void orc_q8_quantize_x(const uint16_t *x, int64_t K, int8_t *q, uint16_t *d)
+{
+    for (int64_t b = 0; b < K / 32; ++b) {
+        float v[32], amax = 0.0f;
+        for (int c = 0; c < 32; ++c) {
+            v[c] = (float)orc_bf16_to_double(x[b * 32 + c]);      /* exact */
+            if (fabsf(v[c]) > amax) amax = fabsf(v[c]);
+        }
+        const float db = amax / 127.0f;
+        d[b] = double_to_f16((double)db);
+        for (int c = 0; c < 32; ++c) {
+            float r = (db != 0.0f) ? roundf(v[c] / db) : 0.0f;
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[b * 32 + c] = (int8_t)r;
+        }
+    }
+}
+
+/* Q8_0 GEMV with a Q8_0 activation: y[n] = sum_b dw[n,b] dx[b] sum_c qw[n,32b+c] qx[32b+c],
+ * the integer dot exact, the rest in fp64 (rows row-contiguous, as orc_q8_gemv). */
+void orc_q8_gemv_q8x(const uint8_t *rows, int64_t N, int64_t K, const int8_t *xq, const uint16_t *xd,
+                     double *y)
+{
+    const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t b = 0; b < nb; ++b) {
+            const uint8_t *blk = rows + (n * nb + b) * Q8_BLOCK_BYTES;
+            int64_t dot = 0;
+            for (int c = 0; c < 32; ++c) dot += (int64_t)(int8_t)blk[2 + c] * (int64_t)xq[b * 32 + c];
+            acc += orc_f16_to_double(rd16(blk)) * orc_f16_to_double(xd[b]) * (double)dot;
+        }
+        y[n] = acc;
+    }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

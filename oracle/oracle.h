@@ -87,6 +87,11 @@ void orc_q8_unpack_rows16(const uint8_t *tiles, int64_t N, int64_t K, uint8_t *r
 /* Q8_0 block quantizer / dequantizer for one row of K floats (K % 32 == 0) */
 void orc_q8_quantize_row(const float *v, int64_t K, uint8_t *blocks);
 void orc_q8_dequantize_row(const uint8_t *blocks, int64_t K, double *v);
+/* Q8_0 quantization of an activation vector (bf16 [K] -> int8 [K] + fp16 [K/32]) and the
+ * GEMV over Q8_0 rows with it (integer dots, fp64 scaling). */
+void orc_q8_quantize_x(const uint16_t *x, int64_t K, int8_t *q, uint16_t *d);
+void orc_q8_gemv_q8x(const uint8_t *rows, int64_t N, int64_t K, const int8_t *xq, const uint16_t *xd,
+                     double *y);
 
 int orc_num_threads(void);
 

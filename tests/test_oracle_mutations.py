@@ -31,6 +31,11 @@ MUTATIONS = [
     ("tile rows not interleaved", "return (int64_t)(c / 4) * 64 + r * 4 + (c % 4);",
      "return (int64_t)r * 32 + c;"),
     ("q8 code read unsigned", "dot += (double)(int8_t)blk[2 + c]", "dot += (double)blk[2 + c]"),
+    ("activation codes rounded to nearest even", "roundf(v[c] / db)", "rintf(v[c] / db)"),
+    ("activation max without abs", "if (fabsf(v[c]) > amax) amax = fabsf(v[c]);", "if (v[c] > amax) amax = v[c];"),
+    ("activation scale dropped", "acc += orc_f16_to_double(rd16(blk)) * orc_f16_to_double(xd[b]) * (double)dot;",
+     "acc += orc_f16_to_double(rd16(blk)) * (double)dot;"),
+    ("activation code read unsigned", "(int64_t)xq[b * 32 + c]", "(int64_t)(uint8_t)xq[b * 32 + c]"),
 ]
 
 

@@ -350,6 +350,100 @@ def test_q8_block_round_trips(orc):
     assert (z == 0).all()
 
 
+def bf16_bits(vals):
+    """bf16 bit patterns of values that bf16 holds exactly (checked)."""
+    v = np.asarray(vals, dtype=np.float32)
+    b = (v.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(np_bf16(b), v.astype(np.float64))
+    return b
+
+
+def test_q8x_quantizer_hand_example(orc):
+    """Activation blocks whose codes follow by hand from the reading: d = max|x| / 127,
+    q = x / d rounded half away from zero.  max|x| = 127 gives d = 1 (codes = x rounded);
+    max|x| = 254 gives d = 2; a zero block gives d = 0 and zero codes.  The halves (0.5,
+    -2.5, 63.5, -100.5, 3 / 2) tell half-away-from-zero from round-to-nearest-even."""
+    b0 = [127, -127, 0.5, -0.5, 1.5, -2.5, 63.5, 0, 2.25, -100.5] + [0] * 22
+    q0 = [127, -127, 1, -1, 2, -3, 64, 0, 2, -101] + [0] * 22
+    b1 = [254, 3, -5, 7, -1, 0.5] + [0] * 26
+    q1 = [127, 2, -3, 4, -1, 0] + [0] * 26          # 3/2 -> 2, -5/2 -> -3, 7/2 -> 4, -1/2 -> -1
+    x = bf16_bits(b0 + b1 + [0] * 32)
+    q, d = orc.q8_quantize_x(x)
+    assert q.tolist() == q0 + q1 + [0] * 32
+    assert np_f16(d).tolist() == [1.0, 2.0, 0.0]
+
+
+def test_q8x_quantizer_invariants(orc):
+    """Random activations: codes in [-127, 127], each nonzero block reaches |q| = 127,
+    q(-x) = -q(x), q(2x) = q(x) with d doubled (powers of two are exact), and the round
+    trip |fp16(d) q - x| <= d/2 + 127 |d - fp16(d)| with d = max|x| / 127."""
+    K = 32 * 96
+    x = syn.make_x(1, K, seed=12)[0]
+    x[32:64] = 0                                    # one all-zero block
+    q, d = orc.q8_quantize_x(x)
+    qb = q.reshape(-1, 32).astype(np.int64)
+    assert np.abs(qb).max() <= 127
+    xv = np_bf16(x).reshape(-1, 32)
+    nz = np.abs(xv).max(1) > 0
+    assert (np.abs(qb[nz]).max(1) == 127).all() and (qb[~nz] == 0).all() and (np_f16(d)[~nz] == 0).all()
+    qn, dn = orc.q8_quantize_x(x ^ np.uint16(0x8000))
+    assert np.array_equal(qn, -q) and np.array_equal(dn, d)
+    x2 = bf16_bits(np_bf16(x).astype(np.float32) * 2)
+    q2, d2 = orc.q8_quantize_x(x2)
+    assert np.array_equal(q2, q) and np.array_equal(np_f16(d2), 2 * np_f16(d))
+    dex = np.abs(xv).max(1) / 127.0
+    d16 = np_f16(d)
+    err = np.abs(d16[:, None] * qb - xv)
+    bound = dex / 2 + 127 * np.abs(dex - d16)
+    assert (err <= bound[:, None] * (1 + 1e-6) + 1e-300).all()
+
+
+def test_q8x_gemv_reduces_to_exact_path(orc):
+    """When the activation is exactly a Q8_0 vector (x = e q with max|q| = 127 and e a
+    power of two) its quantization is lossless, so the integer-dot GEMV equals the exact
+    Q8_0 GEMV (pinned to numpy above) on x; it scales exactly with x; a single nonzero
+    code pair gives dw dx qw qx."""
+    N, K = 48, 512
+    rows = syn.make_q8_rows(N, K, seed=4)
+    rng = np.random.default_rng(5)
+    qx = rng.integers(-127, 128, size=K)
+    qx[::32] = 127                                   # every block reaches 127
+    x = bf16_bits(np.ldexp(qx.astype(np.float32), -6))
+    q, d = orc.q8_quantize_x(x)
+    assert np.array_equal(q.astype(np.int64), qx) and (np_f16(d) == 2.0 ** -6).all()
+    y = orc.q8_gemv_q8x(rows, N, K, q, d)
+    ref = orc.q8_gemv(rows, N, K, x)
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-13 * np.abs(ref).max())
+    q2, d2 = orc.q8_quantize_x(bf16_bits(np_bf16(x).astype(np.float32) * 4))
+    assert np.array_equal(orc.q8_gemv_q8x(rows, N, K, q2, d2), 4 * y)
+    one = np.zeros((16, 1, 34), dtype=np.uint8)
+    one[:, 0, 0:2] = np.array([np.float16(0.5)]).view(np.uint8)      # dw = 0.5
+    one[3, 0, 2 + 7] = np.uint8(np.int8(-9).view(np.uint8))
+    xq = np.zeros(32, dtype=np.int8)
+    xq[7] = 11
+    xd = np.array([np.float16(0.25)]).view(np.uint16)
+    yy = orc.q8_gemv_q8x(one, 16, 32, xq, xd)
+    assert yy[3] == 0.5 * 0.25 * -9 * 11 and (np.delete(yy, 3) == 0).all()
+
+
+def test_q8x_gemv_error_bound(orc):
+    """Random activations: the integer-dot GEMV differs from the exact path by at most
+    sum_b |dw| sum_c |qw| (d_b/2 + 127 |d_b - fp16(d_b)|) per row."""
+    N, K = 32, 1024
+    rows = syn.make_q8_rows(N, K, seed=6)
+    x = syn.make_x(1, K, seed=7)[0]
+    q, d = orc.q8_quantize_x(x)
+    y = orc.q8_gemv_q8x(rows, N, K, q, d)
+    ref = orc.q8_gemv(rows, N, K, x)
+    dw = np_f16(rows[:, :, 0:2].copy().view(np.uint16)[..., 0])
+    qw = np.abs(rows[:, :, 2:].view(np.int8).astype(np.float64)).sum(2)
+    xv = np_bf16(x).reshape(-1, 32)
+    dex = np.abs(xv).max(1) / 127.0
+    tol = (np.abs(dw) * qw * (dex / 2 + 127 * np.abs(dex - np_f16(d)))[None, :]).sum(1)
+    assert (np.abs(y - ref) <= tol * (1 + 1e-9)).all()
+    assert np.abs(y - ref).max() > 0                 # the quantization did change x
+
+
 def test_q8_page_byte_counts():
     """Ember's packed selections for Llama-3.2-1B (16 layers, Q8_0 = 34 bytes per 32
     weights): gate/up + Q/K/V/O = 714.0 MiB, and down adds 272.0 MiB."""
