@@ -6,14 +6,15 @@ batch of synthetic input already resident in HBM.  The headline line reports the
 batch-1 decode workload (hidden 2048, 256 experts top-8 + 1 shared, expert inter 512,
 4-bit affine group-64 weights, T = 1): tokens/s, with the layer's algorithmic weight
 bytes over HBM peak as the roofline.  Extra keys report the prefill (T = 4096), the
-skewed long prefill (T = 16384, 8-bit, Zipf router bias), the dense Q8_0 GEMV and
-(--only smallT) the decode layer at T = 1, 2, 4, 8.
+skewed long prefill (T = 16384, 8-bit, Zipf router bias), the dense Q8_0 GEMV, the
+same GEMVs with a quantized activation (int8 dots, and their deviation from the exact
+path) and (--only smallT) the decode layer at T = 1, 2, 4, 8.
 
 Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256 MB
 Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
 HIP graph; HIP events on the replay stream bracket the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,smallT,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,q8x,smallT,copy]
 """
 from __future__ import annotations
 
@@ -234,6 +235,43 @@ def bench_q8(qs, torch, syn, steps, warmup, layers=16):
     return ms, nbytes
 
 
+def bench_q8x(qs, torch, syn, steps, warmup, layers=16, fused=False):
+    """The same four projections with the activation quantized once per projection input
+    (q8_quantize_x) and int8-dot GEMVs (q8_gemv_q8x), or (fused) quantized inside the
+    GEMV (q8_gemv_qx); also the largest deviation from the exact-activation GEMV,
+    relative to that output's RMS."""
+    shapes = syn.Q8_SHAPES
+    mats = []
+    for (N, K) in shapes:
+        rows = torch.from_numpy(syn.make_q8_rows(N, K, seed=N + K).reshape(-1)).cuda()
+        tiles = qs.q8_pack_rows16(rows, N, K)
+        mats.append([(tiles if l == 0 else tiles.clone()) for l in range(layers)])
+    xs = {K: torch.from_numpy(syn.make_x(1, K, seed=K)[0].view(np.int16)).cuda() for _, K in shapes}
+    xqs = {K: torch.empty((K,), dtype=torch.int8, device="cuda") for _, K in shapes}
+    xds = {K: torch.empty((K // 32,), dtype=torch.int16, device="cuda") for _, K in shapes}
+    ys = [torch.empty((N,), dtype=torch.bfloat16, device="cuda") for N, _ in shapes]
+    torch.cuda.synchronize()
+
+    def step(i):
+        l = i % layers
+        for j, (N, K) in enumerate(shapes):
+            if fused:
+                qs.q8_gemv_qx(mats[j][l], N, K, xs[K], y=ys[j])
+            else:
+                qs.q8_quantize_x(xs[K], xq=xqs[K], xd=xds[K])
+                qs.q8_gemv_q8x(mats[j][l], N, K, xqs[K], xds[K], y=ys[j])
+
+    ms = _graph_time(torch, step, steps, warmup)
+    err = 0.0
+    for j, (N, K) in enumerate(shapes):
+        xq, xd = qs.q8_quantize_x(xs[K])
+        yq = qs.q8_gemv_q8x(mats[j][0], N, K, xq, xd).double()
+        ye = qs.q8_gemv(mats[j][0], N, K, xs[K]).double()
+        err = max(err, float((yq - ye).abs().max() / ye.pow(2).mean().sqrt()))
+    nbytes = sum(q8_weight_bytes(N, K) + 2 * K + 2 * N for N, K in shapes)
+    return ms, nbytes, err
+
+
 def bench_copy(torch, steps, nbytes=1 << 30):
     """Plain device-to-device copy of `nbytes` (torch's copy kernel): the calibration
     workload for the HBM byte counters (it must read and write exactly `nbytes`)."""
@@ -249,7 +287,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="decode,prefill,skew,q8")
+    ap.add_argument("--only", default="decode,prefill,skew,q8,q8x")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
@@ -302,6 +340,14 @@ def main(argv=None):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["q8"] = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
                      "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": nbytes}
+    if "q8x" in only:
+        steps = max(16, args.steps // 4)
+        for key, fused in (("q8x", False), ("q8qx", True)):
+            ms, nbytes, err = bench_q8x(qs, torch, syn, steps, args.warmup, fused=fused)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out[key] = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
+                        "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": nbytes,
+                        "max_err_vs_exact_over_rms": err}
     if "copy" in only:
         ms, nbytes = bench_copy(torch, 8)
         out["copy"] = {"bytes_each_way": nbytes, "ms": ms, "GB_per_s": 2 * nbytes / (ms * 1e-3) / 1e9}

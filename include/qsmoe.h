@@ -191,6 +191,37 @@ qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x,
                      void *y, int32_t y_dtype, void *stream);
 
 /*
+ * Activation quantization for the Q8_0 GEMV ([EMBER]: the activation is quantized once
+ * and the quantized copy is shared by the projections that read it, Q/K/V and gate/up).
+ * Each block of 32 values of x becomes a Q8_0 block, stored split:
+ *     d[b]  = max_c |x[32b + c]| / 127, computed in binary32, stored as fp16 (nearest even)
+ *     q[i]  = x[i] / d[b] in binary32 (the unrounded d), rounded half away from zero,
+ *             clamped to [-127, 127]; an all-zero block has d = 0 and q = 0
+ *   x   [K] bf16 (2-byte aligned);  xq [K] int8 (4-byte aligned);  xd [K/32] fp16
+ *       (2-byte aligned); all device memory, xq / xd written, owned by the caller.
+ * Limits: K % 32 == 0, K <= 8192 (else QSMOE_ERR_UNSUPPORTED); K = 0 enqueues nothing.
+ */
+qsmoe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream);
+
+/*
+ * Dense Q8_0 GEMV with a quantized activation (from q8_quantize_x):
+ *     y[n] = sum_b d[n][b] * xd[b] * sum_{c<32} q[n][32b + c] * xq[32b + c]
+ * the inner sums exact in int32 (v_dot4_i32_i8), the scaling and the sum over b in fp32.
+ *   w_tiles  as for q8_gemv;  xq [K] int8 (4-byte aligned), xd [K/32] fp16;
+ *   y [N], y_dtype QSMOE_BF16 or QSMOE_F32.  Limits as for q8_gemv.
+ */
+qsmoe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd,
+                         void *y, int32_t y_dtype, void *stream);
+
+/*
+ * The same GEMV taking x [K] bf16 (8-byte aligned) and quantizing it inside the kernel
+ * with q8_quantize_x's rule (identical codes and scales, so identical y) while staging
+ * it: no separate launch and no codes in memory.  Limits as for q8_gemv.
+ */
+qsmoe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
+                        int32_t y_dtype, void *stream);
+
+/*
  * Load-time repacking ([EMBER] packed 16-row tile): row-contiguous Q8_0 blocks
  * w_rows [N][K/32] x 34 bytes ([fp16 d][32 x int8]) -> w_tiles (layout of q8_gemv).
  * Pure byte moves, idempotent; w_rows and w_tiles must not overlap.

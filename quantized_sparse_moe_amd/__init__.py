@@ -5,7 +5,8 @@ Argument marshalling only: every step of the layer runs in the HIP kernels of
 device memory and the current stream; outputs and workspaces the caller does not pass
 are allocated here with torch.  The functions carry the names of the C entry points:
 
-    qsmoe_workspace_size, moe_route, moe_layer_forward, q8_gemv, q8_pack_rows16
+    qsmoe_workspace_size, moe_route, moe_layer_forward, q8_gemv, q8_quantize_x,
+    q8_gemv_q8x, q8_gemv_qx, q8_pack_rows16
 
 There is no fallback: if the shared library is missing, loading raises.
 Build it with ``python -m quantized_sparse_moe_amd.build``.
@@ -49,7 +50,8 @@ class qsmoe_layer_desc(ctypes.Structure):
 
 EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size",
            "qsmoe_workspace_size_chunked", "moe_route",
-           "moe_layer_forward", "q8_gemv", "q8_pack_rows16")
+           "moe_layer_forward", "q8_gemv", "q8_quantize_x", "q8_gemv_q8x", "q8_gemv_qx",
+           "q8_pack_rows16")
 
 
 def lib() -> ctypes.CDLL:
@@ -75,6 +77,12 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.argtypes = [P, P, I64, P, I32, P, P, P, SZ, P]
         L.q8_gemv.restype = I32
         L.q8_gemv.argtypes = [P, I64, I64, P, P, I32, P]
+        L.q8_quantize_x.restype = I32
+        L.q8_quantize_x.argtypes = [P, I64, P, P, P]
+        L.q8_gemv_q8x.restype = I32
+        L.q8_gemv_q8x.argtypes = [P, I64, I64, P, P, P, I32, P]
+        L.q8_gemv_qx.restype = I32
+        L.q8_gemv_qx.argtypes = [P, I64, I64, P, P, I32, P]
         L.q8_pack_rows16.restype = I32
         L.q8_pack_rows16.argtypes = [P, I64, I64, P, P]
         _lib = L
@@ -247,6 +255,44 @@ def q8_gemv(w_tiles, N: int, K: int, x, y=None, y_dtype=None, stream=None):
     if code is None:
         raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv: y must be float32 or bfloat16")
     _check(lib().q8_gemv(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), code, _stream(stream)), "q8_gemv")
+    return y
+
+
+def q8_quantize_x(x, K: int = None, xq=None, xd=None, stream=None):
+    """Q8_0 quantization of an activation ``x`` [K] (bf16 bits); returns (codes int8 [K],
+    scales fp16 bits [K/32]), to be shared by the GEMVs that read ``x``."""
+    import torch
+    K = x.numel() if K is None else K
+    if xq is None:
+        xq = torch.empty((K,), dtype=torch.int8, device=x.device)
+    if xd is None:
+        xd = torch.empty((K // 32,), dtype=torch.int16, device=x.device)
+    _check(lib().q8_quantize_x(_ptr(x), K, _ptr(xq), _ptr(xd), _stream(stream)), "q8_quantize_x")
+    return xq, xd
+
+
+def q8_gemv_q8x(w_tiles, N: int, K: int, xq, xd, y=None, y_dtype=None, stream=None):
+    """Dense Q8_0 GEMV with a quantized activation (``q8_quantize_x``); returns ``y`` [N]."""
+    import torch
+    if y is None:
+        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=xq.device)
+    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
+    if code is None:
+        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv_q8x: y must be float32 or bfloat16")
+    _check(lib().q8_gemv_q8x(_ptr(w_tiles), N, K, _ptr(xq), _ptr(xd), _ptr(y), code, _stream(stream)),
+           "q8_gemv_q8x")
+    return y
+
+
+def q8_gemv_qx(w_tiles, N: int, K: int, x, y=None, y_dtype=None, stream=None):
+    """Dense Q8_0 GEMV quantizing ``x`` (bf16) inside the kernel; returns ``y`` [N]."""
+    import torch
+    if y is None:
+        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=x.device)
+    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
+    if code is None:
+        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv_qx: y must be float32 or bfloat16")
+    _check(lib().q8_gemv_qx(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), code, _stream(stream)), "q8_gemv_qx")
     return y
 
 

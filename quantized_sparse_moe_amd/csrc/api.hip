@@ -286,6 +286,39 @@ qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, v
                               (hipStream_t)stream));
 }
 
+qsmoe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream) {
+    if (K < 0) return QSMOE_ERR_INVALID;
+    if (K % 32 || K > 8192) return QSMOE_ERR_UNSUPPORTED;
+    if (K == 0) return QSMOE_OK;
+    if (!x || !aligned(x, 2) || !xq || !aligned(xq, 4) || !xd || !aligned(xd, 2)) return QSMOE_ERR_INVALID;
+    return dev(launch_q8_quantize_x((const uint16_t *)x, K, (int8_t *)xq, (uint16_t *)xd, (hipStream_t)stream));
+}
+
+qsmoe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd, void *y,
+                         int32_t y_dtype, void *stream) {
+    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
+    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
+        return QSMOE_ERR_UNSUPPORTED;
+    if (!w_tiles || !aligned(w_tiles, 16) || !xq || !aligned(xq, 4) || !xd || !aligned(xd, 2) || !y ||
+        !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
+        return QSMOE_ERR_INVALID;
+    return dev(launch_q8_gemv_q8x((const uint8_t *)w_tiles, N, K, (const int8_t *)xq, (const uint16_t *)xd,
+                                  nullptr, y, y_dtype, (hipStream_t)stream));
+}
+
+qsmoe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y, int32_t y_dtype,
+                        void *stream) {
+    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
+    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
+        return QSMOE_ERR_UNSUPPORTED;
+    if (!w_tiles || !aligned(w_tiles, 16) || !x || !aligned(x, 8) || !y || !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
+        return QSMOE_ERR_INVALID;
+    return dev(launch_q8_gemv_q8x((const uint8_t *)w_tiles, N, K, nullptr, nullptr, (const uint16_t *)x, y,
+                                  y_dtype, (hipStream_t)stream));
+}
+
 qsmoe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles, void *stream) {
     if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
     if (N % 16 || K % 32) return QSMOE_ERR_UNSUPPORTED;

@@ -88,6 +88,9 @@ hipError_t launch_prefill_gemms(const Layer &L, int64_t T, const PrefillBufs &b,
 // --------------------------------------------------------------------------- Q8_0
 hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint16_t *x,
                           void *y, int y_dtype, hipStream_t s);
+hipError_t launch_q8_quantize_x(const uint16_t *x, int64_t K, int8_t *xq, uint16_t *xd, hipStream_t s);
+hipError_t launch_q8_gemv_q8x(const uint8_t *tiles, int64_t N, int64_t K, const int8_t *xq, const uint16_t *xd,
+                              const uint16_t *x, void *y, int y_dtype, hipStream_t s);
 hipError_t launch_q8_pack(const uint8_t *rows, int64_t N, int64_t K, uint8_t *tiles,
                           hipStream_t s);
 

@@ -12,6 +12,10 @@
 // Codes are widened exactly: (q ^ 0x80) is q + 128 as an unsigned byte, which the
 // byte-to-float conversion turns into fp32 in one instruction; the +128 is removed per
 // lane with the staged sum of the 8 activations the lane multiplies.
+//
+// [EMBER] also quantizes the activation once (Q8_0 blocks) for all the projections that
+// read it; k_q8_quantize_x and k_q8_gemv_q8x are that variant, with exact int8 dot
+// products.
 #include "common.h"
 #include "internal.h"
 
@@ -122,6 +126,137 @@ __global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv(const uint8_t *__restric
     }
 }
 
+// the activation quantizer's scale and code (one definition for both kernels below)
+__device__ __forceinline__ float q8x_scale(float amax) { return amax / 127.0f; }
+__device__ __forceinline__ int8_t q8x_code(float v, float d) {
+    const float r = d != 0.0f ? roundf(v / d) : 0.0f;
+    return (int8_t)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
+// [EMBER] one activation quantization shared by the projections that read a vector:
+// x (bf16) -> Q8_0 blocks of 32, split into int8 codes [K] and fp16 scales [K/32].
+// d = max|x| / 127 in binary32 (IEEE division), stored as fp16 (round to nearest even);
+// q = x / d (binary32, the unrounded d) rounded half away from zero, clamped to
+// [-127, 127]; an all-zero block gets d = 0 and zero codes.  One thread per value, 32
+// lanes per block.
+__global__ __launch_bounds__(256) void k_q8_quantize_x(const uint16_t *__restrict__ x, int64_t K,
+                                                       int8_t *__restrict__ xq, uint16_t *__restrict__ xd) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = i < K;
+    const float v = live ? __uint_as_float((uint32_t)x[i] << 16) : 0.0f;
+    float amax = fabsf(v);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+    const float d = q8x_scale(amax);
+    if (live) {
+        xq[i] = q8x_code(v, d);
+        if ((i & 31) == 0) xd[i >> 5] = __builtin_bit_cast(uint16_t, (_Float16)d);
+    }
+}
+
+// Q8_0 GEMV with a Q8_0 activation: the tile walk of k_q8_gemv, the products as exact
+// 4-way int8 dot products (v_dot4_i32_i8) of a lane's 8 codes, scaled once per lane and
+// block by dw * dx (both fp16, so their product is exact in fp32).
+// QUANT: the workgroup quantizes x (bf16) itself while staging it, with the arithmetic
+// of k_q8_quantize_x (the same codes and scales, bit for bit),
+// instead of reading codes a separate launch wrote
+template <int UNROLL, bool QUANT>
+__global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv_q8x(const uint8_t *__restrict__ tiles, int64_t K,
+                                                            const int8_t *__restrict__ xq,
+                                                            const uint16_t *__restrict__ xd,
+                                                            const uint16_t *__restrict__ x, void *y,
+                                                            int y_dtype) {
+    extern __shared__ uint32_t q8x[];
+    const int nb = (int)(K / 32);
+    uint32_t *xl = q8x;                              // [nb*4][2]: codes 32b+4j.. and 32b+16+4j..
+    float *dl = (float *)(q8x + (int64_t)nb * 8);    // [nb]
+    __shared__ float red[Q8_WAVES][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if constexpr (QUANT) {
+        // one slot (8 values) per thread, the 4 slots of a block in 4 adjacent lanes
+        for (int sl0 = 0; sl0 < nb * 4; sl0 += Q8_THREADS) {
+            const int sl = sl0 + tid;
+            const bool live = sl < nb * 4;
+            const int b = sl >> 2, j = sl & 3;
+            uint2 lo = {0u, 0u}, hi = {0u, 0u};
+            if (live) {
+                lo = *(const uint2 *)(x + 32 * b + 4 * j);
+                hi = *(const uint2 *)(x + 32 * b + 16 + 4 * j);
+            }
+            const float v[8] = {__uint_as_float(lo.x << 16), __uint_as_float(lo.x & 0xffff0000u),
+                                __uint_as_float(lo.y << 16), __uint_as_float(lo.y & 0xffff0000u),
+                                __uint_as_float(hi.x << 16), __uint_as_float(hi.x & 0xffff0000u),
+                                __uint_as_float(hi.y << 16), __uint_as_float(hi.y & 0xffff0000u)};
+            float amax = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[c]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+            amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+            const float d = q8x_scale(amax);
+            if (live) {
+                uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    p0 |= (uint32_t)(uint8_t)q8x_code(v[c], d) << (8 * c);
+                    p1 |= (uint32_t)(uint8_t)q8x_code(v[4 + c], d) << (8 * c);
+                }
+                xl[2 * sl] = p0;
+                xl[2 * sl + 1] = p1;
+                if (j == 0) dl[b] = f16_to_f32(__builtin_bit_cast(uint16_t, (_Float16)d));
+            }
+        }
+    } else {
+        for (int sl = tid; sl < nb * 4; sl += Q8_THREADS) {
+            const int b = sl >> 2, j = sl & 3;
+            xl[2 * sl] = *(const uint32_t *)(xq + 32 * b + 4 * j);
+            xl[2 * sl + 1] = *(const uint32_t *)(xq + 32 * b + 16 + 4 * j);
+        }
+        for (int b = tid; b < nb; b += Q8_THREADS) dl[b] = f16_to_f32(xd[b]);
+    }
+    __syncthreads();
+
+    const int r = lane & 15, j = lane >> 4;
+    const uint8_t *panel = tiles + (int64_t)blockIdx.x * nb * TILE;
+    float acc = 0.0f;
+    auto tile = [&](int b, uint32_t w0, uint32_t w1, uint16_t dw) __attribute__((always_inline)) {
+        const int sl = b * 4 + j;
+        const int s = __builtin_amdgcn_sdot4((int)w1, (int)xl[2 * sl + 1],
+                                             __builtin_amdgcn_sdot4((int)w0, (int)xl[2 * sl], 0, false), false);
+        acc = __builtin_fmaf(f16_to_f32(dw) * dl[b], (float)s, acc);
+    };
+    int b = wave;
+    for (; b + (UNROLL - 1) * Q8_WAVES < nb; b += UNROLL * Q8_WAVES) {
+        uint32_t w0[UNROLL], w1[UNROLL];
+        uint16_t dd[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const uint8_t *t = panel + (int64_t)(b + u * Q8_WAVES) * TILE;
+            w0[u] = __builtin_nontemporal_load((const uint32_t *)(t + 64 * j + 4 * r));
+            w1[u] = __builtin_nontemporal_load((const uint32_t *)(t + 64 * (j + 4) + 4 * r));
+            dd[u] = __builtin_nontemporal_load((const uint16_t *)(t + 512 + 2 * r));
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) tile(b + u * Q8_WAVES, w0[u], w1[u], dd[u]);
+    }
+    for (; b < nb; b += Q8_WAVES) {
+        const uint8_t *t = panel + (int64_t)b * TILE;
+        tile(b, *(const uint32_t *)(t + 64 * j + 4 * r), *(const uint32_t *)(t + 64 * (j + 4) + 4 * r),
+             *(const uint16_t *)(t + 512 + 2 * r));
+    }
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    if (lane < 16) red[wave][lane] = acc;
+    __syncthreads();
+    if (tid < 16) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < Q8_WAVES; ++w) sum += red[w][tid];
+        const int64_t n = (int64_t)blockIdx.x * 16 + tid;
+        if (y_dtype == QSMOE_F32) ((float *)y)[n] = sum;
+        else ((uint16_t *)y)[n] = f32_to_bf16(sum);
+    }
+}
+
 // one thread per 16-byte chunk of the packed output
 __global__ __launch_bounds__(256) void k_q8_pack(const uint8_t *__restrict__ rows, int64_t N, int64_t K,
                                                  uint8_t *__restrict__ tiles) {
@@ -165,6 +300,23 @@ hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint
     const size_t lds = (size_t)(K / 32) * 32 * 4 + (size_t)(K / 32) * 4 * 4;
     hipLaunchKernelGGL((k_q8_gemv<4>), dim3((unsigned)(N / 16)), dim3(Q8_THREADS), lds, s, tiles, K, x, y,
                        y_dtype);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_quantize_x(const uint16_t *x, int64_t K, int8_t *xq, uint16_t *xd, hipStream_t s) {
+    hipLaunchKernelGGL(k_q8_quantize_x, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, x, K, xq, xd);
+    return hipGetLastError();
+}
+
+hipError_t launch_q8_gemv_q8x(const uint8_t *tiles, int64_t N, int64_t K, const int8_t *xq, const uint16_t *xd,
+                              const uint16_t *x, void *y, int y_dtype, hipStream_t s) {
+    const size_t lds = (size_t)(K / 32) * 8 * 4 + (size_t)(K / 32) * 4;
+    if (x)
+        hipLaunchKernelGGL((k_q8_gemv_q8x<4, true>), dim3((unsigned)(N / 16)), dim3(Q8_THREADS), lds, s, tiles, K,
+                           nullptr, nullptr, x, y, y_dtype);
+    else
+        hipLaunchKernelGGL((k_q8_gemv_q8x<4, false>), dim3((unsigned)(N / 16)), dim3(Q8_THREADS), lds, s, tiles, K,
+                           xq, xd, nullptr, y, y_dtype);
     return hipGetLastError();
 }
 

@@ -172,6 +172,28 @@ def test_q8_validation():
     assert L.q8_pack_rows16(None, 32, 64, FAKE, None) == q.QSMOE_ERR_INVALID
 
 
+def test_q8_activation_validation():
+    L = q.lib()
+    assert L.q8_quantize_x(FAKE, 2050, FAKE, FAKE, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_quantize_x(FAKE, 8224, FAKE, FAKE, None) == q.QSMOE_ERR_UNSUPPORTED
+    assert L.q8_quantize_x(FAKE, -32, FAKE, FAKE, None) == q.QSMOE_ERR_INVALID
+    assert L.q8_quantize_x(FAKE, 0, None, None, None) == q.QSMOE_OK            # nothing to do
+    assert L.q8_quantize_x(FAKE, 64, FAKE + 2, FAKE, None) == q.QSMOE_ERR_INVALID   # codes 4-byte aligned
+    assert L.q8_quantize_x(None, 64, FAKE, FAKE, None) == q.QSMOE_ERR_INVALID
+    g = lambda *a: L.q8_gemv_q8x(*a, None)
+    assert g(FAKE, 2048, 2048, FAKE, FAKE, FAKE, q.QSMOE_F16) == q.QSMOE_ERR_INVALID
+    assert g(FAKE, 2040, 2048, FAKE, FAKE, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_UNSUPPORTED
+    assert g(FAKE, 2048, 2050, FAKE, FAKE, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_UNSUPPORTED
+    assert g(FAKE + 8, 2048, 2048, FAKE, FAKE, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_INVALID
+    assert g(FAKE, 2048, 2048, FAKE + 1, FAKE, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_INVALID
+    assert g(FAKE, 2048, 2048, FAKE, None, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_INVALID
+    h = lambda *a: L.q8_gemv_qx(*a, None)
+    assert h(FAKE, 2048, 2048, FAKE, FAKE, q.QSMOE_F16) == q.QSMOE_ERR_INVALID
+    assert h(FAKE, 2048, 2050, FAKE, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_UNSUPPORTED
+    assert h(FAKE, 2048, 2048, FAKE + 4, FAKE, q.QSMOE_F32) == q.QSMOE_ERR_INVALID   # x 8-byte aligned
+    assert h(FAKE, 2048, 2048, FAKE, None, q.QSMOE_F32) == q.QSMOE_ERR_INVALID
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(q, "_lib", None)
     monkeypatch.setattr(q, "LIB_PATH", str(tmp_path / "missing.so"))

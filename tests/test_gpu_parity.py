@@ -363,3 +363,39 @@ def test_q8_pack_and_gemv(torch, qs, N, K):
     # fp32 accumulation of K products: bound well inside 1e-4 * RMS at these sizes
     assert np.max(np.abs(y - ref)) <= 1e-4 * rms
     check_output(y_to_np(yb, torch), ref, True, f"q8 bf16 {N}x{K}")
+
+
+@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288)])
+def test_q8_activation_quantized_gemv(torch, qs, N, K):
+    """[EMBER] one activation quantization shared by the projections: the activation's
+    codes and scales bit for bit against the oracle (an integer decision taken in binary32
+    on both sides, including an all-zero block and values on rounding halves), then the
+    GEMV with exact int8 dots against the oracle's exact-integer version, the variant that
+    quantizes inside the GEMV bit for bit equal to it; the distance to the
+    exact-activation path stays inside the quantization bound."""
+    rows = syn.make_q8_rows(N, K, seed=N + K)
+    x_np = syn.make_x(1, K, seed=K)[0].copy()
+    if K >= 64:                                                # an all-zero block, then
+        x_np[:64] = 0                                          # block 1: d = 1, halves
+        x_np[32:36] = np.array([127.0, 0.5, -2.5, 63.5], np.float32).view(np.uint32) >> 16
+    tiles = qs.q8_pack_rows16(to_dev(rows.reshape(-1), torch), N, K)
+    xq, xd = qs.q8_quantize_x(to_dev(x_np, torch))
+    torch.cuda.synchronize()
+    q_r, d_r = oracle.q8_quantize_x(x_np)
+    assert np.array_equal(xq.cpu().numpy(), q_r)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint16), d_r)
+    if K >= 64:
+        assert xq[32:36].tolist() == [127, 1, -3, 64]
+    ref = oracle.q8_gemv_q8x(rows, N, K, q_r, d_r)
+    y = qs.q8_gemv_q8x(tiles, N, K, xq, xd)
+    yb = qs.q8_gemv_q8x(tiles, N, K, xq, xd, y_dtype=torch.bfloat16)
+    yf = qs.q8_gemv_qx(tiles, N, K, to_dev(x_np, torch))          # quantizing inside the GEMV
+    torch.cuda.synchronize()
+    assert torch.equal(yf, y)
+    y = y.cpu().numpy().astype(np.float64)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(y - ref)) <= 1e-5 * rms               # fp32 scaling and sums only
+    check_output(y_to_np(yb, torch), ref, True, f"q8x bf16 {N}x{K}")
+    exact = oracle.q8_gemv(rows, N, K, x_np)
+    rel = np.max(np.abs(y - exact)) / np.sqrt(np.mean(exact ** 2))
+    assert 0 < rel < 5e-2, rel                                 # quantized x: close, not equal
