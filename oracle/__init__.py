@@ -33,7 +33,8 @@ def build(force: bool = True, src: str = _SRC, out: str = None) -> str:
 
 class _QMat(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("biases", ctypes.c_void_p), ("mat_stride", ctypes.c_int64)]
+                ("biases", ctypes.c_void_p), ("mat_stride", ctypes.c_int64),
+                ("sb_bf16", ctypes.c_int32)]
 
 
 class _Layer(ctypes.Structure):
@@ -43,7 +44,8 @@ class _Layer(ctypes.Structure):
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", _QMat), ("up", _QMat), ("down", _QMat),
                 ("has_shared", ctypes.c_int32),
-                ("s_gate", _QMat), ("s_up", _QMat), ("s_down", _QMat)]
+                ("s_gate", _QMat), ("s_up", _QMat), ("s_down", _QMat),
+                ("shared_gate_w", ctypes.c_void_p)]
 
 
 def lib():
@@ -113,6 +115,11 @@ class OracleLayer:
         if layer.has_shared:
             d.s_gate, d.s_up = self._gate_up(layer.s_gate_up, I, separate)
             d.s_down = self._mat(layer.s_down, 0, layer.s_down.rows)
+        d.shared_gate_w = None
+        if getattr(layer, "shared_gate_w", None) is not None:
+            g = np.ascontiguousarray(layer.shared_gate_w, dtype=np.uint16)
+            self._keep.append(g)
+            d.shared_gate_w = g.ctypes.data
         self.desc = d
 
     def _mat(self, qm, row0: int, stride: int) -> _QMat:
@@ -123,7 +130,7 @@ class OracleLayer:
         cb = codes.shape[2]
         ng = sc.shape[2]
         return _QMat(codes.ctypes.data + row0 * cb, sc.ctypes.data + row0 * ng * 2,
-                     bi.ctypes.data + row0 * ng * 2, stride)
+                     bi.ctypes.data + row0 * ng * 2, stride, 1 if getattr(qm, "sb_dtype", "f16") == "bf16" else 0)
 
     def _gate_up(self, qm, I: int, separate: bool):
         if not separate:
@@ -195,7 +202,8 @@ def dequant_matrix(qm, e: int, row0: int = 0, rows: Optional[int] = None,
     ng = sc.shape[2]
     rows = R - row0 if rows is None else rows
     m = _QMat(codes.ctypes.data + row0 * cb, sc.ctypes.data + row0 * ng * 2,
-              bi.ctypes.data + row0 * ng * 2, R if stride is None else stride)
+              bi.ctypes.data + row0 * ng * 2, R if stride is None else stride,
+              1 if getattr(qm, "sb_dtype", "f16") == "bf16" else 0)
     out = np.empty((rows, ng * 64), dtype=np.float64)
     lib().orc_dequant_matrix(ctypes.addressof(m), qm.bits, e, rows, ng * 64, out.ctypes.data)
     return out

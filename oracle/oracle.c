@@ -12,7 +12,7 @@
  *   - affine code: W = s*q + b with unsigned q in [0, 2^bits), s and b shared by
  *     64 consecutive columns of one row ([LILY] "Dequantize weights during matrix
  *     multiplication": integer code plus a per-group-of-64 scale and bias);
- *     scale/bias stored as fp16;
+ *     scale/bias stored as fp16 (or bf16, see below);
  *   - 4-bit packing: column 2i in the low nibble of byte i, column 2i+1 in the high;
  *   - router: logits l = Wr x (+ optional per-expert bias), softmax over all
  *     experts, the k most probable kept (ties to the lower expert id) and their
@@ -20,8 +20,10 @@
  *     distinct workload shapes": the router scores 256 experts and picks eight);
  *   - SwiGLU: h = silu(gate) * up with silu(z) = z / (1 + e^-z); gate rows come
  *     first in the fused [gate; up] stack ([OMLX] "Fusion principle");
- *   - shared expert: ungated, weight 1, same shapes as a routed expert
- *     ([LILY]: a shared expert processes every token);
+ *   - shared expert: weight 1, same shapes as a routed expert ([LILY]: a shared
+ *     expert processes every token); the checkpoint variant with a shared-expert
+ *     gate scales its output by sigmoid(g . x), g a bf16 vector over the hidden size;
+ *   - scales and biases fp16, or bf16 in the checkpoint variant the pages print;
  *   - Q8_0 block: [fp16 d][32 x int8 q], value d*q ([EMBER] row-contiguous source);
  *     16-row tile: eight 64-byte groups, group j holding codes 4j..4j+3 of rows
  *     0..15 in row order, then the 16 fp16 scales in row order ([EMBER] packed
@@ -114,8 +116,8 @@ static double weight(const orc_qmat *m, int32_t bits, int64_t e, int64_t r, int6
     else                                   /* 4-bit: even column in the low nibble */
         q = (c & 1) ? (row[c / 2] >> 4) : (row[c / 2] & 0x0f);
     int64_t gi = R * (cols / 64) + c / 64;
-    double s = orc_f16_to_double(m->scales[gi]);
-    double b = orc_f16_to_double(m->biases[gi]);
+    double s = m->sb_bf16 ? orc_bf16_to_double(m->scales[gi]) : orc_f16_to_double(m->scales[gi]);
+    double b = m->sb_bf16 ? orc_bf16_to_double(m->biases[gi]) : orc_f16_to_double(m->biases[gi]);
     return s * (double)q + b;
 }
 
@@ -249,7 +251,13 @@ void orc_layer_forward_with_routing(const orc_layer *L, const uint16_t *x, int64
         }
         if (L->has_shared) {
             orc_expert_mlp(L, &L->s_gate, &L->s_up, &L->s_down, 0, xt, o);
-            for (int64_t c = 0; c < H; ++c) yt[c] += o[c];
+            double gs = 1.0;
+            if (L->shared_gate_w) {
+                double z = 0.0;
+                for (int64_t c = 0; c < H; ++c) z += orc_bf16_to_double(L->shared_gate_w[c]) * xt[c];
+                gs = 1.0 / (1.0 + exp(-z));
+            }
+            for (int64_t c = 0; c < H; ++c) yt[c] += gs * o[c];
         }
         free(xt);
         free(o);

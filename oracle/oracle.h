@@ -34,9 +34,10 @@ extern "C" {
  * scale/bias index (e*mat_stride + r) * cols/64. */
 typedef struct {
     const uint8_t  *codes;
-    const uint16_t *scales;   /* fp16 bit patterns */
-    const uint16_t *biases;   /* fp16 bit patterns */
+    const uint16_t *scales;   /* fp16 bit patterns (bf16 when sb_bf16) */
+    const uint16_t *biases;   /* fp16 bit patterns (bf16 when sb_bf16) */
     int64_t         mat_stride;
+    int32_t         sb_bf16;  /* 1: scales and biases are bfloat16 */
 } orc_qmat;
 
 typedef struct {
@@ -46,6 +47,8 @@ typedef struct {
     orc_qmat gate, up, down;      /* gate/up [E][inter][hidden], down [E][hidden][inter] */
     int32_t  has_shared;
     orc_qmat s_gate, s_up, s_down;/* shared expert, one matrix each         */
+    const uint16_t *shared_gate_w;/* [hidden] bf16: shared output scaled by
+                                     sigmoid(shared_gate_w . x); NULL: weight 1 */
 } orc_layer;
 
 /* decoders of the 16-bit formats */

@@ -12,11 +12,13 @@ weights exist here):
 * affine codes uniform over ``[0, 2^bits)`` (4-bit codes two per byte, so a
   uniform random byte is two uniform codes);
 * per-group-of-64 scales ``s ~ U(0.005, 0.02)`` (divided by 16 for 8-bit codes so
-  that the weight spread matches), stored as fp16;
+  that the weight spread matches), stored as fp16 (or bf16: the checkpoint
+  variant the pages print);
 * biases ``b = fp16(s * (U(-0.5, 0.5) - 2^(bits-1)))``: centred, and not a
   multiple of ``s``, so a consumer that ignores the bias is visibly wrong;
 * router weights ``N(0, std)`` rounded to bfloat16 (``std = 1/sqrt(hidden)``
-  makes the logits roughly ``N(0, 1)``);
+  makes the logits roughly ``N(0, 1)``); the optional shared-expert gate vector the
+  same way;
 * optional Zipf router bias ``b_e = ln(r_e^-s / sum_j j^-s)`` with ``r`` a seeded
   permutation of ``1..E``, so a few experts receive many times the mean load;
 * Q8_0 rows: ``q ~ U{-127..127}`` int8 and ``d ~ U(0.0005, 0.002)`` as fp16, in
@@ -35,7 +37,7 @@ import numpy as np
 GROUP = 64
 
 # stream ids
-_S_X, _S_ROUTER, _S_RBIAS, _S_GU, _S_DN, _S_SGU, _S_SDN, _S_Q8 = range(8)
+_S_X, _S_ROUTER, _S_RBIAS, _S_GU, _S_DN, _S_SGU, _S_SDN, _S_Q8, _S_SGATE = range(9)
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -64,14 +66,15 @@ class QMat:
     """A stack of affine-quantized matrices ``[n][rows][cols]`` (group 64 on cols).
 
     ``codes``  uint8 ``[n][rows][cols*bits/8]`` (4-bit: column 2i low nibble of byte i)
-    ``scales`` uint16 fp16 bits ``[n][rows][cols/64]``
-    ``biases`` uint16 fp16 bits ``[n][rows][cols/64]``
+    ``scales`` uint16 fp16 bits ``[n][rows][cols/64]`` (bf16 bits when sb_dtype == "bf16")
+    ``biases`` uint16, same format as the scales
     """
 
     codes: np.ndarray
     scales: np.ndarray
     biases: np.ndarray
     bits: int
+    sb_dtype: str = "f16"
 
     @property
     def rows(self) -> int:
@@ -104,6 +107,8 @@ class LayerInputs:
     s_gate_up: Optional[QMat]
     s_down: Optional[QMat]
     seed: int = 0
+    scale_dtype: str = "f16"                 # "f16" or "bf16" scales and biases
+    shared_gate_w: Optional[np.ndarray] = None   # uint16 bf16 bits [hidden], or None
 
     @property
     def expert_bytes(self) -> int:
@@ -113,14 +118,18 @@ class LayerInputs:
         return int(round(3 * H * I * per_w))
 
 
-def _qmat(rng: np.random.Generator, n: int, rows: int, cols: int, bits: int) -> QMat:
-    assert cols % GROUP == 0 and bits in (4, 8)
+def _qmat(rng: np.random.Generator, n: int, rows: int, cols: int, bits: int, sb: str = "f16") -> QMat:
+    assert cols % GROUP == 0 and bits in (4, 8) and sb in ("f16", "bf16")
     codes = rng.integers(0, 256, size=(n, rows, cols * bits // 8), dtype=np.uint8)
     s = rng.uniform(0.005, 0.02, size=(n, rows, cols // GROUP))
     if bits == 8:
         s = s / 16.0
-    s16 = s.astype(np.float16)
     off = rng.uniform(-0.5, 0.5, size=s.shape) - 2.0 ** (bits - 1)
+    if sb == "bf16":
+        sbits = to_bf16_bits(s)
+        bbits = to_bf16_bits(bf16_bits_to_f32(sbits).astype(np.float64) * off)
+        return QMat(codes=codes, scales=sbits, biases=bbits, bits=bits, sb_dtype="bf16")
+    s16 = s.astype(np.float16)
     b16 = (s16.astype(np.float64) * off).astype(np.float16)
     return QMat(codes=codes, scales=s16.view(np.uint16), biases=b16.view(np.uint16), bits=bits)
 
@@ -133,19 +142,27 @@ def zipf_router_bias(n_experts: int, s: float, seed: int) -> np.ndarray:
 
 def make_layer(hidden: int, inter: int, n_experts: int, top_k: int, bits: int,
                seed: int = 0, router_std: Optional[float] = None,
-               zipf_s: Optional[float] = None, has_shared: bool = True) -> LayerInputs:
+               zipf_s: Optional[float] = None, has_shared: bool = True,
+               scale_dtype: str = "f16", shared_gate: bool = False) -> LayerInputs:
+    """One layer's weights.  scale_dtype "bf16": scales and biases stored as bfloat16
+    (the checkpoint format the pages print); shared_gate: a bf16 gate vector
+    ``g ~ N(0, 1/hidden)`` whose sigmoid(g . x) scales the shared expert's output."""
     if router_std is None:
         router_std = 1.0 / np.sqrt(hidden)
     rw = _rng(seed, _S_ROUTER).normal(0.0, router_std, size=(n_experts, hidden))
     rb = zipf_router_bias(n_experts, zipf_s, seed) if zipf_s is not None else None
-    gu = _qmat(_rng(seed, _S_GU), n_experts, 2 * inter, hidden, bits)
-    dn = _qmat(_rng(seed, _S_DN), n_experts, hidden, inter, bits)
-    sgu = _qmat(_rng(seed, _S_SGU), 1, 2 * inter, hidden, bits) if has_shared else None
-    sdn = _qmat(_rng(seed, _S_SDN), 1, hidden, inter, bits) if has_shared else None
+    gu = _qmat(_rng(seed, _S_GU), n_experts, 2 * inter, hidden, bits, scale_dtype)
+    dn = _qmat(_rng(seed, _S_DN), n_experts, hidden, inter, bits, scale_dtype)
+    sgu = _qmat(_rng(seed, _S_SGU), 1, 2 * inter, hidden, bits, scale_dtype) if has_shared else None
+    sdn = _qmat(_rng(seed, _S_SDN), 1, hidden, inter, bits, scale_dtype) if has_shared else None
+    sg = None
+    if shared_gate:
+        assert has_shared
+        sg = to_bf16_bits(_rng(seed, _S_SGATE).normal(0.0, 1.0 / np.sqrt(hidden), size=hidden))
     return LayerInputs(hidden=hidden, inter=inter, n_experts=n_experts, top_k=top_k,
                        bits=bits, router_w=to_bf16_bits(rw), router_bias=rb,
                        gate_up=gu, down=dn, has_shared=has_shared, s_gate_up=sgu,
-                       s_down=sdn, seed=seed)
+                       s_down=sdn, seed=seed, scale_dtype=scale_dtype, shared_gate_w=sg)
 
 
 def make_x(T: int, hidden: int, seed: int = 0) -> np.ndarray:

@@ -36,6 +36,11 @@ MUTATIONS = [
     ("activation scale dropped", "acc += orc_f16_to_double(rd16(blk)) * orc_f16_to_double(xd[b]) * (double)dot;",
      "acc += orc_f16_to_double(rd16(blk)) * (double)dot;"),
     ("activation code read unsigned", "(int64_t)xq[b * 32 + c]", "(int64_t)(uint8_t)xq[b * 32 + c]"),
+    ("bf16 scales decoded as fp16",
+     "double s = m->sb_bf16 ? orc_bf16_to_double(m->scales[gi]) : orc_f16_to_double(m->scales[gi]);",
+     "double s = orc_f16_to_double(m->scales[gi]);"),
+    ("shared gate sign", "gs = 1.0 / (1.0 + exp(-z));", "gs = 1.0 / (1.0 + exp(z));"),
+    ("shared gate ignored", "yt[c] += gs * o[c];", "yt[c] += o[c];"),
 ]
 
 

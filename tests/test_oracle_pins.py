@@ -6,6 +6,7 @@ brute force on tiny inputs, special cases that reduce to a numpy library routine
 trips, byte layouts written out from the pages' figure, and byte counts printed
 on the pages.  No GPU is involved.
 """
+import dataclasses
 import itertools
 import math
 import os
@@ -48,8 +49,9 @@ def np_codes(codes_row_bytes, bits):
 def np_dequant(qm, e, row0=0, rows=None):
     rows = qm.codes.shape[1] - row0 if rows is None else rows
     q = np_codes(qm.codes[e, row0:row0 + rows], qm.bits)
-    s = np.repeat(np_f16(qm.scales[e, row0:row0 + rows]), 64, axis=1)
-    b = np.repeat(np_f16(qm.biases[e, row0:row0 + rows]), 64, axis=1)
+    dec = np_bf16 if qm.sb_dtype == "bf16" else np_f16
+    s = np.repeat(dec(qm.scales[e, row0:row0 + rows]), 64, axis=1)
+    b = np.repeat(dec(qm.biases[e, row0:row0 + rows]), 64, axis=1)
     return s * q + b
 
 
@@ -84,7 +86,10 @@ def np_layer(L, x, idx, w):
         o = np_mlp(L, L.gate_up, L.down, int(e), xf[rows])
         y[rows] += w[rows, js][:, None] * o
     if L.has_shared:
-        y += np_mlp(L, L.s_gate_up, L.s_down, 0, xf)
+        g = 1.0
+        if L.shared_gate_w is not None:
+            g = (1.0 / (1.0 + np.exp(-(xf @ np_bf16(L.shared_gate_w)))))[:, None]
+        y += g * np_mlp(L, L.s_gate_up, L.s_down, 0, xf)
     return y
 
 
@@ -240,6 +245,65 @@ def test_whole_layer_matches_numpy_implementation(orc, cfg, T):
     ref = np_layer(L, x, idx, w)
     rms = np.sqrt(np.mean(ref ** 2))
     assert np.max(np.abs(y - ref)) <= 1e-12 * rms
+
+
+@pytest.mark.parametrize("variant", ["bf16", "gate", "bf16+gate"])
+def test_checkpoint_variants_match_numpy_implementation(orc, variant):
+    """bf16 scales and biases, and the shared-expert gate, through the whole layer
+    against the numpy implementation (its own bf16 decoder and sigmoid)."""
+    L = syn.make_layer(**syn.TINY, scale_dtype="bf16" if "bf16" in variant else "f16",
+                       shared_gate="gate" in variant)
+    x = syn.make_x(5, L.hidden, seed=3)
+    y, idx, w = orc.layer_forward(orc.OracleLayer(L), x)
+    ref = np_layer(L, x, idx, w)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.sqrt(np.mean(ref ** 2))
+
+
+def test_bf16_scales_equal_fp16_scales_on_common_values(orc):
+    """Scale and bias values held exactly by both formats (8 significant bits, fp16
+    normal range) give the same layer bit for bit whichever format stores them."""
+    Lh = syn.make_layer(**syn.TINY)
+    for qm in (Lh.gate_up, Lh.down, Lh.s_gate_up, Lh.s_down):
+        for arr in (qm.scales, qm.biases):
+            v = syn.bf16_bits_to_f32(syn.to_bf16_bits(np_f16(arr)))       # 8 significant bits
+            arr[:] = v.astype(np.float16).view(np.uint16)
+            assert np.array_equal(np_f16(arr), v.astype(np.float64))
+    Lb = dataclasses.replace(Lh, scale_dtype="bf16")
+    for name in ("gate_up", "down", "s_gate_up", "s_down"):
+        qh = getattr(Lh, name)
+        setattr(Lb, name, dataclasses.replace(qh, sb_dtype="bf16", scales=syn.to_bf16_bits(np_f16(qh.scales)),
+                                              biases=syn.to_bf16_bits(np_f16(qh.biases))))
+    x = syn.make_x(4, Lh.hidden, seed=9)
+    yh, ih, wh = orc.layer_forward(orc.OracleLayer(Lh), x)
+    yb, ib, wb = orc.layer_forward(orc.OracleLayer(Lb), x)
+    assert np.array_equal(yh, yb) and np.array_equal(ih, ib)
+
+
+def test_shared_gate_closed_forms(orc):
+    """The gate only scales the shared expert's output: with g = 0 it is exactly 1/2 of
+    it; with g x >> 0 the whole of it, with g x << 0 none of it; per token the
+    difference to the no-shared layer is sigmoid(g . x) times the ungated difference."""
+    L = syn.make_layer(**syn.TINY, shared_gate=True)
+    x = syn.make_x(6, L.hidden, seed=5)
+    ol = orc.OracleLayer(L)
+    y, idx, w = orc.layer_forward(ol, x)
+    y1 = orc.layer_forward_with_routing(orc.OracleLayer(dataclasses.replace(L, shared_gate_w=None)), x, idx, w)
+    y0 = orc.layer_forward_with_routing(orc.OracleLayer(dataclasses.replace(L, has_shared=False,
+                                                                            shared_gate_w=None)), x, idx, w)
+    sig = 1.0 / (1.0 + np.exp(-(np_bf16(x) @ np_bf16(L.shared_gate_w))))
+    assert np.allclose(y - y0, sig[:, None] * (y1 - y0), rtol=1e-12, atol=1e-14)
+    half = orc.layer_forward_with_routing(orc.OracleLayer(dataclasses.replace(
+        L, shared_gate_w=np.zeros(L.hidden, np.uint16))), x, idx, w)
+    assert np.allclose(half - y0, 0.5 * (y1 - y0), rtol=1e-13, atol=1e-15)
+    xs = syn.make_x(1, L.hidden, seed=6)
+    big = syn.to_bf16_bits(np_bf16(xs[0]) * 40.0 / np.sum(np_bf16(xs[0]) ** 2) * 2)  # g . x ~ 80
+    for sign, ref in ((1, y1), (-1, y0)):
+        gw = big if sign > 0 else big ^ np.uint16(0x8000)
+        ys = orc.layer_forward_with_routing(orc.OracleLayer(dataclasses.replace(L, shared_gate_w=gw)),
+                                            xs, idx[:1], w[:1])
+        r1 = orc.layer_forward_with_routing(orc.OracleLayer(dataclasses.replace(
+            L, shared_gate_w=None, has_shared=sign > 0)), xs, idx[:1], w[:1])
+        assert np.allclose(ys, r1, rtol=1e-12, atol=1e-14)
 
 
 def test_fused_equals_separate_gate_up(orc):
