@@ -83,7 +83,7 @@ def _dev_layer_copies(qs, torch, L, copies: int):
     for _ in range(copies - 1):
         k = base._keep
         clone = lambda m: tuple(t.clone() if hasattr(t, "clone") else t for t in m)
-        router_w, router_bias, gate, up, down, shared = k
+        router_w, router_bias, gate, up, down, shared, shared_gate_w = k
         c_codes, c_sc, c_bi = gate[0].clone(), gate[1].clone(), gate[2].clone()
         g = (c_codes, c_sc, c_bi, gate[3], gate[4])
         u = (c_codes, c_sc, c_bi, up[3], up[4])
@@ -95,7 +95,8 @@ def _dev_layer_copies(qs, torch, L, copies: int):
             sh = ((s_codes, s_sc, s_bi, sg[3], sg[4]), (s_codes, s_sc, s_bi, su[3], su[4]), clone(sd))
         descs.append(qs.LayerDesc(L.hidden, L.inter, L.n_experts, L.top_k, L.bits, router_w.clone(),
                                   g, u, d, router_bias=None if router_bias is None else router_bias.clone(),
-                                  shared=sh))
+                                  shared=sh, scale_dtype=base.desc.scale_dtype,
+                                  shared_gate_w=None if shared_gate_w is None else shared_gate_w.clone()))
     return descs
 
 

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define QSMOE_ABI_VERSION 1
+#define QSMOE_ABI_VERSION 2
 
 typedef int32_t qsmoe_status;
 #define QSMOE_OK               0
@@ -88,7 +88,10 @@ typedef struct {
  *   gate, up     [n_experts][inter][hidden] stacks;  down [n_experts][hidden][inter]
  *   has_shared   1: the shared expert (s_gate, s_up [inter][hidden], s_down
  *                [hidden][inter], one matrix each) processes every token with weight 1
- *   scale_dtype  QSMOE_F16 (the only supported value)
+ *                (or, with shared_gate_w, with weight sigmoid(shared_gate_w . x))
+ *   scale_dtype  QSMOE_F16 or QSMOE_BF16: the format of every qmat's scales and biases
+ *                (bf16 is the checkpoint format the pages print)
+ *   shared_gate_w  [hidden] bf16 (16-byte aligned) or NULL; needs has_shared
  * Limits (else QSMOE_ERR_UNSUPPORTED): group == 64; bits in {4, 8};
  *   1 <= n_experts <= 256; 1 <= top_k <= min(n_experts, 16);
  *   hidden % 128 == 0, 128 <= hidden <= 8192; inter % 128 == 0, 128 <= inter <= 2048;
@@ -103,6 +106,7 @@ typedef struct {
     qsmoe_qmat gate, up, down;
     int32_t    has_shared;
     qsmoe_qmat s_gate, s_up, s_down;
+    const void *shared_gate_w;
 } qsmoe_layer_desc;
 
 int          qsmoe_abi_version(void);

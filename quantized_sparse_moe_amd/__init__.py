@@ -45,7 +45,8 @@ class qsmoe_layer_desc(ctypes.Structure):
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", qsmoe_qmat), ("up", qsmoe_qmat), ("down", qsmoe_qmat),
                 ("has_shared", ctypes.c_int32),
-                ("s_gate", qsmoe_qmat), ("s_up", qsmoe_qmat), ("s_down", qsmoe_qmat)]
+                ("s_gate", qsmoe_qmat), ("s_up", qsmoe_qmat), ("s_down", qsmoe_qmat),
+                ("shared_gate_w", ctypes.c_void_p)]
 
 
 EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size",
@@ -123,12 +124,13 @@ class LayerDesc:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, bits, router_w, gate, up, down,
-                 router_bias=None, shared=None):
+                 router_bias=None, shared=None, scale_dtype=QSMOE_F16, shared_gate_w=None):
         self.hidden, self.inter, self.n_experts, self.top_k, self.bits = hidden, inter, n_experts, top_k, bits
-        self._keep = [router_w, router_bias, gate, up, down, shared]
+        self._keep = [router_w, router_bias, gate, up, down, shared, shared_gate_w]
         d = qsmoe_layer_desc()
         d.hidden, d.inter, d.n_experts, d.top_k, d.bits, d.group = hidden, inter, n_experts, top_k, bits, 64
-        d.scale_dtype = QSMOE_F16
+        d.scale_dtype = scale_dtype
+        d.shared_gate_w = None if shared_gate_w is None else shared_gate_w.data_ptr()
         d.router_w = router_w.data_ptr()
         d.router_bias = None if router_bias is None else router_bias.data_ptr()
         d.gate, d.up = self._qmat(gate, hidden), self._qmat(up, hidden)
@@ -185,8 +187,11 @@ class LayerDesc:
                   layer.hidden, 0)
             shared = (sg, su, sd)
         rb = None if layer.router_bias is None else dev(np.asarray(layer.router_bias, np.float32))
+        sgw = getattr(layer, "shared_gate_w", None)
         return cls(layer.hidden, I, layer.n_experts, layer.top_k, layer.bits, dev(layer.router_w),
-                   g, u, dn, router_bias=rb, shared=shared)
+                   g, u, dn, router_bias=rb, shared=shared,
+                   scale_dtype=QSMOE_BF16 if getattr(layer, "scale_dtype", "f16") == "bf16" else QSMOE_F16,
+                   shared_gate_w=None if sgw is None else dev(sgw))
 
 
 # ------------------------------------------------------------------- entry points

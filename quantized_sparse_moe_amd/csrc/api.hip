@@ -33,7 +33,8 @@ qsmoe_status check_qmat(const qsmoe_qmat &m, int64_t rows) {
 
 qsmoe_status check_desc(const qsmoe_layer_desc *d) {
     if (!d) return QSMOE_ERR_INVALID;
-    if (d->group != 64 || (d->bits != 4 && d->bits != 8) || d->scale_dtype != QSMOE_F16)
+    if (d->group != 64 || (d->bits != 4 && d->bits != 8) ||
+        (d->scale_dtype != QSMOE_F16 && d->scale_dtype != QSMOE_BF16))
         return QSMOE_ERR_UNSUPPORTED;
     if (d->n_experts < 1 || d->n_experts > 256) return QSMOE_ERR_UNSUPPORTED;
     if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return QSMOE_ERR_UNSUPPORTED;
@@ -43,6 +44,7 @@ qsmoe_status check_desc(const qsmoe_layer_desc *d) {
     if (!d->router_w || !aligned(d->router_w, 16)) return QSMOE_ERR_INVALID;
     if (d->router_bias && !aligned(d->router_bias, 4)) return QSMOE_ERR_INVALID;
     if (d->has_shared != 0 && d->has_shared != 1) return QSMOE_ERR_INVALID;
+    if (d->shared_gate_w && (!d->has_shared || !aligned(d->shared_gate_w, 16))) return QSMOE_ERR_INVALID;
     qsmoe_status s;
     if ((s = check_qmat(d->gate, d->inter)) || (s = check_qmat(d->up, d->inter)) ||
         (s = check_qmat(d->down, d->hidden)))
@@ -83,6 +85,8 @@ Layer to_layer(const qsmoe_layer_desc *d) {
     } else {
         L.s_gate = L.s_up = L.s_down = QMat{nullptr, nullptr, nullptr, 0};
     }
+    L.sb_bf16 = d->scale_dtype == QSMOE_BF16;
+    L.shared_gate_w = (const uint16_t *)d->shared_gate_w;
     return L;
 }
 
@@ -113,7 +117,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     PrefillBufs b;
     b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);      // decode state stays untouched (but word 0)
     b.x16 = c.take<uint16_t>((size_t)(T * H));
-    b.logits = c.take<float>((size_t)(T * E));
+    b.logits = c.take<float>((size_t)(T * (E + 1)));     // + the shared-expert gate's logit
     b.idx = c.take<int32_t>((size_t)(T * K));
     b.w = c.take<float>((size_t)(T * K));
     b.blkcnt = c.take<int32_t>((size_t)(nblk * E));
@@ -125,6 +129,7 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
     b.tile_done = c.take<int32_t>((size_t)prefill_max_tiles(T, (int)K, (int)E));
     b.h = c.take<uint16_t>((size_t)((T * K + T) * I));
     b.slot = c.take<uint16_t>((size_t)((T * K + T) * H));
+    b.sgate = c.take<float>((size_t)T);
     *bytes = c.off;
     return b;
 }

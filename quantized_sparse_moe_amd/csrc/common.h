@@ -44,6 +44,11 @@ namespace qs {
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+// a quantization scale or bias: fp16 bits, or bf16 bits (the upper half of an fp32)
+__device__ __forceinline__ float sb_to_f32(uint32_t bits, int bf16) {
+    return bf16 ? __uint_as_float(bits << 16) : f16_to_f32((uint16_t)bits);
+}
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // round-to-nearest-even to bfloat16 (NaN stays NaN)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {

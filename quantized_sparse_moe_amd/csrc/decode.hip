@@ -97,7 +97,7 @@ __device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float2 *xsum) {
 // wait.  Addresses are a uniform matrix base plus a 32-bit per-lane offset.
 template <int BITS>
 __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
-                             const uint32_t *xs, const float2 *xsum, float hv[2]) {
+                             const uint32_t *xs, const float2 *xsum, int sb_bf16, float hv[2]) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
@@ -125,7 +125,7 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float p = chunk_dot<BITS>(q[r], xs + cc * (CPC / 2), sc[r], bi[r], xsum[cc]);
+            const float p = chunk_dot<BITS>(q[r], xs + cc * (CPC / 2), sc[r], bi[r], xsum[cc], sb_bf16);
             acc[r] += ok ? p : 0.0f;
         }
     }
@@ -137,18 +137,19 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
     }
 }
 
-__device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K) {
+__device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, float *gate) {
     return select_topk_from(ctl, (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE),
-                            tag, E, K);
+                            tag, E, K, gated, gate);
 }
 
 // Consumer: wave 0 waits (bounded) for the published selection, one poll in flight;
-// the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights.
-__device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int *s_idx, float *s_w) {
+// the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights (and,
+// gated, entry K: the shared expert's gate in s_w[K]).
+__device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, int *s_idx, float *s_w) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
-        const bool act = lane < 2 * K;
+        const bool act = lane < 2 * (K + gated);
         const uint64_t none = (uint64_t)tag << 32;
         uint64_t w;
         for (uint32_t n = 0;; ++n) {
@@ -172,14 +173,15 @@ template <int BITS>
 __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_decode(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
     __shared__ uint32_t s_flag;
-    __shared__ int s_idx[16];
-    __shared__ float s_w[16];
+    __shared__ int s_idx[17];
+    __shared__ float s_w[17];
     __shared__ float s_part[NW][DT / 64 * 16];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
     uint32_t *ctl = a.ctl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K;
+    const int sb_bf16 = L.sb_bf16, gated = L.shared_gate_w != nullptr && a.shared;
     int nR = a.nR;
     const int nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
@@ -192,8 +194,8 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int e = b * NW + wave;
         const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
         float acc = 0.0f;
-        if (e < E) {
-            const uint16_t *wr = L.router_w + (int64_t)e * H;
+        if (e < E + gated) {                                  // e = E: the shared expert's gate
+            const uint16_t *wr = e < E ? L.router_w + (int64_t)e * H : L.shared_gate_w;
             for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
                 u32x4 xv[4], wv[4];
 #pragma unroll
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                                              __uint_as_float(wv[k][i] & 0xffff0000u), acc);
                     }
             }
-            acc = wave_sum(acc) + (L.router_bias ? L.router_bias[e] : 0.0f);
+            acc = wave_sum(acc) + ((L.router_bias && e < E) ? L.router_bias[e] : 0.0f);
         }
         if (lane == 0) s_lg[wave] = acc;
         __syncthreads();
@@ -223,9 +225,9 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             for (int t = lane; t < LOGIT_COPIES * PIECES; t += 64) {
                 const int c = t / PIECES, q = t % PIECES, e0 = b * NW + 2 * q;
                 uint32_t *dst = ctl + LOGIT_BASE + c * LOGIT_STRIDE + 2 * e0;
-                if (e0 + 1 < E)
+                if (e0 + 1 < E + gated)
                     st_dev128(dst, (u32x4){__float_as_uint(s_lg[2 * q]), tag, __float_as_uint(s_lg[2 * q + 1]), tag});
-                else if (e0 < E)
+                else if (e0 < E + gated)
                     st_dev64((uint64_t *)dst, __float_as_uint(s_lg[2 * q]) | ((uint64_t)tag << 32));
             }
         }
@@ -236,7 +238,8 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // ------------------------------------------- P: selectors (wave 0 works)
         if (wave != 0) return;
         const int sel = b - nR;
-        const TopkOut tk = select_topk(ctl, tag, E, K);
+        float gate;
+        const TopkOut tk = select_topk(ctl, tag, E, K, gated && !a.route_only, &gate);
         if (a.route_only) {
             if (lane < K) {
                 if (a.out_idx) a.out_idx[lane] = tk.idx;
@@ -245,10 +248,11 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             if (lane == 0) st_dev(ctl + CTL_GEN, tag);       // the only reader of this call's logits
             return;
         }
-        if (lane < K)
+        if (lane < K + gated)                                // entry K: the shared expert's gate
             for (int c = sel; c < TOPK_COPIES; c += a.nP)
                 st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * lane,
-                          (u32x4){(uint32_t)tk.idx, tag, __float_as_uint(tk.w), tag});
+                          lane < K ? (u32x4){(uint32_t)tk.idx, tag, __float_as_uint(tk.w), tag}
+                                   : (u32x4){(uint32_t)E, tag, __float_as_uint(gate), tag});
         return;
     }
     nR += a.nP;                                              // the roles below follow the selectors
@@ -268,12 +272,12 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         if (sh) {
             __syncthreads();
         } else {
-            get_topk(ctl, tag, E, K, s_idx, s_w);            // ends with a barrier
+            get_topk(ctl, tag, E, K, gated, s_idx, s_w);     // ends with a barrier
             e = __builtin_amdgcn_readfirstlane(s_idx[slot]);
         }
         const int jj = j0 < I ? j0 : I - 2;
         float hv[2];
-        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, hv);
+        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, sb_bf16, hv);
         // the workgroup's pb / 2 words (one per row group, consecutive in j) are gathered
         // in LDS and written to every copy in 16-byte pieces
         __shared__ uint32_t s_hw[NW * 64];
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     {
         // ------------------------------------------ D: down + weighted combine
         const int d = b - nR - nS - nG;
-        get_topk(ctl, tag, E, K, s_idx, s_w);
+        get_topk(ctl, tag, E, K, gated, s_idx, s_w);
         if (d == 0 && tid < K) {
             if (a.out_idx) a.out_idx[tid] = s_idx[tid];
             if (a.out_w) a.out_w[tid] = s_w[tid];
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             pc = (uint64_t)(mm.codes + R0 * rb);
             ps = (uint64_t)(mm.scales + R0 * ng);
             pbi = (uint64_t)(mm.biases + R0 * ng);
-            if (routed) wl = s_w[lane];
+            if (routed || gated) wl = s_w[lane];             // lane K, gated: the shared gate
         }
         float yv = 0.0f;
         uint32_t arrived = 0;
@@ -400,7 +404,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 const int vi = live ? v2 : min(vlast, nvec - 1);
                 const int c = lr + k2 * lpr, cc = c < nch ? c : nch - 1;
                 const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + (vi * nch + cc) * CPITCH), sv[i], bv[i],
-                                                hsum[vi * nch + cc]);
+                                                hsum[vi * nch + cc], sb_bf16);
                 const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), vi));
                 yv += (live && c < nch) ? wv * p : 0.0f;       // experts in ascending id, shared last
                 if (++k2 == cpl) { k2 = 0; ++v2; }
@@ -452,7 +456,7 @@ hipError_t launch(DecArgs a, hipStream_t s) {
     a.lprd = lanes_per_row(L.I, L.bits);
     const int pb = 2 * NW * (64 / a.lprg);
     const int bpe = (L.I + pb - 1) / pb;
-    a.nR = (L.E + NW - 1) / NW;
+    a.nR = (L.E + (L.shared_gate_w && a.shared ? 1 : 0) + NW - 1) / NW;   // + the shared gate's logit
     size_t lds = 16;
     a.vs = 1;
     if (a.route_only) {

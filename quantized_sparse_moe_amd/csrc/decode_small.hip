@@ -28,7 +28,7 @@ namespace {
 
 constexpr int SM_TMAX = 4;
 constexpr int SM_LCOPIES = 8;
-constexpr int SM_TE = 256;                                  // logit words per token and copy
+constexpr int SM_TE = 264;                                  // logit words per token and copy (E + gate)
 constexpr int SM_LSTRIDE = 2 * SM_TMAX * SM_TE + 64;        // u32 per logits copy
 static_assert(SM_LCOPIES * SM_LSTRIDE <= LOGIT_COPIES * LOGIT_STRIDE, "small-T logits region");
 constexpr int SM_HCOPIES = 2;
@@ -36,6 +36,7 @@ constexpr int SM_HSTRIDE = H_COPIES * H_STRIDE / SM_HCOPIES;   // u32 per h copy
 constexpr int SM_HWORDS = SM_HSTRIDE / 2 - 32;                 // h words per copy
 constexpr size_t SMALL_LDS_MAX = 76 * 1024;                    // dynamic LDS of a small-batch call
 static_assert(2 * SM_TMAX * 16 <= TOPK_STRIDE / 2, "small-T selection region");
+static_assert(4 * (64 + SM_TMAX) <= TOPK_STRIDE, "small-T gate entries");
 
 struct SmallArgs {
     Layer L;
@@ -62,21 +63,24 @@ struct SmallSel {
     int ul[SM_TMAX * 16];
     int jt[SM_TMAX * 16][SM_TMAX];
     int nu;
+    float sg[SM_TMAX];                                      // the shared expert's gate per token
 };
-__device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, SmallSel &S) {
+// (gated: entry 64 + t holds token t's shared-expert gate)
+__device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, int gated, SmallSel &S) {
     const int tid = threadIdx.x, n = T * K;
     if (tid < 8) S.ub[tid] = 0u;
     if (tid < SM_TMAX * 16 * SM_TMAX) (&S.jt[0][0])[tid] = -1;
     if (tid < 64) {
         const int lane = tid;
         const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
-        const bool act = lane < n;
+        const bool act = lane < n, actg = gated && lane < T;
         const uint64_t none = (uint64_t)tag << 32;
-        uint64_t w0, w1;
+        uint64_t w0, w1, wg;
         for (uint32_t it = 0;; ++it) {
             w0 = act ? ld_dev64(tp + 2 * lane) : none;
             w1 = act ? ld_dev64(tp + 2 * lane + 1) : none;
-            if (__ballot(tag_of(w0) != tag || tag_of(w1) != tag) == 0ull) break;
+            wg = actg ? ld_dev64(tp + 2 * (64 + lane) + 1) : none;
+            if (__ballot(tag_of(w0) != tag || tag_of(w1) != tag || tag_of(wg) != tag) == 0ull) break;
             if (it > SPIN_LIMIT) {
                 if (lane == 0) raise_error(ctl);
                 break;
@@ -87,6 +91,7 @@ __device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, 
             S.si[lane] = min(max((int)(uint32_t)w0, 0), E - 1);
             S.sw[lane] = __uint_as_float((uint32_t)w1);
         }
+        if (lane < SM_TMAX) S.sg[lane] = actg ? __uint_as_float((uint32_t)wg) : 1.0f;
     }
     __syncthreads();
     if (tid < n) atomicOr(&S.ub[S.si[tid] >> 5], 1u << (S.si[tid] & 31));
@@ -248,7 +253,7 @@ __device__ __forceinline__ float wave_sum16(float (&v)[SM_TMAX * 4]) {
 template <int BITS>
 __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, const PairW &w0,
                                     const uint32_t *xs, int T, int tmask, uint32_t *hq, int wpi,
-                                    int wi) {
+                                    int wi, int sb_bf16) {
     constexpr int CPC = 128 / BITS, XP = small_xpitch<BITS>();
     const int lane = threadIdx.x & 63;
     const int lr = lane % lpr;
@@ -312,8 +317,8 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
                         au[t][o] = __builtin_amdgcn_fdot2(as_h2(du[j][i]), as_h2(xx[j][i]), au[t][o], false);
                     }
             }
-            const float sg = f16_to_f32((uint16_t)w.sc[2 * p]), bg = f16_to_f32((uint16_t)w.bi[2 * p]);
-            const float su = f16_to_f32((uint16_t)w.sc[2 * p + 1]), bu = f16_to_f32((uint16_t)w.bi[2 * p + 1]);
+            const float sg = sb_to_f32(w.sc[2 * p], sb_bf16), bg = sb_to_f32(w.bi[2 * p], sb_bf16);
+            const float su = sb_to_f32(w.sc[2 * p + 1], sb_bf16), bu = sb_to_f32(w.bi[2 * p + 1], sb_bf16);
 #pragma unroll
             for (int t = 0; t < SM_TMAX; ++t) {
                 if (t >= T || !((tmask >> t) & 1)) continue;
@@ -376,6 +381,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     uint32_t *ctl = a.ctl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K, T = a.T;
+    const int sb_bf16 = L.sb_bf16, gated = L.shared_gate_w != nullptr && a.shared;
     const int nR = a.nR, nP = a.nP, nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
     const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
@@ -388,8 +394,8 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         __syncthreads();
         const int e = b * NW + wave;
         float acc[SM_TMAX] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (e < E) {
-            const uint16_t *wr = L.router_w + (int64_t)e * H;
+        if (e < E + gated) {                                  // e = E: the shared expert's gate
+            const uint16_t *wr = e < E ? L.router_w + (int64_t)e * H : L.shared_gate_w;
             for (int c0 = lane; c0 < H / 8; c0 += 4 * 64) {
                 u32x4 wv[4];
 #pragma unroll
@@ -429,9 +435,9 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 const int e0 = b * NW + 2 * q;
                 if (t >= T) continue;
                 uint32_t *dst = ctl + LOGIT_BASE + c * SM_LSTRIDE + 2 * (t * SM_TE + e0);
-                if (e0 + 1 < E)
+                if (e0 + 1 < E + gated)
                     st_dev128(dst, (u32x4){__float_as_uint(s_lg[t][2 * q]), tag, __float_as_uint(s_lg[t][2 * q + 1]), tag});
-                else if (e0 < E)
+                else if (e0 < E + gated)
                     st_dev64((uint64_t *)dst, __float_as_uint(s_lg[t][2 * q]) | ((uint64_t)tag << 32));
             }
         }
@@ -442,11 +448,13 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int sel = b - nR;
         if (wave < T) {
             const uint64_t *lg = (const uint64_t *)(ctl + LOGIT_BASE + (sel % SM_LCOPIES) * SM_LSTRIDE) + wave * SM_TE;
-            const TopkOut tk = select_topk_from(ctl, lg, tag, E, K);
+            float gate;
+            const TopkOut tk = select_topk_from(ctl, lg, tag, E, K, gated, &gate);
             if (lane < K) {
                 S.si[wave * K + lane] = tk.idx;
                 S.sw[wave * K + lane] = tk.w;
             }
+            if (lane == 0) S.sg[wave] = gate;
         }
         __syncthreads();
         if (a.route_only) {
@@ -461,6 +469,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             for (int c = sel; c < TOPK_COPIES; c += nP)
                 st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * tid,
                           (u32x4){(uint32_t)S.si[tid], tag, __float_as_uint(S.sw[tid]), tag});
+        if (gated && tid < T)                                // entry 64 + t: token t's shared gate
+            for (int c = sel; c < TOPK_COPIES; c += nP)
+                st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * (64 + tid),
+                          (u32x4){(uint32_t)E, tag, __float_as_uint(S.sg[tid]), tag});
         return;
     }
     const int nRP = nR + nP;
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         stage_x_tokens<BITS>(a.x, T, H, xs);
         int nitems = 1;
         if (!sh) {
-            small_get_sel(ctl, tag, E, K, T, S);             // ends with a barrier
+            small_get_sel(ctl, tag, E, K, T, gated, S);             // ends with a barrier
             nitems = (S.nu * bpe - g + nG - 1) / nG;         // items g, g + nG, ... < |U| bpe
         } else {
             __syncthreads();
@@ -517,7 +529,8 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             }
             int tmask = 0;
             for (int t = 0; t < T; ++t) tmask |= (sh || S.jt[u][t] >= 0) ? (1 << t) : 0;
-            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, T, tmask, hq + m * T * wpi, wpi, wi);
+            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, T, tmask, hq + m * T * wpi, wpi, wi,
+                                      sb_bf16);
         }
         __syncthreads();
         const int pieces = (wpi + 1) / 2;
@@ -546,7 +559,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // four row groups of 64 / lprd rows; wave w takes row group w % 4 and the union
         // slots of parity w / 4 (the shared expert is slot |U|)
         const int d = b - nRP - nS - nG;
-        small_get_sel(ctl, tag, E, K, T, S);
+        small_get_sel(ctl, tag, E, K, T, gated, S);
         if (d == 0 && tid < T * K) {
             if (a.out_idx) a.out_idx[tid] = S.si[tid];
             if (a.out_w) a.out_w[tid] = S.sw[tid];
@@ -620,10 +633,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     if (t >= T) break;
                     const int j = v < nu ? S.jt[v][t] : K;
                     if (!live || j < 0) continue;                // uniform: the token did not choose it
-                    const float wt = v < nu ? S.sw[t * K + j] : 1.0f;
+                    const float wt = v < nu ? S.sw[t * K + j] : S.sg[t];   // shared: its gate (or 1)
                     const int ch = (t * (K + 1) + j) * nch + cc;
                     const float p = chunk_dot<BITS>(w.q[i], (const uint32_t *)(hs16 + ch * CPITCH), w.sv[i], w.bv[i],
-                                                    hsum[ch]);
+                                                    hsum[ch], sb_bf16);
                     yv[t] += c < nch ? wt * p : 0.0f;
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -732,7 +745,7 @@ hipError_t launch_small(SmallArgs a, hipStream_t s) {
     a.lprd = lanes_per_row(L.I, L.bits);
     const int pb = 2 * NW * (64 / a.lprg);
     const int bpe = (L.I + pb - 1) / pb;
-    a.nR = (L.E + NW - 1) / NW;
+    a.nR = (L.E + (L.shared_gate_w && a.shared ? 1 : 0) + NW - 1) / NW;   // + the shared gate's logit
     size_t lds = (size_t)a.T * L.H * 2;                // R: x of all tokens, raw
     if (a.route_only) {
         a.nP = 1;

@@ -105,10 +105,11 @@ __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_
 //   sum (s q + b) x = s A_e + (s / 16) A_o + (b - 1024 s) X_e + (b - 64 s) X_o
 // with A_e, A_o the dot products of the magic values with x.  8-bit: 1024 + q for all.
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 X) {
+__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 X,
+                                           int sb_bf16) {
     const u32x4 *xv = (const u32x4 *)xs;
     const uint32_t magic = QS_MAGIC;
-    const float s = f16_to_f32((uint16_t)s16), b = f16_to_f32((uint16_t)b16);
+    const float s = sb_to_f32(s16, sb_bf16), b = sb_to_f32(b16, sb_bf16);
     if constexpr (BITS == 4) {
         const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
         float ae[2] = {0.0f, 0.0f}, ao[2] = {0.0f, 0.0f};
@@ -142,14 +143,18 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, u
 // the top-k: lanes j < K return (id, weight) of the j-th selected expert in ascending
 // id.  One poll is in flight at a time: a read still in flight when the data is found
 // would have to be waited for before its registers are reused, a full extra round trip.
-__device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t tag, int E, int K) {
+// gated: logit E is the shared-expert gate's, polled with the others; *gate gets
+// sigmoid of it (every lane).
+__device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t tag, int E, int K, int gated,
+                                    float *gate) {
     const int lane = threadIdx.x & 63;
     const uint64_t none = (uint64_t)tag << 32;
-    uint64_t w[4];
+    uint64_t w[4], wg;
     for (uint32_t n = 0;; ++n) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
-        bool miss = false;
+        wg = (gated && lane == 0) ? ld_dev64(lg + E) : none;
+        bool miss = tag_of(wg) != tag;
 #pragma unroll
         for (int i = 0; i < 4; ++i) miss |= tag_of(w[i]) != tag;
         if (__ballot(miss) == 0ull) break;
@@ -164,6 +169,7 @@ __device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t 
     for (int i = 0; i < 4; ++i) v[i] = no_nan(__uint_as_float((uint32_t)w[i]));
     TopkOut tk = wave_topk_regs(v, E, K);
     tk.idx = min(max(tk.idx, 0), E - 1);
+    *gate = sigmoid(__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane((int)(uint32_t)wg)));
     return tk;
 }
 // lanes sharing one row: the largest power of two <= min(64, 16-byte chunks per row)

@@ -88,6 +88,7 @@ struct GemmArgs {
     int nb;                          // column blocks per tile
     int wlog;                        // log2 of the scale / bias window (groups per row per load)
     int32_t *tile_done;              // [tiles] gate/up column blocks finished (zeroed by binning)
+    const float *sgate;              // [T] shared-expert gate per token (gated layers), or null
     int nb_gateup;                   // down pass: the gate/up column blocks a tile waits for
     uint32_t *err;                   // bounded-wait error flag
 };
@@ -306,8 +307,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rs = 64 * wave + 16 * j + n16;
-            const _Float16 sv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + rs * pitch));
-            const _Float16 bv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + C::S_BYTES + rs * pitch));
+            const uint16_t sbits = *(const uint16_t *)(sw + rs * pitch);
+            const uint16_t bbits = *(const uint16_t *)(sw + C::S_BYTES + rs * pitch);
+            // bf16 scales and biases become fp16 exactly (8 significant bits, in range)
+            const _Float16 sv = L.sb_bf16 ? (_Float16)__uint_as_float((uint32_t)sbits << 16)
+                                          : __builtin_bit_cast(_Float16, sbits);
+            const _Float16 bv = L.sb_bf16 ? (_Float16)__uint_as_float((uint32_t)bbits << 16)
+                                          : __builtin_bit_cast(_Float16, bbits);
             sc[j] = (f16x2){sv, sv};
             const _Float16 sv16 = sv * (_Float16)0.0625f;        // exact: scales are normal numbers
             sc16[j] = (f16x2){sv16, sv16};
@@ -457,7 +463,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
             // routed rows: the (token, slot) row with its routing weight; shared rows:
             // row T*K + t with weight 1
             const int64_t p = routed_down ? (int64_t)s_pos[row] : (int64_t)tile.row0 + row;
-            const float wv = routed_down ? s_w[row] : 1.0f;
+            const float wv = routed_down ? s_w[row] : a.sgate ? a.sgate[tile.row0 + row - TK] : 1.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
@@ -587,6 +593,7 @@ hipError_t launch_prefill_gemms(const Layer &L, int64_t T, const PrefillBufs &b,
     a.w = b.w;
     a.slot = b.slot;
     a.tile_done = b.tile_done;
+    a.sgate = (L.shared_gate_w && L.has_shared) ? b.sgate : nullptr;
     a.err = b.ctl;
     a.nb_gateup = 0;
     a.y = y;

@@ -23,6 +23,8 @@ struct Layer {
     QMat gate, up, down;
     int has_shared;
     QMat s_gate, s_up, s_down;
+    int sb_bf16;                   // scales and biases are bf16 (else fp16)
+    const uint16_t *shared_gate_w; // bf16 [H]: shared output scaled by sigmoid(g . x); or null
 };
 
 // -------------------------------------------------------------------- decode T = 1
@@ -73,6 +75,7 @@ struct PrefillBufs {
     uint32_t *ctl;                 // the workspace's state region (word 0: bounded-wait error flag)
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
     uint16_t *slot;                // [T*K + T][H] fp16: w_j * o_j per (token, slot), then shared o
+    float *sgate;                  // [T] shared-expert gate sigmoid(g . x_t) (gated layers)
 };
 
 int64_t prefill_max_routed_tiles(int64_t T, int K, int E);

@@ -28,7 +28,9 @@ struct LogitArgs {
     const uint16_t *x;              // [T][H] bf16
     const uint16_t *wr;             // [E][H] bf16
     const float *bias;              // [E] or null
-    float *logits;                  // [T][E]
+    const uint16_t *gate_w;         // [H] bf16 shared-expert gate, logit column E; or null
+    float *logits;                  // [T][LS]
+    int LS;                         // logit row stride: E (+ 1 with a gate)
     uint16_t *x16;                  // [T][H] fp16 in code order, or null
     int64_t T;
     int H, E;
@@ -52,13 +54,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const int64_t t = t0 + sr + 16 * i;
         xrow[i] = t < a.T ? t : -1;
         const int e = e0 + sr + 16 * i;
-        wrow[i] = e < E ? e : -1;
+        wrow[i] = e < a.LS ? e : -1;                        // e = E: the shared gate's row
     }
     auto load = [&](int kc, u32x4 (&xv)[4], u32x4 (&wv)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             xv[i] = xrow[i] >= 0 ? *(const u32x4 *)(a.x + xrow[i] * H + kc + sc) : (u32x4){0u, 0u, 0u, 0u};
-            wv[i] = wrow[i] >= 0 ? *(const u32x4 *)(a.wr + (int64_t)wrow[i] * H + kc + sc) : (u32x4){0u, 0u, 0u, 0u};
+            wv[i] = wrow[i] >= 0 ? *(const u32x4 *)((wrow[i] < E ? a.wr + (int64_t)wrow[i] * H : a.gate_w) + kc + sc)
+                                 : (u32x4){0u, 0u, 0u, 0u};
         }
     };
     f32x4 acc[4];
@@ -114,20 +117,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
         const int e = e0 + 16 * n + n16;
-        if (e >= E) continue;
-        const float b = a.bias ? a.bias[e] : 0.0f;
+        if (e >= a.LS) continue;
+        const float b = (a.bias && e < E) ? a.bias[e] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t t = t0 + wave * 16 + 4 * cg + r;
-            if (t < a.T) a.logits[t * E + e] = acc[n][r] + b;
+            if (t < a.T) a.logits[t * a.LS + e] = acc[n][r] + b;
         }
     }
 }
 
 struct TopkArgs {
-    const float *logits;            // [T][E]
+    const float *logits;            // [T][LS]
     int64_t T;
-    int E, K;
+    int E, K, LS;
+    float *sgate;                   // [T] sigmoid of logit column E (gated layers), or null
     int32_t *idx;                   // [T][K]
     float *w;
     int32_t *out_idx;               // optional copies for the caller
@@ -151,13 +155,14 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
         const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            v[q][i] = (t < a.T && lane + 64 * i < E) ? a.logits[t * E + lane + 64 * i] : 0.0f;
+            v[q][i] = (t < a.T && lane + 64 * i < E) ? a.logits[t * a.LS + lane + 64 * i] : 0.0f;
     }
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
         const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
         if (t >= a.T) break;
         const TopkOut tk = wave_topk_regs(v[q], E, K);
+        if (a.sgate && lane == 0) a.sgate[t] = sigmoid(a.logits[t * a.LS + E]);
         if (lane < K) {
             a.idx[t * K + lane] = tk.idx;
             a.w[t * K + lane] = tk.w;
@@ -179,12 +184,15 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     la.x = x;
     la.wr = L.router_w;
     la.bias = L.router_bias;
+    const bool gated = L.shared_gate_w && L.has_shared && write_x16;   // moe_route needs no gate
+    la.gate_w = gated ? L.shared_gate_w : nullptr;
+    la.LS = L.E + (gated ? 1 : 0);
     la.logits = b.logits;
     la.x16 = write_x16 ? b.x16 : nullptr;
     la.T = T;
     la.H = L.H;
     la.E = L.E;
-    const dim3 lgrid((unsigned)((T + LT - 1) / LT), (unsigned)((L.E + LE - 1) / LE));
+    const dim3 lgrid((unsigned)((T + LT - 1) / LT), (unsigned)((la.LS + LE - 1) / LE));
     if (L.bits == 4)
         hipLaunchKernelGGL((k_logits<4>), lgrid, dim3(256), 0, s, la);
     else
@@ -194,6 +202,8 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     ta.T = T;
     ta.E = L.E;
     ta.K = L.K;
+    ta.LS = la.LS;
+    ta.sgate = gated ? b.sgate : nullptr;
     ta.idx = b.idx;
     ta.w = b.w;
     ta.out_idx = out_idx;

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert q.abi_version() == 1
+    assert q.abi_version() == 2
     for s in (0, -1, -2, -3, -4):
         assert q.status_string(s) and q.status_string(s) != "unknown status"
     assert q.status_string(7) == "unknown status"
@@ -71,19 +71,33 @@ def route(d, T=16, x=FAKE, ws=FAKE, ws_bytes=1 << 40, idx=FAKE, w=FAKE):
 
 @pytest.mark.parametrize("field,value,status", [
     ("bits", 3, q.QSMOE_ERR_UNSUPPORTED), ("bits", 2, q.QSMOE_ERR_UNSUPPORTED),
-    ("group", 32, q.QSMOE_ERR_UNSUPPORTED), ("scale_dtype", q.QSMOE_BF16, q.QSMOE_ERR_UNSUPPORTED),
+    ("group", 32, q.QSMOE_ERR_UNSUPPORTED), ("scale_dtype", q.QSMOE_F32, q.QSMOE_ERR_UNSUPPORTED),
     ("n_experts", 0, q.QSMOE_ERR_UNSUPPORTED), ("n_experts", 257, q.QSMOE_ERR_UNSUPPORTED),
     ("top_k", 0, q.QSMOE_ERR_UNSUPPORTED), ("top_k", 17, q.QSMOE_ERR_UNSUPPORTED),
     ("hidden", 2000, q.QSMOE_ERR_UNSUPPORTED), ("hidden", 64, q.QSMOE_ERR_UNSUPPORTED),
     ("hidden", 8320, q.QSMOE_ERR_UNSUPPORTED), ("inter", 576, q.QSMOE_ERR_UNSUPPORTED),
     ("inter", 2176, q.QSMOE_ERR_UNSUPPORTED), ("router_w", None, q.QSMOE_ERR_INVALID),
     ("router_w", FAKE + 8, q.QSMOE_ERR_INVALID), ("has_shared", 2, q.QSMOE_ERR_INVALID),
+    ("shared_gate_w", FAKE + 8, q.QSMOE_ERR_INVALID),
 ])
 def test_descriptor_validation(field, value, status):
     d = desc(**{field: value})
     assert fwd(d) == status
     assert route(d) == status
     assert q.lib().qsmoe_workspace_size(ctypes.byref(d), 16) == ctypes.c_size_t(-1).value
+
+
+def test_checkpoint_variants_accepted():
+    """bf16 scales and a shared-expert gate are valid descriptors (checked through the
+    workspace query, which validates without enqueueing anything); a gate without the
+    shared expert is not."""
+    ws = lambda d: q.lib().qsmoe_workspace_size(ctypes.byref(d), 16)
+    bad = ctypes.c_size_t(-1).value
+    assert ws(desc(scale_dtype=q.QSMOE_BF16)) != bad
+    assert ws(desc(shared_gate_w=FAKE)) != bad
+    d = desc(shared_gate_w=FAKE)
+    d.has_shared = 0
+    assert ws(d) == bad and fwd(d) == q.QSMOE_ERR_INVALID
 
 
 def test_top_k_above_experts_and_lds_limit():

@@ -271,19 +271,20 @@ def _shifted_desc(torch, qs, base, shift):
         codes, scales, biases, stride, row0 = m
         return (codes, moved(scales), moved(biases), stride, row0)
 
-    rw, rb, g, u, d, sh = base._keep
+    rw, rb, g, u, d, sh, sgw = base._keep
     shared = None if sh is None else tuple(qm(m) for m in sh)
     desc = qs.LayerDesc(base.hidden, base.inter, base.n_experts, base.top_k, base.bits, rw, qm(g), qm(u), qm(d),
-                        router_bias=rb, shared=shared)
+                        router_bias=rb, shared=shared, scale_dtype=base.desc.scale_dtype, shared_gate_w=sgw)
     desc._made = made
     return desc
 
 
-@pytest.mark.parametrize("cfg", ["PREFILL", "SKEW"])
-def test_scale_staging_paths_bit_identical(torch, qs, cfg):
+@pytest.mark.parametrize("cfg,variant", [("PREFILL", False), ("SKEW", False), ("PREFILL", True)])
+def test_scale_staging_paths_bit_identical(torch, qs, cfg, variant):
     """The grouped GEMM stages scales and biases 8, 2 or 1 groups per row at a time
-    depending on their alignment; every path must give the same bits (T = 64 and T = 1)."""
-    L = layer(cfg)
+    depending on their alignment; every path must give the same bits (T = 64 and T = 1),
+    also with bf16 scales and the gated shared expert."""
+    L = layer(cfg, scale_dtype="bf16", shared_gate=True) if variant else layer(cfg)
     base = qs.LayerDesc.from_host(L)
     x_np = syn.make_x(64, L.hidden, seed=29)
     ref = [run_layer(torch, qs, L, x_np[:T], desc=base)[0] for T in (64, 1)]
@@ -399,3 +400,17 @@ def test_q8_activation_quantized_gemv(torch, qs, N, K):
     exact = oracle.q8_gemv(rows, N, K, x_np)
     rel = np.max(np.abs(y - exact)) / np.sqrt(np.mean(exact ** 2))
     assert 0 < rel < 5e-2, rel                                 # quantized x: close, not equal
+
+
+# ------------------------------------------------------------ checkpoint variants
+@pytest.mark.parametrize("cfg,T", [("DECODE", 1), ("DECODE", 3), ("DECODE", 40), ("SKEW", 2), ("SKEW", 64)])
+def test_checkpoint_variants_parity(torch, qs, cfg, T):
+    """bf16 scales and biases together with the sigmoid-gated shared expert, on the T = 1
+    kernel, the small-batch kernel and the grouped path, 4- and 8-bit, both output types;
+    then the gate alone and bf16 alone at the same shape."""
+    for sd, gate in (("bf16", True), ("f16", True), ("bf16", False)):
+        L = layer(cfg, scale_dtype=sd, shared_gate=gate)
+        x_np = syn.make_x(T, L.hidden, seed=200 + T)
+        for bf16_out in (False, True):
+            y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
+            oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} T={T} {sd} gate={gate}")

@@ -25,7 +25,7 @@ MUTATIONS = [
     ("ties to the higher id", "(l[a] == l[b] && a < b)", "(l[a] == l[b] && a > b)"),
     ("down operand transposed", "acc += weight(d, L->bits, e, n, i, I) * h[i];",
      "acc += weight(d, L->bits, e, i % L->hidden, n % L->inter, I) * h[i];"),
-    ("shared expert half weight", "yt[c] += o[c];", "yt[c] += 0.5 * o[c];"),
+    ("shared expert half weight", "yt[c] += gs * o[c];", "yt[c] += 0.5 * gs * o[c];"),
     ("gate and up swapped", "h[i] = silu(gi) * ui;", "h[i] = silu(ui) * gi;"),
     ("router bias ignored", "if (L->router_bias) acc += (double)L->router_bias[e];", ""),
     ("tile rows not interleaved", "return (int64_t)(c / 4) * 64 + r * 4 + (c % 4);",
