@@ -14,7 +14,7 @@ Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256
 Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
 HIP graph; HIP events on the replay stream bracket the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,q8x,smallT,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,q8x,smallT,variant,copy]
 """
 from __future__ import annotations
 
@@ -36,7 +36,7 @@ GROUP = 64
 # figure holds only for the kernel sources it was measured on, identified by their
 # sha256; once they change the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/decode_state.h", "csrc/common.h", "csrc/internal.h")
-DECODE_TRAFFIC = {"sources_sha256": "2a904e64027429d8fd11586d71a0685cb4a183a2c9e6b8f7bb70c6718bf5e129", "bytes": 17887567}
+DECODE_TRAFFIC = {"sources_sha256": "809a365d831f192d75f86b0c74c249122c7909de5279579da9ddaf3e0b8c5eb2", "bytes": 17974594}
 
 
 # ----------------------------------------------------------- algorithmic accounting
@@ -149,8 +149,8 @@ def cpu_baseline_decode(L, ntok: int):
 
 
 # ----------------------------------------------------------------------- workloads
-def bench_decode(qs, torch, syn, steps, warmup, copies=40):
-    L = syn.make_layer(**syn.DECODE)
+def bench_decode(qs, torch, syn, steps, warmup, copies=40, **variant):
+    L = syn.make_layer(**syn.DECODE, **variant)
     descs = _dev_layer_copies(qs, torch, L, copies)
     xs = [torch.from_numpy(syn.make_x(1, L.hidden, seed=100 + l).view(np.int16)).cuda() for l in range(copies)]
     ys = [torch.empty((1, L.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
@@ -317,6 +317,12 @@ def main(argv=None):
                            "frac": gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
                            "kernel": "decode layer (router+shared gate/up, routed gate/up, down+combine)",
                            "bytes_per_launch": nbytes}
+    if "variant" in only:
+        # same decode layer with bf16 scales / biases and the sigmoid-gated shared expert
+        Lv, ms, nbytes = bench_decode(qs, torch, syn, args.steps, args.warmup, scale_dtype="bf16",
+                                      shared_gate=True)
+        out["decode_bf16_gated"] = {"ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
+                                    "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
     if "prefill" in only:
         steps = max(4, args.steps // 100)
         L, ms, flops = bench_prefill(qs, torch, syn, syn.PREFILL, syn.PREFILL_T, steps,
