@@ -8,7 +8,7 @@ batch-1 decode workload (hidden 2048, 256 experts top-8 + 1 shared, expert inter
 bytes over HBM peak as the roofline.  Extra keys report the prefill (T = 4096), the
 skewed long prefill (T = 16384, 8-bit, Zipf router bias), the dense Q8_0 GEMV, the
 same GEMVs with a quantized activation (int8 dots, and their deviation from the exact
-path) and (--only smallT) the decode layer at T = 1, 2, 4, 8.
+path) and (--only smallT) the decode layer at T = 1, 2, 4, 5, 8.
 
 Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256 MB
 Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
@@ -165,7 +165,7 @@ def bench_decode(qs, torch, syn, steps, warmup, copies=40, **variant):
     return L, ms, nbytes
 
 
-def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 8), copies=40):
+def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 5, 8), copies=40):
     """Small batches of the decode layer (the verification / batched-decode shape): per T,
     the time per call and the bytes a call must read -- router weights, each expert that
     any of the T tokens selects (once), the shared expert, x and y -- per token."""

@@ -170,6 +170,7 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T,
  * Path: T == 1 runs the batch-1 decode kernel (register dequantization on the vector
  * ALUs, fp32 intermediates); T = 2 .. 4 the same kernel design over all tokens at once,
  * each expert any token selected read once (when (top_k + 1) * inter * T <= 49216);
+ * T = 5 .. 8 two such launches of ceil(T/2) and floor(T/2) tokens (when both fit);
  * larger T runs the grouped-GEMM path (MFMA on fp16 operands dequantized in registers,
  * fp32 accumulation, fp16 intermediates).
  * For a given T the result does not depend on whether gate/up are fused or separate,

@@ -166,6 +166,16 @@ qsmoe_status check_ws(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t ws_
 
 inline qsmoe_status dev(hipError_t e) { return e == hipSuccess ? QSMOE_OK : QSMOE_ERR_DEVICE; }
 
+// Batches of SMALL_TMAX + 1 .. 2 SMALL_TMAX tokens (verification batches of a few rows) run
+// as two small-batch launches of ceil(T/2) and floor(T/2) tokens: a token's result depends
+// only on its own row, so the split changes the time, not the values. Returns the first
+// part's size, or 0 when the grouped path is taken.
+static int64_t small_split(const Layer &L, int64_t T) {
+    const int64_t T0 = (T + 1) / 2;
+    if (T <= SMALL_TMAX || T > 2 * SMALL_TMAX) return 0;
+    return decode_small_eligible(L, T0) && decode_small_eligible(L, T - T0) ? T0 : 0;
+}
+
 // tokens * hidden must stay addressable with the kernels' 32-bit row offsets
 constexpr int64_t MAX_TOKENS = 1 << 20;
 
@@ -221,6 +231,16 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_small_route(L, (const uint16_t *)x, T, b, topk_idx, topk_w, st));
     }
+    if (const int64_t T0 = small_split(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        const int64_t K = d->top_k;
+        const uint16_t *xx = (const uint16_t *)x;
+        hipError_t e = launch_decode_small_route(L, xx, T0, b, topk_idx, topk_w, st);
+        if (e == hipSuccess)
+            e = launch_decode_small_route(L, xx + T0 * d->hidden, T - T0, b, topk_idx + T0 * K, topk_w + T0 * K, st);
+        return dev(e);
+    }
     size_t n;
     const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
     PrefillBufs b = carve_prefill(d, C, ws, &n);
@@ -259,6 +279,17 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
         size_t n;
         const DecodeBufs b = carve_decode(d, ws, &n);
         return dev(launch_decode_small_layer(L, xx, T, b, y, y_dtype, topk_idx, topk_w, st));
+    }
+    if (const int64_t T0 = small_split(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        const int64_t K = d->top_k, H = d->hidden;
+        void *y1 = (char *)y + (size_t)(T0 * H) * (y_dtype == QSMOE_F32 ? 4 : 2);
+        e = launch_decode_small_layer(L, xx, T0, b, y, y_dtype, topk_idx, topk_w, st);
+        if (e == hipSuccess)
+            e = launch_decode_small_layer(L, xx + T0 * H, T - T0, b, y1, y_dtype, topk_idx ? topk_idx + T0 * K : nullptr,
+                                          topk_w ? topk_w + T0 * K : nullptr, st);
+        return dev(e);
     }
     // chunks of the prefill sequence: every token goes through the same kernels whatever
     // the chunk it falls in, so the result is bit-identical to one unchunked pass

@@ -26,7 +26,7 @@ namespace qs {
 
 namespace {
 
-constexpr int SM_TMAX = 4;
+constexpr int SM_TMAX = SMALL_TMAX;
 constexpr int SM_LCOPIES = 8;
 constexpr int SM_TE = 264;                                  // logit words per token and copy (E + gate)
 constexpr int SM_LSTRIDE = 2 * SM_TMAX * SM_TE + 64;        // u32 per logits copy

@@ -40,6 +40,7 @@ struct DecodeBufs {
 hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
                                int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);
 // T = 2 .. 4 tokens in one launch, the routed experts read once for all of them
+constexpr int SMALL_TMAX = 4;   // tokens of one small-batch decode launch
 bool decode_small_eligible(const Layer &L, int64_t T);
 hipError_t launch_decode_small_layer(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b, void *y,
                                      int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);

@@ -161,17 +161,20 @@ def test_grouped_small_parity(torch, qs, cfg, T):
         oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} T={T}")
 
 
-@pytest.mark.parametrize("cfg,T", [("DECODE", 2), ("DECODE", 3), ("DECODE", 4),
-                                   ("SKEW", 2), ("SKEW", 3), ("SKEW", 4)])
+@pytest.mark.parametrize("cfg,T", [("DECODE", 2), ("DECODE", 3), ("DECODE", 4), ("DECODE", 5), ("DECODE", 8),
+                                   ("SKEW", 2), ("SKEW", 3), ("SKEW", 4), ("SKEW", 6), ("SKEW", 7)])
 def test_small_batch_decode_parity(torch, qs, cfg, T):
-    """Small-batch decode (T = 2..4 in one launch, 4- and 8-bit codes at hidden 2048):
-    every token vs the oracle in both output types; then T copies of one token, which
-    share all their experts (the union is k experts) and must give T identical rows."""
+    """Small-batch decode (T = 2..4 in one launch, 5..8 as two launches of ceil(T/2) and
+    floor(T/2) tokens; 4- and 8-bit codes at hidden 2048): every token vs the oracle in
+    both output types, and the routing of moe_route equal to the layer's; then T copies of
+    one token, which share all their experts and must give T identical rows."""
     L = layer(cfg)
     x_np = syn.make_x(T, L.hidden, seed=100 + T)
     for bf16_out in (False, True):
         y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
         oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} small T={T}")
+    ri, rw = qs.moe_route(qs.LayerDesc.from_host(L), to_dev(x_np, torch))
+    assert (ri.cpu().numpy() == idx).all() and (rw.cpu().numpy() == w).all()
     xd = np.repeat(x_np[:1], T, axis=0)
     y, idx, w = run_layer(torch, qs, L, xd)
     oracle_check(L, xd, y_to_np(y, torch), idx, w, False, f"{cfg} small T={T} repeated token")
