@@ -175,6 +175,10 @@ def test_small_batch_decode_parity(torch, qs, cfg, T):
         oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} small T={T}")
     ri, rw = qs.moe_route(qs.LayerDesc.from_host(L), to_dev(x_np, torch))
     assert (ri.cpu().numpy() == idx).all() and (rw.cpu().numpy() == w).all()
+    if T > 4:                                 # the parts, called on their own, give the same bits
+        y_all = run_layer(torch, qs, L, x_np)[0]
+        for a, b in ((0, (T + 1) // 2), ((T + 1) // 2, T)):
+            assert torch.equal(run_layer(torch, qs, L, x_np[a:b])[0], y_all[a:b]), (T, a, b)
     xd = np.repeat(x_np[:1], T, axis=0)
     y, idx, w = run_layer(torch, qs, L, xd)
     oracle_check(L, xd, y_to_np(y, torch), idx, w, False, f"{cfg} small T={T} repeated token")
