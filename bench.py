@@ -36,6 +36,8 @@ GROUP = 64
 # figure holds only for the kernel sources it was measured on, identified by their
 # sha256; once they change the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/decode_state.h", "csrc/common.h", "csrc/internal.h")
+GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/internal.h")
+PREFILL_TRAFFIC = {"sources_sha256": "a1d683c4130b605d777143281266a3820d5ae4e79a84a41909bb194fcc1f9e12", "bytes": 1002660106}
 DECODE_TRAFFIC = {"sources_sha256": "8886823710cf56d48e32cf7a72c37fe7ab5888a9605d6196767a04915e92ef1d", "bytes": 17974594}
 
 
@@ -65,14 +67,20 @@ def layer_flops(T: int, H: int, I: int, E: int, K: int, shared: bool = True) -> 
     return 2 * T * E * H + 2 * T * (K + (1 if shared else 0)) * 3 * H * I
 
 
-def decode_traffic():
+def measured_traffic(sources, rec):
+    """HBM bytes per launch from the committed counter runs, or None once the kernel's
+    sources differ from the ones the counters were taken on."""
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_sparse_moe_amd")
-    for f in DECODE_SOURCES:
+    for f in sources:
         with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
-    return DECODE_TRAFFIC["bytes"] if h.hexdigest() == DECODE_TRAFFIC["sources_sha256"] else None
+    return rec["bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
+def decode_traffic():
+    return measured_traffic(DECODE_SOURCES, DECODE_TRAFFIC)
 
 
 # ------------------------------------------------------------------------- helpers
@@ -331,7 +339,8 @@ def main(argv=None):
         out["prefill"] = {"tokens_per_s": syn.PREFILL_T / (ms * 1e-3), "ms_per_step": ms, "T": syn.PREFILL_T,
                           "steps": steps,
                           "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFS,
-                                       "unit": "TFLOP/s", "frac": tf / MFMA_F16_PEAK_TFS, "traffic": None,
+                                       "unit": "TFLOP/s", "frac": tf / MFMA_F16_PEAK_TFS,
+                                       "traffic": measured_traffic(GEMM_SOURCES, PREFILL_TRAFFIC),
                                        "flops_per_step": flops}}
     if "skew" in only:
         steps = max(2, args.steps // 400)
