@@ -59,6 +59,7 @@ def lib():
         L.orc_f16_to_double.argtypes = [ctypes.c_uint16]
         L.orc_bf16_to_double.restype = ctypes.c_double
         L.orc_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_f64_to_f16.argtypes = [P, I64, P]
         L.orc_dequant_matrix.argtypes = [P, I32, I64, I64, I64, P]
         L.orc_router_logits.argtypes = [P, P, I64, P]
         L.orc_route.argtypes = [P, P, I64, P, P, P]
@@ -269,6 +270,15 @@ def q8_gemv_q8x(rows: np.ndarray, N: int, K: int, xq: np.ndarray, xd: np.ndarray
 
 def f16_to_double(h: int) -> float:
     return lib().orc_f16_to_double(int(h))
+
+
+def f64_to_f16(v: np.ndarray) -> np.ndarray:
+    """The oracle's binary64 -> binary16 encoder (used by its Q8_0 quantizers) over an
+    array; returns the uint16 bit patterns."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().orc_f64_to_f16(_p(v), v.size, _p(out))
+    return out
 
 
 def bf16_to_double(b: int) -> float:

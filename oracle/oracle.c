@@ -77,7 +77,7 @@ double orc_bf16_to_double(uint16_t b)
 static uint16_t double_to_f16(double v)
 {
     uint16_t sign = 0;
-    if (v < 0) { sign = 0x8000; v = -v; }
+    if (signbit(v)) { sign = 0x8000; v = -v; }   /* -0.0 keeps its sign, as IEEE 754 conversion does */
     if (v == 0) return sign;
     if (v >= 65520.0) return sign | 0x7c00;
     int e;
@@ -98,6 +98,12 @@ static uint16_t double_to_f16(double v)
     expo = e - 1;
     uint16_t frac = (uint16_t)((rv / ldexp(1.0, expo) - 1.0) * 1024.0);
     return sign | (uint16_t)((expo + 15) << 10) | frac;
+}
+
+/* the encoder above over an array: the fp16 bit patterns of v[0..n) */
+void orc_f64_to_f16(const double *v, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = double_to_f16(v[i]);
 }
 
 /* ------------------------------------------------------------ affine dequantize */

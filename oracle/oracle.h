@@ -54,6 +54,8 @@ typedef struct {
 /* decoders of the 16-bit formats */
 double orc_f16_to_double(uint16_t h);
 double orc_bf16_to_double(uint16_t b);
+/* binary64 -> binary16 bit patterns, round to nearest, ties to even; overflow to inf */
+void orc_f64_to_f16(const double *v, int64_t n, uint16_t *out);
 
 /* W[r, c] of matrix `e` of `m` (rows x cols), fp64.  out is [rows][cols]. */
 void orc_dequant_matrix(const orc_qmat *m, int32_t bits, int64_t e, int64_t rows,

@@ -41,6 +41,10 @@ MUTATIONS = [
      "double s = orc_f16_to_double(m->scales[gi]);"),
     ("shared gate sign", "gs = 1.0 / (1.0 + exp(-z));", "gs = 1.0 / (1.0 + exp(z));"),
     ("shared gate ignored", "yt[c] += gs * o[c];", "yt[c] += o[c];"),
+    ("fp16 encoder ties away from zero", "if (rem > 0.5 || (rem == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
+     "if (rem >= 0.5) r += 1.0;"),
+    ("fp16 encoder truncates", "if (rem > 0.5 || (rem == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;", ""),
+    ("fp16 encoder subnormal step", "if (expo < -14) expo = -14;", "if (expo < -15) expo = -15;"),
 ]
 
 

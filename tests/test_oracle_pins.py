@@ -110,6 +110,31 @@ def test_f16_decoder_all_patterns(orc):
     assert orc.f16_to_double(0xC000) == -2.0
 
 
+def test_f16_encoder_matches_numpy(orc):
+    """The oracle's binary64 -> binary16 encoder (it writes the Q8_0 scales) against
+    numpy's own conversion, which rounds a double to the nearest half directly, ties to
+    even: 1e5 random doubles over the whole half range (normal, subnormal, overflow),
+    then every kind of exact halfway point between neighbouring halves and the doubles
+    just beside them, where a wrong tie rule or a double rounding would show."""
+    rng = np.random.default_rng(7)
+    mag = np.exp2(rng.uniform(-27.0, 17.0, 100_000)) * rng.choice([-1.0, 1.0], 100_000)
+    with np.errstate(over="ignore"):
+        ref = mag.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.f64_to_f16(mag), ref)
+    # halfway points: between half h and its successor (all finite non-negative halves)
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2                                    # exact in binary64
+    for v in (mid, np.nextafter(mid, 0.0), np.nextafter(mid, np.inf), -mid):
+        assert np.array_equal(orc.f64_to_f16(v), v.astype(np.float16).view(np.uint16))
+    even = np.where(h % 2 == 0, h, h + 1).astype(np.uint16)
+    assert np.array_equal(orc.f64_to_f16(mid), even)       # ties to the even pattern
+    # the largest half, the overflow threshold (65520 = 65504 + half an ulp) and zero signs
+    edge = np.array([65504.0, 65519.99, 65520.0, 1e9, 0.0, -0.0, 2.0 ** -25, 2.0 ** -24 * 1.5])
+    assert orc.f64_to_f16(edge).tolist() == [0x7BFF, 0x7BFF, 0x7C00, 0x7C00, 0x0000, 0x8000, 0x0000, 0x0002]
+
+
 def test_bf16_decoder_all_patterns(orc):
     bits = np.arange(0, 65536, 5, dtype=np.uint32).astype(np.uint16)
     ref = np_bf16(bits)
