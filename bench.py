@@ -162,7 +162,7 @@ def bench_decode(qs, torch, syn, steps, warmup, copies=40, **variant):
     descs = _dev_layer_copies(qs, torch, L, copies)
     xs = [torch.from_numpy(syn.make_x(1, L.hidden, seed=100 + l).view(np.int16)).cuda() for l in range(copies)]
     ys = [torch.empty((1, L.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
-    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qs.moe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
 
     def step(i):
         l = i % copies
@@ -185,7 +185,7 @@ def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 5, 8), copies=40):
         xs = [torch.from_numpy(syn.make_x(T, L.hidden, seed=1000 * T + l).view(np.int16)).cuda()
               for l in range(copies)]
         ys = [torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
-        ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(qs.moe_workspace_size(descs[0], T), dtype=torch.uint8, device="cuda")
         union = []
         for l in range(copies):
             idx, _ = qs.moe_route(descs[l], xs[l], workspace=ws)
@@ -213,7 +213,7 @@ def bench_prefill(qs, torch, syn, cfg, T, steps, warmup, copies):
     y = torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda")
     # a workspace for the whole T, so that the call runs unchunked (one pass over the
     # expert weights); with the default size a long prompt runs in 4096-token chunks
-    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], T, chunk=T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qs.moe_workspace_size(descs[0], T, chunk=T), dtype=torch.uint8, device="cuda")
 
     def step(i):
         qs.moe_layer_forward(descs[i % copies], x, y=y, workspace=ws)

@@ -44,19 +44,26 @@
 extern "C" {
 #endif
 
-#define QSMOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
-typedef int32_t qsmoe_status;
-#define QSMOE_OK               0
-#define QSMOE_ERR_INVALID     -1   /* NULL / misaligned pointer, negative size, bad enum   */
-#define QSMOE_ERR_UNSUPPORTED -2   /* shape or format outside the supported limits         */
-#define QSMOE_ERR_WORKSPACE   -3   /* workspace NULL or smaller than qsmoe_workspace_size  */
-#define QSMOE_ERR_DEVICE      -4   /* a HIP launch failed (hipGetLastError)                */
+typedef int32_t moe_status;
+#define MOE_OK               0
+#define MOE_ERR_INVALID     -1   /* NULL / misaligned pointer, negative size, bad enum   */
+#define MOE_ERR_UNSUPPORTED -2   /* shape or format outside the supported limits         */
+#define MOE_ERR_WORKSPACE   -3   /* workspace NULL, misaligned or too small              */
+#define MOE_ERR_DEVICE      -4   /* a HIP launch failed (hipGetLastError)                */
+
+/* Bits of the workspace error word (read with moe_workspace_status).  Every wait of one
+ * workgroup for another inside a launch is bounded; a wait that gives up sets its bit and
+ * lets the kernel finish, so the grid always drains, and that call's outputs are not to be
+ * trusted.  A correct call on a device that runs the whole grid sets no bit. */
+#define MOE_WS_ERR_DECODE_WAIT 1u   /* a one-launch decode kernel (T <= 8) gave up a wait  */
+#define MOE_WS_ERR_GEMM_WAIT   2u   /* a grouped-GEMM down tile gave up waiting for its h  */
 
 /* element types */
-#define QSMOE_BF16 0
-#define QSMOE_F16  1
-#define QSMOE_F32  2
+#define MOE_BF16 0
+#define MOE_F16  1
+#define MOE_F32  2
 
 /*
  * A stack of affine-quantized matrices, each [rows][cols], quantized in groups of
@@ -79,7 +86,7 @@ typedef struct {
     const void *scales;
     const void *biases;
     int64_t     mat_stride;
-} qsmoe_qmat;
+} moe_qmat;
 
 /*
  * One MoE FFN layer ([LILY] "Qwen creates three distinct workload shapes").
@@ -89,58 +96,72 @@ typedef struct {
  *   has_shared   1: the shared expert (s_gate, s_up [inter][hidden], s_down
  *                [hidden][inter], one matrix each) processes every token with weight 1
  *                (or, with shared_gate_w, with weight sigmoid(shared_gate_w . x))
- *   scale_dtype  QSMOE_F16 or QSMOE_BF16: the format of every qmat's scales and biases
+ *   scale_dtype  MOE_F16 or MOE_BF16: the format of every qmat's scales and biases
  *                (bf16 is the checkpoint format the pages print)
  *   shared_gate_w  [hidden] bf16 (16-byte aligned) or NULL; needs has_shared
- * Limits (else QSMOE_ERR_UNSUPPORTED): group == 64; bits in {4, 8};
+ * Limits (else MOE_ERR_UNSUPPORTED): group == 64; bits in {4, 8};
  *   1 <= n_experts <= 256; 1 <= top_k <= min(n_experts, 16);
- *   hidden % 128 == 0, 128 <= hidden <= 8192; inter % 128 == 0, 128 <= inter <= 2048;
- *   (top_k + 1) * inter <= 24576 (the decode down kernel keeps every h in LDS).
- * Every qmat needs mat_stride >= its rows (QSMOE_ERR_INVALID otherwise).
+ *   hidden % 64 == 0, 64 <= hidden <= 8192; inter % 64 == 0, 64 <= inter <= 2048;
+ *   (top_k + 1) * inter <= 24576 (the batch-1 kernel hands every h value of a call
+ *   between workgroups through a fixed region of the workspace).
+ * Every qmat needs mat_stride >= its rows (MOE_ERR_INVALID otherwise).
  */
 typedef struct {
     int32_t hidden, inter, n_experts, top_k, bits, group;
     int32_t scale_dtype;
     const void  *router_w;
     const float *router_bias;
-    qsmoe_qmat gate, up, down;
+    moe_qmat gate, up, down;
     int32_t    has_shared;
-    qsmoe_qmat s_gate, s_up, s_down;
+    moe_qmat s_gate, s_up, s_down;
     const void *shared_gate_w;
-} qsmoe_layer_desc;
+} moe_layer_desc;
 
-int          qsmoe_abi_version(void);
-const char  *qsmoe_status_string(qsmoe_status s);   /* static string, never NULL */
+int          moe_abi_version(void);                 /* MOE_ABI_VERSION of the library */
+const char  *moe_status_string(moe_status s);   /* static string, never NULL */
 
 /*
  * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
  * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
- * 256-byte aligned.  Its first 1 MiB holds the state of the T = 1 path (a call
- * counter, completion counters, and tagged words the workgroups of one call hand to
- * each other): it must be zero before the first call that uses the workspace (e.g.
- * allocate it zero-filled) and then belongs to the library; a caller that writes it
- * must zero it again before the next call.  The rest is scratch whose contents are
- * undefined between calls.  Calls that share one workspace must not overlap in time
- * (issue them on one stream).  T >= 2 is processed in chunks inside one call
- * ([LILY] "Reduce intermediate and state traffic": bounded intermediate buffers): this
- * size is for chunks of QSMOE_PREFILL_CHUNK tokens, so it stops growing there (~200 MiB
- * for any T >= 4096 at hidden 2048, inter 512, top-8).
+ * 256-byte aligned.  Its first 1 MiB is the state of the one-launch decode kernels
+ * (T <= 8): a call counter, completion counters, tagged words the workgroups of one call
+ * hand to each other, and the error word.  It must be zero before the first call that
+ * uses the workspace (allocate it zero-filled) and then belongs to the library: every
+ * call leaves it ready for the next one, so no clearing launch is needed per call
+ * ([EMBER] "packed Q8 decode": one reusable decode workspace instead of per-layer
+ * temporaries).  A caller that writes it must zero it again before the next call.  The
+ * rest is scratch whose contents are undefined between calls.  Calls that share one
+ * workspace must not overlap in time (issue them on one stream).  T >= 2 is processed in
+ * chunks inside one call ([LILY] "Reduce intermediate and state traffic": bounded
+ * intermediate buffers): this size is for chunks of MOE_PREFILL_CHUNK tokens, so it stops
+ * growing there (~200 MiB for any T >= 4096 at hidden 2048, inter 512, top-8).
  */
-size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T);
+size_t moe_workspace_size(const moe_layer_desc *d, int64_t T);
 
 /* Default tokens per prefill chunk (T >= 2). */
-#define QSMOE_PREFILL_CHUNK 4096
+#define MOE_PREFILL_CHUNK 4096
 
 /*
  * Bytes of workspace for T tokens run in chunks of `chunk` tokens (0: the default
- * QSMOE_PREFILL_CHUNK; chunk >= T: unchunked).  moe_route / moe_layer_forward take the
- * largest chunk whose buffers fit in the ws_bytes they are given (at least the default),
- * so a caller that can spare the memory avoids re-reading the expert weights once per
- * chunk.  Chunking changes no result: every token is computed by the same kernels
- * whatever chunk it falls in, bit for bit.  SIZE_MAX for an invalid descriptor, T or
- * chunk < 0.
+ * MOE_PREFILL_CHUNK; chunk >= T: unchunked; 1 counts as 2).  moe_route /
+ * moe_layer_forward accept any workspace at least as large as the chunk-2 size and take
+ * the largest chunk whose buffers fit in the ws_bytes they are given, so a caller that can
+ * spare the memory avoids re-reading the expert weights once per chunk, and one short of
+ * memory can bound it.  Chunking changes no result: every token is computed by the same
+ * kernels whatever chunk it falls in, bit for bit.  SIZE_MAX for an invalid descriptor,
+ * T > 2^20 or chunk < 0.
  */
-size_t qsmoe_workspace_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk);
+size_t moe_workspace_size_chunked(const moe_layer_desc *d, int64_t T, int64_t chunk);
+
+/*
+ * Enqueues on `stream` a copy of the workspace's error word (MOE_WS_ERR_* bits, 0 when
+ * every call so far completed every wait) into *status_out, a device uint32, and, when
+ * `clear` is nonzero, resets the word to 0 afterwards.  ws must be a workspace of
+ * ws_bytes >= 1 MiB used by moe_route / moe_layer_forward (or freshly zeroed); the call
+ * is ordered with the layer calls on the same stream.
+ */
+moe_status moe_workspace_status(void *ws, size_t ws_bytes, uint32_t *status_out, int32_t clear,
+                                void *stream);
 
 /*
  * Router only ([LILY] "Qwen creates three distinct workload shapes"): fp32 logits
@@ -150,10 +171,10 @@ size_t qsmoe_workspace_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_
  *   x        [T][hidden] bf16
  *   topk_idx [T][top_k] int32, ascending expert id within a token (written)
  *   topk_w   [T][top_k] fp32, aligned with topk_idx (written)
- *   ws       device workspace of ws_bytes >= qsmoe_workspace_size(d, T)
- * T == 0 returns QSMOE_OK and enqueues nothing; T > 2^20 is QSMOE_ERR_UNSUPPORTED.
+ *   ws       device workspace of ws_bytes >= moe_workspace_size(d, T)
+ * T == 0 returns MOE_OK and enqueues nothing; T > 2^20 is MOE_ERR_UNSUPPORTED.
  */
-qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T,
+moe_status moe_route(const moe_layer_desc *d, const void *x, int64_t T,
                        int32_t *topk_idx, float *topk_w,
                        void *ws, size_t ws_bytes, void *stream);
 
@@ -165,18 +186,18 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T,
  * accumulated in fp32 in that fixed order ([LILY] "Reduce intermediate and state
  * traffic"; [OMLX] "Fusion principle").
  *   x        [T][hidden] bf16, |x| < 65504 (activations are consumed as fp16)
- *   y        [T][hidden], y_dtype QSMOE_BF16 (round-to-nearest-even) or QSMOE_F32
+ *   y        [T][hidden], y_dtype MOE_BF16 (round-to-nearest-even) or MOE_F32
  *   topk_idx, topk_w  optional outputs as in moe_route (NULL to skip)
  * Path: T == 1 runs the batch-1 decode kernel (register dequantization on the vector
  * ALUs, fp32 intermediates); T = 2 .. 4 the same kernel design over all tokens at once,
- * each expert any token selected read once (when (top_k + 1) * inter * T <= 49216);
+ * each expert any token selected read once (when T * (top_k + 1) * inter <= 98496);
  * T = 5 .. 8 two such launches of ceil(T/2) and floor(T/2) tokens (when both fit);
  * larger T runs the grouped-GEMM path (MFMA on fp16 operands dequantized in registers,
  * fp32 accumulation, fp16 intermediates).
  * For a given T the result does not depend on whether gate/up are fused or separate,
  * nor on the other tokens of the call (tokens are independent), bit for bit.
  */
-qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t T,
+moe_status moe_layer_forward(const moe_layer_desc *d, const void *x, int64_t T,
                                void *y, int32_t y_dtype,
                                int32_t *topk_idx, float *topk_w,
                                void *ws, size_t ws_bytes, void *stream);
@@ -189,10 +210,10 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
  *            rows 16p..16p+15, columns 32b..32b+31): eight 64-byte groups, group j =
  *            rows 0..15 x codes 4j..4j+3 (4 bytes per row, rows in order), then the
  *            16 fp16 scales in row order.  16-byte aligned.
- *   x        [K] bf16;  y  [N], y_dtype QSMOE_BF16 or QSMOE_F32
- * Limits: N % 16 == 0, K % 32 == 0, N >= 16, 32 <= K <= 8192 (else QSMOE_ERR_UNSUPPORTED).
+ *   x        [K] bf16;  y  [N], y_dtype MOE_BF16 or MOE_F32
+ * Limits: N % 16 == 0, K % 32 == 0, N >= 16, 32 <= K <= 8192 (else MOE_ERR_UNSUPPORTED).
  */
-qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x,
+moe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x,
                      void *y, int32_t y_dtype, void *stream);
 
 /*
@@ -204,18 +225,18 @@ qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x,
  *             clamped to [-127, 127]; an all-zero block has d = 0 and q = 0
  *   x   [K] bf16 (2-byte aligned);  xq [K] int8 (4-byte aligned);  xd [K/32] fp16
  *       (2-byte aligned); all device memory, xq / xd written, owned by the caller.
- * Limits: K % 32 == 0, K <= 8192 (else QSMOE_ERR_UNSUPPORTED); K = 0 enqueues nothing.
+ * Limits: K % 32 == 0, K <= 8192 (else MOE_ERR_UNSUPPORTED); K = 0 enqueues nothing.
  */
-qsmoe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream);
+moe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream);
 
 /*
  * Dense Q8_0 GEMV with a quantized activation (from q8_quantize_x):
  *     y[n] = sum_b d[n][b] * xd[b] * sum_{c<32} q[n][32b + c] * xq[32b + c]
  * the inner sums exact in int32 (v_dot4_i32_i8), the scaling and the sum over b in fp32.
  *   w_tiles  as for q8_gemv;  xq [K] int8 (4-byte aligned), xd [K/32] fp16;
- *   y [N], y_dtype QSMOE_BF16 or QSMOE_F32.  Limits as for q8_gemv.
+ *   y [N], y_dtype MOE_BF16 or MOE_F32.  Limits as for q8_gemv.
  */
-qsmoe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd,
+moe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd,
                          void *y, int32_t y_dtype, void *stream);
 
 /*
@@ -223,7 +244,7 @@ qsmoe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *
  * with q8_quantize_x's rule (identical codes and scales, so identical y) while staging
  * it: no separate launch and no codes in memory.  Limits as for q8_gemv.
  */
-qsmoe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
+moe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
                         int32_t y_dtype, void *stream);
 
 /*
@@ -232,7 +253,7 @@ qsmoe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x
  * Pure byte moves, idempotent; w_rows and w_tiles must not overlap.
  * Limits: N % 16 == 0, K % 32 == 0.
  */
-qsmoe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles,
+moe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles,
                             void *stream);
 
 #ifdef __cplusplus

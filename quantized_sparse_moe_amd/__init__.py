@@ -5,8 +5,8 @@ Argument marshalling only: every step of the layer runs in the HIP kernels of
 device memory and the current stream; outputs and workspaces the caller does not pass
 are allocated here with torch.  The functions carry the names of the C entry points:
 
-    qsmoe_workspace_size, moe_route, moe_layer_forward, q8_gemv, q8_quantize_x,
-    q8_gemv_q8x, q8_gemv_qx, q8_pack_rows16
+    moe_workspace_size, moe_workspace_status, moe_route, moe_layer_forward, q8_gemv,
+    q8_quantize_x, q8_gemv_q8x, q8_gemv_qx, q8_pack_rows16
 
 There is no fallback: if the shared library is missing, loading raises.
 Build it with ``python -m quantized_sparse_moe_amd.build``.
@@ -20,8 +20,9 @@ from typing import Optional, Tuple
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsmoe.so")
 
-QSMOE_OK, QSMOE_ERR_INVALID, QSMOE_ERR_UNSUPPORTED, QSMOE_ERR_WORKSPACE, QSMOE_ERR_DEVICE = 0, -1, -2, -3, -4
-QSMOE_BF16, QSMOE_F16, QSMOE_F32 = 0, 1, 2
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = 0, -1, -2, -3, -4
+MOE_BF16, MOE_F16, MOE_F32 = 0, 1, 2
+MOE_WS_ERR_DECODE_WAIT, MOE_WS_ERR_GEMM_WAIT = 1, 2      # bits of the workspace error word
 
 _lib = None
 
@@ -32,25 +33,25 @@ class QsmoeError(RuntimeError):
         super().__init__(f"{where}: {status_string(status)} (status {status})")
 
 
-class qsmoe_qmat(ctypes.Structure):
+class moe_qmat(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("biases", ctypes.c_void_p), ("mat_stride", ctypes.c_int64)]
 
 
-class qsmoe_layer_desc(ctypes.Structure):
+class moe_layer_desc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("scale_dtype", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
-                ("gate", qsmoe_qmat), ("up", qsmoe_qmat), ("down", qsmoe_qmat),
+                ("gate", moe_qmat), ("up", moe_qmat), ("down", moe_qmat),
                 ("has_shared", ctypes.c_int32),
-                ("s_gate", qsmoe_qmat), ("s_up", qsmoe_qmat), ("s_down", qsmoe_qmat),
+                ("s_gate", moe_qmat), ("s_up", moe_qmat), ("s_down", moe_qmat),
                 ("shared_gate_w", ctypes.c_void_p)]
 
 
-EXPORTS = ("qsmoe_abi_version", "qsmoe_status_string", "qsmoe_workspace_size",
-           "qsmoe_workspace_size_chunked", "moe_route",
+EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size",
+           "moe_workspace_size_chunked", "moe_workspace_status", "moe_route",
            "moe_layer_forward", "q8_gemv", "q8_quantize_x", "q8_gemv_q8x", "q8_gemv_qx",
            "q8_pack_rows16")
 
@@ -64,14 +65,16 @@ def lib() -> ctypes.CDLL:
                               "`python -m quantized_sparse_moe_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-        L.qsmoe_abi_version.restype = ctypes.c_int
-        L.qsmoe_abi_version.argtypes = []
-        L.qsmoe_status_string.restype = ctypes.c_char_p
-        L.qsmoe_status_string.argtypes = [I32]
-        L.qsmoe_workspace_size.restype = SZ
-        L.qsmoe_workspace_size.argtypes = [P, I64]
-        L.qsmoe_workspace_size_chunked.restype = SZ
-        L.qsmoe_workspace_size_chunked.argtypes = [P, I64, I64]
+        L.moe_abi_version.restype = ctypes.c_int
+        L.moe_abi_version.argtypes = []
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [I32]
+        L.moe_workspace_size.restype = SZ
+        L.moe_workspace_size.argtypes = [P, I64]
+        L.moe_workspace_size_chunked.restype = SZ
+        L.moe_workspace_size_chunked.argtypes = [P, I64, I64]
+        L.moe_workspace_status.restype = I32
+        L.moe_workspace_status.argtypes = [P, SZ, P, I32, P]
         L.moe_route.restype = I32
         L.moe_route.argtypes = [P, P, I64, P, P, P, SZ, P]
         L.moe_layer_forward.restype = I32
@@ -91,15 +94,15 @@ def lib() -> ctypes.CDLL:
 
 
 def status_string(status: int) -> str:
-    return lib().qsmoe_status_string(int(status)).decode()
+    return lib().moe_status_string(int(status)).decode()
 
 
 def abi_version() -> int:
-    return lib().qsmoe_abi_version()
+    return lib().moe_abi_version()
 
 
 def _check(status: int, where: str) -> None:
-    if status != QSMOE_OK:
+    if status != MOE_OK:
         raise QsmoeError(status, where)
 
 
@@ -114,9 +117,23 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _alloc_stream(stream):
+    """The stream that buffers allocated here for a call on `stream` belong to.
+
+    torch's caching allocator hands a freed block only to later work on the stream it was
+    allocated on, and torch.zeros fills on the current stream: allocating under the call's
+    own stream orders the fill before the kernel and keeps the block from being reused
+    while the kernel may still run.  A raw stream handle cannot be told to torch, so a
+    call on one must pass every buffer itself."""
+    import torch
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        return stream or torch.cuda.current_stream()
+    raise QsmoeError(MOE_ERR_INVALID, "a raw stream handle needs caller-provided outputs and workspace")
+
+
 # ---------------------------------------------------------------- layer descriptor
 class LayerDesc:
-    """A ``qsmoe_layer_desc`` plus the device tensors it points into.
+    """A ``moe_layer_desc`` plus the device tensors it points into.
 
     ``gate``, ``up``, ``down`` (and ``s_gate``, ``s_up``, ``s_down`` for the shared
     expert) are ``(codes, scales, biases, mat_stride, row0)`` tuples of device tensors:
@@ -124,10 +141,10 @@ class LayerDesc:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, bits, router_w, gate, up, down,
-                 router_bias=None, shared=None, scale_dtype=QSMOE_F16, shared_gate_w=None):
+                 router_bias=None, shared=None, scale_dtype=MOE_F16, shared_gate_w=None):
         self.hidden, self.inter, self.n_experts, self.top_k, self.bits = hidden, inter, n_experts, top_k, bits
         self._keep = [router_w, router_bias, gate, up, down, shared, shared_gate_w]
-        d = qsmoe_layer_desc()
+        d = moe_layer_desc()
         d.hidden, d.inter, d.n_experts, d.top_k, d.bits, d.group = hidden, inter, n_experts, top_k, bits, 64
         d.scale_dtype = scale_dtype
         d.shared_gate_w = None if shared_gate_w is None else shared_gate_w.data_ptr()
@@ -141,11 +158,11 @@ class LayerDesc:
                                           self._qmat(shared[2], inter))
         self.desc = d
 
-    def _qmat(self, m, cols: int) -> qsmoe_qmat:
+    def _qmat(self, m, cols: int) -> moe_qmat:
         codes, scales, biases, stride, row0 = m
         rb = cols * self.bits // 8
         ng = cols // 64
-        return qsmoe_qmat(codes.data_ptr() + row0 * rb, scales.data_ptr() + row0 * ng * 2,
+        return moe_qmat(codes.data_ptr() + row0 * rb, scales.data_ptr() + row0 * ng * 2,
                           biases.data_ptr() + row0 * ng * 2, stride)
 
     @property
@@ -190,34 +207,56 @@ class LayerDesc:
         sgw = getattr(layer, "shared_gate_w", None)
         return cls(layer.hidden, I, layer.n_experts, layer.top_k, layer.bits, dev(layer.router_w),
                    g, u, dn, router_bias=rb, shared=shared,
-                   scale_dtype=QSMOE_BF16 if getattr(layer, "scale_dtype", "f16") == "bf16" else QSMOE_F16,
+                   scale_dtype=MOE_BF16 if getattr(layer, "scale_dtype", "f16") == "bf16" else MOE_F16,
                    shared_gate_w=None if sgw is None else dev(sgw))
 
 
 # ------------------------------------------------------------------- entry points
-# tokens per prefill chunk inside one call (QSMOE_PREFILL_CHUNK in include/qsmoe.h)
+# tokens per prefill chunk inside one call (MOE_PREFILL_CHUNK in include/qsmoe.h)
 PREFILL_CHUNK = 4096
 
 
-def qsmoe_workspace_size(desc: LayerDesc, T: int, chunk: Optional[int] = None) -> int:
+def moe_workspace_size(desc: LayerDesc, T: int, chunk: Optional[int] = None) -> int:
     """Workspace bytes for T tokens; `chunk` (tokens per prefill chunk, T for none) as in
-    qsmoe_workspace_size_chunked, default QSMOE_PREFILL_CHUNK."""
+    moe_workspace_size_chunked, default MOE_PREFILL_CHUNK."""
     if chunk is None:
-        n = lib().qsmoe_workspace_size(desc.ptr, int(T))
+        n = lib().moe_workspace_size(desc.ptr, int(T))
     else:
-        n = lib().qsmoe_workspace_size_chunked(desc.ptr, int(T), int(chunk))
+        n = lib().moe_workspace_size_chunked(desc.ptr, int(T), int(chunk))
     if n == ctypes.c_size_t(-1).value:
-        raise QsmoeError(QSMOE_ERR_UNSUPPORTED, "qsmoe_workspace_size")
+        raise QsmoeError(MOE_ERR_UNSUPPORTED, "moe_workspace_size")
     return n
 
 
-def _workspace(desc: LayerDesc, T: int, workspace, device):
+def new_workspace(desc: LayerDesc, T: int, chunk: Optional[int] = None, device="cuda", stream=None):
+    """A zero-filled workspace for T tokens, allocated and filled on `stream`."""
     import torch
-    n = qsmoe_workspace_size(desc, T)
+    with torch.cuda.stream(_alloc_stream(stream)):
+        return torch.zeros(max(moe_workspace_size(desc, T, chunk), 256), dtype=torch.uint8, device=device)
+
+
+def _workspace(desc: LayerDesc, T: int, workspace, device, stream):
     if workspace is None:
         # zero-filled: the start of the workspace holds decode state that must begin at zero
-        workspace = torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+        workspace = new_workspace(desc, T, device=device, stream=stream)
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _empty(shape, dtype, device, stream):
+    import torch
+    with torch.cuda.stream(_alloc_stream(stream)):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def moe_workspace_status(workspace, clear: bool = False, out=None, stream=None):
+    """Enqueue a read of the workspace's error word (MOE_WS_ERR_* bits); returns a device
+    uint32 tensor [1] (int32 view) that holds it once the stream reaches the read."""
+    import torch
+    if out is None:
+        out = _empty((1,), torch.int32, workspace.device, stream)
+    _check(lib().moe_workspace_status(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _ptr(out), 1 if clear else 0, _stream(stream)), "moe_workspace_status")
+    return out
 
 
 def moe_route(desc: LayerDesc, x, topk_idx=None, topk_w=None, workspace=None,
@@ -226,10 +265,10 @@ def moe_route(desc: LayerDesc, x, topk_idx=None, topk_w=None, workspace=None,
     import torch
     T = x.shape[0]
     if topk_idx is None:
-        topk_idx = torch.empty((T, desc.top_k), dtype=torch.int32, device=x.device)
+        topk_idx = _empty((T, desc.top_k), torch.int32, x.device, stream)
     if topk_w is None:
-        topk_w = torch.empty((T, desc.top_k), dtype=torch.float32, device=x.device)
-    ws, nbytes = _workspace(desc, T, workspace, x.device)
+        topk_w = _empty((T, desc.top_k), torch.float32, x.device, stream)
+    ws, nbytes = _workspace(desc, T, workspace, x.device, stream)
     _check(lib().moe_route(desc.ptr, _ptr(x), T, _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes,
                            _stream(stream)), "moe_route")
     return topk_idx, topk_w
@@ -241,25 +280,31 @@ def moe_layer_forward(desc: LayerDesc, x, y=None, y_dtype=None, topk_idx=None, t
     import torch
     T = x.shape[0]
     if y is None:
-        y = torch.empty((T, desc.hidden), dtype=y_dtype or torch.float32, device=x.device)
-    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
+        y = _empty((T, desc.hidden), y_dtype or torch.float32, x.device, stream)
+    code = MOE_F32 if y.dtype == torch.float32 else MOE_BF16 if y.dtype == torch.bfloat16 else None
     if code is None:
-        raise QsmoeError(QSMOE_ERR_INVALID, "moe_layer_forward: y must be float32 or bfloat16")
-    ws, nbytes = _workspace(desc, T, workspace, x.device)
+        raise QsmoeError(MOE_ERR_INVALID, "moe_layer_forward: y must be float32 or bfloat16")
+    ws, nbytes = _workspace(desc, T, workspace, x.device, stream)
     _check(lib().moe_layer_forward(desc.ptr, _ptr(x), T, _ptr(y), code, _ptr(topk_idx), _ptr(topk_w),
                                    _ptr(ws), nbytes, _stream(stream)), "moe_layer_forward")
     return y
+
+
+def _out_code(y, where):
+    import torch
+    code = MOE_F32 if y.dtype == torch.float32 else MOE_BF16 if y.dtype == torch.bfloat16 else None
+    if code is None:
+        raise QsmoeError(MOE_ERR_INVALID, f"{where}: y must be float32 or bfloat16")
+    return code
 
 
 def q8_gemv(w_tiles, N: int, K: int, x, y=None, y_dtype=None, stream=None):
     """Dense Q8_0 GEMV over 16-row packed tiles; returns ``y`` [N] (fp32 or bf16)."""
     import torch
     if y is None:
-        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=x.device)
-    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
-    if code is None:
-        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv: y must be float32 or bfloat16")
-    _check(lib().q8_gemv(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), code, _stream(stream)), "q8_gemv")
+        y = _empty((N,), y_dtype or torch.float32, x.device, stream)
+    _check(lib().q8_gemv(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), _out_code(y, "q8_gemv"), _stream(stream)),
+           "q8_gemv")
     return y
 
 
@@ -269,9 +314,9 @@ def q8_quantize_x(x, K: int = None, xq=None, xd=None, stream=None):
     import torch
     K = x.numel() if K is None else K
     if xq is None:
-        xq = torch.empty((K,), dtype=torch.int8, device=x.device)
+        xq = _empty((K,), torch.int8, x.device, stream)
     if xd is None:
-        xd = torch.empty((K // 32,), dtype=torch.int16, device=x.device)
+        xd = _empty((K // 32,), torch.int16, x.device, stream)
     _check(lib().q8_quantize_x(_ptr(x), K, _ptr(xq), _ptr(xd), _stream(stream)), "q8_quantize_x")
     return xq, xd
 
@@ -280,12 +325,9 @@ def q8_gemv_q8x(w_tiles, N: int, K: int, xq, xd, y=None, y_dtype=None, stream=No
     """Dense Q8_0 GEMV with a quantized activation (``q8_quantize_x``); returns ``y`` [N]."""
     import torch
     if y is None:
-        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=xq.device)
-    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
-    if code is None:
-        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv_q8x: y must be float32 or bfloat16")
-    _check(lib().q8_gemv_q8x(_ptr(w_tiles), N, K, _ptr(xq), _ptr(xd), _ptr(y), code, _stream(stream)),
-           "q8_gemv_q8x")
+        y = _empty((N,), y_dtype or torch.float32, xq.device, stream)
+    _check(lib().q8_gemv_q8x(_ptr(w_tiles), N, K, _ptr(xq), _ptr(xd), _ptr(y), _out_code(y, "q8_gemv_q8x"),
+                             _stream(stream)), "q8_gemv_q8x")
     return y
 
 
@@ -293,11 +335,9 @@ def q8_gemv_qx(w_tiles, N: int, K: int, x, y=None, y_dtype=None, stream=None):
     """Dense Q8_0 GEMV quantizing ``x`` (bf16) inside the kernel; returns ``y`` [N]."""
     import torch
     if y is None:
-        y = torch.empty((N,), dtype=y_dtype or torch.float32, device=x.device)
-    code = QSMOE_F32 if y.dtype == torch.float32 else QSMOE_BF16 if y.dtype == torch.bfloat16 else None
-    if code is None:
-        raise QsmoeError(QSMOE_ERR_INVALID, "q8_gemv_qx: y must be float32 or bfloat16")
-    _check(lib().q8_gemv_qx(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), code, _stream(stream)), "q8_gemv_qx")
+        y = _empty((N,), y_dtype or torch.float32, x.device, stream)
+    _check(lib().q8_gemv_qx(_ptr(w_tiles), N, K, _ptr(x), _ptr(y), _out_code(y, "q8_gemv_qx"), _stream(stream)),
+           "q8_gemv_qx")
     return y
 
 
@@ -305,6 +345,6 @@ def q8_pack_rows16(w_rows, N: int, K: int, w_tiles=None, stream=None):
     """Row-contiguous Q8_0 blocks -> 16-row packed tiles (load-time, on the device)."""
     import torch
     if w_tiles is None:
-        w_tiles = torch.empty((N // 16 * (K // 32) * 544,), dtype=torch.uint8, device=w_rows.device)
+        w_tiles = _empty((N // 16 * (K // 32) * 544,), torch.uint8, w_rows.device, stream)
     _check(lib().q8_pack_rows16(_ptr(w_rows), N, K, _ptr(w_tiles), _stream(stream)), "q8_pack_rows16")
     return w_tiles

@@ -24,28 +24,28 @@ inline size_t up(size_t n) { return (n + ALIGN - 1) / ALIGN * ALIGN; }
 
 inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-qsmoe_status check_qmat(const qsmoe_qmat &m, int64_t rows) {
-    if (!m.codes || !m.scales || !m.biases) return QSMOE_ERR_INVALID;
-    if (!aligned(m.codes, 16) || !aligned(m.scales, 2) || !aligned(m.biases, 2)) return QSMOE_ERR_INVALID;
-    if (m.mat_stride < rows) return QSMOE_ERR_INVALID;
-    return QSMOE_OK;
+moe_status check_qmat(const moe_qmat &m, int64_t rows) {
+    if (!m.codes || !m.scales || !m.biases) return MOE_ERR_INVALID;
+    if (!aligned(m.codes, 16) || !aligned(m.scales, 2) || !aligned(m.biases, 2)) return MOE_ERR_INVALID;
+    if (m.mat_stride < rows) return MOE_ERR_INVALID;
+    return MOE_OK;
 }
 
-qsmoe_status check_desc(const qsmoe_layer_desc *d) {
-    if (!d) return QSMOE_ERR_INVALID;
+moe_status check_desc(const moe_layer_desc *d) {
+    if (!d) return MOE_ERR_INVALID;
     if (d->group != 64 || (d->bits != 4 && d->bits != 8) ||
-        (d->scale_dtype != QSMOE_F16 && d->scale_dtype != QSMOE_BF16))
-        return QSMOE_ERR_UNSUPPORTED;
-    if (d->n_experts < 1 || d->n_experts > 256) return QSMOE_ERR_UNSUPPORTED;
-    if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return QSMOE_ERR_UNSUPPORTED;
-    if (d->hidden < 128 || d->hidden > 8192 || d->hidden % 128) return QSMOE_ERR_UNSUPPORTED;
-    if (d->inter < 128 || d->inter > 2048 || d->inter % 128) return QSMOE_ERR_UNSUPPORTED;
-    if ((int64_t)(d->top_k + 1) * d->inter > 24576) return QSMOE_ERR_UNSUPPORTED;
-    if (!d->router_w || !aligned(d->router_w, 16)) return QSMOE_ERR_INVALID;
-    if (d->router_bias && !aligned(d->router_bias, 4)) return QSMOE_ERR_INVALID;
-    if (d->has_shared != 0 && d->has_shared != 1) return QSMOE_ERR_INVALID;
-    if (d->shared_gate_w && (!d->has_shared || !aligned(d->shared_gate_w, 16))) return QSMOE_ERR_INVALID;
-    qsmoe_status s;
+        (d->scale_dtype != MOE_F16 && d->scale_dtype != MOE_BF16))
+        return MOE_ERR_UNSUPPORTED;
+    if (d->n_experts < 1 || d->n_experts > 256) return MOE_ERR_UNSUPPORTED;
+    if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->n_experts) return MOE_ERR_UNSUPPORTED;
+    if (d->hidden < 64 || d->hidden > 8192 || d->hidden % 64) return MOE_ERR_UNSUPPORTED;
+    if (d->inter < 64 || d->inter > 2048 || d->inter % 64) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)(d->top_k + 1) * d->inter > 24576) return MOE_ERR_UNSUPPORTED;
+    if (!d->router_w || !aligned(d->router_w, 16)) return MOE_ERR_INVALID;
+    if (d->router_bias && !aligned(d->router_bias, 4)) return MOE_ERR_INVALID;
+    if (d->has_shared != 0 && d->has_shared != 1) return MOE_ERR_INVALID;
+    if (d->shared_gate_w && (!d->has_shared || !aligned(d->shared_gate_w, 16))) return MOE_ERR_INVALID;
+    moe_status s;
     if ((s = check_qmat(d->gate, d->inter)) || (s = check_qmat(d->up, d->inter)) ||
         (s = check_qmat(d->down, d->hidden)))
         return s;
@@ -53,10 +53,10 @@ qsmoe_status check_desc(const qsmoe_layer_desc *d) {
         ((s = check_qmat(d->s_gate, d->inter)) || (s = check_qmat(d->s_up, d->inter)) ||
          (s = check_qmat(d->s_down, d->hidden))))
         return s;
-    return QSMOE_OK;
+    return MOE_OK;
 }
 
-QMat to_qmat(const qsmoe_qmat &m) {
+QMat to_qmat(const moe_qmat &m) {
     QMat q;
     q.codes = (const uint8_t *)m.codes;
     q.scales = (const uint16_t *)m.scales;
@@ -65,7 +65,7 @@ QMat to_qmat(const qsmoe_qmat &m) {
     return q;
 }
 
-Layer to_layer(const qsmoe_layer_desc *d) {
+Layer to_layer(const moe_layer_desc *d) {
     Layer L;
     L.H = d->hidden;
     L.I = d->inter;
@@ -85,7 +85,7 @@ Layer to_layer(const qsmoe_layer_desc *d) {
     } else {
         L.s_gate = L.s_up = L.s_down = QMat{nullptr, nullptr, nullptr, 0};
     }
-    L.sb_bf16 = d->scale_dtype == QSMOE_BF16;
+    L.sb_bf16 = d->scale_dtype == MOE_BF16;
     L.shared_gate_w = (const uint16_t *)d->shared_gate_w;
     return L;
 }
@@ -102,7 +102,7 @@ struct Carver {
     }
 };
 
-DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
+DecodeBufs carve_decode(const moe_layer_desc *d, void *ws, size_t *bytes) {
     Carver c{(char *)ws};
     DecodeBufs b;
     b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);
@@ -110,7 +110,7 @@ DecodeBufs carve_decode(const qsmoe_layer_desc *d, void *ws, size_t *bytes) {
     return b;
 }
 
-PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t *bytes) {
+PrefillBufs carve_prefill(const moe_layer_desc *d, int64_t T, void *ws, size_t *bytes) {
     Carver c{(char *)ws};
     const int64_t H = d->hidden, I = d->inter, K = d->top_k, E = d->n_experts;
     const int64_t nblk = (T + ROUTER_TOKENS - 1) / ROUTER_TOKENS;
@@ -136,20 +136,22 @@ PrefillBufs carve_prefill(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t
 
 // T >= 2 runs in chunks, one after another on the stream, each through the whole
 // prefill sequence in the same workspace: chunks of `chunk` tokens need this much
-size_t ws_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk) {
+size_t ws_size_chunked(const moe_layer_desc *d, int64_t T, int64_t chunk) {
     size_t n = 0;
     if (T <= 0) return 0;
     if (T == 1) carve_decode(d, nullptr, &n);
     else carve_prefill(d, T < chunk ? T : chunk, nullptr, &n);
     return n;
 }
-size_t ws_size(const qsmoe_layer_desc *d, int64_t T) { return ws_size_chunked(d, T, QSMOE_PREFILL_CHUNK); }
+size_t ws_size(const moe_layer_desc *d, int64_t T) { return ws_size_chunked(d, T, MOE_PREFILL_CHUNK); }
 
-// the largest chunk (at least min(T, QSMOE_PREFILL_CHUNK)) whose buffers fit in ws_bytes
-int64_t pick_chunk(const qsmoe_layer_desc *d, int64_t T, size_t ws_bytes) {
-    int64_t lo = T < QSMOE_PREFILL_CHUNK ? T : QSMOE_PREFILL_CHUNK;
+// the smallest chunk a workspace may be sized for
+constexpr int64_t MIN_CHUNK = 2;
+
+// the largest chunk whose buffers fit in ws_bytes (check_ws has made sure MIN_CHUNK fits)
+int64_t pick_chunk(const moe_layer_desc *d, int64_t T, size_t ws_bytes) {
     if (ws_size_chunked(d, T, T) <= ws_bytes) return T;
-    int64_t hi = T;                                   // lo fits, hi does not
+    int64_t lo = MIN_CHUNK, hi = T;                   // lo fits, hi does not
     while (hi - lo > 1) {
         const int64_t mid = lo + (hi - lo) / 2;
         if (ws_size_chunked(d, T, mid) <= ws_bytes) lo = mid;
@@ -158,13 +160,13 @@ int64_t pick_chunk(const qsmoe_layer_desc *d, int64_t T, size_t ws_bytes) {
     return lo;
 }
 
-qsmoe_status check_ws(const qsmoe_layer_desc *d, int64_t T, void *ws, size_t ws_bytes) {
-    if (!ws || !aligned(ws, ALIGN)) return QSMOE_ERR_WORKSPACE;
-    if (ws_bytes < ws_size(d, T)) return QSMOE_ERR_WORKSPACE;
-    return QSMOE_OK;
+moe_status check_ws(const moe_layer_desc *d, int64_t T, void *ws, size_t ws_bytes) {
+    if (!ws || !aligned(ws, ALIGN)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < ws_size_chunked(d, T, MIN_CHUNK)) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
 }
 
-inline qsmoe_status dev(hipError_t e) { return e == hipSuccess ? QSMOE_OK : QSMOE_ERR_DEVICE; }
+inline moe_status dev(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
 // Batches of SMALL_TMAX + 1 .. 2 SMALL_TMAX tokens (verification batches of a few rows) run
 // as two small-batch launches of ceil(T/2) and floor(T/2) tokens: a token's result depends
@@ -183,41 +185,47 @@ constexpr int64_t MAX_TOKENS = 1 << 20;
 
 extern "C" {
 
-int qsmoe_abi_version(void) { return QSMOE_ABI_VERSION; }
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-const char *qsmoe_status_string(qsmoe_status s) {
+const char *moe_status_string(moe_status s) {
     switch (s) {
-        case QSMOE_OK: return "ok";
-        case QSMOE_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size or enum)";
-        case QSMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
-        case QSMOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
-        case QSMOE_ERR_DEVICE: return "HIP launch failed";
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID: return "invalid argument (null or misaligned pointer, bad size or enum)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_DEVICE: return "HIP launch failed";
         default: return "unknown status";
     }
 }
 
-size_t qsmoe_workspace_size(const qsmoe_layer_desc *d, int64_t T) {
-    if (check_desc(d) != QSMOE_OK) return SIZE_MAX;
+size_t moe_workspace_size(const moe_layer_desc *d, int64_t T) {
+    if (check_desc(d) != MOE_OK) return SIZE_MAX;
     if (T > MAX_TOKENS) return SIZE_MAX;
     return ws_size(d, T);
 }
 
-size_t qsmoe_workspace_size_chunked(const qsmoe_layer_desc *d, int64_t T, int64_t chunk) {
-    if (check_desc(d) != QSMOE_OK) return SIZE_MAX;
+size_t moe_workspace_size_chunked(const moe_layer_desc *d, int64_t T, int64_t chunk) {
+    if (check_desc(d) != MOE_OK) return SIZE_MAX;
     if (T > MAX_TOKENS || chunk < 0) return SIZE_MAX;
-    if (chunk == 0) chunk = QSMOE_PREFILL_CHUNK;
-    return ws_size_chunked(d, T, chunk < 2 ? 2 : chunk);
+    if (chunk == 0) chunk = MOE_PREFILL_CHUNK;
+    return ws_size_chunked(d, T, chunk < MIN_CHUNK ? MIN_CHUNK : chunk);
 }
 
-qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int32_t *topk_idx,
+moe_status moe_workspace_status(void *ws, size_t ws_bytes, uint32_t *status_out, int32_t clear, void *stream) {
+    if (!ws || !aligned(ws, ALIGN) || !status_out || !aligned(status_out, 4)) return MOE_ERR_INVALID;
+    if (ws_bytes < WS_CTL_BYTES) return MOE_ERR_WORKSPACE;
+    return dev(launch_ws_status((uint32_t *)ws, status_out, clear != 0, (hipStream_t)stream));
+}
+
+moe_status moe_route(const moe_layer_desc *d, const void *x, int64_t T, int32_t *topk_idx,
                        float *topk_w, void *ws, size_t ws_bytes, void *stream) {
-    qsmoe_status s = check_desc(d);
+    moe_status s = check_desc(d);
     if (s) return s;
-    if (T < 0) return QSMOE_ERR_INVALID;
-    if (T > MAX_TOKENS) return QSMOE_ERR_UNSUPPORTED;
-    if (T == 0) return QSMOE_OK;
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T > MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if (T == 0) return MOE_OK;
     if (!x || !aligned(x, 16) || !topk_idx || !topk_w || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
-        return QSMOE_ERR_INVALID;
+        return MOE_ERR_INVALID;
     if ((s = check_ws(d, T, ws, ws_bytes))) return s;
     const Layer L = to_layer(d);
     hipStream_t st = (hipStream_t)stream;
@@ -249,22 +257,22 @@ qsmoe_status moe_route(const qsmoe_layer_desc *d, const void *x, int64_t T, int3
         b.idx = topk_idx + t0 * K;
         b.w = topk_w + t0 * K;
         const hipError_t e = launch_prefill_router(L, (const uint16_t *)x + t0 * H, Tc, b, false, nullptr, nullptr, st);
-        if (e != hipSuccess) return QSMOE_ERR_DEVICE;
+        if (e != hipSuccess) return MOE_ERR_DEVICE;
     }
-    return QSMOE_OK;
+    return MOE_OK;
 }
 
-qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t T, void *y,
+moe_status moe_layer_forward(const moe_layer_desc *d, const void *x, int64_t T, void *y,
                                int32_t y_dtype, int32_t *topk_idx, float *topk_w, void *ws,
                                size_t ws_bytes, void *stream) {
-    qsmoe_status s = check_desc(d);
+    moe_status s = check_desc(d);
     if (s) return s;
-    if (T < 0) return QSMOE_ERR_INVALID;
-    if (T > MAX_TOKENS) return QSMOE_ERR_UNSUPPORTED;
-    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
-    if (T == 0) return QSMOE_OK;
-    if (!x || !aligned(x, 16) || !y || !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2)) return QSMOE_ERR_INVALID;
-    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return QSMOE_ERR_INVALID;
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T > MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16) || !y || !aligned(y, y_dtype == MOE_F32 ? 4 : 2)) return MOE_ERR_INVALID;
+    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID;
     if ((s = check_ws(d, T, ws, ws_bytes))) return s;
     const Layer L = to_layer(d);
     hipStream_t st = (hipStream_t)stream;
@@ -284,7 +292,7 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
         size_t n;
         const DecodeBufs b = carve_decode(d, ws, &n);
         const int64_t K = d->top_k, H = d->hidden;
-        void *y1 = (char *)y + (size_t)(T0 * H) * (y_dtype == QSMOE_F32 ? 4 : 2);
+        void *y1 = (char *)y + (size_t)(T0 * H) * (y_dtype == MOE_F32 ? 4 : 2);
         e = launch_decode_small_layer(L, xx, T0, b, y, y_dtype, topk_idx, topk_w, st);
         if (e == hipSuccess)
             e = launch_decode_small_layer(L, xx + T0 * H, T - T0, b, y1, y_dtype, topk_idx ? topk_idx + T0 * K : nullptr,
@@ -296,7 +304,7 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
     size_t n;
     const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
     const PrefillBufs b = carve_prefill(d, C, ws, &n);
-    const size_t ysz = y_dtype == QSMOE_F32 ? 4 : 2;
+    const size_t ysz = y_dtype == MOE_F32 ? 4 : 2;
     for (int64_t t0 = 0; t0 < T; t0 += C) {
         const int64_t Tc = T - t0 < C ? T - t0 : C;
         void *yc = (char *)y + (size_t)(t0 * H) * ysz;
@@ -304,65 +312,65 @@ qsmoe_status moe_layer_forward(const qsmoe_layer_desc *d, const void *x, int64_t
                                   topk_w ? topk_w + t0 * K : nullptr, st);
         if (e == hipSuccess) e = launch_prefill_binning(L, Tc, b, st);
         if (e == hipSuccess) e = launch_prefill_gemms(L, Tc, b, yc, y_dtype, st);
-        if (e != hipSuccess) return QSMOE_ERR_DEVICE;
+        if (e != hipSuccess) return MOE_ERR_DEVICE;
     }
-    return QSMOE_OK;
+    return MOE_OK;
 }
 
-qsmoe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
+moe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,
                      int32_t y_dtype, void *stream) {
-    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
-    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N < 0 || K < 0) return MOE_ERR_INVALID;
+    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
     if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
-        return QSMOE_ERR_UNSUPPORTED;
+        return MOE_ERR_UNSUPPORTED;
     if (!w_tiles || !aligned(w_tiles, 16) || !x || !aligned(x, 16) || !y ||
-        !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
-        return QSMOE_ERR_INVALID;
+        !aligned(y, y_dtype == MOE_F32 ? 4 : 2))
+        return MOE_ERR_INVALID;
     return dev(launch_q8_gemv((const uint8_t *)w_tiles, N, K, (const uint16_t *)x, y, y_dtype,
                               (hipStream_t)stream));
 }
 
-qsmoe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream) {
-    if (K < 0) return QSMOE_ERR_INVALID;
-    if (K % 32 || K > 8192) return QSMOE_ERR_UNSUPPORTED;
-    if (K == 0) return QSMOE_OK;
-    if (!x || !aligned(x, 2) || !xq || !aligned(xq, 4) || !xd || !aligned(xd, 2)) return QSMOE_ERR_INVALID;
+moe_status q8_quantize_x(const void *x, int64_t K, void *xq, void *xd, void *stream) {
+    if (K < 0) return MOE_ERR_INVALID;
+    if (K % 32 || K > 8192) return MOE_ERR_UNSUPPORTED;
+    if (K == 0) return MOE_OK;
+    if (!x || !aligned(x, 2) || !xq || !aligned(xq, 4) || !xd || !aligned(xd, 2)) return MOE_ERR_INVALID;
     return dev(launch_q8_quantize_x((const uint16_t *)x, K, (int8_t *)xq, (uint16_t *)xd, (hipStream_t)stream));
 }
 
-qsmoe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd, void *y,
+moe_status q8_gemv_q8x(const void *w_tiles, int64_t N, int64_t K, const void *xq, const void *xd, void *y,
                          int32_t y_dtype, void *stream) {
-    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
-    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N < 0 || K < 0) return MOE_ERR_INVALID;
+    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
     if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
-        return QSMOE_ERR_UNSUPPORTED;
+        return MOE_ERR_UNSUPPORTED;
     if (!w_tiles || !aligned(w_tiles, 16) || !xq || !aligned(xq, 4) || !xd || !aligned(xd, 2) || !y ||
-        !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
-        return QSMOE_ERR_INVALID;
+        !aligned(y, y_dtype == MOE_F32 ? 4 : 2))
+        return MOE_ERR_INVALID;
     return dev(launch_q8_gemv_q8x((const uint8_t *)w_tiles, N, K, (const int8_t *)xq, (const uint16_t *)xd,
                                   nullptr, y, y_dtype, (hipStream_t)stream));
 }
 
-qsmoe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y, int32_t y_dtype,
+moe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y, int32_t y_dtype,
                         void *stream) {
-    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
-    if (y_dtype != QSMOE_BF16 && y_dtype != QSMOE_F32) return QSMOE_ERR_INVALID;
+    if (N < 0 || K < 0) return MOE_ERR_INVALID;
+    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
     if (N % 16 || K % 32 || N < 16 || K < 32 || K > 8192 || N / 16 > INT32_MAX)
-        return QSMOE_ERR_UNSUPPORTED;
-    if (!w_tiles || !aligned(w_tiles, 16) || !x || !aligned(x, 8) || !y || !aligned(y, y_dtype == QSMOE_F32 ? 4 : 2))
-        return QSMOE_ERR_INVALID;
+        return MOE_ERR_UNSUPPORTED;
+    if (!w_tiles || !aligned(w_tiles, 16) || !x || !aligned(x, 8) || !y || !aligned(y, y_dtype == MOE_F32 ? 4 : 2))
+        return MOE_ERR_INVALID;
     return dev(launch_q8_gemv_q8x((const uint8_t *)w_tiles, N, K, nullptr, nullptr, (const uint16_t *)x, y,
                                   y_dtype, (hipStream_t)stream));
 }
 
-qsmoe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles, void *stream) {
-    if (N < 0 || K < 0) return QSMOE_ERR_INVALID;
-    if (N % 16 || K % 32) return QSMOE_ERR_UNSUPPORTED;
-    if (N == 0 || K == 0) return QSMOE_OK;
-    if (!w_rows || !w_tiles || !aligned(w_tiles, 16)) return QSMOE_ERR_INVALID;
+moe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles, void *stream) {
+    if (N < 0 || K < 0) return MOE_ERR_INVALID;
+    if (N % 16 || K % 32) return MOE_ERR_UNSUPPORTED;
+    if (N == 0 || K == 0) return MOE_OK;
+    if (!w_rows || !w_tiles || !aligned(w_tiles, 16)) return MOE_ERR_INVALID;
     const size_t bytes = (size_t)N * (size_t)(K / 32) * 34;
     const uintptr_t a = (uintptr_t)w_rows, b = (uintptr_t)w_tiles;
-    if (a < b + bytes && b < a + bytes) return QSMOE_ERR_INVALID;   // overlap
+    if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID;   // overlap
     return dev(launch_q8_pack((const uint8_t *)w_rows, N, K, (uint8_t *)w_tiles, (hipStream_t)stream));
 }
 

@@ -152,10 +152,11 @@ __device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, i
         const bool act = lane < 2 * (K + gated);
         const uint64_t none = (uint64_t)tag << 32;
         uint64_t w;
+        const uint32_t lim = wait_bound(ctl);
         for (uint32_t n = 0;; ++n) {
             w = act ? ld_dev64(tp + lane) : none;
             if (__ballot(tag_of(w) != tag) == 0ull) break;
-            if (n > SPIN_LIMIT) {
+            if (n > lim) {
                 if (lane == 0) raise_error(ctl);
                 break;
             }
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // 16-byte pieces (one 64-byte run per copy)
         __shared__ float s_lg[NW];
         const int e = b * NW + wave;
-        const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+        const uint32_t tag = call_tag(ctl);
         float acc = 0.0f;
         if (e < E + gated) {                                  // e = E: the shared expert's gate
             const uint16_t *wr = e < E ? L.router_w + (int64_t)e * H : L.shared_gate_w;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
         return;
     }
-    const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+    const uint32_t tag = call_tag(ctl);
     if (b < nR + a.nP) {
         // ------------------------------------------- P: selectors (wave 0 works)
         if (wave != 0) return;
@@ -366,6 +367,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 // 16-byte write, and the chunk sums by a DPP sum over the chunk's groups
                 const uint64_t *hw = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE);
                 const int ngrp = nvec * I / 8;
+                const uint32_t lim = wait_bound(ctl);
                 for (int g0 = 0; g0 < ngrp; g0 += DT) {
                     const int g = g0 + tid;
                     const bool live = g < ngrp;
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     for (uint32_t t = 0;; ++t) {
                         ld_dev256(hw + 4 * gg, w0, w1);
                         if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
-                        if (t > SPIN_LIMIT) {
+                        if (t > lim) {
                             raise_error(ctl);
                             break;
                         }
@@ -418,7 +420,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         if (gv == 0 && lr == 0 && n < H) {
             float y = s_part[0][rloc];
             for (int j = 1; j < a.vs; ++j) y += s_part[j][rloc];
-            if (a.y_dtype == QSMOE_F32) ((float *)a.y)[n] = y;
+            if (a.y_dtype == MOE_F32) ((float *)a.y)[n] = y;
             else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
         }
         // the last of the D workgroups to have arrived (every other workgroup of the call
@@ -499,12 +501,24 @@ DecArgs make_args(const Layer &L, const uint16_t *x, const DecodeBufs &b) {
     a.L = L;
     a.x = x;
     a.ctl = b.ctl;
-    a.y_dtype = QSMOE_F32;
+    a.y_dtype = MOE_F32;
     a.shared = L.has_shared;
     return a;
 }
 
 }  // namespace
+
+namespace {
+__global__ void k_ws_status(uint32_t *ctl, uint32_t *out, int clear) {
+    out[0] = clear ? __hip_atomic_exchange(ctl + CTL_ERR, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : ld_dev(ctl + CTL_ERR);
+}
+}  // namespace
+
+hipError_t launch_ws_status(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t s) {
+    hipLaunchKernelGGL(k_ws_status, dim3(1), dim3(1), 0, s, ctl, out, clear ? 1 : 0);
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
                                int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s) {

@@ -76,12 +76,13 @@ __device__ void small_get_sel(uint32_t *ctl, uint32_t tag, int E, int K, int T, 
         const bool act = lane < n, actg = gated && lane < T;
         const uint64_t none = (uint64_t)tag << 32;
         uint64_t w0, w1, wg;
+        const uint32_t lim = wait_bound(ctl);
         for (uint32_t it = 0;; ++it) {
             w0 = act ? ld_dev64(tp + 2 * lane) : none;
             w1 = act ? ld_dev64(tp + 2 * lane + 1) : none;
             wg = actg ? ld_dev64(tp + 2 * (64 + lane) + 1) : none;
             if (__ballot(tag_of(w0) != tag || tag_of(w1) != tag || tag_of(wg) != tag) == 0ull) break;
-            if (it > SPIN_LIMIT) {
+            if (it > lim) {
                 if (lane == 0) raise_error(ctl);
                 break;
             }
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     const int sb_bf16 = L.sb_bf16, gated = L.shared_gate_w != nullptr && a.shared;
     const int nR = a.nR, nP = a.nP, nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
-    const uint32_t tag = ld_dev(ctl + CTL_GEN) + 1;
+    const uint32_t tag = call_tag(ctl);
 
     if (b < nR) {
         // -------------------------------------------- R: one expert per wave, all tokens
@@ -651,6 +652,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             // order, chunk sums by a DPP sum over the chunk's groups
             const uint32_t *hw = ctl + H_BASE + (d % SM_HCOPIES) * SM_HSTRIDE;
             const int ngrp = nslot * I / 8;
+            const uint32_t lim = wait_bound(ctl);
             for (int g0 = 0; g0 < ngrp; g0 += DT) {
                 const int g = g0 + tid;
                 const bool live = g < ngrp;
@@ -662,7 +664,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 for (uint32_t it = 0; used; ++it) {
                     ld_dev256(hw + 8 * gg, w0, w1);
                     if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
-                    if (it > SPIN_LIMIT) {
+                    if (it > lim) {
                         raise_error(ctl);
                         break;
                     }
@@ -704,7 +706,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const int nn = d * 4 * rpw + r;
             if (nn < H) {
                 const float yy = s_part[t * 4 * rpw + r] + s_part[(SM_TMAX + t) * 4 * rpw + r];
-                if (a.y_dtype == QSMOE_F32) ((float *)a.y)[(int64_t)t * H + nn] = yy;
+                if (a.y_dtype == MOE_F32) ((float *)a.y)[(int64_t)t * H + nn] = yy;
                 else ((uint16_t *)a.y)[(int64_t)t * H + nn] = f32_to_bf16(yy);
             }
         }
@@ -773,7 +775,7 @@ SmallArgs make_small_args(const Layer &L, const uint16_t *x, int64_t T, const De
     a.x = x;
     a.ctl = b.ctl;
     a.T = (int)T;
-    a.y_dtype = QSMOE_F32;
+    a.y_dtype = MOE_F32;
     a.shared = L.has_shared;
     return a;
 }

@@ -23,7 +23,10 @@ constexpr int NGRP = 16;                    // group counters of the completion 
 
 // Decode state at the start of the workspace, in uint32 units.  It must be zero before
 // the first call and is kept by the library between calls.
-constexpr int CTL_ERR = 0;                  // set if a bounded wait ever gave up
+constexpr int CTL_ERR = 0;                  // MOE_WS_ERR_* bits: a bounded wait gave up
+constexpr int CTL_SPIN = 32;                // 0: every wait polls at most SPIN_LIMIT times;
+                                            // else at most this many (set only by a test of
+                                            // the give-up path, which must not hang)
 constexpr int CTL_GEN = 64;                 // calls completed; this call's tag is gen + 1
 constexpr int CNT_BASE = 128;               // + g * 64: completion group counters
 constexpr int CNT_TOP = CNT_BASE + NGRP * 64;
@@ -52,9 +55,12 @@ __device__ __forceinline__ void st_dev64(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16 bytes (two tagged words) written through to device scope in one store: hand-off
-// lines are written whole by one instruction, not merged from many small writes
+// lines are written whole by one instruction, not merged from many small writes.  A
+// store wider than 8 bytes reads its data registers after it issues, and a vector-ALU
+// write to them within two wait states replaces data not yet read; the compiler pads its
+// own stores for that but cannot see inside this one, so the padding is part of it.
 __device__ __forceinline__ void st_dev128(void *p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 4" ::"v"(p), "v"(v) : "memory");
 }
 // 32 bytes (four tagged words) read at device scope with two 16-byte loads, waited for
 // here (the compiler does not track loads issued from inline assembly)
@@ -79,7 +85,20 @@ __device__ __forceinline__ uint32_t add_dev(uint32_t *p) {
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 
 __device__ void raise_error(uint32_t *ctl) {
-    __hip_atomic_fetch_or(ctl + CTL_ERR, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(ctl + CTL_ERR, MOE_WS_ERR_DECODE_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the bound on the polls of one wait
+__device__ __forceinline__ uint32_t wait_bound(const uint32_t *ctl) {
+    const uint32_t v = ld_dev(ctl + CTL_SPIN);
+    return v ? v : SPIN_LIMIT;
+}
+
+// this call's tag: the generation of the last completed call plus one, skipping 0 (the
+// tag of words never written since the workspace was zeroed) when the counter wraps
+__device__ __forceinline__ uint32_t call_tag(const uint32_t *ctl) {
+    const uint32_t t = ld_dev(ctl + CTL_GEN) + 1u;
+    return t ? t : 1u;
 }
 
 // back-off between polls of a word another workgroup has not yet written
@@ -150,6 +169,7 @@ __device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t 
     const int lane = threadIdx.x & 63;
     const uint64_t none = (uint64_t)tag << 32;
     uint64_t w[4], wg;
+    const uint32_t lim = wait_bound(ctl);
     for (uint32_t n = 0;; ++n) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) w[i] = lane + 64 * i < E ? ld_dev64(lg + lane + 64 * i) : none;
@@ -158,7 +178,7 @@ __device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t 
 #pragma unroll
         for (int i = 0; i < 4; ++i) miss |= tag_of(w[i]) != tag;
         if (__ballot(miss) == 0ull) break;
-        if (n > SPIN_LIMIT) {
+        if (n > lim) {
             if (lane == 0) raise_error(ctl);
             break;
         }

@@ -182,7 +182,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         if (MODE == 0) {
             const int j = (rs >> 4) & 3;
             m = (j < 2) ? (shared ? L.s_gate : L.gate) : (shared ? L.s_up : L.up);
-            return nbi * 128 + (rs >> 6) * 32 + (j & 1) * 16 + (rs & 15);
+            // h column; past I (the last block when I % 128 == 64) a valid row is re-read
+            // and its results discarded
+            const int col = nbi * 128 + (rs >> 6) * 32 + (j & 1) * 16 + (rs & 15);
+            return col < I ? col : I - 1;
         }
         m = shared ? L.s_down : L.down;
         const int col = nbi * BN + rs;
@@ -378,11 +381,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         // counted themselves in; they run earlier in the grid (lower workgroup index,
         // dispatched first), so the wait ends; it is bounded regardless
         if (tid == 0) {
+            // the bound: 2^24 polls, or the workspace's test bound (state word 32) when set
+            const uint32_t tb = __hip_atomic_load(a.err + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t lim = tb ? tb : (1u << 24);
             for (uint32_t it = 0;
                  __hip_atomic_load(a.tile_done + tix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.nb_gateup;
                  ++it) {
-                if (it > (1u << 24)) {
-                    __hip_atomic_fetch_or(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (it > lim) {
+                    __hip_atomic_fetch_or(a.err, MOE_WS_ERR_GEMM_WAIT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(8);
@@ -426,24 +432,36 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         uint16_t *hout = a.h + (int64_t)tile.row0 * I + nbi * 128 + wave * 32 + chunk * 8;
         // h goes out at device scope (sc1, written through), and once every wave's stores
         // have completed the workgroup counts itself in for the tile's down pass
+        const bool cols_live = nbi * 128 + wave * 32 < I;      // this wave's 32 h columns exist
 #pragma unroll
         for (int q = 0; q < BM / 16; ++q) {
             const int row = (lane >> 2) + 16 * q;
-            if (row < nrows) {
+            if (row < nrows && cols_live) {
                 const u32x4 v = *(const u32x4 *)(hs + row * HP + chunk * 8);
-                asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(hout + (int64_t)row * I), "v"(v) : "memory");
+                // (padded: a vector-ALU write to the data registers of a store wider than 8
+                // bytes within two wait states replaces data the store has not yet read)
+                asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 4" ::"v"(hout + (int64_t)row * I), "v"(v)
+                             : "memory");
             }
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // release at agent scope before the count: an L2 write-back, waited for, then the
+        // atomic.  A store acknowledged to its wave is not yet visible to device-scope loads
+        // of other workgroups; without the release a down tile could read h rows before
+        // they arrive (the sequence is written out: the compiler's own release omitted the
+        // wait after the write-back here)
+        if (tid == 0) {
+            asm volatile("buffer_wbl2 sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
+            __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         return;
     }
 
     // MODE 1: 32 rows at a time through a per-wave fp32 staging area; lane l then
     // owns row 32*hp + (l % 32) and 32 of the wave's 64 columns
     const int colbase = nbi * BN + wave * 64;
-    if (colbase >= H) return;                                    // columns past H (H % 256 == 128)
+    if (colbase >= H) return;                                    // columns past H (H % 256 != 0)
     constexpr int FP = 68;                                       // floats per staged row
     float *fs = (float *)(smem + wave * (32 * FP * 4));
     const int er = lane & 31, ecol = colbase + 32 * (lane >> 5);
@@ -515,7 +533,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ sl
                 sum[2 * q] += (float)h2[0];
                 sum[2 * q + 1] += (float)h2[1];
             }
-    if (y_dtype == QSMOE_F32) {
+    if (y_dtype == MOE_F32) {
         float *yp = (float *)y + t * H + col;
         *(f32x4 *)yp = (f32x4){sum[0], sum[1], sum[2], sum[3]};
         *(f32x4 *)(yp + 4) = (f32x4){sum[4], sum[5], sum[6], sum[7]};
@@ -555,7 +573,7 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
     const int64_t maxs = L.has_shared ? (a.T + GEMM_BM - 1) / GEMM_BM : 0;
     // [gate; up] + SwiGLU over routed and shared tiles
     GemmArgs a0 = a;
-    a0.nb = L.I / 128;
+    a0.nb = (L.I + 127) / 128;
     {
         const QMat *ms[4] = {&L.gate, &L.up, &L.s_gate, &L.s_up};
         a0.wlog = window_log(ms, L.has_shared ? 4 : 2, L.H, C::WMAX);

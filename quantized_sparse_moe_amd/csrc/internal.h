@@ -37,6 +37,9 @@ struct DecodeBufs {
     uint32_t *ctl;                 // WS_CTL_BYTES of decode state
 };
 
+// the workspace's error word (word 0 of the state) copied to *out, then optionally cleared
+hipError_t launch_ws_status(uint32_t *ctl, uint32_t *out, bool clear, hipStream_t s);
+
 hipError_t launch_decode_layer(const Layer &L, const uint16_t *x, const DecodeBufs &b, void *y,
                                int y_dtype, int32_t *out_idx, float *out_w, hipStream_t s);
 // T = 2 .. 4 tokens in one launch, the routed experts read once for all of them

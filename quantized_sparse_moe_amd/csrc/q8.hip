@@ -121,7 +121,7 @@ __global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv(const uint8_t *__restric
 #pragma unroll
         for (int w = 0; w < Q8_WAVES; ++w) s += red[w][tid];
         const int64_t n = (int64_t)blockIdx.x * 16 + tid;
-        if (y_dtype == QSMOE_F32) ((float *)y)[n] = s;
+        if (y_dtype == MOE_F32) ((float *)y)[n] = s;
         else ((uint16_t *)y)[n] = f32_to_bf16(s);
     }
 }
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv_q8x(const uint8_t *__res
 #pragma unroll
         for (int w = 0; w < Q8_WAVES; ++w) sum += red[w][tid];
         const int64_t n = (int64_t)blockIdx.x * 16 + tid;
-        if (y_dtype == QSMOE_F32) ((float *)y)[n] = sum;
+        if (y_dtype == MOE_F32) ((float *)y)[n] = sum;
         else ((uint16_t *)y)[n] = f32_to_bf16(sum);
     }
 }

@@ -56,12 +56,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const int e = e0 + sr + 16 * i;
         wrow[i] = e < a.LS ? e : -1;                        // e = E: the shared gate's row
     }
+    // (a chunk past the end of a row, when H % 128 == 64, loads zeros)
     auto load = [&](int kc, u32x4 (&xv)[4], u32x4 (&wv)[4]) {
+        const bool in = kc + sc < H;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            xv[i] = xrow[i] >= 0 ? *(const u32x4 *)(a.x + xrow[i] * H + kc + sc) : (u32x4){0u, 0u, 0u, 0u};
-            wv[i] = wrow[i] >= 0 ? *(const u32x4 *)((wrow[i] < E ? a.wr + (int64_t)wrow[i] * H : a.gate_w) + kc + sc)
-                                 : (u32x4){0u, 0u, 0u, 0u};
+            xv[i] = in && xrow[i] >= 0 ? *(const u32x4 *)(a.x + xrow[i] * H + kc + sc) : (u32x4){0u, 0u, 0u, 0u};
+            wv[i] = in && wrow[i] >= 0
+                        ? *(const u32x4 *)((wrow[i] < E ? a.wr + (int64_t)wrow[i] * H : a.gate_w) + kc + sc)
+                        : (u32x4){0u, 0u, 0u, 0u};
         }
     };
     f32x4 acc[4];
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         for (int i = 0; i < 4; ++i) {
             *(u32x4 *)(xa + (sr + 16 * i) * LPITCH + sc) = xv[i];
             *(u32x4 *)(wa + (sr + 16 * i) * LPITCH + sc) = wv[i];
-            if (write_x16 && xrow[i] >= 0) {                // this chunk's share of the fp16 copy
+            if (write_x16 && xrow[i] >= 0 && kc + sc < H) {   // this chunk's share of the fp16 copy
                 u32x4 h;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)

@@ -15,7 +15,7 @@ Elsewhere the selected experts must match exactly.
 import numpy as np
 
 TAU = 1e-5
-W_TOL = 1e-5          # |w_gpu - w_ref|: fp32 logits (error ~1e-6) through exp/normalise
+W_TOL = 1e-6          # |w_gpu - w_ref| at unambiguous tokens (the stated routing-weight bound)
 
 
 def to_dev(a, torch):
@@ -48,8 +48,10 @@ def check_output(y, ref, bf16_out: bool, what: str = ""):
     return rel
 
 
-def check_routing(idx_gpu, w_gpu, idx_ref, w_ref, gap):
-    """Exact expert sets at unambiguous tokens; returns the ambiguous-token mask."""
+def check_routing(idx_gpu, w_gpu, idx_ref, w_ref, gap, w_tol=None):
+    """Exact expert sets at unambiguous tokens; returns (the ambiguous-token mask, the
+    largest |w_gpu - w_ref| at unambiguous tokens)."""
+    w_tol = W_TOL if w_tol is None else w_tol
     idx_gpu = np.asarray(idx_gpu)
     amb = np.asarray(gap) < TAU
     ok = ~amb
@@ -57,9 +59,17 @@ def check_routing(idx_gpu, w_gpu, idx_ref, w_ref, gap):
     bad = np.nonzero((idx_gpu[ok] != idx_ref[ok]).any(axis=1))[0]
     assert bad.size == 0, f"{bad.size} unambiguous tokens route differently"
     werr = np.abs(np.asarray(w_gpu, np.float64)[ok] - w_ref[ok])
-    assert werr.size == 0 or werr.max() <= W_TOL, f"max |w err| = {werr.max():.3e}"
+    wmax = float(werr.max()) if werr.size else 0.0
+    assert wmax <= w_tol, f"max |w err| = {wmax:.3e}"
     assert np.allclose(np.asarray(w_gpu, np.float64).sum(axis=1), 1.0, atol=1e-5)
-    return amb
+    return amb, wmax
+
+
+def report(what: str, **kv):
+    """One line per parity case (shown with pytest -s / -rP): the error, the ambiguous
+    tokens, the largest routing-weight error."""
+    print(f"[parity] {what}: " + ", ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}"
+                                         for k, v in kv.items()), flush=True)
 
 
 def sample_tokens(T: int, n: int, seed: int = 0):

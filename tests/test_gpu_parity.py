@@ -1,8 +1,9 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
 
 Sizes: small cases the oracle finishes in seconds (several tiles plus ragged tails),
-and the full workload sizes in the launch configuration the benchmark times, checked
-on sampled tokens (tokens are independent, so the oracle evaluates just those rows).
+and the full workload sizes in the launch configuration the benchmark times (a
+workspace for the whole T, bf16 output), checked on sampled tokens (tokens are
+independent, so the oracle evaluates just those rows).
 Bit-exact invariants: fused [gate; up] == separate gate and up, repeat calls,
 token permutation and chunking.
 """
@@ -13,7 +14,7 @@ import pytest
 
 import oracle
 import qsmoe_synth as syn
-from gpu_util import (TAU, W_TOL, check_output, check_routing, sample_tokens, to_dev, y_to_np)
+from gpu_util import (TAU, W_TOL, check_output, check_routing, report, sample_tokens, to_dev, y_to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,12 +64,14 @@ def oracle_check(L, x_np, y, idx, w, bf16_out, what, rows=None, torch=None):
     ol = oracle.OracleLayer(L)
     xs = x_np[rows]
     idx_r, w_r, gap = oracle.route(ol, xs)
-    amb = check_routing(idx[rows], w[rows], idx_r, w_r, gap)
+    amb, wmax = check_routing(idx[rows], w[rows], idx_r, w_r, gap)
     # evaluate the oracle on the GPU's routing where it is ambiguous, its own elsewhere
     use_idx = np.where(amb[:, None], idx[rows], idx_r)
     use_w = np.where(amb[:, None], w[rows].astype(np.float64), w_r)
     ref = oracle.layer_forward_with_routing(ol, xs, use_idx, use_w)
-    return check_output(y[rows], ref, bf16_out, what), int(amb.sum())
+    rel = check_output(y[rows], ref, bf16_out, what)
+    report(what, err_over_rms=rel, ambiguous=f"{int(amb.sum())}/{len(rows)}", w_err=wmax)
+    return rel, int(amb.sum())
 
 
 # ------------------------------------------------------------------------- routing
@@ -83,7 +86,8 @@ def test_route_parity(torch, qs, cfg, T, nsample):
     idx, w = idx.cpu().numpy(), w.cpu().numpy()
     rows = np.arange(T) if nsample is None else sample_tokens(T, nsample, seed=T)
     idx_r, w_r, gap = oracle.route(oracle.OracleLayer(L), x_np[rows])
-    check_routing(idx[rows], w[rows], idx_r, w_r, gap)
+    amb, wmax = check_routing(idx[rows], w[rows], idx_r, w_r, gap)
+    report(f"route {cfg} T={T}", ambiguous=f"{int(amb.sum())}/{len(rows)}", w_err=wmax)
     assert ((idx >= 0) & (idx < L.n_experts)).all()
 
 
@@ -188,21 +192,68 @@ def test_small_batch_decode_parity(torch, qs, cfg, T):
 
 @pytest.mark.parametrize("cfg,T", [("PREFILL", 4096), ("SKEW", 16384)])
 def test_full_size_sampled(torch, qs, cfg, T):
-    """Full workload size in the benchmark's launch configuration; sampled tokens vs
-    the oracle, plus a bit-identical repeat."""
+    """Full workload size in the launch configuration the benchmark times: a workspace
+    for the whole T (one unchunked pass), bf16 output as the benchmark writes it, and
+    fp32 output; sampled tokens vs the oracle in both, a bit-identical repeat.  Then the
+    same call with the default workspace (4096-token chunks: four for the skewed
+    workload) must give the same bits."""
     L = layer(cfg)
     x_np = syn.make_x(T, L.hidden, seed=0)
     desc = qs.LayerDesc.from_host(L)
-    y, idx, w = run_layer(torch, qs, L, x_np, desc=desc)
-    y2, idx2, w2 = run_layer(torch, qs, L, x_np, desc=desc)
-    assert torch.equal(y, y2) and (idx == idx2).all() and (w == w2).all()
-    rows = sample_tokens(T, 24, seed=1)
-    oracle_check(L, x_np, y_to_np(y, torch), idx, w, False, f"{cfg} T={T} sampled", rows=rows)
+    x = to_dev(x_np, torch)
+    rows = sample_tokens(T, 64, seed=1)
+    ws_full = qs.new_workspace(desc, T, chunk=T)
+    outs = {}
+    for bf16_out in (True, False):
+        idx = torch.empty((T, L.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, L.top_k), dtype=torch.float32, device="cuda")
+        y = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16 if bf16_out else torch.float32,
+                                 topk_idx=idx, topk_w=w, workspace=ws_full)
+        torch.cuda.synchronize()
+        idx, w = idx.cpu().numpy(), w.cpu().numpy()
+        oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"{cfg} T={T} unchunked bf16={bf16_out}",
+                     rows=rows)
+        outs[bf16_out] = (y, idx, w)
+    y2 = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16, workspace=ws_full)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, outs[True][0])
+    del ws_full
+    yc = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16)            # default: chunks of 4096
+    torch.cuda.synchronize()
+    assert torch.equal(yc, outs[True][0]), "chunked != unchunked"
     # the bins were uneven as the workload intends
+    idx = outs[True][1]
     counts = np.bincount(idx.reshape(-1), minlength=L.n_experts)
     assert counts.sum() == T * L.top_k
     if cfg == "SKEW":
         assert (counts > 10 * counts.mean()).sum() >= 3
+    report(f"{cfg} T={T} bins", max_rows=int(counts.max()), empty=int((counts == 0).sum()))
+
+
+def test_tiny_through_grouped_path(torch, qs):
+    """The tiny layer (16 experts top-2, 8-bit) through the grouped path (T = 40, every
+    token vs the oracle in both output types), next to its small-batch and T = 1 runs."""
+    L = layer("TINY")
+    x_np = syn.make_x(40, L.hidden, seed=0)
+    for bf16_out in (False, True):
+        y, idx, w = run_layer(torch, qs, L, x_np, bf16_out=bf16_out)
+        oracle_check(L, x_np, y_to_np(y, torch), idx, w, bf16_out, f"tiny grouped T=40 bf16={bf16_out}")
+
+
+def test_small_workspace_bounds_memory(torch, qs):
+    """A workspace sized for 1024-token chunks (a quarter of the default) is accepted and
+    gives the same bits as the default and the unchunked ones (8-bit, T = 4096 + 77)."""
+    L = layer("SKEW")
+    desc = qs.LayerDesc.from_host(L)
+    T = 4096 + 77
+    x = to_dev(syn.make_x(T, L.hidden, seed=3), torch)
+    ys = []
+    for chunk in (1024, None, T):
+        ws = qs.new_workspace(desc, T, chunk=chunk)
+        ys.append(qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16, workspace=ws))
+        torch.cuda.synchronize()
+        del ws
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
 
 
 # ----------------------------------------------------------------- bit invariants
@@ -246,7 +297,7 @@ def test_chunked_prefill_bit_identical(torch, qs):
     x = to_dev(x_np, torch)
     outs = []
     for chunk in (None, T, 5000):
-        ws = torch.zeros(qs.qsmoe_workspace_size(desc, T, chunk), dtype=torch.uint8, device="cuda")
+        ws = qs.new_workspace(desc, T, chunk=chunk)
         idx = torch.empty((T, L.top_k), dtype=torch.int32, device="cuda")
         w = torch.empty((T, L.top_k), dtype=torch.float32, device="cuda")
         y = qs.moe_layer_forward(desc, x, y_dtype=torch.bfloat16, topk_idx=idx, topk_w=w, workspace=ws)
@@ -309,7 +360,7 @@ def test_decode_repeat_bit_identical(torch, qs):
     L = layer("DECODE")
     descs = [qs.LayerDesc.from_host(L), qs.LayerDesc.from_host(L, fused=False)]
     xs = [to_dev(syn.make_x(1, L.hidden, seed=s), torch) for s in (21, 22, 23)]
-    ws = torch.zeros(qs.qsmoe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(qs.moe_workspace_size(descs[0], 1), dtype=torch.uint8, device="cuda")
     ref = [qs.moe_layer_forward(descs[0], x, workspace=ws) for x in xs]
     torch.cuda.synchronize()
     outs = []
