@@ -203,6 +203,24 @@ moe_status moe_layer_forward(const moe_layer_desc *d, const void *x, int64_t T,
                                void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_layer_forward for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same results, bit for bit, with the workspace replaced by a
+ * 64 MiB array the library holds on each GPU from load until the process ends.  This
+ * call allocates nothing.  The caller still passes x, y and the optional topk outputs
+ * (as for moe_layer_forward).  The array is shared by every call of this entry point on
+ * one GPU and keeps the last call's contents: calls that overlap in time on one GPU race
+ * (issue them on one stream).  Prompts longer than the array holds run in chunks that
+ * fit it (no result changes, only more passes over the expert weights); a layer whose
+ * 2-token chunk does not fit returns MOE_ERR_WORKSPACE (none within the limits above
+ * does).  Errors and limits otherwise as for moe_layer_forward; MOE_ERR_DEVICE when the
+ * array's address cannot be obtained on the current device.
+ */
+moe_status moe_layer_forward_static(const moe_layer_desc *d, const void *x, int64_t T,
+                                    void *y, int32_t y_dtype,
+                                    int32_t *topk_idx, float *topk_w, void *stream);
+
+/*
  * Dense Q8_0 decode GEMV over 16-row packed tiles ([EMBER] packed 16-row tile):
  *     y[n] = sum_b d[n][b] * sum_{c<32} q[n][32b + c] * x[32b + c]
  * with fp32 accumulation.

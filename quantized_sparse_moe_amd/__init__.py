@@ -52,7 +52,7 @@ class moe_layer_desc(ctypes.Structure):
 
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size",
            "moe_workspace_size_chunked", "moe_workspace_status", "moe_route",
-           "moe_layer_forward", "q8_gemv", "q8_quantize_x", "q8_gemv_q8x", "q8_gemv_qx",
+           "moe_layer_forward", "moe_layer_forward_static", "q8_gemv", "q8_quantize_x", "q8_gemv_q8x", "q8_gemv_qx",
            "q8_pack_rows16")
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route.argtypes = [P, P, I64, P, P, P, SZ, P]
         L.moe_layer_forward.restype = I32
         L.moe_layer_forward.argtypes = [P, P, I64, P, I32, P, P, P, SZ, P]
+        L.moe_layer_forward_static.restype = I32
+        L.moe_layer_forward_static.argtypes = [P, P, I64, P, I32, P, P, P]
         L.q8_gemv.restype = I32
         L.q8_gemv.argtypes = [P, I64, I64, P, P, I32, P]
         L.q8_quantize_x.restype = I32
@@ -287,6 +289,20 @@ def moe_layer_forward(desc: LayerDesc, x, y=None, y_dtype=None, topk_idx=None, t
     ws, nbytes = _workspace(desc, T, workspace, x.device, stream)
     _check(lib().moe_layer_forward(desc.ptr, _ptr(x), T, _ptr(y), code, _ptr(topk_idx), _ptr(topk_w),
                                    _ptr(ws), nbytes, _stream(stream)), "moe_layer_forward")
+    return y
+
+
+def moe_layer_forward_static(desc: LayerDesc, x, y=None, y_dtype=None, topk_idx=None, topk_w=None,
+                             stream=None):
+    """The whole layer without a workspace (the library's static per-GPU array); the C
+    call allocates nothing -- pass ``y`` to allocate nothing here either."""
+    import torch
+    T = x.shape[0]
+    if y is None:
+        y = _empty((T, desc.hidden), y_dtype or torch.float32, x.device, stream)
+    _check(lib().moe_layer_forward_static(desc.ptr, _ptr(x), T, _ptr(y), _out_code(y, "moe_layer_forward_static"),
+                                          _ptr(topk_idx), _ptr(topk_w), _stream(stream)),
+           "moe_layer_forward_static")
     return y
 
 

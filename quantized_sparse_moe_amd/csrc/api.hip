@@ -9,8 +9,10 @@
 // [EMBER]: decode reuses one caller-provided workspace instead of per-layer temporaries.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -181,6 +183,98 @@ static int64_t small_split(const Layer &L, int64_t T) {
 // tokens * hidden must stay addressable with the kernels' 32-bit row offsets
 constexpr int64_t MAX_TOKENS = 1 << 20;
 
+// the argument checks of a layer call (workspace aside), all on the host; T == 0 passes
+moe_status check_layer_call(const moe_layer_desc *d, const void *x, int64_t T, const void *y, int32_t y_dtype,
+                            const int32_t *topk_idx, const float *topk_w) {
+    moe_status s = check_desc(d);
+    if (s) return s;
+    if (T < 0) return MOE_ERR_INVALID;
+    if (T > MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
+    if (T == 0) return MOE_OK;
+    if (!x || !aligned(x, 16) || !y || !aligned(y, y_dtype == MOE_F32 ? 4 : 2)) return MOE_ERR_INVALID;
+    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID;
+    return MOE_OK;
+}
+
+moe_status forward_impl(const moe_layer_desc *d, const void *x, int64_t T, void *y, int32_t y_dtype,
+                        int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    moe_status s = check_layer_call(d, x, T, y, y_dtype, topk_idx, topk_w);
+    if (s || T == 0) return s;
+    if ((s = check_ws(d, T, ws, ws_bytes))) return s;
+    const Layer L = to_layer(d);
+    hipStream_t st = (hipStream_t)stream;
+    const uint16_t *xx = (const uint16_t *)x;
+    hipError_t e;
+    if (T == 1) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        return dev(launch_decode_layer(L, xx, b, y, y_dtype, topk_idx, topk_w, st));
+    }
+    if (decode_small_eligible(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        return dev(launch_decode_small_layer(L, xx, T, b, y, y_dtype, topk_idx, topk_w, st));
+    }
+    if (const int64_t T0 = small_split(L, T)) {
+        size_t n;
+        const DecodeBufs b = carve_decode(d, ws, &n);
+        const int64_t K = d->top_k, H = d->hidden;
+        void *y1 = (char *)y + (size_t)(T0 * H) * (y_dtype == MOE_F32 ? 4 : 2);
+        e = launch_decode_small_layer(L, xx, T0, b, y, y_dtype, topk_idx, topk_w, st);
+        if (e == hipSuccess)
+            e = launch_decode_small_layer(L, xx + T0 * H, T - T0, b, y1, y_dtype, topk_idx ? topk_idx + T0 * K : nullptr,
+                                          topk_w ? topk_w + T0 * K : nullptr, st);
+        return dev(e);
+    }
+    // chunks of the prefill sequence: every token goes through the same kernels whatever
+    // the chunk it falls in, so the result is bit-identical to one unchunked pass
+    size_t n;
+    const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
+    const PrefillBufs b = carve_prefill(d, C, ws, &n);
+    const size_t ysz = y_dtype == MOE_F32 ? 4 : 2;
+    for (int64_t t0 = 0; t0 < T; t0 += C) {
+        const int64_t Tc = T - t0 < C ? T - t0 : C;
+        void *yc = (char *)y + (size_t)(t0 * H) * ysz;
+        e = launch_prefill_router(L, xx + t0 * H, Tc, b, true, topk_idx ? topk_idx + t0 * K : nullptr,
+                                  topk_w ? topk_w + t0 * K : nullptr, st);
+        if (e == hipSuccess) e = launch_prefill_binning(L, Tc, b, st);
+        if (e == hipSuccess) e = launch_prefill_gemms(L, Tc, b, yc, y_dtype, st);
+        if (e != hipSuccess) return MOE_ERR_DEVICE;
+    }
+    return MOE_OK;
+}
+
+// The static scratch of moe_layer_forward_static: device memory beyond the inputs and
+// outputs for callers that cannot allocate (code under HIP graph capture, tight serving
+// loops).  Each GPU holds its own copy from module load until the process ends; it is
+// zero at load (static storage), so the decode state at its start begins valid, and every
+// call leaves that state ready for the next one.  In host code `scratch` is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is handed to kernels.
+constexpr size_t SCRATCH_BYTES = 64u << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mu;
+
+moe_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MOE_ERR_DEVICE;
+    void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_DEVICE;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,59 +356,21 @@ moe_status moe_route(const moe_layer_desc *d, const void *x, int64_t T, int32_t 
     return MOE_OK;
 }
 
-moe_status moe_layer_forward(const moe_layer_desc *d, const void *x, int64_t T, void *y,
-                               int32_t y_dtype, int32_t *topk_idx, float *topk_w, void *ws,
-                               size_t ws_bytes, void *stream) {
-    moe_status s = check_desc(d);
-    if (s) return s;
-    if (T < 0) return MOE_ERR_INVALID;
-    if (T > MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
-    if (y_dtype != MOE_BF16 && y_dtype != MOE_F32) return MOE_ERR_INVALID;
-    if (T == 0) return MOE_OK;
-    if (!x || !aligned(x, 16) || !y || !aligned(y, y_dtype == MOE_F32 ? 4 : 2)) return MOE_ERR_INVALID;
-    if ((topk_idx && !aligned(topk_idx, 4)) || (topk_w && !aligned(topk_w, 4))) return MOE_ERR_INVALID;
-    if ((s = check_ws(d, T, ws, ws_bytes))) return s;
-    const Layer L = to_layer(d);
-    hipStream_t st = (hipStream_t)stream;
-    const uint16_t *xx = (const uint16_t *)x;
-    hipError_t e;
-    if (T == 1) {
-        size_t n;
-        const DecodeBufs b = carve_decode(d, ws, &n);
-        return dev(launch_decode_layer(L, xx, b, y, y_dtype, topk_idx, topk_w, st));
-    }
-    if (decode_small_eligible(L, T)) {
-        size_t n;
-        const DecodeBufs b = carve_decode(d, ws, &n);
-        return dev(launch_decode_small_layer(L, xx, T, b, y, y_dtype, topk_idx, topk_w, st));
-    }
-    if (const int64_t T0 = small_split(L, T)) {
-        size_t n;
-        const DecodeBufs b = carve_decode(d, ws, &n);
-        const int64_t K = d->top_k, H = d->hidden;
-        void *y1 = (char *)y + (size_t)(T0 * H) * (y_dtype == MOE_F32 ? 4 : 2);
-        e = launch_decode_small_layer(L, xx, T0, b, y, y_dtype, topk_idx, topk_w, st);
-        if (e == hipSuccess)
-            e = launch_decode_small_layer(L, xx + T0 * H, T - T0, b, y1, y_dtype, topk_idx ? topk_idx + T0 * K : nullptr,
-                                          topk_w ? topk_w + T0 * K : nullptr, st);
-        return dev(e);
-    }
-    // chunks of the prefill sequence: every token goes through the same kernels whatever
-    // the chunk it falls in, so the result is bit-identical to one unchunked pass
-    size_t n;
-    const int64_t C = pick_chunk(d, T, ws_bytes), K = d->top_k, H = d->hidden;
-    const PrefillBufs b = carve_prefill(d, C, ws, &n);
-    const size_t ysz = y_dtype == MOE_F32 ? 4 : 2;
-    for (int64_t t0 = 0; t0 < T; t0 += C) {
-        const int64_t Tc = T - t0 < C ? T - t0 : C;
-        void *yc = (char *)y + (size_t)(t0 * H) * ysz;
-        e = launch_prefill_router(L, xx + t0 * H, Tc, b, true, topk_idx ? topk_idx + t0 * K : nullptr,
-                                  topk_w ? topk_w + t0 * K : nullptr, st);
-        if (e == hipSuccess) e = launch_prefill_binning(L, Tc, b, st);
-        if (e == hipSuccess) e = launch_prefill_gemms(L, Tc, b, yc, y_dtype, st);
-        if (e != hipSuccess) return MOE_ERR_DEVICE;
-    }
-    return MOE_OK;
+moe_status moe_layer_forward(const moe_layer_desc *d, const void *x, int64_t T, void *y, int32_t y_dtype,
+                             int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    return forward_impl(d, x, T, y, y_dtype, topk_idx, topk_w, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer_forward_static(const moe_layer_desc *d, const void *x, int64_t T, void *y, int32_t y_dtype,
+                                    int32_t *topk_idx, float *topk_w, void *stream) {
+    // the argument checks of moe_layer_forward come first, so a call that is refused
+    // touches no device
+    moe_status s = check_layer_call(d, x, T, y, y_dtype, topk_idx, topk_w);
+    if (s || T == 0) return s;
+    if (ws_size_chunked(d, T, MIN_CHUNK) > SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((s = scratch_for_current_device(&ws))) return s;
+    return forward_impl(d, x, T, y, y_dtype, topk_idx, topk_w, ws, SCRATCH_BYTES, stream);
 }
 
 moe_status q8_gemv(const void *w_tiles, int64_t N, int64_t K, const void *x, void *y,

@@ -182,6 +182,21 @@ def test_workspace_sizes():
     assert route(d, T=16384, ws_bytes=g(16384, 2) - 1) == q.MOE_ERR_WORKSPACE
 
 
+def test_static_entry_validation():
+    """The no-workspace entry point refuses bad calls on the host, before it looks up its
+    device array (so these run without a GPU)."""
+    L = q.lib()
+    st = lambda d, T=16, x=FAKE, y=FAKE, y_dtype=q.MOE_F32: L.moe_layer_forward_static(
+        ctypes.byref(d), x, T, y, y_dtype, None, None, None)
+    assert st(desc(bits=3)) == q.MOE_ERR_UNSUPPORTED
+    assert st(desc(), T=-1) == q.MOE_ERR_INVALID
+    assert st(desc(), T=0) == q.MOE_OK
+    assert st(desc(), x=None) == q.MOE_ERR_INVALID
+    assert st(desc(), y=FAKE + 2) == q.MOE_ERR_INVALID
+    assert st(desc(), y_dtype=q.MOE_F16) == q.MOE_ERR_INVALID
+    assert st(desc(), T=(1 << 20) + 1) == q.MOE_ERR_UNSUPPORTED
+
+
 def test_workspace_status_validation():
     L = q.lib()
     assert L.moe_workspace_status(None, 1 << 20, FAKE, 0, None) == q.MOE_ERR_INVALID
