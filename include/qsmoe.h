@@ -123,7 +123,7 @@ const char  *moe_status_string(moe_status s);   /* static string, never NULL */
 /*
  * Bytes of device workspace moe_route / moe_layer_forward need for T tokens
  * (0 when T <= 0; SIZE_MAX when the descriptor is invalid).  The workspace must be
- * 256-byte aligned.  Its first 1 MiB is the state of the one-launch decode kernels
+ * 256-byte aligned.  Its first 2 MiB are the state of the one-launch decode kernels
  * (T <= 8): a call counter, completion counters, tagged words the workgroups of one call
  * hand to each other, and the error word.  It must be zero before the first call that
  * uses the workspace (allocate it zero-filled) and then belongs to the library: every
@@ -157,7 +157,7 @@ size_t moe_workspace_size_chunked(const moe_layer_desc *d, int64_t T, int64_t ch
  * Enqueues on `stream` a copy of the workspace's error word (MOE_WS_ERR_* bits, 0 when
  * every call so far completed every wait) into *status_out, a device uint32, and, when
  * `clear` is nonzero, resets the word to 0 afterwards.  ws must be a workspace of
- * ws_bytes >= 1 MiB used by moe_route / moe_layer_forward (or freshly zeroed); the call
+ * ws_bytes >= 2 MiB used by moe_route / moe_layer_forward (or freshly zeroed); the call
  * is ordered with the layer calls on the same stream.
  */
 moe_status moe_workspace_status(void *ws, size_t ws_bytes, uint32_t *status_out, int32_t clear,

@@ -118,12 +118,17 @@ class LayerInputs:
         return int(round(3 * H * I * per_w))
 
 
-def _qmat(rng: np.random.Generator, n: int, rows: int, cols: int, bits: int, sb: str = "f16") -> QMat:
+def _qmat(rng: np.random.Generator, n: int, rows: int, cols: int, bits: int, sb: str = "f16",
+          scale_range=None) -> QMat:
     assert cols % GROUP == 0 and bits in (4, 8) and sb in ("f16", "bf16")
     codes = rng.integers(0, 256, size=(n, rows, cols * bits // 8), dtype=np.uint8)
-    s = rng.uniform(0.005, 0.02, size=(n, rows, cols // GROUP))
-    if bits == 8:
-        s = s / 16.0
+    if scale_range is None:
+        s = rng.uniform(0.005, 0.02, size=(n, rows, cols // GROUP))
+        if bits == 8:
+            s = s / 16.0
+    else:                                    # log-uniform over [lo, hi]
+        lo, hi = scale_range
+        s = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(n, rows, cols // GROUP)))
     off = rng.uniform(-0.5, 0.5, size=s.shape) - 2.0 ** (bits - 1)
     if sb == "bf16":
         sbits = to_bf16_bits(s)
@@ -143,18 +148,19 @@ def zipf_router_bias(n_experts: int, s: float, seed: int) -> np.ndarray:
 def make_layer(hidden: int, inter: int, n_experts: int, top_k: int, bits: int,
                seed: int = 0, router_std: Optional[float] = None,
                zipf_s: Optional[float] = None, has_shared: bool = True,
-               scale_dtype: str = "f16", shared_gate: bool = False) -> LayerInputs:
+               scale_dtype: str = "f16", shared_gate: bool = False, scale_range=None) -> LayerInputs:
     """One layer's weights.  scale_dtype "bf16": scales and biases stored as bfloat16
     (the checkpoint format the pages print); shared_gate: a bf16 gate vector
-    ``g ~ N(0, 1/hidden)`` whose sigmoid(g . x) scales the shared expert's output."""
+    ``g ~ N(0, 1/hidden)`` whose sigmoid(g . x) scales the shared expert's output;
+    scale_range (lo, hi): scales drawn log-uniformly over [lo, hi] instead."""
     if router_std is None:
         router_std = 1.0 / np.sqrt(hidden)
     rw = _rng(seed, _S_ROUTER).normal(0.0, router_std, size=(n_experts, hidden))
     rb = zipf_router_bias(n_experts, zipf_s, seed) if zipf_s is not None else None
-    gu = _qmat(_rng(seed, _S_GU), n_experts, 2 * inter, hidden, bits, scale_dtype)
-    dn = _qmat(_rng(seed, _S_DN), n_experts, hidden, inter, bits, scale_dtype)
-    sgu = _qmat(_rng(seed, _S_SGU), 1, 2 * inter, hidden, bits, scale_dtype) if has_shared else None
-    sdn = _qmat(_rng(seed, _S_SDN), 1, hidden, inter, bits, scale_dtype) if has_shared else None
+    gu = _qmat(_rng(seed, _S_GU), n_experts, 2 * inter, hidden, bits, scale_dtype, scale_range)
+    dn = _qmat(_rng(seed, _S_DN), n_experts, hidden, inter, bits, scale_dtype, scale_range)
+    sgu = _qmat(_rng(seed, _S_SGU), 1, 2 * inter, hidden, bits, scale_dtype, scale_range) if has_shared else None
+    sdn = _qmat(_rng(seed, _S_SDN), 1, hidden, inter, bits, scale_dtype, scale_range) if has_shared else None
     sg = None
     if shared_gate:
         assert has_shared
@@ -165,9 +171,9 @@ def make_layer(hidden: int, inter: int, n_experts: int, top_k: int, bits: int,
                        s_down=sdn, seed=seed, scale_dtype=scale_dtype, shared_gate_w=sg)
 
 
-def make_x(T: int, hidden: int, seed: int = 0) -> np.ndarray:
-    """bf16 bit patterns [T][hidden] of N(0, 1) activations."""
-    return to_bf16_bits(_rng(seed, _S_X).standard_normal((T, hidden)))
+def make_x(T: int, hidden: int, seed: int = 0, std: float = 1.0) -> np.ndarray:
+    """bf16 bit patterns [T][hidden] of N(0, std^2) activations."""
+    return to_bf16_bits(std * _rng(seed, _S_X).standard_normal((T, hidden)))
 
 
 def make_q8_rows(N: int, K: int, seed: int = 0) -> np.ndarray:

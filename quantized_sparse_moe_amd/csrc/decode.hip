@@ -67,19 +67,22 @@ struct DecArgs {
 };
 
 // x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk fp32 sums of
-// the even and of the odd columns
+// the even and of the odd columns, under the row's range scale 2^e (returned; 0 for rows
+// of ordinary magnitude, which are staged in one pass); s_wm holds one word per wave.
+// Ends with a barrier.
 template <int BITS>
-__device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float2 *xsum) {
+__device__ void stage_x_pass(const uint16_t *x, int nch, float f, uint32_t *xs, float2 *xsum, uint32_t &mb) {
     constexpr int CPC = 128 / BITS;
-    for (int c = threadIdx.x; c < H / CPC; c += DT) {
+    for (int c = threadIdx.x; c < nch; c += DT) {
         float se = 0.0f, so = 0.0f;
         for (int g = 0; g < CPC / 8; ++g) {
             const u32x4 v = *(const u32x4 *)(x + c * CPC + 8 * g);
             u32x4 nat;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[i] << 16));
-                const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[i] & 0xffff0000u));
+                mb = max(mb, max((v[i] << 16) & 0x7fffffffu, v[i] & 0x7fff0000u));
+                const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[i] << 16) * f);
+                const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[i] & 0xffff0000u) * f);
                 se += (float)lo;
                 so += (float)hi;
                 nat[i] = pack_f16x2(lo, hi);
@@ -89,15 +92,34 @@ __device__ void stage_x(const uint16_t *x, int H, uint32_t *xs, float2 *xsum) {
         xsum[c] = make_float2(se, so);
     }
 }
+template <int BITS>
+__device__ int stage_x(const uint16_t *x, int H, uint32_t *xs, float2 *xsum, uint32_t *s_wm) {
+    const int nch = H * BITS / 128;
+    uint32_t mb = 0u;                                        // largest |x| as ordered bits
+    stage_x_pass<BITS>(x, nch, 1.0f, xs, xsum, mb);
+    mb = wave_max_u32(mb);
+    if ((threadIdx.x & 63) == 0) s_wm[threadIdx.x >> 6] = mb;
+    __syncthreads();
+    uint32_t all = s_wm[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) all = max(all, s_wm[w]);
+    const int e = range_exp(__uint_as_float(all));
+    if (e != 0) {                                            // rows of extreme magnitude only
+        stage_x_pass<BITS>(x, nch, exp2i(e), xs, xsum, mb);
+        __syncthreads();
+    }
+    return e;
+}
 
 // [gate; up] row pairs j0 and j0 + 1 of expert e in matrix stacks (mg, mu): SwiGLU
-// values (in every lane of the row group; lpr lanes share a pair).  Each step loads one
+// values (in every lane of the row group; lpr lanes share a pair), g and u taken out of
+// x's range scale by xinv.  Each step loads one
 // chunk of each of the 4 rows; loads are unconditional (a lane past the row end re-reads
 // the last chunk and discards it) so that all of a step's loads are issued before any
 // wait.  Addresses are a uniform matrix base plus a 32-bit per-lane offset.
 template <int BITS>
 __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr,
-                             const uint32_t *xs, const float2 *xsum, int sb_bf16, float hv[2]) {
+                             const uint32_t *xs, const float2 *xsum, int sb_bf16, float xinv, float hv[2]) {
     constexpr int CPC = 128 / BITS;
     const int lr = (threadIdx.x & 63) % lpr;
     const int nch = H / CPC, ng = H / 64;
@@ -131,8 +153,8 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        const float g = group_sum(acc[2 * p], lpr);
-        const float u = group_sum(acc[2 * p + 1], lpr);
+        const float g = group_sum(acc[2 * p], lpr) * xinv;
+        const float u = group_sum(acc[2 * p + 1], lpr) * xinv;
         hv[p] = silu(g) * u;
     }
 }
@@ -177,6 +199,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     __shared__ int s_idx[17];
     __shared__ float s_w[17];
     __shared__ float s_part[NW][DT / 64 * 16];
+    __shared__ uint32_t s_wm[NW];
     constexpr int CPC = 128 / BITS;
     const Layer &L = a.L;
     uint32_t *ctl = a.ctl;
@@ -268,34 +291,47 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int bpe = (I + pb - 1) / pb;                   // workgroups per expert
         const int slot = sh ? K : g / bpe;                   // h row (K = shared)
         const int j0 = (sh ? g : g % bpe) * pb + 2 * (wave * rpw + lane / a.lprg);
-        stage_x<BITS>(a.x, H, xs, xsum);
+        const int xe = stage_x<BITS>(a.x, H, xs, xsum, s_wm);     // ends with a barrier
         int e = 0;
-        if (sh) {
-            __syncthreads();
-        } else {
+        if (!sh) {
             get_topk(ctl, tag, E, K, gated, s_idx, s_w);     // ends with a barrier
             e = __builtin_amdgcn_readfirstlane(s_idx[slot]);
         }
         const int jj = j0 < I ? j0 : I - 2;
         float hv[2];
-        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, sb_bf16, hv);
-        // the workgroup's pb / 2 words (one per row group, consecutive in j) are gathered
-        // in LDS and written to every copy in 16-byte pieces
-        __shared__ uint32_t s_hw[NW * 64];
+        pairs_swiglu<BITS>(sh ? L.s_gate : L.gate, sh ? L.s_up : L.up, e, jj, H, a.lprg, xs, xsum, sb_bf16,
+                           exp2i(-xe), hv);
+        // the workgroup's pb values (two per row group, consecutive in j: one slice of h)
+        // are gathered in LDS; fp16 pairs under the slice's range scale 2^es go to every
+        // copy in 16-byte pieces, and es itself to the slice's word
+        __shared__ float s_hv[2 * NW * 64];
         const int wi = wave * rpw + lane / a.lprg;           // word within the workgroup
-        if (lane % a.lprg == 0) s_hw[wi] = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1]));
+        if (lane % a.lprg == 0) {
+            s_hv[2 * wi] = hv[0];
+            s_hv[2 * wi + 1] = hv[1];
+        }
         __syncthreads();
         const int jb = j0 - 2 * wi;                          // first j of the workgroup
         const int nw = min(pb, I - jb) / 2;                  // valid words
+        if (tid >= H_COPIES * ((nw + 1) / 2) && tid >= H_COPIES) return;   // no store to make
+        // (each storing thread finds the slice's largest magnitude itself: no barrier)
+        uint32_t mb = 0u;
+        for (int i = 0; i < 2 * nw; ++i) mb = max(mb, __float_as_uint(s_hv[i]) & 0x7fffffffu);
+        const int es = range_exp(__uint_as_float(mb));
+        const float f = exp2i(es);
+        auto word = [&](int i) { return pack_f16x2(f32_to_f16_ftz(s_hv[2 * i] * f), f32_to_f16_ftz(s_hv[2 * i + 1] * f)); };
         const int pieces = (nw + 1) / 2;
         for (int t = tid; t < H_COPIES * pieces; t += DT) {
             const int cp = t / pieces, q = t % pieces;
             uint32_t *dst = ctl + H_BASE + cp * H_STRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
             if (2 * q + 1 < nw)
-                st_dev128(dst, (u32x4){s_hw[2 * q], tag, s_hw[2 * q + 1], tag});
+                st_dev128(dst, (u32x4){word(2 * q), tag, word(2 * q + 1), tag});
             else
-                st_dev64((uint64_t *)dst, s_hw[2 * q] | ((uint64_t)tag << 32));
+                st_dev64((uint64_t *)dst, word(2 * q) | ((uint64_t)tag << 32));
         }
+        if (tid < H_COPIES)
+            st_dev64((uint64_t *)(ctl + H_BASE + tid * H_STRIDE + H_EXP + 2 * (slot * bpe + jb / pb)),
+                     (uint32_t)es | ((uint64_t)tag << 32));
         return;
     }
     {
@@ -323,6 +359,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         constexpr int CPITCH = CPC + 8;
         uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * nch chunks
         float2 *hsum = (float2 *)(dsm + nvec * nch * CPITCH / 2);   // chunk sums (even, odd columns)
+        float *hinv = (float *)(hsum + nvec * nch);                 // chunk range scales, inverted
         // lane j < nvec holds row 0 of vector j's down matrix (the k routed experts in
         // ascending id, then the shared one) and its combine weight
         uint64_t pc = 0, ps = 0, pbi = 0;
@@ -363,26 +400,47 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             __builtin_amdgcn_sched_barrier(0);
             if (base == 0) {
                 // all of h (S and G) as it arrives.  Thread t takes groups of 8
-                // consecutive values (4 words): fp16 into LDS in code order with one
-                // 16-byte write, and the chunk sums by a DPP sum over the chunk's groups
+                // consecutive values (4 words) and the word of the slice they belong to:
+                // the chunk's slices are brought to their smallest range scale (exact: a
+                // power of two), fp16 into LDS in code order with one 16-byte write, and
+                // the chunk sums by a DPP sum over the chunk's groups
                 const uint64_t *hw = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE);
+                const uint64_t *he = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE + H_EXP);
                 const int ngrp = nvec * I / 8;
+                const int pbg = 2 * NW * (64 / a.lprg);               // values per slice
+                const int nsl = (I + pbg - 1) / pbg;                  // slices per vector
                 const uint32_t lim = wait_bound(ctl);
                 for (int g0 = 0; g0 < ngrp; g0 += DT) {
                     const int g = g0 + tid;
                     const bool live = g < ngrp;
                     const int gg = live ? g : ngrp - 1;
+                    const int sv = (8 * gg) / I, sj = (8 * gg) % I;
+                    const uint64_t *ep = he + sv * nsl + sj / pbg;
                     u32x4 w0, w1;                                // words (value pair, tag) x 4
+                    uint64_t we;
                     for (uint32_t t = 0;; ++t) {
+                        we = ld_dev64(ep);
                         ld_dev256(hw + 4 * gg, w0, w1);
-                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
+                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag && tag_of(we) == tag) break;
                         if (t > lim) {
                             raise_error(ctl);
                             break;
                         }
                         poll_pause(t);
                     }
-                    const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                    const int es = (int)(uint32_t)we;
+                    int ec = es;                                 // the chunk's smallest slice scale
+                    if (CPC / 8 >= 2) ec = min(ec, (int)dpp_u32<0xB1>((uint32_t)ec + 128u) - 128);
+                    if (CPC / 8 >= 4) ec = min(ec, (int)dpp_u32<0x4E>((uint32_t)ec + 128u) - 128);
+                    u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                    if (ec != es) {                              // (slices of extreme magnitude only)
+                        const float fr = exp2i(ec - es);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const f16x2 hh = as_h2(nat[j]);
+                            nat[j] = pack_f16x2(f32_to_f16_ftz((float)hh[0] * fr), f32_to_f16_ftz((float)hh[1] * fr));
+                        }
+                    }
                     float se = 0.0f, so = 0.0f;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -393,7 +451,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
                     se = group_sum(se, CPC / 8);                 // groups of a chunk are adjacent lanes
                     so = group_sum(so, CPC / 8);
-                    if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
+                    if (live && (g % (CPC / 8)) == 0) {
+                        hsum[g / (CPC / 8)] = make_float2(se, so);
+                        hinv[g / (CPC / 8)] = exp2i(-ec);
+                    }
                 }
                 __syncthreads();
                 // this workgroup has all it reads of the call's state: count it in now
@@ -406,7 +467,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 const int vi = live ? v2 : min(vlast, nvec - 1);
                 const int c = lr + k2 * lpr, cc = c < nch ? c : nch - 1;
                 const float p = chunk_dot<BITS>(q[i], (const uint32_t *)(hs16 + (vi * nch + cc) * CPITCH), sv[i], bv[i],
-                                                hsum[vi * nch + cc], sb_bf16);
+                                                hsum[vi * nch + cc], sb_bf16) * hinv[vi * nch + cc];
                 const float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), vi));
                 yv += (live && c < nch) ? wv * p : 0.0f;       // experts in ascending id, shared last
                 if (++k2 == cpl) { k2 = 0; ++v2; }
@@ -485,7 +546,7 @@ hipError_t launch(DecArgs a, hipStream_t s) {
         // every selector has started before the call can complete
         while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
         const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 8;
-        const size_t lds_d = (size_t)nvec * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nvec * (L.I / cpc) * 8;
+        const size_t lds_d = (size_t)nvec * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nvec * (L.I / cpc) * 12;
         lds = lds_g > lds_d ? lds_g : lds_d;
     }
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;

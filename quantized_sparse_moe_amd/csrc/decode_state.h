@@ -38,7 +38,11 @@ constexpr int LOGIT_STRIDE = 2 * 256 + 64;  // per copy: E words of 64 bits, log
 constexpr int LOGIT_BASE = CNT_TOP + 64;
 constexpr int H_COPIES = 8;
 constexpr int H_WORDS_MAX = 24576 / 2;      // (top_k + 1) * inter <= 24576
-constexpr int H_STRIDE = 2 * H_WORDS_MAX + 64;  // per copy: (K+1)*I/2 words, fp16 h[j], h[j+1] | tag << 32
+// per copy (T = 1): (K+1)*I/2 words (fp16 h[j], h[j+1] scaled by 2^e | tag << 32), then
+// one word (e | tag << 32) per slice of h that one gate/up workgroup computes
+constexpr int HEXP_MAX = 2304;              // slices per copy: (K+1) * I / 16 <= 1536
+constexpr int H_EXP = 2 * H_WORDS_MAX;      // u32 offset of the slice words in a copy
+constexpr int H_STRIDE = 2 * (H_WORDS_MAX + HEXP_MAX) + 64;
 constexpr int H_BASE = LOGIT_BASE + LOGIT_COPIES * LOGIT_STRIDE;
 constexpr int TOPK_COPIES = 32;
 constexpr int TOPK_STRIDE = 1088;           // per copy: 2 words of 64 bits per selected expert,
@@ -116,6 +120,19 @@ __device__ void finish_call(uint32_t *ctl, uint32_t tag) {
 }
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
+
+// Power-of-two range scale of a row of fp16 operands: the largest magnitude m of the row
+// is kept where fp16 holds it with full precision.  0 when m is 0 or already in
+// [2^-8, 2^15); otherwise the e with m 2^e in [2^14, 2^15) (clamped to +-120), so that
+// multiplying by 2^e and later by 2^-e is exact.  Rows of ordinary magnitude are left
+// exactly as they are.
+__device__ __forceinline__ int range_exp(float m) {
+    if (!(m > 0.0f) || (m >= 0.00390625f && m < 32768.0f)) return 0;
+    const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;     // floor(log2 m) (normal m)
+    const int e = 14 - ex;
+    return e < -120 ? -120 : (e > 120 ? 120 : e);
+}
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
 // sum_c (s q_c + b) x_c over one 16-byte chunk of codes; X = (sum of x over the even
 // columns, over the odd columns).  4-bit: the low nibble of each byte (even columns)

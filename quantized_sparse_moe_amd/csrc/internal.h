@@ -31,7 +31,7 @@ struct Layer {
 // Decode state at the start of every workspace: zero before the first call, then kept
 // by the library between calls (call generation, completion counters, and the tagged
 // logit and h words the workgroups of one call hand to each other).
-constexpr size_t WS_CTL_BYTES = 1024 * 1024;
+constexpr size_t WS_CTL_BYTES = 2 * 1024 * 1024;
 
 struct DecodeBufs {
     uint32_t *ctl;                 // WS_CTL_BYTES of decode state

@@ -159,7 +159,7 @@ def test_workspace_sizes():
     d = desc()
     f = lambda T: q.lib().moe_workspace_size(ctypes.byref(d), T)
     assert f(0) == 0 and f(-3) == 0
-    assert 0 < f(1) <= 1 << 20                                           # decode: its 1 MiB state
+    assert 0 < f(1) <= 2 << 20                                           # decode: its 2 MiB state
     prev = f(2)
     for T in (3, 17, 64, 1000, 4096):
         assert f(T) >= prev
@@ -203,7 +203,7 @@ def test_workspace_status_validation():
     assert L.moe_workspace_status(FAKE + 64, 1 << 20, FAKE, 0, None) == q.MOE_ERR_INVALID
     assert L.moe_workspace_status(FAKE, 1 << 20, None, 0, None) == q.MOE_ERR_INVALID
     assert L.moe_workspace_status(FAKE, 1 << 20, FAKE + 2, 0, None) == q.MOE_ERR_INVALID
-    assert L.moe_workspace_status(FAKE, (1 << 20) - 1, FAKE, 1, None) == q.MOE_ERR_WORKSPACE
+    assert L.moe_workspace_status(FAKE, (2 << 20) - 1, FAKE, 1, None) == q.MOE_ERR_WORKSPACE
 
 
 def test_binding_constants_match_header():
