@@ -119,6 +119,8 @@ PrefillBufs carve_prefill(const moe_layer_desc *d, int64_t T, void *ws, size_t *
     PrefillBufs b;
     b.ctl = c.take<uint32_t>(WS_CTL_BYTES / 4);      // decode state stays untouched (but word 0)
     b.x16 = c.take<uint16_t>((size_t)(T * H));
+    b.xmax = c.take<uint32_t>((size_t)(T * 8));
+    b.xexp = c.take<int32_t>((size_t)T);
     b.logits = c.take<float>((size_t)(T * (E + 1)));     // + the shared-expert gate's logit
     b.idx = c.take<int32_t>((size_t)(T * K));
     b.w = c.take<float>((size_t)(T * K));
@@ -127,10 +129,12 @@ PrefillBufs carve_prefill(const moe_layer_desc *d, int64_t T, void *ws, size_t *
     b.expert_off = c.take<int32_t>((size_t)(2 * E + 1));
     b.perm = c.take<int32_t>((size_t)(T * K));
     b.tiles = c.take<Tile>((size_t)prefill_max_tiles(T, (int)K, (int)E));
-    b.ntiles = c.take<int32_t>(2);
+    b.ntiles = c.take<int32_t>(3);
     b.tile_done = c.take<int32_t>((size_t)prefill_max_tiles(T, (int)K, (int)E));
     b.h = c.take<uint16_t>((size_t)((T * K + T) * I));
+    b.hexp = c.take<int8_t>((size_t)((T * K + T) * HEXP_STRIDE));
     b.slot = c.take<uint16_t>((size_t)((T * K + T) * H));
+    b.sexp = c.take<int8_t>((size_t)(sexp_rows(T, (int)K) * (H / 64)));
     b.sgate = c.take<float>((size_t)T);
     *bytes = c.off;
     return b;

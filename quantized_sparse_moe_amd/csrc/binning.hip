@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_tiles(const int32_t *__restrict__ count
         t.pad = 0;
         tiles[routed + m] = t;
     }
-    if (tid == 0) { ntiles[0] = routed; ntiles[1] = routed + nsh; }
+    if (tid == 0) { ntiles[0] = routed; ntiles[1] = routed + nsh; ntiles[2] = 0; }
 }
 
 // Stable scatter of the assignments of one 32-token block into the expert bins.

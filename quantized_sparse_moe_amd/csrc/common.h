@@ -64,6 +64,36 @@ __device__ __forceinline__ _Float16 f32_to_f16_ftz(float v) {
     return (__builtin_fabsf(v) < 6.103515625e-05f) ? (_Float16)0.0f : (_Float16)v;
 }
 
+// ------------------------------------------------------------------ range scaling
+// fp16 operands carry power-of-two range scales wherever a row of values could leave
+// fp16's range (65504 at the top; the flush above at 2^-14 at the bottom).  A scale 2^e
+// and its later removal by 2^-e are exact, so a row that is scaled gives the same
+// products as an unscaled row in a wider format.
+//
+// floor(log2 m) for m > 0 (subnormal fp32 counts as -127)
+__device__ __forceinline__ int ilog2f(float m) { return (int)((__float_as_uint(m) >> 23) & 0xffu) - 127; }
+__device__ __forceinline__ int clamp_exp(int e) { return e < -120 ? -120 : (e > 120 ? 120 : e); }
+// 2^e for |e| <= 126
+__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// Scale of a row whose largest magnitude is m: 0 when m is 0 or in [2^-2, 2^15), where
+// fp16 holds the row with at most 2^-12 of its largest value lost to the flush; else
+// the e with m 2^e in [2^14, 2^15) (clamped to +-120).  Rows of ordinary magnitude are
+// left exactly as they are.
+__device__ __forceinline__ int range_exp(float m) {
+    if (!(m > 0.0f) || (m >= 0.25f && m < 32768.0f)) return 0;
+    return clamp_exp(14 - ilog2f(m));
+}
+// The same for row pieces that are later joined under one scale (the column blocks of an
+// h row): multiples of 8 only, so that pieces of similar magnitude share their scale and
+// the join rarely has to rescale.  0 on [2^-2, 2^15); above, m 2^e lands in [2^7, 2^15);
+// below, in [2^-2, 2^6).
+__device__ __forceinline__ int block_exp(float m) {
+    if (!(m > 0.0f) || (m >= 0.25f && m < 32768.0f)) return 0;
+    const int l = ilog2f(m);
+    return clamp_exp(l > 14 ? -8 * ((l - 14 + 7) >> 3) : 8 * ((-2 - l + 7) >> 3));
+}
+
 // reinterpret a dword as two fp16 (by value: never bit_cast a vector-element lvalue)
 __device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 

@@ -27,6 +27,7 @@ constexpr int CTL_ERR = 0;                  // MOE_WS_ERR_* bits: a bounded wait
 constexpr int CTL_SPIN = 32;                // 0: every wait polls at most SPIN_LIMIT times;
                                             // else at most this many (set only by a test of
                                             // the give-up path, which must not hang)
+                                            // (word 33: CTL_HBLOCK_EXACT, read by the grouped GEMM)
 constexpr int CTL_GEN = 64;                 // calls completed; this call's tag is gen + 1
 constexpr int CNT_BASE = 128;               // + g * 64: completion group counters
 constexpr int CNT_TOP = CNT_BASE + NGRP * 64;
@@ -121,18 +122,6 @@ __device__ void finish_call(uint32_t *ctl, uint32_t tag) {
 
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
 
-// Power-of-two range scale of a row of fp16 operands: the largest magnitude m of the row
-// is kept where fp16 holds it with full precision.  0 when m is 0 or already in
-// [2^-8, 2^15); otherwise the e with m 2^e in [2^14, 2^15) (clamped to +-120), so that
-// multiplying by 2^e and later by 2^-e is exact.  Rows of ordinary magnitude are left
-// exactly as they are.
-__device__ __forceinline__ int range_exp(float m) {
-    if (!(m > 0.0f) || (m >= 0.00390625f && m < 32768.0f)) return 0;
-    const int ex = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;     // floor(log2 m) (normal m)
-    const int e = 14 - ex;
-    return e < -120 ? -120 : (e > 120 ? 120 : e);
-}
-__device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
 
 // sum_c (s q_c + b) x_c over one 16-byte chunk of codes; X = (sum of x over the even
 // columns, over the odd columns).  4-bit: the low nibble of each byte (even columns)

@@ -4,8 +4,7 @@
 // never expanded in memory; each workgroup dequantizes the weight tile it is about to
 // multiply, straight into MFMA operand registers, with fp32 accumulation.
 // [LILY] "Keep expert routing on the GPU" / "Match tile size to expert load": work is
-// enumerated as (expert row block, column block) items from the device-side block map;
-// a partial row block skips its empty 16-row MFMA subtiles.
+// enumerated as (expert row block, column block) items from the device-side block map.
 // [OMLX] "Fusion principle": gate row j and up row j of one expert are handled by the
 // same wave, so SwiGLU is formed in registers and only h leaves the kernel.
 //
@@ -23,13 +22,12 @@
 // (global_load_lds), which take no registers and no ALU.  Scales and biases come 8 groups
 // (16 bytes) per row at a time every 8 K steps (4-bit; 2 groups for 8-bit, whose larger
 // code stages leave less LDS): a per-step 2-byte load per row costs the address unit as
-// much as a 16-byte one, and cost 17 % of the layer time.  A ring of stages keeps two K
-// steps in flight (one for 8-bit codes, whose stages are larger) while the current
-// one is multiplied; each wave waits only for its own loads (vmcnt) and one barrier
-// per step publishes the stage to the whole workgroup.  The position of each 16-byte
-// chunk in LDS is XOR-swizzled by row so that the MFMA operand reads are free of bank
-// conflicts (direct-to-LDS loads place lane l at byte 16 l, so the swizzle is chosen
-// by which global chunk each lane fetches).
+// much as a 16-byte one.  A ring of two stages holds the K step being multiplied and the
+// next one in flight; each wave waits only for its own loads (vmcnt) and one barrier per
+// step publishes the stage to the whole workgroup.  The position of each 16-byte chunk of
+// an activation row in LDS is XOR-swizzled by (row / 2) mod 8, so that the 16 lanes a
+// 128-bit fragment read serves at once hit all 64 banks (direct-to-LDS loads place lane l
+// at byte 16 l, so the swizzle is chosen by which global chunk each lane fetches).
 //
 // Operands: activations fp16 (x copy from the router, h from the gate/up pass) with
 // each group of 8 columns permuted into the order the packed codes unpack in (see
@@ -37,6 +35,24 @@
 // the 1024-magic.  (fp16 rather than bf16 operands: at these sizes weights rounded to
 // bf16 leave ~2e-2 x RMS of error in the layer output, fp16 ~2e-3; the matrix rate is
 // the same.)
+//
+// Range: fp16 holds neither bf16's range nor every product of the layer, so every fp16
+// operand carries an exact power-of-two scale, removed in fp32 after the MFMAs.
+//   - x: per token (x16 row t is x 2^a_t, chosen by the router).
+//   - weights: per workgroup (its 256 weight rows), 2^p with p set before the K loop
+//     from a bound on their |w| (max over rows and groups of |s| (2^bits - 1) + |b|), so
+//     the largest weight lies in [2^14, 2^15): the scales and biases are converted to
+//     fp16 s 2^p, b 2^p when their window lands in LDS (bf16 or fp16 in; exact), and
+//     s 2^p / 16 stays a normal number for every group within 2^24 of the largest.  One
+//     factor per tile is taken out with the row factors, at no cost per element.
+//   - h: per (row, 128-column block), 2^e with e from the block's largest |h|: 0 for
+//     blocks in [2^-2, 2^15), else a multiple of 8 (blocks of similar magnitude share
+//     it).  The down pass multiplies h row r under the smallest e_r of its blocks: a tile
+//     whose rows all have one e per row reads h as it is; otherwise each wave rescales
+//     the chunks it loaded by 2^(e_r - e) in LDS before the stage is published.
+//   - slot rows: per (row, 64-column block), 2^e from the block's largest value, taken
+//     out by the combine.
+// With every scale 0 (ordinary data) the arithmetic is exactly that of unscaled fp16.
 //
 // Modes: 0 = [gate; up] + SwiGLU -> h (routed rows gathered through perm, shared rows
 // direct); 1 = down projection: routed tiles -> slot row t*k + j = w_tj * o (fp16),
@@ -76,21 +92,39 @@ static_assert(Cfg<4>::NSTAGE == 2 && Cfg<8>::NSTAGE == 2, "every stage wait is a
 struct GemmArgs {
     Layer L;
     int64_t T;
-    const uint16_t *x16;             // [T][H] fp16 (permuted)
-    uint16_t *h;                     // [(T*K + T)][I] fp16 (permuted)
+    const uint16_t *x16;             // [T][H] fp16 (permuted); row t is x_t 2^xexp[t]
+    const int32_t *xexp;             // [T]
+    uint16_t *h;                     // [(T*K + T)][I] fp16 (permuted), per-block scaled
+    int8_t *hexp;                    // [(T*K + T)][HEXP_STRIDE] the scale of each 128-column block
     const int32_t *perm;
     const Tile *tiles;
-    const int32_t *ntiles;
+    int32_t *ntiles;                 // tile counts; [2] = 1 once a down workgroup stored a scaled slot block
     const float *w;                  // [T*K]
     uint16_t *slot;                  // [T*K + T][H]
+    int8_t *sexp;                    // [H / 64][sexp_rows(T, K)]
     void *y;
     int y_dtype;
     int nb;                          // column blocks per tile
     int wlog;                        // log2 of the scale / bias window (groups per row per load)
+    int sb16;                        // scale / bias rows are runs of 8 groups, 16-byte aligned
     int32_t *tile_done;              // [tiles] gate/up column blocks finished (zeroed by binning)
     const float *sgate;              // [T] shared-expert gate per token (gated layers), or null
     int nb_gateup;                   // down pass: the gate/up column blocks a tile waits for
-    uint32_t *err;                   // bounded-wait error flag
+    uint32_t *err;                   // the workspace's state words (0: bounded-wait error flag)
+};
+
+// per-row values of a tile beside the ring: the gate/up pass needs each row's 2^-a of x,
+// the down pass each row's (token, slot) position, weight, and h block scales
+struct DownRows {
+    int pos[BM];
+    float w[BM];                     // routing weight (or shared gate) x 2^-e_r
+    int8_t e[BM];                    // e_r: the smallest block scale of h row r
+    int8_t hx[BM * HEXP_STRIDE];     // the block scales of each row
+    int mixed[4];                    // per wave: some row's block scales differ
+};
+union TileRows {
+    float xs[BM];
+    DownRows dn;
 };
 
 typedef __attribute__((address_space(3))) void lds_t;
@@ -154,7 +188,8 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f1
 }
 
 template <int BITS, int MODE>
-__device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint8_t *smem) {
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint8_t *smem, TileRows &sx,
+                                          uint32_t *s_wb) {
     using C = Cfg<BITS>;
     const Layer &L = a.L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -194,41 +229,51 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
     const int row_bytes = Kdim * BITS / 8;
     const int ngrp = Kdim / 64;
 
-    // ---- per-lane sources of the direct-to-LDS loads
-    const uint16_t *asrc[C::A_DMA];
-    {
-        const int ach = (lane & 7) ^ (lane >> 3);      // swizzled chunk this lane fetches
+    // ---- per-lane sources of the direct-to-LDS loads.  Activation piece i of this wave
+    // is rows 8 p .. 8 p + 7 of the tile (p = A_DMA wave + i); the lane fetches, for row
+    // 8 p + lane / 8, the chunk that the swizzle stores at position lane % 8.  Sources are
+    // kept as 16-byte chunk indices from a uniform base (x16, or the tile's first h row).
+    auto apiece = [&](int i, int &r, int &ach) __attribute__((always_inline)) {
+        const int rpos = 8 * (C::A_DMA * wave + i) + (lane >> 3);
+        ach = (lane & 7) ^ ((rpos >> 1) & 7);
+        r = rpos < nrows ? rpos : nrows - 1;             // rows past the tile repeat a valid one
+    };
+    const uint16_t *abase = MODE == 0 ? a.x16 : a.h + (int64_t)tile.row0 * I;
+    uint32_t achunk[C::A_DMA];
 #pragma unroll
-        for (int i = 0; i < C::A_DMA; ++i) {
-            int r = 8 * C::A_DMA * wave + 8 * i + (lane >> 3);
-            r = r < nrows ? r : nrows - 1;             // rows past the tile repeat a valid one
-            int64_t src;
-            if (MODE == 0) {
-                const int64_t t = shared ? (tile.row0 - TK + r) : (a.perm[tile.row0 + r] / K);
-                src = t * H;
-                asrc[i] = a.x16 + src + 8 * ach;
-            } else {
-                src = (int64_t)(tile.row0 + r) * I;
-                asrc[i] = a.h + src + 8 * ach;
-            }
+    for (int i = 0; i < C::A_DMA; ++i) {
+        int r, ach;
+        apiece(i, r, ach);
+        if (MODE == 0) {
+            const int64_t t = shared ? (tile.row0 - TK + r) : (a.perm[tile.row0 + r] / K);
+            achunk[i] = (uint32_t)(t * (H / 8) + ach);
+        } else {
+            achunk[i] = (uint32_t)(r * (I / 8) + ach);
         }
     }
-    const uint8_t *bsrc[C::B_DMA];
+    // code sources: the matrix of DMA d is the same for the whole wave (MODE 0: the first
+    // half of the DMAs fetch gate rows, the second half up rows), so each is a uniform
+    // matrix base plus a 32-bit lane offset
+    const uint8_t *bbase[C::B_DMA];
+    uint32_t boff[C::B_DMA];
 #pragma unroll
     for (int d = 0; d < C::B_DMA; ++d) {
         QMat m;
+        int rs, sel;
         if constexpr (BITS == 4) {
-            const int rs = 64 * wave + 32 * d + (lane >> 1);
-            const int hsel = (lane & 1) ^ ((rs >> 2) & 1);
-            const int r = wrow(rs, m);
-            bsrc[d] = m.codes + (e * m.stride + r) * row_bytes + 16 * hsel;
+            rs = 64 * wave + 32 * d + (lane >> 1);
+            sel = (lane & 1) ^ ((rs >> 2) & 1);
         } else {
-            const int rs = 64 * wave + 16 * d + (lane >> 2);
-            const int q = (lane & 3) ^ ((rs >> 1) & 3);
-            const int r = wrow(rs, m);
-            bsrc[d] = m.codes + (e * m.stride + r) * row_bytes + 16 * q;
+            rs = 64 * wave + 16 * d + (lane >> 2);
+            sel = (lane & 3) ^ ((rs >> 1) & 3);
         }
+        const int r = wrow(rs, m);
+        const QMat mu = MODE == 0 ? (2 * d < C::B_DMA ? (shared ? L.s_gate : L.gate) : (shared ? L.s_up : L.up))
+                                  : (shared ? L.s_down : L.down);
+        bbase[d] = mu.codes + e * mu.stride * row_bytes;
+        boff[d] = (uint32_t)(r * row_bytes + 16 * sel);
     }
+    // this thread's weight row (slot 64 wave + lane): its scale / bias windows, and its range
     const uint16_t *ssrc, *bisrc;
     {
         QMat m;
@@ -241,14 +286,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::A_DMA; ++i) {
-            if (MODE == 1) dma16_dev(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
-            else dma16(asrc[i] + k * BK, st + (8 * C::A_DMA * wave + 8 * i) * 128);
+            const uint16_t *src = abase + (uint64_t)achunk[i] * 8 + k * BK;
+            if (MODE == 1) dma16_dev(src, st + (8 * C::A_DMA * wave + 8 * i) * 128);
+            else dma16(src, st + (8 * C::A_DMA * wave + 8 * i) * 128);
         }
         uint8_t *bst = st + C::A_BYTES;
 #pragma unroll
         for (int d = 0; d < C::B_DMA; ++d) {
-            if constexpr (BITS == 4) dma16(bsrc[d] + k * 32, bst + (64 * wave + 32 * d) * 32);
-            else dma16(bsrc[d] + k * 64, bst + (64 * wave + 16 * d) * 64);
+            if constexpr (BITS == 4) dma16(bbase[d] + boff[d] + k * 32, bst + (64 * wave + 32 * d) * 32);
+            else dma16(bbase[d] + boff[d] + k * 64, bst + (64 * wave + 16 * d) * 64);
         }
         // scales and biases: W = 2^wlog groups of each row every W K steps, into a ring of
         // two windows (one 2-byte read per lane costs the address unit as much as a 16-byte
@@ -268,114 +314,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         }
     };
 
-    f32x4 acc[MT][4];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc[i][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    const int n16 = lane & 15, cg = lane >> 4;
-    constexpr int CW = BITS == 4 ? 2 : 4;           // code dwords per lane and subtile per K step
-
-    // wait until stage `k` has landed: `newer` stages were issued after it
-    auto wait_stage = [&](int newer) __attribute__((always_inline)) {
-        if (newer >= 2) wait_dma<2 * C::DMA>();
-        else if (newer == 1) wait_dma<C::DMA>();
-        else wait_dma<0>();
-    };
-    // operands of K step k from the LDS ring: per weight subtile j, the code dwords of
-    // K slice s of this lane, and the scale and bias
-    auto load_codes = [&](int k, int s, uint32_t (&cw)[4][CW / 2]) __attribute__((always_inline)) {
-        const uint8_t *bst = smem + (k % C::NSTAGE) * C::STAGE + C::A_BYTES;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rs = 64 * wave + 16 * j + n16;
-            if constexpr (BITS == 4) {
-                const int hsel = (cg >> 1) ^ ((rs >> 2) & 1);
-                cw[j][0] = *(const uint32_t *)(bst + rs * 32 + hsel * 16 + (cg & 1) * 8 + 4 * s);
-            } else {
-                const int q = cg ^ ((rs >> 1) & 3);
-                const uint32_t *p = (const uint32_t *)(bst + rs * 64 + q * 16 + 8 * s);
-                cw[j][0] = p[0];
-                cw[j][1] = p[1];
-            }
-        }
-    };
-    auto load_sb = [&](int k, f16x2 (&sc)[4], f16x2 (&sc16)[4], f16x2 (&bi)[4]) __attribute__((always_inline)) {
-        // row rs, group k % W of the window: 16 (W = 8) or 4 bytes per row, 2 bytes per
-        // group (W = 1: the low half of the dword a 2-byte load fills)
-        const int pitch = a.wlog == 3 ? 16 : 4;
-        const uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES +
-                            2 * (k & ((1 << a.wlog) - 1));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int rs = 64 * wave + 16 * j + n16;
-            const uint16_t sbits = *(const uint16_t *)(sw + rs * pitch);
-            const uint16_t bbits = *(const uint16_t *)(sw + C::S_BYTES + rs * pitch);
-            // bf16 scales and biases become fp16 exactly (8 significant bits, in range)
-            const _Float16 sv = L.sb_bf16 ? (_Float16)__uint_as_float((uint32_t)sbits << 16)
-                                          : __builtin_bit_cast(_Float16, sbits);
-            const _Float16 bv = L.sb_bf16 ? (_Float16)__uint_as_float((uint32_t)bbits << 16)
-                                          : __builtin_bit_cast(_Float16, bbits);
-            sc[j] = (f16x2){sv, sv};
-            const _Float16 sv16 = sv * (_Float16)0.0625f;        // exact: scales are normal numbers
-            sc16[j] = (f16x2){sv16, sv16};
-            bi[j] = (f16x2){bv, bv};
-        }
-    };
-    uint32_t cw[4][CW / 2];
-    f16x2 sc[4], sc16[4], bi[4];
-    DqConst dk;
-    dk.lo = BITS == 4 ? 0x000F000Fu : 0x00FF00FFu;
-    dk.hi = 0x00F000F0u;
-    dk.magic = QS_MAGIC;
-    auto deq = [&](const uint32_t (&cw)[4][CW / 2], f16x8 (&B)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (BITS == 4) B[j] = dequant8<4>(cw[j][0], 0u, sc[j], sc16[j], bi[j], dk);
-            else B[j] = dequant8<8>(cw[j][0], cw[j][1], sc[j], sc16[j], bi[j], dk);
-        }
-    };
-
-
-    // The K loop: per 64-wide step, one barrier (stage k visible, stage k-1 consumed),
-    // the refill of stage k-1's buffer with stage k+NSTAGE-1, then two MFMA blocks
-    // (32-wide slices), each on a weight slice dequantized just before it.  All ten row
-    // subtiles run, so every fragment read of a block is issued ahead of its MFMAs.
-    auto kloop = [&]() __attribute__((always_inline)) {
-        for (int k = 0; k < nk; ++k) {
-            // stage k has landed once at most the later stages' loads are outstanding
-            const int issued = k + C::NSTAGE - 1 < nk ? C::NSTAGE - 2 : nk - 1 - k;
-            wait_stage(issued < 0 ? 0 : issued);
-            block_sync();
-            if (k + C::NSTAGE - 1 < nk) issue(k + C::NSTAGE - 1);
-            const uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
-            load_sb(k, sc, sc16, bi);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int pos = (2 * cg + s) ^ (n16 & 7);
-                f16x8 A[MT];
-#pragma unroll
-                for (int i = 0; i < MT; ++i) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
-                load_codes(k, s, cw);
-                f16x8 B[4];
-                deq(cw, B);
-#pragma unroll
-                for (int i = 0; i < MT; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], B[j], acc[i][j], 0, 0, 0);
-            }
-        }
-    };
-    // MODE 1: the (token, slot) position and routing weight of tile row `tid` (tid < BM)
-    // are fetched now, their latency hidden by the K loop, and parked in LDS after it
-    __shared__ int s_pos[BM];
-    __shared__ float s_w[BM];
+    // ---- the down pass waits for its tile's h rows and reads their block scales
+    bool slow = false;                   // some row's h blocks differ in scale: rescale in LDS
+    const bool routed_down = MODE == 1 && !shared;
+    const int my_row = tid < nrows ? tid : nrows - 1;
+    // the (token, slot) position and routing weight (or shared gate) of tile row `tid`,
+    // fetched first, so that they have landed when the rows' factors are set below
     int my_pos = 0;
     float my_w = 0.0f;
-    const bool routed_down = MODE == 1 && !shared;
-    if (routed_down && tid < BM) my_pos = a.perm[tile.row0 + (tid < nrows ? tid : nrows - 1)];
+    if (MODE == 1 && tid < BM) {
+        if (routed_down) {
+            my_pos = a.perm[tile.row0 + my_row];
+            my_w = a.w[my_pos];
+        } else {
+            my_w = a.sgate ? a.sgate[tile.row0 + my_row - TK] : 1.0f;
+        }
+    }
     if (MODE == 1) {
         // this tile's h rows are complete once all gate/up column blocks of the tile have
         // counted themselves in; they run earlier in the grid (lower workgroup index,
@@ -399,31 +353,323 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
 #pragma unroll
     for (int p = 0; p < C::NSTAGE - 1; ++p)
         if (p < nk) issue(p);
-    if (routed_down && tid < BM) my_w = a.w[my_pos];
-    kloop();
-    if (routed_down && tid < BM) {
-        s_pos[tid] = my_pos;
-        s_w[tid] = my_w;
+    u32x4 hw = {0u, 0u, 0u, 0u};         // down pass: the block scales of h row `tid`
+    if (MODE == 1 && tid < BM) {
+        // (device scope: written by other workgroups of this launch)
+        const uint32_t *hp = (const uint32_t *)(a.hexp + (int64_t)(tile.row0 + my_row) * HEXP_STRIDE);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hw[q] = __hip_atomic_load(hp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    int my_xe = 0;                       // gate/up pass: the scale exponent of x in row `tid`
+    if (MODE == 0 && tid < BM) {
+        const int64_t t = shared ? (tile.row0 - TK + my_row) : (a.perm[tile.row0 + my_row] / K);
+        my_xe = a.xexp[t];
+    }
+    // ---- the bound max_g |s_g| (2^bits - 1) + |b_g| on the |w| of this thread's weight
+    // row; the largest over the workgroup's rows sets the prescale 2^p (largest weight in
+    // [2^14, 2^15))
+    float wsc, winv;
+    bool convert;                        // the scale windows need converting (bf16 in, or p != 0)
+    {
+        constexpr float QMAX = (float)((1 << BITS) - 1);
+        const int bf = L.sb_bf16;
+        float M = 0.0f, smin = __builtin_inff();
+        auto bound = [&](uint32_t sbits, uint32_t bbits) __attribute__((always_inline)) {
+            const float sv = fabsf(sb_to_f32(sbits & 0xffffu, bf));
+            M = fmaxf(M, fmaf(sv, QMAX, fabsf(sb_to_f32(bbits & 0xffffu, bf))));
+            smin = fminf(smin, sv > 0.0f ? sv : __builtin_inff());
+        };
+        if (a.sb16) {                                             // rows of 8-group runs, 16-byte aligned
+#pragma unroll 4
+            for (int g = 0; g < ngrp; g += 8) {
+                const u32x4 sv = *(const u32x4 *)(ssrc + g), bv = *(const u32x4 *)(bisrc + g);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    bound(sv[q], bv[q]);
+                    bound(sv[q] >> 16, bv[q] >> 16);
+                }
+            }
+        } else if (a.wlog == 1) {                                 // 2-group runs, 4-byte aligned
+#pragma unroll 4
+            for (int g = 0; g < ngrp; g += 2) {
+                const uint32_t sv = *(const uint32_t *)(ssrc + g), bv = *(const uint32_t *)(bisrc + g);
+                bound(sv, bv);
+                bound(sv >> 16, bv >> 16);
+            }
+        } else {
+#pragma unroll 4
+            for (int g = 0; g < ngrp; ++g) bound(ssrc[g], bisrc[g]);
+        }
+        // (non-negative floats order as their bit patterns; the minimum as the maximum of
+        // the complements)
+        const uint32_t mw = wave_max_u32(__float_as_uint(M)), nw = wave_max_u32(~__float_as_uint(smin));
+        if (lane == 0) {
+            s_wb[wave] = mw;
+            s_wb[4 + wave] = nw;
+        }
+        __syncthreads();
+        M = __uint_as_float(max(max(s_wb[0], s_wb[1]), max(s_wb[2], s_wb[3])));
+        smin = __uint_as_float(~max(max(s_wb[4], s_wb[5]), max(s_wb[6], s_wb[7])));
+        // no prescale where the weights already sit in fp16's range: largest bound in
+        // [2^-2, 2^15) and (4-bit) every nonzero s / 16 a normal number
+        const bool in_range = M >= 0.25f && M < 32768.0f && (BITS == 8 || smin >= 0.0009765625f);
+        const int p = in_range || !(M > 0.0f) ? 0 : clamp_exp(14 - ilog2f(M));
+        wsc = exp2i(p);
+        winv = exp2i(-p);
+        convert = L.sb_bf16 || p != 0;
+    }
+    // ---- per-row factors, parked in LDS until the epilogue (published by the K loop's
+    // first barrier): gate/up, 2^-a 2^-p (x's and the weights' scales); down, the routing
+    // weight times 2^-e_r 2^-p, with the row's block scales for the rescale
+    if (MODE == 0 && tid < BM) sx.xs[tid] = exp2i(-my_xe) * winv;
+    if (MODE == 1) {
+        bool mixed = false;
+        if (tid < BM) {
+            int lo = 127, hi = -128;
+#pragma unroll
+            for (int bk = 0; bk < HEXP_STRIDE; ++bk)
+                if (bk < a.nb_gateup) {
+                    const int v = (int)(int8_t)(hw[bk >> 2] >> (8 * (bk & 3)));
+                    lo = v < lo ? v : lo;
+                    hi = v > hi ? v : hi;
+                }
+            mixed = lo != hi;
+            sx.dn.e[tid] = (int8_t)lo;
+            *(u32x4 *)(sx.dn.hx + tid * HEXP_STRIDE) = hw;
+            sx.dn.pos[tid] = my_pos;
+            sx.dn.w[tid] = my_w * exp2i(-lo) * winv;
+        }
+        // (each wave's flag is read after the K loop's first barrier; the ballot is taken
+        // by the whole wave)
+        const bool wm = __builtin_amdgcn_ballot_w64(mixed) != 0;
+        if (lane == 0) sx.dn.mixed[wave] = wm;
+    }
+
+    f32x4 acc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    const int n16 = lane & 15, cg = lane >> 4;
+    constexpr int CW = BITS == 4 ? 2 : 4;           // code dwords per lane and subtile per K step
+
+    // wait until stage `k` has landed: `newer` stages were issued after it
+    auto wait_stage = [&](int newer) __attribute__((always_inline)) {
+        if (newer >= 2) wait_dma<2 * C::DMA>();
+        else if (newer == 1) wait_dma<C::DMA>();
+        else wait_dma<0>();
+    };
+    // the scale / bias window of K step k (its first step), as this thread loaded it for
+    // its own row: converted in place to fp16 s 2^p, b 2^p (exact)
+    auto convert_window = [&](int k) __attribute__((always_inline)) {
+        uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES;
+        const int rs = 64 * wave + lane, bf = L.sb_bf16;
+        auto cv = [&](uint32_t bits) __attribute__((always_inline)) -> uint32_t {
+            return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(sb_to_f32(bits & 0xffffu, bf) * wsc));
+        };
+        auto cv2 = [&](uint32_t v) __attribute__((always_inline)) -> uint32_t { return cv(v) | (cv(v >> 16) << 16); };
+        if (C::WMAX == 8 && a.wlog == 3) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x4 *p = (u32x4 *)(sw + h * C::S_BYTES + rs * 16);
+                u32x4 v = *p;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] = cv2(v[q]);
+                *p = v;
+            }
+        } else if (a.wlog == 1) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t *p = (uint32_t *)(sw + h * C::S_BYTES + rs * 4);
+                *p = cv2(*p);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t *p = (uint32_t *)(sw + h * C::S_BYTES + rs * 4);
+                *p = cv(*p);
+            }
+        }
+    };
+    // down pass, tiles whose rows mix h block scales: the chunks this thread loaded for K
+    // step k, brought from their block's scale 2^e to the row's 2^e_r (e_r <= e)
+    auto rescale_a = [&](int k) __attribute__((always_inline)) {
+        uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::A_DMA; ++i) {
+            int r, ach;
+            apiece(i, r, ach);
+            const int blk = (k * BK + 8 * ach) >> 7;
+            const int d = (int)sx.dn.e[r] - (int)sx.dn.hx[r * HEXP_STRIDE + blk];
+            if (d != 0) {
+                const float f = d < -100 ? 0.0f : exp2i(d);
+                u32x4 *p = (u32x4 *)(st + (8 * C::A_DMA * wave + 8 * i) * 128 + lane * 16);
+                u32x4 v = *p;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f16x2 h2 = as_h2(v[q]);
+                    v[q] = pack_f16x2(f32_to_f16_ftz((float)h2[0] * f), f32_to_f16_ftz((float)h2[1] * f));
+                }
+                *p = v;
+            }
+        }
+    };
+    // operands of K step k from the LDS ring: per weight subtile j, the code dwords of
+    // K slice s of this lane, and the scale and bias
+    auto load_codes = [&](int k, int s, uint32_t (&cw)[4][CW / 2]) __attribute__((always_inline)) {
+        const uint8_t *bst = smem + (k % C::NSTAGE) * C::STAGE + C::A_BYTES;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rs = 64 * wave + 16 * j + n16;
+            if constexpr (BITS == 4) {
+                const int hsel = (cg >> 1) ^ ((rs >> 2) & 1);
+                cw[j][0] = *(const uint32_t *)(bst + rs * 32 + hsel * 16 + (cg & 1) * 8 + 4 * s);
+            } else {
+                const int q = cg ^ ((rs >> 1) & 3);
+                const uint32_t *p = (const uint32_t *)(bst + rs * 64 + q * 16 + 8 * s);
+                cw[j][0] = p[0];
+                cw[j][1] = p[1];
+            }
+        }
+    };
+    auto load_sb = [&](int k, f16x2 (&sc)[4], f16x2 (&sc16)[4], f16x2 (&bi)[4]) __attribute__((always_inline)) {
+        // row rs, group k % W of the window: 16 (W = 8) or 4 bytes per row, 2 bytes per
+        // group (W = 1: the low half of the dword a 2-byte load fills); fp16, prescaled
+        const int pitch = a.wlog == 3 ? 16 : 4;
+        const uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES +
+                            2 * (k & ((1 << a.wlog) - 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rs = 64 * wave + 16 * j + n16;
+            const _Float16 sv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + rs * pitch));
+            const _Float16 bv = __builtin_bit_cast(_Float16, *(const uint16_t *)(sw + C::S_BYTES + rs * pitch));
+            sc[j] = (f16x2){sv, sv};
+            const _Float16 sv16 = sv * (_Float16)0.0625f;        // exact: prescaled scales are normal
+            sc16[j] = (f16x2){sv16, sv16};
+            bi[j] = (f16x2){bv, bv};
+        }
+    };
+    uint32_t cw[4][CW / 2];
+    f16x2 sc[4], sc16[4], bi[4];
+    DqConst dk;
+    dk.lo = BITS == 4 ? 0x000F000Fu : 0x00FF00FFu;
+    dk.hi = 0x00F000F0u;
+    dk.magic = QS_MAGIC;
+    auto deq = [&](const uint32_t (&cw)[4][CW / 2], f16x8 (&B)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (BITS == 4) B[j] = dequant8<4>(cw[j][0], 0u, sc[j], sc16[j], bi[j], dk);
+            else B[j] = dequant8<8>(cw[j][0], cw[j][1], sc[j], sc16[j], bi[j], dk);
+        }
+    };
+
+    // The K loop: per 64-wide step, one barrier (stage k visible, stage k-1 consumed),
+    // the refill of stage k-1's buffer with stage k+NSTAGE-1, then two MFMA blocks
+    // (32-wide slices), each on a weight slice dequantized just before it.  All ten row
+    // subtiles run, so every fragment read of a block is issued ahead of its MFMAs.
+    // Before the barrier each thread finishes what it loaded itself: a new scale window
+    // is converted, and (down pass, mixed tiles) its activation chunks are rescaled.
+    auto kloop = [&]() __attribute__((always_inline)) {
+        for (int k = 0; k < nk; ++k) {
+            // stage k has landed once at most the later stages' loads are outstanding
+            const int issued = k + C::NSTAGE - 1 < nk ? C::NSTAGE - 2 : nk - 1 - k;
+            wait_stage(issued < 0 ? 0 : issued);
+            if (convert && (k & ((1 << a.wlog) - 1)) == 0) convert_window(k);
+            if (MODE == 1 && slow) rescale_a(k);
+            block_sync();
+            if (MODE == 1 && k == 0) {
+                // the down pass learns here whether the tile mixes h block scales; if so,
+                // step 0's chunks are rescaled now, behind one more barrier
+                slow = (sx.dn.mixed[0] | sx.dn.mixed[1] | sx.dn.mixed[2] | sx.dn.mixed[3]) != 0;
+                if (slow) {
+                    rescale_a(0);
+                    block_sync();
+                }
+            }
+            if (k + C::NSTAGE - 1 < nk) issue(k + C::NSTAGE - 1);
+            const uint8_t *st = smem + (k % C::NSTAGE) * C::STAGE;
+            load_sb(k, sc, sc16, bi);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int pos = (2 * cg + s) ^ ((n16 >> 1) & 7);
+                f16x8 A[MT];
+#pragma unroll
+                for (int i = 0; i < MT; ++i) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
+                load_codes(k, s, cw);
+                f16x8 B[4];
+                deq(cw, B);
+#pragma unroll
+                for (int i = 0; i < MT; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    };
+    kloop();
     block_sync();                     // the ring is free: epilogues stage through it
 
     // ---- epilogues.  acc[i][j][r]: tile row i*16 + 4*cg + r, weight row slot 64*wave + 16*j + n16
     if (MODE == 0) {
         constexpr int HP = 40;                                   // fp16 per staged row
         uint16_t *hs = (uint16_t *)(smem + wave * (BM * HP * 2));
+        uint32_t *s_hm = (uint32_t *)(smem + 4 * (BM * HP * 2)); // [4][BM] row maxima per wave
+        const bool cols_live = nbi * 128 + wave * 32 < I;      // this wave's 32 h columns exist
+        // h = silu(g) u in fp32 (scales of x and of the weight rows taken out), in place of
+        // the gate accumulators; then the largest |h| of each row over this wave's columns
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i < msub) {
+                const f32x4 rf = *(const f32x4 *)(sx.xs + i * 16 + 4 * cg);
+                uint32_t m[4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = j * 16 + n16;
-                    const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
+                for (int r = 0; r < 4; ++r) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float g = acc[i][j][r];
-                        const float hv = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[i][j + 2][r];
-                        hs[(i * 16 + 4 * cg + r) * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(hv));
+                    for (int j = 0; j < 2; ++j) {
+                        const float g = acc[i][j][r] * rf[r];
+                        const float u = acc[i][j + 2][r] * rf[r];
+                        acc[i][j][r] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
                     }
+                    uint32_t v = cols_live ? __float_as_uint(__builtin_fmaxf(__builtin_fabsf(acc[i][0][r]),
+                                                                            __builtin_fabsf(acc[i][1][r])))
+                                           : 0u;
+                    v = max(v, dpp_u32<0xB1>(v));
+                    v = max(v, dpp_u32<0x4E>(v));
+                    v = max(v, dpp_u32<0x141>(v));
+                    v = max(v, dpp_u32<0x140>(v));
+                    m[r] = v;
+                }
+                if (n16 == 0) *(u32x4 *)(s_hm + wave * BM + i * 16 + 4 * cg) = (u32x4){m[0], m[1], m[2], m[3]};
+            }
+        }
+        __syncthreads();
+        // the block's scale per row (from the four waves' maxima), then h 2^e staged as fp16
+        const bool exact = __hip_atomic_load(a.err + CTL_HBLOCK_EXACT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < msub) {
+                u32x4 mb = *(const u32x4 *)(s_hm + i * 16 + 4 * cg);
+#pragma unroll
+                for (int w = 1; w < 4; ++w) {
+                    const u32x4 o = *(const u32x4 *)(s_hm + w * BM + i * 16 + 4 * cg);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mb[r] = max(mb[r], o[r]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float m = __uint_as_float(mb[r]);
+                    const int eh = exact ? (m > 0.0f ? clamp_exp(14 - ilog2f(m)) : 0) : block_exp(m);
+                    const float f = exp2i(eh);
+                    const int row = i * 16 + 4 * cg + r;
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int col = j * 16 + n16;
+                        const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
+                        hs[row * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(acc[i][j][r] * f));
+                    }
+                    if (wave == 0 && n16 == 0 && row < nrows)
+                        a.hexp[(int64_t)(tile.row0 + row) * HEXP_STRIDE + nbi] = (int8_t)eh;
                 }
             }
         }
@@ -432,7 +678,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         uint16_t *hout = a.h + (int64_t)tile.row0 * I + nbi * 128 + wave * 32 + chunk * 8;
         // h goes out at device scope (sc1, written through), and once every wave's stores
         // have completed the workgroup counts itself in for the tile's down pass
-        const bool cols_live = nbi * 128 + wave * 32 < I;      // this wave's 32 h columns exist
 #pragma unroll
         for (int q = 0; q < BM / 16; ++q) {
             const int row = (lane >> 2) + 16 * q;
@@ -448,9 +693,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         __syncthreads();
         // release at agent scope before the count: an L2 write-back, waited for, then the
         // atomic.  A store acknowledged to its wave is not yet visible to device-scope loads
-        // of other workgroups; without the release a down tile could read h rows before
-        // they arrive (the sequence is written out: the compiler's own release omitted the
-        // wait after the write-back here)
+        // of other workgroups; without the release a down tile could read h rows (or their
+        // block scales) before they arrive (the sequence is written out: the compiler's own
+        // release omitted the wait after the write-back here)
         if (tid == 0) {
             asm volatile("buffer_wbl2 sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
             __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -459,12 +704,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
     }
 
     // MODE 1: 32 rows at a time through a per-wave fp32 staging area; lane l then
-    // owns row 32*hp + (l % 32) and 32 of the wave's 64 columns
+    // owns row 32*hp + (l % 32) and 32 of the wave's 64 columns, and the lane pair of a
+    // row sets the scale of the row's 64 columns from their largest value
     const int colbase = nbi * BN + wave * 64;
     if (colbase >= H) return;                                    // columns past H (H % 256 != 0)
     constexpr int FP = 68;                                       // floats per staged row
     float *fs = (float *)(smem + wave * (32 * FP * 4));
     const int er = lane & 31, ecol = colbase + 32 * (lane >> 5);
+    int8_t *sexp_blk = a.sexp + (int64_t)(colbase >> 6) * sexp_rows(a.T, K);
 #pragma unroll
     for (int hp = 0; hp < MT / 2; ++hp) {
         if (32 * hp >= nrows) break;
@@ -473,26 +720,44 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) fs[(ii * 16 + 4 * cg + r) * FP + j * 16 + n16] = acc[2 * hp + ii][j][r];
+                for (int r = 0; r < 4; ++r)
+                    fs[(ii * 16 + 4 * cg + r) * FP + j * 16 + n16] = acc[2 * hp + ii][j][r];
         wave_lds_sync();
         const int row = 32 * hp + er;
-        if (row < nrows) {
-            const float *src = fs + er * FP + 32 * (lane >> 5);
-            // routed rows: the (token, slot) row with its routing weight; shared rows:
-            // row T*K + t with weight 1
-            const int64_t p = routed_down ? (int64_t)s_pos[row] : (int64_t)tile.row0 + row;
-            const float wv = routed_down ? s_w[row] : a.sgate ? a.sgate[tile.row0 + row - TK] : 1.0f;
+        const bool live = row < nrows;
+        // routed rows: the (token, slot) row with its routing weight; shared rows:
+        // row T*K + t with the shared gate (or 1); both with h's row scale and the
+        // weights' prescale taken out
+        const float wv = sx.dn.w[live ? row : 0];
+        const float *src = fs + er * FP + 32 * (lane >> 5);
+        f32x4 v[8];
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            v[c] = *(const f32x4 *)(src + 4 * c);
+            mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(v[c][0]), __builtin_fabsf(v[c][1])));
+            mx = __builtin_fmaxf(mx, __builtin_fmaxf(__builtin_fabsf(v[c][2]), __builtin_fabsf(v[c][3])));
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * __builtin_fabsf(wv);
+        const int es = range_exp(mx);
+        const float f = wv * exp2i(es);
+        if (live) {
+            const int64_t p = routed_down ? (int64_t)sx.dn.pos[row] : (int64_t)tile.row0 + row;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const f32x4 v0 = *(const f32x4 *)(src + 8 * c), v1 = *(const f32x4 *)(src + 8 * c + 4);
+                const f32x4 v0 = v[2 * c] * f, v1 = v[2 * c + 1] * f;
                 u32x4 o;
-                o[0] = pack_f16x2((_Float16)(v0[0] * wv), (_Float16)(v0[1] * wv));
-                o[1] = pack_f16x2((_Float16)(v0[2] * wv), (_Float16)(v0[3] * wv));
-                o[2] = pack_f16x2((_Float16)(v1[0] * wv), (_Float16)(v1[1] * wv));
-                o[3] = pack_f16x2((_Float16)(v1[2] * wv), (_Float16)(v1[3] * wv));
+                o[0] = pack_f16x2(f32_to_f16_ftz(v0[0]), f32_to_f16_ftz(v0[1]));
+                o[1] = pack_f16x2(f32_to_f16_ftz(v0[2]), f32_to_f16_ftz(v0[3]));
+                o[2] = pack_f16x2(f32_to_f16_ftz(v1[0]), f32_to_f16_ftz(v1[1]));
+                o[3] = pack_f16x2(f32_to_f16_ftz(v1[2]), f32_to_f16_ftz(v1[3]));
                 *(u32x4 *)(a.slot + p * H + ecol + 8 * c) = o;
             }
+            if (lane < 32) sexp_blk[p] = (int8_t)es;
         }
+        // a nonzero scale anywhere sends the combine through its scaled path
+        if (__builtin_amdgcn_ballot_w64(live && es != 0) != 0 && lane == 0) a.ntiles[2] = 1;
         wave_lds_sync();
     }
 }
@@ -503,13 +768,17 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
 template <int BITS>
 __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a0, GemmArgs a1, int g0) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<BITS>::LDS];
-    if ((int)blockIdx.x < g0) gemm_body<BITS, 0>(a0, (int)blockIdx.x, smem);
-    else gemm_body<BITS, 1>(a1, (int)blockIdx.x - g0, smem);
+    __shared__ TileRows sx;
+    __shared__ uint32_t s_wb[8];
+    if ((int)blockIdx.x < g0) gemm_body<BITS, 0>(a0, (int)blockIdx.x, smem, sx, s_wb);
+    else gemm_body<BITS, 1>(a1, (int)blockIdx.x - g0, smem, sx, s_wb);
 }
 
 // The combine: y[t] = sum of the token's k slot rows in ascending expert id, then its
-// shared-expert row, in fp32; one thread per 8 columns of a token (16-byte loads).
-__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ slot, void *y, int y_dtype,
+// shared-expert row, in fp32, each slot value taken out of its block scale (read only when
+// the down pass flagged a nonzero one); one thread per 8 columns of a token (16-byte loads).
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ slot, const int8_t *__restrict__ sexp,
+                                                 const int32_t *__restrict__ scaled, void *y, int y_dtype,
                                                  int64_t T, int K, int H, int shared) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (token, 8-column chunk)
     const int cpr = H / 8;
@@ -517,12 +786,20 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ sl
     const int64_t t = i / cpr;
     const int col = (int)(i % cpr) * 8;
     u32x4 v[17];
+    float f[17];
 #pragma unroll
     for (int j = 0; j < 17; ++j)
         if (j < K || (j == K && shared)) {
             const int64_t row = j < K ? t * K + j : T * K + t;
             v[j] = *(const u32x4 *)(slot + row * H + col);
+            f[j] = 1.0f;
         }
+    if (*scaled) {                       // some slot block carries a scale (extreme data only)
+        const int8_t *se = sexp + (int64_t)(col >> 6) * sexp_rows(T, K);
+#pragma unroll
+        for (int j = 0; j < 17; ++j)
+            if (j < K || (j == K && shared)) f[j] = exp2i(-(int)se[j < K ? t * K + j : T * K + t]);
+    }
     float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 17; ++j)
@@ -530,8 +807,8 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *__restrict__ sl
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f16x2 h2 = as_h2(v[j][q]);
-                sum[2 * q] += (float)h2[0];
-                sum[2 * q + 1] += (float)h2[1];
+                sum[2 * q] = fmaf((float)h2[0], f[j], sum[2 * q]);
+                sum[2 * q + 1] = fmaf((float)h2[1], f[j], sum[2 * q + 1]);
             }
     if (y_dtype == MOE_F32) {
         float *yp = (float *)y + t * H + col;
@@ -578,6 +855,7 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
         const QMat *ms[4] = {&L.gate, &L.up, &L.s_gate, &L.s_up};
         a0.wlog = window_log(ms, L.has_shared ? 4 : 2, L.H, C::WMAX);
         if (a0.wlog == 2) a0.wlog = 1;                     // windows of 8, 2 or 1 groups
+        a0.sb16 = window_log(ms, L.has_shared ? 4 : 2, L.H, 8) == 3;
     }
     // down: routed tiles -> weighted slot rows, shared tiles -> their own slot rows
     GemmArgs a1 = a;
@@ -587,12 +865,13 @@ hipError_t gemms(GemmArgs a, hipStream_t s) {
         const QMat *ms[2] = {&L.down, &L.s_down};
         a1.wlog = window_log(ms, L.has_shared ? 2 : 1, L.I, C::WMAX);
         if (a1.wlog == 2) a1.wlog = 1;
+        a1.sb16 = window_log(ms, L.has_shared ? 2 : 1, L.I, 8) == 3;
     }
     const unsigned g0 = grid_for(maxr + maxs, a0.nb), g1 = grid_for(maxr + maxs, a1.nb);
     hipLaunchKernelGGL((k_gemm<BITS>), dim3(g0 + g1), dim3(NT), 0, s, a0, a1, (int)g0);
     const int64_t n = a.T * (L.H / 8);
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.slot, a.y, a.y_dtype,
-                       a.T, L.K, L.H, L.has_shared);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.slot, a.sexp,
+                       a.ntiles + 2, a.y, a.y_dtype, a.T, L.K, L.H, L.has_shared);
     return hipGetLastError();
 }
 
@@ -604,7 +883,10 @@ hipError_t launch_prefill_gemms(const Layer &L, int64_t T, const PrefillBufs &b,
     a.L = L;
     a.T = T;
     a.x16 = b.x16;
+    a.xexp = b.xexp;
     a.h = b.h;
+    a.hexp = b.hexp;
+    a.sexp = b.sexp;
     a.perm = b.perm;
     a.tiles = b.tiles;
     a.ntiles = b.ntiles;

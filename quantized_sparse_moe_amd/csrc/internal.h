@@ -64,24 +64,40 @@ struct Tile {                      // one row block of one expert bin
     int32_t pad;
 };
 
+// fp16 operands of the grouped path carry power-of-two range scales: x 2^a per token
+// (a in xexp), h 2^e per (row, 128-column block) (e in hexp, HEXP_STRIDE bytes per row,
+// one per block), slot rows 2^e per (row, 64-column block) (sexp, block-major: the
+// exponents of one block for all slot rows together, rows padded to a multiple of 16)
+constexpr int HEXP_STRIDE = 16;    // inter <= 2048: at most 16 blocks of 128 columns
+// a state word read by the grouped GEMM: nonzero gives every h block the scale that puts
+// its largest value in [2^14, 2^15) instead of the shared one (0 for ordinary blocks), so
+// that nearly every down tile must rescale (set only by tests of that rescale)
+constexpr int CTL_HBLOCK_EXACT = 33;
+
 struct PrefillBufs {
-    uint16_t *x16;                 // [T][H] fp16, columns permuted per 8-group (code order)
+    uint16_t *x16;                 // [T][H] fp16 x 2^a, columns permuted per 8-group (code order)
+    uint32_t *xmax;                // [T][8] largest |x| per token and logits expert block
+    int32_t *xexp;                 // [T] the a of each token's x16 row
     float *logits;                 // [T][E] router logits
     int32_t *idx;                  // [T][K]
     float *w;                      // [T][K]
-    int32_t *blkcnt;               // [nblk][E]  assignments per (32-token block, expert)
+    int32_t *blkcnt;               // [nblk][E]  assignments per (16-token block, expert)
     int32_t *blkoff;               // [nblk][E]  first position of that block's rows in the expert bin
     int32_t *expert_off;           // [E+1]
     int32_t *perm;                 // [T*K]      position -> t*K + j
     Tile *tiles;                   // [max_tiles] routed full, routed partial, then shared tiles
-    int32_t *ntiles;               // [2] routed tiles, routed + shared tiles
+    int32_t *ntiles;               // [3] routed tiles, routed + shared tiles, and a flag the
+                                   // down pass sets when some slot block has a nonzero scale
     int32_t *tile_done;            // [max_tiles] gate/up column blocks finished per tile
     uint32_t *ctl;                 // the workspace's state region (word 0: bounded-wait error flag)
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
+    int8_t *hexp;                  // [(T*K + T)][HEXP_STRIDE]
     uint16_t *slot;                // [T*K + T][H] fp16: w_j * o_j per (token, slot), then shared o
+    int8_t *sexp;                  // [H / 64][sexp_rows(T, K)]
     float *sgate;                  // [T] shared-expert gate sigmoid(g . x_t) (gated layers)
 };
 
+__host__ __device__ inline int64_t sexp_rows(int64_t T, int K) { return (T * K + T + 15) / 16 * 16; }
 int64_t prefill_max_routed_tiles(int64_t T, int K, int E);
 int64_t prefill_max_tiles(int64_t T, int K, int E);
 

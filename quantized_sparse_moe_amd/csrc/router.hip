@@ -10,7 +10,10 @@
 // tiled 64 tokens x 64 experts per workgroup with both operands staged in LDS, so each
 // router row is read once per 64 tokens.  The workgroups of a token block also write
 // the fp16 copy of x (taking K chunks in turn), each group of 8 columns permuted into
-// the code order used by the expert GEMMs.  The top-k pass then gives one wave to each token.
+// the code order used by the expert GEMMs, and the largest |x| of each token over the
+// chunks they wrote.  The top-k pass then gives one wave to each token; it also picks
+// the token's range scale 2^a from those maxima (0 for ordinary rows) and, for a row
+// outside fp16's range, writes the copy again as x 2^a.
 #include "common.h"
 #include "internal.h"
 
@@ -32,12 +35,13 @@ struct LogitArgs {
     float *logits;                  // [T][LS]
     int LS;                         // logit row stride: E (+ 1 with a gate)
     uint16_t *x16;                  // [T][H] fp16 in code order, or null
+    uint32_t *xmax;                 // [T][8] largest |x| (fp32 bits) per token and expert block
     int64_t T;
     int H, E;
 };
 
 template <int BITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_logits(LogitArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_logits(LogitArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xa[LT * LPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t wa[LE * LPITCH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     f32x4 acc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    uint32_t xm[4] = {0u, 0u, 0u, 0u};              // largest |x| written, per staged row
     // chunk kc: registers -> LDS (and the fp16 copy of x), then 4 x 4 MFMAs; two chunks
     // are in flight in registers while one is multiplied (one workgroup per CU at the
     // prefill sizes, so the loads' latency is hidden by this workgroup alone)
@@ -84,9 +89,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             if (write_x16 && xrow[i] >= 0 && kc + sc < H) {   // this chunk's share of the fp16 copy
                 u32x4 h;
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c) {
+                    xm[i] = max(xm[i], max((xv[i][c] << 16) & 0x7fffffffu, xv[i][c] & 0x7fff0000u));
                     h[c] = pack_f16x2(f32_to_f16_ftz(__uint_as_float(xv[i][c] << 16)),
                                       f32_to_f16_ftz(__uint_as_float(xv[i][c] & 0xffff0000u)));
+                }
                 *(u32x4 *)(a.x16 + xrow[i] * H + kc + sc) = perm8<BITS>(h);
             }
         }
@@ -116,6 +123,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             mult();
         }
     }
+    // the 16 lanes staging a row hold its maxima: one word per (token, expert block)
+    if (a.x16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t m = xm[i];
+            m = max(m, dpp_u32<0xB1>(m));
+            m = max(m, dpp_u32<0x4E>(m));
+            m = max(m, dpp_u32<0x141>(m));
+            m = max(m, dpp_u32<0x140>(m));
+            if ((tid & 15) == 0 && xrow[i] >= 0) a.xmax[xrow[i] * 8 + blockIdx.y] = m;
+        }
+    }
     // acc[n][r]: token 16 * wave + 4 * cg + r, expert e0 + 16 * n + n16
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -140,10 +159,18 @@ struct TopkArgs {
     int32_t *out_idx;               // optional copies for the caller
     float *out_w;
     int32_t *blkcnt;                // [T / 16][E] or null
+    // range scale of the fp16 copy of x (prefill only; x16 null otherwise)
+    const uint16_t *x;              // [T][H] bf16
+    uint16_t *x16;                  // [T][H] fp16 in code order
+    const uint32_t *xmax;           // [T][8]
+    int nxmax;                      // expert blocks of the logits grid (words of xmax used)
+    int32_t *xexp;                  // [T] the exponent a of each token's copy (x 2^a)
+    int H;
 };
 
 // One wave per token (4 tokens per wave), 16 tokens per workgroup: the block's expert
 // histogram is counted in LDS with integer atomics and written once.
+template <int BITS>
 __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     __shared__ int hist[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -164,6 +191,25 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     for (int q = 0; q < TPW; ++q) {
         const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
         if (t >= a.T) break;
+        if (a.x16) {
+            // the token's range scale; a row outside fp16's range is copied again, scaled
+            uint32_t m = 0u;
+            for (int y = 0; y < a.nxmax; ++y) m = max(m, a.xmax[t * 8 + y]);
+            const int xe = range_exp(__uint_as_float(m));
+            if (lane == 0) a.xexp[t] = xe;
+            if (xe != 0) {
+                const float f = exp2i(xe);
+                for (int c = lane * 8; c < a.H; c += 512) {
+                    const u32x4 xv = *(const u32x4 *)(a.x + t * a.H + c);
+                    u32x4 h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        h[i] = pack_f16x2(f32_to_f16_ftz(__uint_as_float(xv[i] << 16) * f),
+                                          f32_to_f16_ftz(__uint_as_float(xv[i] & 0xffff0000u) * f));
+                    *(u32x4 *)(a.x16 + t * a.H + c) = perm8<BITS>(h);
+                }
+            }
+        }
         const TopkOut tk = wave_topk_regs(v[q], E, K);
         if (a.sgate && lane == 0) a.sgate[t] = sigmoid(a.logits[t * a.LS + E]);
         if (lane < K) {
@@ -192,6 +238,7 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     la.LS = L.E + (gated ? 1 : 0);
     la.logits = b.logits;
     la.x16 = write_x16 ? b.x16 : nullptr;
+    la.xmax = b.xmax;
     la.T = T;
     la.H = L.H;
     la.E = L.E;
@@ -212,7 +259,17 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     ta.out_idx = out_idx;
     ta.out_w = out_w;
     ta.blkcnt = write_x16 ? b.blkcnt : nullptr;
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)((T + TK_TOKENS - 1) / TK_TOKENS)), dim3(256), 0, s, ta);
+    ta.x = x;
+    ta.x16 = write_x16 ? b.x16 : nullptr;
+    ta.xmax = b.xmax;
+    ta.nxmax = (int)lgrid.y;
+    ta.xexp = b.xexp;
+    ta.H = L.H;
+    const dim3 tgrid((unsigned)((T + TK_TOKENS - 1) / TK_TOKENS));
+    if (L.bits == 4)
+        hipLaunchKernelGGL((k_topk<4>), tgrid, dim3(256), 0, s, ta);
+    else
+        hipLaunchKernelGGL((k_topk<8>), tgrid, dim3(256), 0, s, ta);
     return hipGetLastError();
 }
 
