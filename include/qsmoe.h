@@ -185,7 +185,11 @@ moe_status moe_route(const moe_layer_desc *d, const void *x, int64_t T,
  *     y[t] = sum over the selected experts in ascending id of w_j * o_j  +  o_shared,
  * accumulated in fp32 in that fixed order ([LILY] "Reduce intermediate and state
  * traffic"; [OMLX] "Fusion principle").
- *   x        [T][hidden] bf16, |x| < 65504 (activations are consumed as fp16)
+ *   x        [T][hidden] bf16, any finite values: every fp16 operand of the kernels
+ *            (x, the dequantized weights, h, the routed outputs) carries an exact
+ *            power-of-two range scale, so results stay within the parity bound of
+ *            an fp64 evaluation for activations, scales and biases anywhere in
+ *            bf16's range, as long as the intermediate values fit in fp32
  *   y        [T][hidden], y_dtype MOE_BF16 (round-to-nearest-even) or MOE_F32
  *   topk_idx, topk_w  optional outputs as in moe_route (NULL to skip)
  * Path: T == 1 runs the batch-1 decode kernel (register dequantization on the vector
@@ -193,7 +197,7 @@ moe_status moe_route(const moe_layer_desc *d, const void *x, int64_t T,
  * each expert any token selected read once (when T * (top_k + 1) * inter <= 98496);
  * T = 5 .. 8 two such launches of ceil(T/2) and floor(T/2) tokens (when both fit);
  * larger T runs the grouped-GEMM path (MFMA on fp16 operands dequantized in registers,
- * fp32 accumulation, fp16 intermediates).
+ * fp32 accumulation, fp16 intermediates, each under its range scale).
  * For a given T the result does not depend on whether gate/up are fused or separate,
  * nor on the other tokens of the call (tokens are independent), bit for bit.
  */

@@ -33,7 +33,9 @@ constexpr int SM_LSTRIDE = 2 * SM_TMAX * SM_TE + 64;        // u32 per logits co
 static_assert(SM_LCOPIES * SM_LSTRIDE <= LOGIT_COPIES * LOGIT_STRIDE, "small-T logits region");
 constexpr int SM_HCOPIES = 2;
 constexpr int SM_HSTRIDE = H_COPIES * H_STRIDE / SM_HCOPIES;   // u32 per h copy
-constexpr int SM_HWORDS = SM_HSTRIDE / 2 - 32;                 // h words per copy
+constexpr int SM_HEXPW = 2304;                                 // block-scale words per copy
+constexpr int SM_HWORDS = SM_HSTRIDE / 2 - 64 - SM_HEXPW;      // h words per copy
+constexpr int SM_HEXP = 2 * (SM_HWORDS + 32);                  // u32 offset of the scale words
 constexpr size_t SMALL_LDS_MAX = 76 * 1024;                    // dynamic LDS of a small-batch call
 static_assert(2 * SM_TMAX * 16 <= TOPK_STRIDE / 2, "small-T selection region");
 static_assert(4 * (64 + SM_TMAX) <= TOPK_STRIDE, "small-T gate entries");
@@ -119,23 +121,26 @@ template <int BITS>
 constexpr int small_xpitch() { return 64 / BITS + 4; }
 
 // x of T tokens (bf16, [T][H]) -> LDS fp16 in code order (chunk c of token t at
-// xs + (t nch + c) * pitch, its column sums right after it), one (token, chunk) per thread
+// xs + (t nch + c) * pitch, its column sums right after it), one (token, chunk) per thread,
+// each token under its range scale 2^e_t (0 for rows of ordinary magnitude, which are
+// staged in one pass); the returned LDS array holds 2^-e_t.  Ends with a barrier.
 template <int BITS>
-__device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs) {
+__device__ __forceinline__ uint32_t stage_x_row(const uint16_t *x, int t, int H, uint32_t *xs, float f) {
     constexpr int CPC = 128 / BITS, XP = small_xpitch<BITS>();
     const int nch = H / CPC;
-    for (int i = threadIdx.x; i < T * nch; i += DT) {
-        const int t = i / nch, c = i % nch;
+    uint32_t m = 0u;                                         // largest |x| as ordered bits
+    for (int c = threadIdx.x & 63; c < nch; c += 64) {
         const uint16_t *xc = x + (int64_t)t * H + c * CPC;
-        uint32_t *xd = xs + i * XP;
+        uint32_t *xd = xs + (t * nch + c) * XP;
         float se = 0.0f, so = 0.0f;
         for (int g = 0; g < CPC / 8; ++g) {
             const u32x4 v = *(const u32x4 *)(xc + 8 * g);
             u32x4 nat;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[k] << 16));
-                const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[k] & 0xffff0000u));
+                m = max(m, max((v[k] << 16) & 0x7fffffffu, v[k] & 0x7fff0000u));
+                const _Float16 lo = f32_to_f16_ftz(__uint_as_float(v[k] << 16) * f);
+                const _Float16 hi = f32_to_f16_ftz(__uint_as_float(v[k] & 0xffff0000u) * f);
                 se += (float)lo;
                 so += (float)hi;
                 nat[k] = pack_f16x2(lo, hi);
@@ -144,6 +149,22 @@ __device__ void stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs) {
         }
         *(float2 *)(xd + CPC / 2) = make_float2(se, so);
     }
+    return m;
+}
+// wave t stages token t: the wave finds the row's largest |x| itself and, for a row of
+// extreme magnitude only, stages it again under 2^e; the returned LDS array holds 2^-e_t,
+// visible after the caller's next barrier
+template <int BITS>
+__device__ const float *stage_x_tokens(const uint16_t *x, int T, int H, uint32_t *xs) {
+    __shared__ float s_xinv[SM_TMAX];
+    const int t = threadIdx.x >> 6;
+    if (t < T) {
+        const uint32_t m = wave_max_u32(stage_x_row<BITS>(x, t, H, xs, 1.0f));
+        const int e = range_exp(__uint_as_float(m));
+        if (e != 0) stage_x_row<BITS>(x, t, H, xs, exp2i(e));
+        if ((threadIdx.x & 63) == 0) s_xinv[t] = exp2i(-e);
+    }
+    return s_xinv;
 }
 
 // one chunk step of gate/up row pairs j0, j0 + 1 of expert e: per lane, the 16-byte
@@ -253,8 +274,8 @@ __device__ __forceinline__ float wave_sum16(float (&v)[SM_TMAX * 4]) {
 // lane are reduced together.
 template <int BITS>
 __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j0, int H, int lpr, const PairW &w0,
-                                    const uint32_t *xs, int T, int tmask, uint32_t *hq, int wpi,
-                                    int wi, int sb_bf16) {
+                                    const uint32_t *xs, int T, int tmask, float *hq, int pb,
+                                    int wi, int sb_bf16, const float *xinv) {
     constexpr int CPC = 128 / BITS, XP = small_xpitch<BITS>();
     const int lane = threadIdx.x & 63;
     const int lr = lane % lpr;
@@ -348,13 +369,16 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
     }
     if (lpr == 64) {
         // value 4 t + r ends in lanes 16 t + 4 r .. + 3: gate (r = 0, 2) meets up (r + 1)
-        // four lanes up, and the pair's second h value sits eight lanes up
-        const float v = wave_sum16(acc);
+        // four lanes up, and the pair's second h value sits eight lanes up (x's scale of
+        // token t taken out first)
+        const int t = lane >> 4;
+        const float v = wave_sum16(acc) * xinv[t];
         const float h = silu(v) * dpp<0x104>(v);
         const float h1 = dpp<0x108>(h);
-        const int t = lane >> 4;
-        if ((lane & 15) == 0 && t < T)
-            hq[t * wpi + wi] = pack_f16x2(f32_to_f16_ftz(h), f32_to_f16_ftz(h1));
+        if ((lane & 15) == 0 && t < T) {
+            hq[t * pb + 2 * wi] = h;
+            hq[t * pb + 2 * wi + 1] = h1;
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < SM_TMAX; ++t) {
@@ -362,11 +386,14 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
             float hv[2];
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                const float g = group_sum(acc[4 * t + 2 * p], lpr);
-                const float u = group_sum(acc[4 * t + 2 * p + 1], lpr);
+                const float g = group_sum(acc[4 * t + 2 * p], lpr) * xinv[t];
+                const float u = group_sum(acc[4 * t + 2 * p + 1], lpr) * xinv[t];
                 hv[p] = silu(g) * u;
             }
-            if (lr == 0) hq[t * wpi + wi] = pack_f16x2(f32_to_f16_ftz(hv[0]), f32_to_f16_ftz(hv[1]));
+            if (lr == 0) {
+                hq[t * pb + 2 * wi] = hv[0];
+                hq[t * pb + 2 * wi + 1] = hv[1];
+            }
         }
     }
 }
@@ -487,7 +514,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int bpe = (I + pb - 1) / pb;
         const bool sh = b < nRP + nS;
         const int g = sh ? b - nRP : b - nRP - nS;
-        stage_x_tokens<BITS>(a.x, T, H, xs);
+        const float *xinv = stage_x_tokens<BITS>(a.x, T, H, xs);
         int nitems = 1;
         if (!sh) {
             small_get_sel(ctl, tag, E, K, T, gated, S);             // ends with a barrier
@@ -512,10 +539,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         }
         // the waves run through the items on their own (no barrier between items); each
         // wave's next item streams into its LDS slot while the current one is computed
-        // from registers; the h words of all items collect in LDS and are stored once at
-        // the end
+        // from registers; the h values of all items collect in LDS and are stored once at
+        // the end, as fp16 pairs under one range scale per (item, token)
         const int wpi = pb / 2;                              // h words per item and token
-        uint32_t *hq = xs + SM_TMAX * (H / CPC) * XP;        // [item][T][wpi]
+        float *hq = (float *)(xs + SM_TMAX * (H / CPC) * XP);   // [item][T][pb]
         for (int m = 0; m < nitems; ++m) {
             int u, rbk, e, jj;
             item_at(m, u, rbk, e, jj);
@@ -530,8 +557,21 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             }
             int tmask = 0;
             for (int t = 0; t < T; ++t) tmask |= (sh || S.jt[u][t] >= 0) ? (1 << t) : 0;
-            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, T, tmask, hq + m * T * wpi, wpi, wi,
-                                      sb_bf16);
+            pairs_swiglu_tokens<BITS>(mg, mu, e, jj, H, a.lprg, wcur, xs, T, tmask, hq + m * T * pb, pb, wi,
+                                      sb_bf16, xinv);
+        }
+        __syncthreads();
+        // the scale of each (item, token): from the largest |h| of its valid values
+        __shared__ int s_es[SM_TMAX * SM_TMAX];
+        if (tid < nitems * T) {
+            const int m = tid / T;
+            int u, rbk, e, jj;
+            item_at(m, u, rbk, e, jj);
+            const int nv = min(pb, I - rbk * pb);
+            const float *hv = hq + tid * pb;
+            uint32_t mb = 0u;
+            for (int i = 0; i < nv; ++i) mb = max(mb, __float_as_uint(hv[i]) & 0x7fffffffu);
+            s_es[tid] = range_exp(__uint_as_float(mb));
         }
         __syncthreads();
         const int pieces = (wpi + 1) / 2;
@@ -546,12 +586,18 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             const int nw = min(pb, I - jb) / 2;
             if (2 * q >= nw) continue;
             const int slot = t * (K + 1) + (sh ? K : S.jt[u][t]);
-            const uint32_t *src = hq + (m * T + t) * wpi + 2 * q;
+            const int es = s_es[m * T + t];
+            const float f = exp2i(es);
+            const float *src = hq + (m * T + t) * pb + 4 * q;
+            auto word = [&](int i) { return pack_f16x2(f32_to_f16_ftz(src[2 * i] * f), f32_to_f16_ftz(src[2 * i + 1] * f)); };
             uint32_t *dst = ctl + H_BASE + cp * SM_HSTRIDE + 2 * (slot * (I / 2) + jb / 2 + 2 * q);
             if (2 * q + 1 < nw)
-                st_dev128(dst, (u32x4){src[0], tag, src[1], tag});
+                st_dev128(dst, (u32x4){word(0), tag, word(1), tag});
             else
-                st_dev64((uint64_t *)dst, src[0] | ((uint64_t)tag << 32));
+                st_dev64((uint64_t *)dst, word(0) | ((uint64_t)tag << 32));
+            if (q == 0)
+                st_dev64((uint64_t *)(ctl + H_BASE + cp * SM_HSTRIDE + SM_HEXP + 2 * (slot * bpe + rbk)),
+                         (uint32_t)es | ((uint64_t)tag << 32));
         }
         return;
     }
@@ -581,7 +627,8 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         constexpr int CPITCH = CPC + 8;
         uint16_t *hs16 = (uint16_t *)dsm;                     // [nslot][nch] chunks, padded
         float2 *hsum = (float2 *)(dsm + nslot * nch * CPITCH / 2);
-        float *s_part = (float *)(hsum + nslot * nch);        // [2][T][4 rpw]: the two parities' sums
+        float *hinv = (float *)(hsum + nslot * nch);          // 2^-e of each chunk's h scale
+        float *s_part = hinv + nslot * nch;                   // [2][T][4 rpw]: the two parities' sums
         uint32_t arrived = 0;
         // item it: union slot v = par + 2 (it / cpl), chunk lr + lpr (it % cpl).  Lane j < |U|
         // holds row 0 of routed slot j's down matrix; a slot's bases are read from its lane
@@ -637,7 +684,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     const float wt = v < nu ? S.sw[t * K + j] : S.sg[t];   // shared: its gate (or 1)
                     const int ch = (t * (K + 1) + j) * nch + cc;
                     const float p = chunk_dot<BITS>(w.q[i], (const uint32_t *)(hs16 + ch * CPITCH), w.sv[i], w.bv[i],
-                                                    hsum[ch], sb_bf16);
+                                                    hsum[ch], sb_bf16) * hinv[ch];
                     yv[t] += c < nch ? wt * p : 0.0f;
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -648,29 +695,49 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         if (NB < nit) dload(NB, wb);
         __builtin_amdgcn_sched_barrier(0);
         {
-            // all of h: groups of 8 values, 16-byte device loads, fp16 into LDS in code
-            // order, chunk sums by a DPP sum over the chunk's groups
+            // all of h: groups of 8 values, 16-byte device loads with their block's scale
+            // word, brought to the chunk's smallest block scale (a power of two), fp16
+            // into LDS in code order, chunk sums by a DPP sum over the chunk's groups
             const uint32_t *hw = ctl + H_BASE + (d % SM_HCOPIES) * SM_HSTRIDE;
+            const uint64_t *he = (const uint64_t *)(hw + SM_HEXP);
+            const int pbg = 2 * NW * (64 / a.lprg);           // values per item block (a power of two)
+            const int pbsh = 31 - __builtin_clz(pbg);
+            const int bpe = (I + pbg - 1) / pbg;
             const int ngrp = nslot * I / 8;
             const uint32_t lim = wait_bound(ctl);
             for (int g0 = 0; g0 < ngrp; g0 += DT) {
                 const int g = g0 + tid;
                 const bool live = g < ngrp;
                 const int gg = live ? g : ngrp - 1;
-                const int j = (gg / (I / 8)) % (K + 1);
+                const int sv = gg / (I / 8), sj = 8 * (gg - sv * (I / 8));
+                const int j = sv % (K + 1);
                 // slots nobody writes (a token's shared slot without a shared expert)
                 const bool used = j < K || a.shared;
                 u32x4 w0 = {0u, tag, 0u, tag}, w1 = {0u, tag, 0u, tag};
+                uint64_t we = (uint64_t)tag << 32;
                 for (uint32_t it = 0; used; ++it) {
+                    we = ld_dev64(he + sv * bpe + (sj >> pbsh));
                     ld_dev256(hw + 8 * gg, w0, w1);
-                    if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag) break;
+                    if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag && tag_of(we) == tag) break;
                     if (it > lim) {
                         raise_error(ctl);
                         break;
                     }
                     poll_pause(it);
                 }
-                const u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                const int es = (int)(uint32_t)we;
+                int ec = es;                                 // the chunk's smallest block scale
+                if (CPC / 8 >= 2) ec = min(ec, (int)dpp_u32<0xB1>((uint32_t)ec + 128u) - 128);
+                if (CPC / 8 >= 4) ec = min(ec, (int)dpp_u32<0x4E>((uint32_t)ec + 128u) - 128);
+                u32x4 nat = {w0[0], w0[2], w1[0], w1[2]};
+                if (ec != es) {                              // (blocks of extreme magnitude only)
+                    const float fr = exp2i(ec - es);
+#pragma unroll
+                    for (int jx = 0; jx < 4; ++jx) {
+                        const f16x2 hh = as_h2(nat[jx]);
+                        nat[jx] = pack_f16x2(f32_to_f16_ftz((float)hh[0] * fr), f32_to_f16_ftz((float)hh[1] * fr));
+                    }
+                }
                 float se = 0.0f, so = 0.0f;
 #pragma unroll
                 for (int jx = 0; jx < 4; ++jx) {
@@ -681,7 +748,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 if (live) *(u32x4 *)(hs16 + (g / (CPC / 8)) * CPITCH + 8 * (g % (CPC / 8))) = perm8<BITS>(nat);
                 se = group_sum(se, CPC / 8);
                 so = group_sum(so, CPC / 8);
-                if (live && (g % (CPC / 8)) == 0) hsum[g / (CPC / 8)] = make_float2(se, so);
+                if (live && (g % (CPC / 8)) == 0) {
+                    hsum[g / (CPC / 8)] = make_float2(se, so);
+                    hinv[g / (CPC / 8)] = exp2i(-ec);
+                }
             }
             __syncthreads();
             if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
@@ -735,8 +805,8 @@ size_t small_lds_bytes(const Layer &L, int T) {
     const int rows = 4 * (64 / lanes_per_row(L.I, L.bits));
     const size_t nslot = (size_t)T * (L.K + 1);
     const size_t g = (size_t)NW * PAIR_DMA_BYTES + (size_t)SM_TMAX * (L.H / cpc) * (cpc / 2 + 4) * 4 +
-                     (size_t)SM_TMAX * SM_TMAX * (pb / 2) * 4;
-    const size_t d = nslot * (L.I / cpc) * (cpc + 8) * 2 + nslot * (L.I / cpc) * 8 + (size_t)2 * SM_TMAX * rows * 4;
+                     (size_t)SM_TMAX * SM_TMAX * pb * 4;
+    const size_t d = nslot * (L.I / cpc) * (cpc + 8) * 2 + nslot * (L.I / cpc) * 12 + (size_t)2 * SM_TMAX * rows * 4;
     const size_t r = (size_t)T * L.H * 2;
     return std::max(std::max(g, d), r);
 }
@@ -785,8 +855,9 @@ SmallArgs make_small_args(const Layer &L, const uint16_t *x, int64_t T, const De
 // (LDS bound: two workgroups per CU keep the whole grid resident on these shapes; larger
 // ones take the grouped path)
 bool decode_small_eligible(const Layer &L, int64_t T) {
+    const int pb = 2 * NW * (64 / lanes_per_row(L.H, L.bits));
     return T >= 2 && T <= SM_TMAX && T * (L.K + 1) * L.I / 2 <= SM_HWORDS && L.E <= SM_TE &&
-           small_lds_bytes(L, (int)T) <= SMALL_LDS_MAX;
+           T * (L.K + 1) * ((L.I + pb - 1) / pb) <= SM_HEXPW && small_lds_bytes(L, (int)T) <= SMALL_LDS_MAX;
 }
 
 hipError_t launch_decode_small_layer(const Layer &L, const uint16_t *x, int64_t T, const DecodeBufs &b, void *y,

@@ -7,8 +7,8 @@ Inputs: bf16 activations x ~ N(0, std^2) with std 300 (h reaches ~1e7, the down 
 range); bf16 scales drawn log-uniformly over [1e-5, 1e-1] (many below fp16's normal
 range, where a plain fp16 conversion loses bits), with 4- and 8-bit codes; bf16 scales
 all near 1e-7 and all near 3e3 (every weight below, or the largest above, fp16's normal
-range).  T = 1 runs the one-launch decode kernel, T = 40 the grouped GEMMs.  Tolerance as
-for every parity case.
+range).  T = 1 runs the one-launch decode kernel, T = 3 the small-batch kernel, T = 40
+the grouped GEMMs.  Tolerance as for every parity case.
 
 The grouped path's down pass rescales h blocks of one row that carry different scales;
 ordinary inputs rarely produce such rows, so a state word forces a distinct scale on
@@ -81,7 +81,7 @@ def run_case(torch, qs, L, x_np, what, std=1.0):
 
 @pytest.mark.parametrize("cfg", ["DECODE", "SKEW"])
 @pytest.mark.parametrize("std", [300.0, 3e4, 1e-6])
-@pytest.mark.parametrize("T", [1, 40])
+@pytest.mark.parametrize("T", [1, 3, 40])
 def test_range_extremes(torch, qs, cfg, std, T):
     L = wide_layer(cfg)
     x_np = syn.make_x(T, L.hidden, seed=400 + T, std=std)
@@ -90,7 +90,7 @@ def test_range_extremes(torch, qs, cfg, std, T):
 
 @pytest.mark.parametrize("cfg", ["DECODE", "SKEW"])
 @pytest.mark.parametrize("scale_range", [(5e-8, 2e-7), (2e3, 5e3)])
-@pytest.mark.parametrize("T", [1, 40])
+@pytest.mark.parametrize("T", [1, 3, 40])
 def test_range_of_scales(torch, qs, cfg, scale_range, T):
     L = wide_layer(cfg, scale_range)
     x_np = syn.make_x(T, L.hidden, seed=500 + T)
