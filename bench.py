@@ -6,15 +6,28 @@ batch of synthetic input already resident in HBM.  The headline line reports the
 batch-1 decode workload (hidden 2048, 256 experts top-8 + 1 shared, expert inter 512,
 4-bit affine group-64 weights, T = 1): tokens/s, with the layer's algorithmic weight
 bytes over HBM peak as the roofline.  Extra keys report the prefill (T = 4096), the
-skewed long prefill (T = 16384, 8-bit, Zipf router bias), the dense Q8_0 GEMV, the
-same GEMVs with a quantized activation (int8 dots, and their deviation from the exact
-path) and (--only smallT) the decode layer at T = 1, 2, 4, 5, 8.
+skewed long prefill (T = 16384, 8-bit, Zipf router bias), the tiny layer (T = 4), the
+dense Q8_0 GEMV (all four projections, and each shape alone), the same GEMVs with a
+quantized activation, and (--only smallT) the decode layer at T = 1, 2, 4, 5, 8.
 
-Decode cycles through 40 distinct copies of the layer (18 GB, far beyond the 256 MB
-Infinity Cache) so every step streams its experts from HBM.  Steps are captured in one
-HIP graph; HIP events on the replay stream bracket the timed region.
+Timing protocol.
+  - Decode cycles through 40 distinct copies of the layer (the 40 layers of a token's
+    pass; 17.5 GB, far beyond the 256 MB on-die cache), so every step streams its
+    experts from HBM.  The headline times exactly --steps steps after --warmup untimed
+    ones, between device synchronizations, with HIP events on the replay stream.
+  - Every workload is also captured as a HIP graph (decode: 40 steps, one per copy) and
+    replayed in >= 30 rounds; each round runs every workload once in a seeded random
+    order, the decode graph twice (a duplicated configuration: the spread between its
+    two medians is the noise control).  Each replay is bracketed by its own events, the
+    round's replays are enqueued back to back.  Median and minimum per step are
+    reported; the prefill and skew rates use the median.
+  - Measured ceilings: a read-only stream over an 8 GiB buffer and an MFMA-only fp16
+    loop (the library's moe_calib_* helpers), best of 5, next to the published peaks.
+  - cpu_baseline: the fp64 oracle on the host's cores, on bounded samples of the same
+    workloads (decode at top level; tiny, prefill, skew and Q8_0 under cpu_baselines).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only decode,prefill,skew,q8,q8x,smallT,variant,copy]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--rounds R]
+                    [--only decode,prefill,skew,tiny,q8,q8x,ceil,smallT,variant,copy]
 """
 from __future__ import annotations
 
@@ -29,16 +42,22 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFS = 2500.0     # MI355X dense fp16/bf16 MFMA, TFLOP/s
 GROUP = 64
+DECODE_COPIES = 40
+ORDER_SEED = 20261202
 
-# HBM traffic of one decode-kernel launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
-# (KiB per dispatch, median over the timed launches), each scaled by what the same
-# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  A
-# figure holds only for the kernel sources it was measured on, identified by their
-# sha256; once they change the traffic is reported as null until measured again.
+# HBM traffic of one kernel launch: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per
+# dispatch, median over the timed launches), each scaled by what the same counter reads
+# for a plain 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  A figure holds only
+# for the kernel sources it was measured on, identified by their sha256; once they change
+# the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/decode_state.h", "csrc/common.h", "csrc/internal.h")
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/internal.h")
 PREFILL_TRAFFIC = {"sources_sha256": "a1d683c4130b605d777143281266a3820d5ae4e79a84a41909bb194fcc1f9e12", "bytes": 1002660106}
 DECODE_TRAFFIC = {"sources_sha256": "8886823710cf56d48e32cf7a72c37fe7ab5888a9605d6196767a04915e92ef1d", "bytes": 17974594}
+# MFMA utilisation of the grouped GEMM from rocprofv3 --pmc (medians per dispatch):
+# busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); keyed like
+# the traffic.
+GEMM_COUNTERS = {"sources_sha256": None}
 
 
 # ----------------------------------------------------------- algorithmic accounting
@@ -67,20 +86,30 @@ def layer_flops(T: int, H: int, I: int, E: int, K: int, shared: bool = True) -> 
     return 2 * T * E * H + 2 * T * (K + (1 if shared else 0)) * 3 * H * I
 
 
-def measured_traffic(sources, rec):
-    """HBM bytes per launch from the committed counter runs, or None once the kernel's
-    sources differ from the ones the counters were taken on."""
+def _sources_sha(sources) -> str:
     import hashlib
     h = hashlib.sha256()
     pkg = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_sparse_moe_amd")
     for f in sources:
         with open(os.path.join(pkg, f), "rb") as fh:
             h.update(fh.read())
-    return rec["bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+    return h.hexdigest()
+
+
+def measured_traffic(sources, rec):
+    """HBM bytes per launch from the committed counter runs, or None once the kernel's
+    sources differ from the ones the counters were taken on."""
+    return rec["bytes"] if _sources_sha(sources) == rec["sources_sha256"] else None
 
 
 def decode_traffic():
     return measured_traffic(DECODE_SOURCES, DECODE_TRAFFIC)
+
+
+def gemm_counters(bits: int):
+    if GEMM_COUNTERS.get("sources_sha256") != _sources_sha(GEMM_SOURCES):
+        return None
+    return GEMM_COUNTERS.get(f"k_gemm<{bits}>")
 
 
 # ------------------------------------------------------------------------- helpers
@@ -108,31 +137,79 @@ def _dev_layer_copies(qs, torch, L, copies: int):
     return descs
 
 
-def _graph_time(torch, fn_steps, steps: int, warmup: int):
-    """Capture `steps` calls in a HIP graph, replay once untimed (after `warmup` eager
-    steps), then time one replay with events on the replay stream. Returns ms/step."""
-    stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        for i in range(warmup):
-            fn_steps(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for i in range(steps):
-            fn_steps(i)
-    torch.cuda.synchronize()
-    g.replay()                      # untimed replay
-    torch.cuda.synchronize()
+class Graph:
+    """`steps` calls of fn(i) captured once (after `warmup` eager calls); replays run on
+    the current stream."""
+
+    def __init__(self, torch, fn, steps: int, warmup: int = 2, first: int = 0):
+        self.torch, self.steps = torch, steps
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(first + i)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g, stream=stream):
+            for i in range(steps):
+                fn(first + i)
+        torch.cuda.synchronize()
+        self.g.replay()                 # untimed
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.g.replay()
+
+
+def _event(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+def time_exact_steps(torch, graphs):
+    """Replay the graphs in order between device synchronizations, bracketed by events on
+    the replay stream; returns (ms, steps)."""
     cur = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = _event(torch), _event(torch)
     torch.cuda.synchronize()
-    start.record(cur)
-    g.replay()
-    end.record(cur)
-    end.synchronize()
+    a.record(cur)
+    for g in graphs:
+        g.replay()
+    b.record(cur)
+    b.synchronize()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return a.elapsed_time(b), sum(g.steps for g in graphs)
+
+
+def interleaved_rounds(torch, graphs: dict, rounds: int, duplicate: str = None, seed: int = ORDER_SEED):
+    """`rounds` rounds; in each, every graph is replayed once (and `duplicate` a second time
+    under the name duplicate + '#2') in a seeded random order, each replay between its own
+    events, all of a round enqueued back to back.  Returns name -> per-step ms list."""
+    cur = torch.cuda.current_stream()
+    rng = np.random.default_rng(seed)
+    names = list(graphs) + ([duplicate + "#2"] if duplicate else [])
+    times = {n: [] for n in names}
+    torch.cuda.synchronize()
+    for _ in range(rounds):
+        order = [names[i] for i in rng.permutation(len(names))]
+        evs = []
+        for n in order:
+            g = graphs[n.split("#")[0]]
+            a, b = _event(torch), _event(torch)
+            a.record(cur)
+            g.replay()
+            b.record(cur)
+            evs.append((n, g.steps, a, b))
+        evs[-1][3].synchronize()
+        for n, st, a, b in evs:
+            times[n].append(a.elapsed_time(b) / st)
+    torch.cuda.synchronize()
+    return times
+
+
+def stats(ms_list):
+    v = np.asarray(ms_list, np.float64)
+    return {"replays": int(v.size), "median_ms": float(np.median(v)), "min_ms": float(v.min()),
+            "max_ms": float(v.max()), "p25_ms": float(np.percentile(v, 25)), "p75_ms": float(np.percentile(v, 75))}
 
 
 def cpu_cores() -> int:
@@ -142,22 +219,54 @@ def cpu_cores() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline_decode(L, ntok: int):
-    """fp64 oracle on a bounded sample of decode tokens (baseline only)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ----------------------------------------------------------------- cpu baselines
+def _oracle():
     import oracle
     oracle.build(force=False)
+    return oracle
+
+
+def cpu_baseline_layer(L, ntok: int, what: str, seed: int = 123):
+    """fp64 oracle over `ntok` tokens of a layer workload (baseline only)."""
+    oracle = _oracle()
     import qsmoe_synth as syn
-    x = syn.make_x(ntok, L.hidden, seed=123)
+    x = syn.make_x(ntok, L.hidden, seed=seed)
     ol = oracle.OracleLayer(L)
     t = time.perf_counter()
     oracle.layer_forward(ol, x)
     dt = time.perf_counter() - t
     return {"value": ntok / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{ntok} tokens of the decode workload, one layer, fp64, {dt:.1f} s"}
+            "sample": f"{ntok} tokens of the {what} workload, one layer, fp64, {dt:.2f} s"}
+
+
+def cpu_baseline_q8(syn, reps: int = 5):
+    """fp64 oracle Q8_0 GEMVs of the four projections; median of `reps` runs."""
+    oracle = _oracle()
+    mats = [(N, K, syn.make_q8_rows(N, K, seed=N + K), syn.make_x(1, K, seed=K)[0]) for N, K in syn.Q8_SHAPES]
+    ts = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        for N, K, rows, x in mats:
+            oracle.q8_gemv(rows, N, K, x)
+        ts.append(time.perf_counter() - t)
+    dt = float(np.median(ts))
+    return {"value": 1.0 / dt, "unit": "layers/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the four Q8_0 projections of one layer, fp64, median of {reps}: {dt * 1e3:.1f} ms"}
 
 
 # ----------------------------------------------------------------------- workloads
-def bench_decode(qs, torch, syn, steps, warmup, copies=40, **variant):
+def make_decode(qs, torch, syn, warmup, copies=DECODE_COPIES, **variant):
     L = syn.make_layer(**syn.DECODE, **variant)
     descs = _dev_layer_copies(qs, torch, L, copies)
     xs = [torch.from_numpy(syn.make_x(1, L.hidden, seed=100 + l).view(np.int16)).cuda() for l in range(copies)]
@@ -168,9 +277,82 @@ def bench_decode(qs, torch, syn, steps, warmup, copies=40, **variant):
         l = i % copies
         qs.moe_layer_forward(descs[l], xs[l], y=ys[l], workspace=ws)
 
-    ms = _graph_time(torch, step, steps, warmup)
     nbytes = decode_layer_bytes(L.hidden, L.inter, L.n_experts, L.top_k, L.bits)
-    return L, ms, nbytes
+    return L, step, nbytes, (descs, xs, ys, ws)
+
+
+def make_prefill(qs, torch, syn, cfg, T, copies):
+    L = syn.make_layer(**cfg)
+    descs = _dev_layer_copies(qs, torch, L, copies)
+    x = torch.from_numpy(syn.make_x(T, L.hidden, seed=0).view(np.int16)).cuda()
+    y = torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda")
+    # a workspace for the whole T, so that the call runs unchunked (one pass over the
+    # expert weights); with the default size a long prompt runs in 4096-token chunks
+    ws = torch.zeros(qs.moe_workspace_size(descs[0], T, chunk=T), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        qs.moe_layer_forward(descs[i % copies], x, y=y, workspace=ws)
+
+    return L, step, layer_flops(T, L.hidden, L.inter, L.n_experts, L.top_k), (descs, x, y, ws)
+
+
+def make_q8(qs, torch, syn, layers=16, shapes=None):
+    shapes = shapes or syn.Q8_SHAPES
+    mats = []
+    for (N, K) in shapes:
+        rows = torch.from_numpy(syn.make_q8_rows(N, K, seed=N + K).reshape(-1)).cuda()
+        tiles = qs.q8_pack_rows16(rows, N, K)
+        mats.append([(tiles if l == 0 else tiles.clone()) for l in range(layers)])
+    xs = {K: torch.from_numpy(syn.make_x(1, K, seed=K)[0].view(np.int16)).cuda() for _, K in shapes}
+    ys = {N: torch.empty((N,), dtype=torch.bfloat16, device="cuda") for N, _ in shapes}
+    torch.cuda.synchronize()
+
+    def step(i):
+        l = i % layers
+        for j, (N, K) in enumerate(shapes):
+            qs.q8_gemv(mats[j][l], N, K, xs[K], y=ys[N])
+
+    nbytes = sum(q8_weight_bytes(N, K) + 2 * K + 2 * N for N, K in shapes)
+    return step, nbytes, (mats, xs, ys)
+
+
+def bench_q8x(qs, torch, syn, steps, warmup, layers=16, fused=False):
+    """The four projections with the activation quantized once per projection input
+    (q8_quantize_x) and int8-dot GEMVs (q8_gemv_q8x), or (fused) quantized inside the
+    GEMV (q8_gemv_qx); also the largest deviation from the exact-activation GEMV,
+    relative to that output's RMS."""
+    shapes = syn.Q8_SHAPES
+    mats = []
+    for (N, K) in shapes:
+        rows = torch.from_numpy(syn.make_q8_rows(N, K, seed=N + K).reshape(-1)).cuda()
+        tiles = qs.q8_pack_rows16(rows, N, K)
+        mats.append([(tiles if l == 0 else tiles.clone()) for l in range(layers)])
+    xs = {K: torch.from_numpy(syn.make_x(1, K, seed=K)[0].view(np.int16)).cuda() for _, K in shapes}
+    xqs = {K: torch.empty((K,), dtype=torch.int8, device="cuda") for _, K in shapes}
+    xds = {K: torch.empty((K // 32,), dtype=torch.int16, device="cuda") for _, K in shapes}
+    ys = [torch.empty((N,), dtype=torch.bfloat16, device="cuda") for N, _ in shapes]
+    torch.cuda.synchronize()
+
+    def step(i):
+        l = i % layers
+        for j, (N, K) in enumerate(shapes):
+            if fused:
+                qs.q8_gemv_qx(mats[j][l], N, K, xs[K], y=ys[j])
+            else:
+                qs.q8_quantize_x(xs[K], xq=xqs[K], xd=xds[K])
+                qs.q8_gemv_q8x(mats[j][l], N, K, xqs[K], xds[K], y=ys[j])
+
+    g = Graph(torch, step, steps, warmup)
+    ms, n = time_exact_steps(torch, [g])
+    ms /= n
+    err = 0.0
+    for j, (N, K) in enumerate(shapes):
+        xq, xd = qs.q8_quantize_x(xs[K])
+        yq = qs.q8_gemv_q8x(mats[j][0], N, K, xq, xd).double()
+        ye = qs.q8_gemv(mats[j][0], N, K, xs[K]).double()
+        err = max(err, float((yq - ye).abs().max() / ye.pow(2).mean().sqrt()))
+    nbytes = sum(q8_weight_bytes(N, K) + 2 * K + 2 * N for N, K in shapes)
+    return ms, nbytes, err
 
 
 def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 5, 8), copies=40):
@@ -196,7 +378,9 @@ def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 5, 8), copies=40):
             l = i % copies
             qs.moe_layer_forward(descs[l], xs[l], y=ys[l], workspace=ws)
 
-        ms = _graph_time(torch, step, steps, warmup)
+        g = Graph(torch, step, steps, warmup)
+        ms, n = time_exact_steps(torch, [g])
+        ms /= n
         experts = float(np.mean(union))
         nbytes = L.n_experts * L.hidden * 2 + (experts + 1) * eb + 2 * T * L.hidden * 2
         res.append({"T": T, "us_per_call": ms * 1e3, "tokens_per_s": T / (ms * 1e-3),
@@ -206,97 +390,52 @@ def bench_small_t(qs, torch, syn, steps, warmup, Ts=(1, 2, 4, 5, 8), copies=40):
     return res
 
 
-def bench_prefill(qs, torch, syn, cfg, T, steps, warmup, copies):
-    L = syn.make_layer(**cfg)
-    descs = _dev_layer_copies(qs, torch, L, copies)
-    x = torch.from_numpy(syn.make_x(T, L.hidden, seed=0).view(np.int16)).cuda()
-    y = torch.empty((T, L.hidden), dtype=torch.bfloat16, device="cuda")
-    # a workspace for the whole T, so that the call runs unchunked (one pass over the
-    # expert weights); with the default size a long prompt runs in 4096-token chunks
-    ws = torch.zeros(qs.moe_workspace_size(descs[0], T, chunk=T), dtype=torch.uint8, device="cuda")
-
-    def step(i):
-        qs.moe_layer_forward(descs[i % copies], x, y=y, workspace=ws)
-
-    ms = _graph_time(torch, step, steps, warmup)
-    flops = layer_flops(T, L.hidden, L.inter, L.n_experts, L.top_k)
-    return L, ms, flops
-
-
-def bench_q8(qs, torch, syn, steps, warmup, layers=16):
-    shapes = syn.Q8_SHAPES
-    mats = []
-    for (N, K) in shapes:
-        rows = torch.from_numpy(syn.make_q8_rows(N, K, seed=N + K).reshape(-1)).cuda()
-        tiles = qs.q8_pack_rows16(rows, N, K)
-        mats.append([(tiles if l == 0 else tiles.clone()) for l in range(layers)])
-    xs = {K: torch.from_numpy(syn.make_x(1, K, seed=K)[0].view(np.int16)).cuda() for _, K in shapes}
-    ys = {N: torch.empty((N,), dtype=torch.bfloat16, device="cuda") for N, _ in shapes}
-    torch.cuda.synchronize()
-
-    def step(i):
-        l = i % layers
-        for j, (N, K) in enumerate(shapes):
-            qs.q8_gemv(mats[j][l], N, K, xs[K], y=ys[N])
-
-    ms = _graph_time(torch, step, steps, warmup)
-    nbytes = sum(q8_weight_bytes(N, K) + 2 * K + 2 * N for N, K in shapes)
-    return ms, nbytes
-
-
-def bench_q8x(qs, torch, syn, steps, warmup, layers=16, fused=False):
-    """The same four projections with the activation quantized once per projection input
-    (q8_quantize_x) and int8-dot GEMVs (q8_gemv_q8x), or (fused) quantized inside the
-    GEMV (q8_gemv_qx); also the largest deviation from the exact-activation GEMV,
-    relative to that output's RMS."""
-    shapes = syn.Q8_SHAPES
-    mats = []
-    for (N, K) in shapes:
-        rows = torch.from_numpy(syn.make_q8_rows(N, K, seed=N + K).reshape(-1)).cuda()
-        tiles = qs.q8_pack_rows16(rows, N, K)
-        mats.append([(tiles if l == 0 else tiles.clone()) for l in range(layers)])
-    xs = {K: torch.from_numpy(syn.make_x(1, K, seed=K)[0].view(np.int16)).cuda() for _, K in shapes}
-    xqs = {K: torch.empty((K,), dtype=torch.int8, device="cuda") for _, K in shapes}
-    xds = {K: torch.empty((K // 32,), dtype=torch.int16, device="cuda") for _, K in shapes}
-    ys = [torch.empty((N,), dtype=torch.bfloat16, device="cuda") for N, _ in shapes]
-    torch.cuda.synchronize()
-
-    def step(i):
-        l = i % layers
-        for j, (N, K) in enumerate(shapes):
-            if fused:
-                qs.q8_gemv_qx(mats[j][l], N, K, xs[K], y=ys[j])
-            else:
-                qs.q8_quantize_x(xs[K], xq=xqs[K], xd=xds[K])
-                qs.q8_gemv_q8x(mats[j][l], N, K, xqs[K], xds[K], y=ys[j])
-
-    ms = _graph_time(torch, step, steps, warmup)
-    err = 0.0
-    for j, (N, K) in enumerate(shapes):
-        xq, xd = qs.q8_quantize_x(xs[K])
-        yq = qs.q8_gemv_q8x(mats[j][0], N, K, xq, xd).double()
-        ye = qs.q8_gemv(mats[j][0], N, K, xs[K]).double()
-        err = max(err, float((yq - ye).abs().max() / ye.pow(2).mean().sqrt()))
-    nbytes = sum(q8_weight_bytes(N, K) + 2 * K + 2 * N for N, K in shapes)
-    return ms, nbytes, err
-
-
-def bench_copy(torch, steps, nbytes=1 << 30):
+def bench_copy(torch, nbytes=1 << 30):
     """Plain device-to-device copy of `nbytes` (torch's copy kernel): the calibration
     workload for the HBM byte counters (it must read and write exactly `nbytes`)."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty_like(a)
-    ms = _graph_time(torch, lambda i: b.copy_(a), steps, 2)
-    return ms, nbytes
+    g = Graph(torch, lambda i: b.copy_(a), 8, 2)
+    ms, n = time_exact_steps(torch, [g])
+    return ms / n, nbytes
 
 
+def measure_ceilings(qs, torch, read_bytes=8 << 30, mfma_iters=4000, mfma_blocks=512, reps=5):
+    """Best of `reps`: the read-only stream's GB/s and the MFMA-only loop's TFLOP/s."""
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device="cuda").fill_(3)
+    cur = torch.cuda.current_stream()
+    best_r = best_m = float("inf")
+    qs.moe_calib_read(buf)
+    qs.moe_calib_mfma(mfma_iters // 10, mfma_blocks)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        a, b, c = _event(torch), _event(torch), _event(torch)
+        a.record(cur)
+        qs.moe_calib_read(buf)
+        b.record(cur)
+        qs.moe_calib_mfma(mfma_iters, mfma_blocks)
+        c.record(cur)
+        c.synchronize()
+        best_r = min(best_r, a.elapsed_time(b))
+        best_m = min(best_m, b.elapsed_time(c))
+    del buf
+    flops = mfma_blocks * 4 * mfma_iters * 8 * 16384
+    return {"hbm_read": {"GB_per_s": read_bytes / (best_r * 1e-3) / 1e9, "bytes": read_bytes,
+                         "kernel": "moe_calib_read: read-only stream, 16-byte nontemporal loads", "best_of": reps},
+            "mfma_f16": {"TFLOP_per_s": flops / (best_m * 1e-3) / 1e12, "flops": flops,
+                         "kernel": "moe_calib_mfma: v_mfma_f32_16x16x32_f16 on registers, 8 chains per wave",
+                         "best_of": reps}}
+
+
+# --------------------------------------------------------------------------- main
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--rounds", type=int, default=40)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="decode,prefill,skew,q8,q8x")
+    ap.add_argument("--only", default="decode,prefill,skew,tiny,q8,q8x,ceil")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are "
@@ -307,13 +446,23 @@ def main(argv=None):
     import quantized_sparse_moe_amd as qs
     qs.lib()
     only = set(args.only.split(","))
+    rounds = max(30, args.rounds)
     out = {"metric": "MoE-layer tokens/s (decode T=1, prefill T=4096) + % HBM / MFMA roofline",
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
            "data": "synthetic"}
-    Ld = None
+    graphs, keep, meta = {}, [], {}
+    Ld = Lp = Ls = Lt = None
+
     if "decode" in only:
-        Ld, ms, nbytes = bench_decode(qs, torch, syn, args.steps, args.warmup)
+        Ld, step, nbytes, k = make_decode(qs, torch, syn, args.warmup)
+        keep.append(k)
+        # the headline: exactly --steps steps (after --warmup), copies cycling
+        full, rem = divmod(args.steps, DECODE_COPIES)
+        g40 = Graph(torch, step, DECODE_COPIES, args.warmup)
+        parts = [g40] * full + ([Graph(torch, step, rem, 0)] if rem else [])
+        ms_total, n = time_exact_steps(torch, parts)
+        ms = ms_total / n
         out["value"] = 1.0 / (ms * 1e-3)
         out["ms_per_step"] = ms
         out["config"] = {"workload": "decode MoE layer: hidden 2048, 256 experts top-8 + 1 shared, "
@@ -323,52 +472,132 @@ def main(argv=None):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
-                           "kernel": "decode layer (router+shared gate/up, routed gate/up, down+combine)",
+                           "kernel": "k_decode<4>: the whole layer in one launch (one launch per step)",
                            "bytes_per_launch": nbytes}
-    if "variant" in only:
-        # same decode layer with bf16 scales / biases and the sigmoid-gated shared expert
-        Lv, ms, nbytes = bench_decode(qs, torch, syn, args.steps, args.warmup, scale_dtype="bf16",
-                                      shared_gate=True)
-        out["decode_bf16_gated"] = {"ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
-                                    "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+        graphs["decode"] = g40
+        meta["decode"] = {"bytes": nbytes}
     if "prefill" in only:
-        steps = max(4, args.steps // 100)
-        L, ms, flops = bench_prefill(qs, torch, syn, syn.PREFILL, syn.PREFILL_T, steps,
-                                     max(2, args.warmup // 10), copies=4)
-        tf = flops / (ms * 1e-3) / 1e12
-        out["prefill"] = {"tokens_per_s": syn.PREFILL_T / (ms * 1e-3), "ms_per_step": ms, "T": syn.PREFILL_T,
-                          "steps": steps,
-                          "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFS,
-                                       "unit": "TFLOP/s", "frac": tf / MFMA_F16_PEAK_TFS,
-                                       "traffic": measured_traffic(GEMM_SOURCES, PREFILL_TRAFFIC),
-                                       "flops_per_step": flops}}
+        Lp, step, flops, k = make_prefill(qs, torch, syn, syn.PREFILL, syn.PREFILL_T, copies=4)
+        keep.append(k)
+        graphs["prefill"] = Graph(torch, step, 4, 2)
+        meta["prefill"] = {"flops": flops, "T": syn.PREFILL_T, "bits": 4}
     if "skew" in only:
-        steps = max(2, args.steps // 400)
-        L, ms, flops = bench_prefill(qs, torch, syn, syn.SKEW, syn.SKEW_T, steps, 1, copies=1)
-        tf = flops / (ms * 1e-3) / 1e12
-        out["skew"] = {"tokens_per_s": syn.SKEW_T / (ms * 1e-3), "ms_per_step": ms, "T": syn.SKEW_T,
-                       "steps": steps, "tflops": tf, "frac_mfma": tf / MFMA_F16_PEAK_TFS}
-    if "smallT" in only:
-        out["small_t"] = bench_small_t(qs, torch, syn, max(40, args.steps // 10), args.warmup)
+        Ls, step, flops, k = make_prefill(qs, torch, syn, syn.SKEW, syn.SKEW_T, copies=1)
+        keep.append(k)
+        graphs["skew"] = Graph(torch, step, 1, 2)
+        meta["skew"] = {"flops": flops, "T": syn.SKEW_T, "bits": 8}
+    if "tiny" in only:
+        Lt, step, flops, k = make_prefill(qs, torch, syn, syn.TINY, syn.TINY_T, copies=16)
+        keep.append(k)
+        graphs["tiny"] = Graph(torch, step, 16, 2)
+        meta["tiny"] = {"flops": flops, "T": syn.TINY_T}
     if "q8" in only:
-        steps = max(16, args.steps // 4)
-        ms, nbytes = bench_q8(qs, torch, syn, steps, args.warmup)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out["q8"] = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
-                     "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": nbytes}
+        step, nbytes, k = make_q8(qs, torch, syn)
+        keep.append(k)
+        graphs["q8"] = Graph(torch, step, 16, 2)
+        meta["q8"] = {"bytes": nbytes}
+        for (N, K) in syn.Q8_SHAPES:
+            step, nb, k = make_q8(qs, torch, syn, shapes=[(N, K)])
+            keep.append(k)
+            graphs[f"q8_{N}x{K}"] = Graph(torch, step, 16, 2)
+            meta[f"q8_{N}x{K}"] = {"bytes": nb}
+
+    ceil = measure_ceilings(qs, torch) if "ceil" in only else None
+    if ceil:
+        out["ceilings"] = ceil
+
+    if graphs:
+        times = interleaved_rounds(torch, graphs, rounds, duplicate="decode" if "decode" in graphs else None)
+        timing = {n: stats(v) for n, v in times.items()}
+        out["timing"] = {"protocol": f"{rounds} rounds, each workload's graph replayed once per round in a "
+                                     f"seeded random order (seed {ORDER_SEED}), decode twice (noise control); "
+                                     "per-step ms per replay",
+                         "workloads": timing}
+        if "decode" in timing:
+            a, b = timing["decode"]["median_ms"], timing["decode#2"]["median_ms"]
+            out["timing"]["noise_control"] = {"config": "decode", "median_ms_a": a, "median_ms_b": b,
+                                              "rel_diff": abs(a - b) / min(a, b)}
+            rb = meta["decode"]["bytes"] / (timing["decode"]["median_ms"] * 1e-3) / 1e9
+            out["roofline"]["replay_median"] = {"ms_per_step": timing["decode"]["median_ms"], "achieved": rb,
+                                                "frac": rb / HBM_PEAK_GBS}
+            if ceil:
+                cr = ceil["hbm_read"]["GB_per_s"]
+                out["roofline"]["ceiling"] = {"measured_peak": cr, "unit": "GB/s", "frac": out["roofline"]["achieved"] / cr,
+                                              "kind": "read-only stream, 8 GiB"}
+        for key in ("prefill", "skew", "tiny"):
+            if key not in timing:
+                continue
+            ms = timing[key]["median_ms"]
+            m = meta[key]
+            tf = m["flops"] / (ms * 1e-3) / 1e12
+            rec = {"tokens_per_s": m["T"] / (ms * 1e-3), "ms_per_step": ms, "T": m["T"],
+                   "min_ms": timing[key]["min_ms"], "replays": timing[key]["replays"],
+                   "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_F16_PEAK_TFS, "unit": "TFLOP/s",
+                                "frac": tf / MFMA_F16_PEAK_TFS, "flops_per_step": m["flops"],
+                                "scope": "the whole layer (all its kernels) per step"}}
+            if ceil:
+                cm = ceil["mfma_f16"]["TFLOP_per_s"]
+                rec["roofline"]["ceiling"] = {"measured_peak": cm, "unit": "TFLOP/s", "frac": tf / cm,
+                                              "kind": "MFMA-only fp16 loop"}
+            if key == "prefill":
+                rec["roofline"]["traffic"] = measured_traffic(GEMM_SOURCES, PREFILL_TRAFFIC)
+            if key in ("prefill", "skew"):
+                rec["gemm_counters"] = gemm_counters(m["bits"])
+            out[key] = rec
+        if "q8" in timing:
+            ms = timing["q8"]["median_ms"]
+            gbs = meta["q8"]["bytes"] / (ms * 1e-3) / 1e9
+            q8 = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
+                  "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": meta["q8"]["bytes"], "shapes": {}}
+            for (N, K) in syn.Q8_SHAPES:
+                n = f"q8_{N}x{K}"
+                sm = timing[n]["median_ms"]
+                sg = meta[n]["bytes"] / (sm * 1e-3) / 1e9
+                q8["shapes"][f"{N}x{K}"] = {"us": sm * 1e3, "GB_per_s": sg, "frac_hbm": sg / HBM_PEAK_GBS,
+                                            "bytes": meta[n]["bytes"]}
+            if ceil:
+                q8["frac_ceiling"] = gbs / ceil["hbm_read"]["GB_per_s"]
+            out["q8"] = q8
+
     if "q8x" in only:
         steps = max(16, args.steps // 4)
         for key, fused in (("q8x", False), ("q8qx", True)):
-            ms, nbytes, err = bench_q8x(qs, torch, syn, steps, args.warmup, fused=fused)
+            ms, nbytes, err = bench_q8x(qs, torch, syn, steps, 2, fused=fused)
             gbs = nbytes / (ms * 1e-3) / 1e9
             out[key] = {"layers_per_s": 1.0 / (ms * 1e-3), "ms_per_layer": ms, "GB_per_s": gbs,
                         "frac_hbm": gbs / HBM_PEAK_GBS, "bytes_per_layer": nbytes,
                         "max_err_vs_exact_over_rms": err}
+    if "variant" in only:
+        # the decode layer with bf16 scales / biases and the sigmoid-gated shared expert
+        Lv, step, nbytes, k = make_decode(qs, torch, syn, 2, scale_dtype="bf16", shared_gate=True)
+        g = Graph(torch, step, DECODE_COPIES, 2)
+        ms, n = time_exact_steps(torch, [g] * 4)
+        ms /= n
+        out["decode_bf16_gated"] = {"ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
+                                    "GB_per_s": nbytes / (ms * 1e-3) / 1e9}
+        del k
+    if "smallT" in only:
+        out["small_t"] = bench_small_t(qs, torch, syn, max(40, args.steps // 10), 2)
     if "copy" in only:
-        ms, nbytes = bench_copy(torch, 8)
+        ms, nbytes = bench_copy(torch)
         out["copy"] = {"bytes_each_way": nbytes, "ms": ms, "GB_per_s": 2 * nbytes / (ms * 1e-3) / 1e9}
-    if not args.no_cpu and Ld is not None:
-        out["cpu_baseline"] = cpu_baseline_decode(Ld, 1024)
+    del keep, graphs
+
+    if not args.no_cpu:
+        cb = {}
+        if Ld is not None:
+            out["cpu_baseline"] = cpu_baseline_layer(Ld, 1024, "decode (T = 1 rows)")
+            out["cpu_baseline"]["cpu_model"] = cpu_model()
+        if Lt is not None:
+            cb["tiny"] = cpu_baseline_layer(Lt, 4 * 64, "tiny (64 calls of T = 4)")
+        if Lp is not None:
+            cb["prefill"] = cpu_baseline_layer(Lp, 32, "prefill (32 of its 4096 tokens)")
+        if Ls is not None:
+            cb["skew"] = cpu_baseline_layer(Ls, 16, "skew 8-bit (16 of its 16384 tokens)")
+        if "q8" in only:
+            cb["q8"] = cpu_baseline_q8(syn)
+        if cb:
+            out["cpu_baselines"] = cb
     print(json.dumps(out), flush=True)
     return 0
 

@@ -278,6 +278,21 @@ moe_status q8_gemv_qx(const void *w_tiles, int64_t N, int64_t K, const void *x, 
 moe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tiles,
                             void *stream);
 
+/*
+ * Measured ceilings ([LILY] "Limits of further optimization": kernels are judged
+ * against the fastest sustained rate of their resource, next to the data-sheet peak).
+ * Measurement helpers only; they compute nothing the layer uses.
+ *   moe_calib_read  one read-only pass over buf (bytes % 16 == 0, 16-byte aligned) with
+ *                   16-byte nontemporal loads: time it to get the sustained HBM read
+ *                   rate (use a buffer far larger than the 256 MB on-die cache).
+ *   moe_calib_mfma  `blocks` workgroups of 4 waves, each wave issuing iters x 8
+ *                   v_mfma_f32_16x16x32_f16 (16384 flops each) on register operands:
+ *                   the sustained dense fp16 matrix rate.
+ * Both enqueue one kernel on `stream` and store nothing.
+ */
+moe_status moe_calib_read(const void *buf, size_t bytes, void *stream);
+moe_status moe_calib_mfma(int32_t iters, int32_t blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,7 +53,7 @@ class moe_layer_desc(ctypes.Structure):
 EXPORTS = ("moe_abi_version", "moe_status_string", "moe_workspace_size",
            "moe_workspace_size_chunked", "moe_workspace_status", "moe_route",
            "moe_layer_forward", "moe_layer_forward_static", "q8_gemv", "q8_quantize_x", "q8_gemv_q8x", "q8_gemv_qx",
-           "q8_pack_rows16")
+           "q8_pack_rows16", "moe_calib_read", "moe_calib_mfma")
 
 
 def lib() -> ctypes.CDLL:
@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.q8_gemv_qx.argtypes = [P, I64, I64, P, P, I32, P]
         L.q8_pack_rows16.restype = I32
         L.q8_pack_rows16.argtypes = [P, I64, I64, P, P]
+        L.moe_calib_read.restype = I32
+        L.moe_calib_read.argtypes = [P, SZ, P]
+        L.moe_calib_mfma.restype = I32
+        L.moe_calib_mfma.argtypes = [I32, I32, P]
         _lib = L
     return _lib
 
@@ -364,3 +368,13 @@ def q8_pack_rows16(w_rows, N: int, K: int, w_tiles=None, stream=None):
         w_tiles = _empty((N // 16 * (K // 32) * 544,), torch.uint8, w_rows.device, stream)
     _check(lib().q8_pack_rows16(_ptr(w_rows), N, K, _ptr(w_tiles), _stream(stream)), "q8_pack_rows16")
     return w_tiles
+
+
+def moe_calib_read(buf, stream=None):
+    """Enqueue one read-only pass over the device buffer `buf` (measured HBM ceiling)."""
+    _check(lib().moe_calib_read(_ptr(buf), buf.numel() * buf.element_size(), _stream(stream)), "moe_calib_read")
+
+
+def moe_calib_mfma(iters: int, blocks: int, stream=None):
+    """Enqueue the MFMA-only loop: blocks x 4 waves x iters x 8 MFMAs of 16384 flops."""
+    _check(lib().moe_calib_mfma(iters, blocks, _stream(stream)), "moe_calib_mfma")

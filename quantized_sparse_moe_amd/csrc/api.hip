@@ -434,4 +434,16 @@ moe_status q8_pack_rows16(const void *w_rows, int64_t N, int64_t K, void *w_tile
     return dev(launch_q8_pack((const uint8_t *)w_rows, N, K, (uint8_t *)w_tiles, (hipStream_t)stream));
 }
 
+moe_status moe_calib_read(const void *buf, size_t bytes, void *stream) {
+    if (!buf || !aligned(buf, 16) || bytes % 16) return MOE_ERR_INVALID;
+    if (bytes == 0) return MOE_OK;
+    return dev(launch_calib_read(buf, (int64_t)bytes, nullptr, (hipStream_t)stream));
+}
+
+moe_status moe_calib_mfma(int32_t iters, int32_t blocks, void *stream) {
+    if (iters < 0 || blocks < 0) return MOE_ERR_INVALID;
+    if (iters == 0 || blocks == 0) return MOE_OK;
+    return dev(launch_calib_mfma(iters, blocks, nullptr, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -117,4 +117,8 @@ hipError_t launch_q8_gemv_q8x(const uint8_t *tiles, int64_t N, int64_t K, const 
 hipError_t launch_q8_pack(const uint8_t *rows, int64_t N, int64_t K, uint8_t *tiles,
                           hipStream_t s);
 
+// ---------------------------------------------------------------- measured ceilings
+hipError_t launch_calib_read(const void *buf, int64_t bytes, uint32_t *out, hipStream_t s);
+hipError_t launch_calib_mfma(int iters, int blocks, float *out, hipStream_t s);
+
 }  // namespace qs
