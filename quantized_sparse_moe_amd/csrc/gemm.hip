@@ -25,9 +25,9 @@
 // much as a 16-byte one.  A ring of two stages holds the K step being multiplied and the
 // next one in flight; each wave waits only for its own loads (vmcnt) and one barrier per
 // step publishes the stage to the whole workgroup.  The position of each 16-byte chunk of
-// an activation row in LDS is XOR-swizzled by (row / 2) mod 8, so that the 16 lanes a
-// 128-bit fragment read serves at once hit all 64 banks (direct-to-LDS loads place lane l
-// at byte 16 l, so the swizzle is chosen by which global chunk each lane fetches).
+// an activation row in LDS is XOR-swizzled by row (a_swizzle), so that the fragment reads
+// are free of bank conflicts (direct-to-LDS loads place lane l at byte 16 l, so the
+// swizzle is chosen by which global chunk each lane fetches).
 //
 // Operands: activations fp16 (x copy from the router, h from the gate/up pass) with
 // each group of 8 columns permuted into the order the packed codes unpack in (see
@@ -126,6 +126,13 @@ union TileRows {
     float xs[BM];
     DownRows dn;
 };
+
+// The LDS position of 16-byte chunk c of activation row r is c ^ a_swizzle(r).  A 128-bit
+// read is served 16 lanes per cycle from 64 four-byte banks, the lanes of one cycle being
+// those of one wave half with equal parity of lane bits 2..4 (measured on gfx950 with the
+// LDS bank-conflict counter); under this key the ten fragment reads of a K slice (lane
+// n16 + 16 cg: row n16, chunk 2 cg + s) hit 64 distinct banks in every cycle.
+__device__ __forceinline__ int a_swizzle(int r) { return ((r >> 1) & 1) | (r & 4); }
 
 typedef __attribute__((address_space(3))) void lds_t;
 
@@ -235,7 +242,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
     // kept as 16-byte chunk indices from a uniform base (x16, or the tile's first h row).
     auto apiece = [&](int i, int &r, int &ach) __attribute__((always_inline)) {
         const int rpos = 8 * (C::A_DMA * wave + i) + (lane >> 3);
-        ach = (lane & 7) ^ ((rpos >> 1) & 7);
+        ach = (lane & 7) ^ a_swizzle(rpos);
         r = rpos < nrows ? rpos : nrows - 1;             // rows past the tile repeat a valid one
     };
     const uint16_t *abase = MODE == 0 ? a.x16 : a.h + (int64_t)tile.row0 * I;
@@ -592,7 +599,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
             load_sb(k, sc, sc16, bi);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const int pos = (2 * cg + s) ^ ((n16 >> 1) & 7);
+                const int pos = (2 * cg + s) ^ a_swizzle(n16);
                 f16x8 A[MT];
 #pragma unroll
                 for (int i = 0; i < MT; ++i) A[i] = *(const f16x8 *)(st + (i * 16 + n16) * 128 + pos * 16);
@@ -668,8 +675,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
                         const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
                         hs[row * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(acc[i][j][r] * f));
                     }
-                    if (wave == 0 && n16 == 0 && row < nrows)
-                        a.hexp[(int64_t)(tile.row0 + row) * HEXP_STRIDE + nbi] = (int8_t)eh;
+                    if (wave == 0 && n16 == 0 && row < nrows)      // (device scope, as h)
+                        __hip_atomic_store(a.hexp + (int64_t)(tile.row0 + row) * HEXP_STRIDE + nbi, (int8_t)eh,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
@@ -689,17 +697,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
                              : "memory");
             }
         }
+        // every store the down pass reads (h rows, their block scales) is a device-scope
+        // (sc1) store, coherent across the XCDs once complete: the count follows once all
+        // of them have completed, with no L2 write-back (which, once per workgroup, cost a
+        // tenth of the launch)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // release at agent scope before the count: an L2 write-back, waited for, then the
-        // atomic.  A store acknowledged to its wave is not yet visible to device-scope loads
-        // of other workgroups; without the release a down tile could read h rows (or their
-        // block scales) before they arrive (the sequence is written out: the compiler's own
-        // release omitted the wait after the write-back here)
-        if (tid == 0) {
-            asm volatile("buffer_wbl2 sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
-            __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tid == 0) __hip_atomic_fetch_add(a.tile_done + tix, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
