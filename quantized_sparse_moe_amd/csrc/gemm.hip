@@ -39,12 +39,14 @@
 // Range: fp16 holds neither bf16's range nor every product of the layer, so every fp16
 // operand carries an exact power-of-two scale, removed in fp32 after the MFMAs.
 //   - x: per token (x16 row t is x 2^a_t, chosen by the router).
-//   - weights: per workgroup (its 256 weight rows), 2^p with p set before the K loop
-//     from a bound on their |w| (max over rows and groups of |s| (2^bits - 1) + |b|), so
-//     the largest weight lies in [2^14, 2^15): the scales and biases are converted to
-//     fp16 s 2^p, b 2^p when their window lands in LDS (bf16 or fp16 in; exact), and
-//     s 2^p / 16 stays a normal number for every group within 2^24 of the largest.  One
-//     factor per tile is taken out with the row factors, at no cost per element.
+//   - weights: per wave (its 64 weight rows), 2^p with p set before the K loop from a
+//     bound on their |w| (max over rows and groups of |s| (2^bits - 1) + |b|), so the
+//     largest weight lies in [2^14, 2^15); p = 0 (scales used as loaded) when fp16
+//     scales already keep every weight and every s / 16 in fp16's normal range.  Scales
+//     and biases are converted to fp16 s 2^p, b 2^p when their window lands in LDS, by
+//     the thread that loaded them (bf16 or fp16 in; exact), and s 2^p / 16 stays normal
+//     for every group within 2^24 of the largest.
+//     The factor is taken out with the row factors, at no cost per element.
 //   - h: per (row, 128-column block), 2^e with e from the block's largest |h|: 0 for
 //     blocks in [2^-2, 2^15), else a multiple of 8 (blocks of similar magnitude share
 //     it).  The down pass multiplies h row r under the smallest e_r of its blocks: a tile
@@ -195,11 +197,13 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w0, uint32_t w1, f16x2 sc, f1
 }
 
 template <int BITS, int MODE>
-__device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint8_t *smem, TileRows &sx,
-                                          uint32_t *s_wb) {
+__device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint8_t *smem, TileRows &sx) {
     using C = Cfg<BITS>;
     const Layer &L = a.L;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the test word that forces exact h block scales (read now: its latency is hidden)
+    const bool exact = MODE == 0 && __hip_atomic_load(a.err + CTL_HBLOCK_EXACT, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) != 0;
 
     // ---- which tile and column block: the nb column blocks of a tile (which share its
     // activation rows) run on one XCD; consecutive tiles go round the XCDs in list order
@@ -373,10 +377,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         my_xe = a.xexp[t];
     }
     // ---- the bound max_g |s_g| (2^bits - 1) + |b_g| on the |w| of this thread's weight
-    // row; the largest over the workgroup's rows sets the prescale 2^p (largest weight in
-    // [2^14, 2^15))
+    // row; the largest over the wave's 64 rows sets the wave's prescale 2^p (largest weight
+    // in [2^14, 2^15)).  Per wave, no barrier: the loads' latency passes under the first
+    // stage's, and the factor is taken out by the wave itself (its own output columns).
     float wsc, winv;
-    bool convert;                        // the scale windows need converting (bf16 in, or p != 0)
+    bool convert;                        // scales / biases need converting (bf16 in, or p != 0)
     {
         constexpr float QMAX = (float)((1 << BITS) - 1);
         const int bf = L.sb_bf16;
@@ -409,14 +414,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         }
         // (non-negative floats order as their bit patterns; the minimum as the maximum of
         // the complements)
-        const uint32_t mw = wave_max_u32(__float_as_uint(M)), nw = wave_max_u32(~__float_as_uint(smin));
-        if (lane == 0) {
-            s_wb[wave] = mw;
-            s_wb[4 + wave] = nw;
-        }
-        __syncthreads();
-        M = __uint_as_float(max(max(s_wb[0], s_wb[1]), max(s_wb[2], s_wb[3])));
-        smin = __uint_as_float(~max(max(s_wb[4], s_wb[5]), max(s_wb[6], s_wb[7])));
+        M = __uint_as_float(wave_max_u32(__float_as_uint(M)));
+        smin = __uint_as_float(~wave_max_u32(~__float_as_uint(smin)));
         // no prescale where the weights already sit in fp16's range: largest bound in
         // [2^-2, 2^15) and (4-bit) every nonzero s / 16 a normal number
         const bool in_range = M >= 0.25f && M < 32768.0f && (BITS == 8 || smin >= 0.0009765625f);
@@ -426,9 +425,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         convert = L.sb_bf16 || p != 0;
     }
     // ---- per-row factors, parked in LDS until the epilogue (published by the K loop's
-    // first barrier): gate/up, 2^-a 2^-p (x's and the weights' scales); down, the routing
-    // weight times 2^-e_r 2^-p, with the row's block scales for the rescale
-    if (MODE == 0 && tid < BM) sx.xs[tid] = exp2i(-my_xe) * winv;
+    // first barrier): gate/up, 2^-a (x's scale); down, the routing weight times 2^-e_r,
+    // with the row's block scales for the rescale
+    if (MODE == 0 && tid < BM) sx.xs[tid] = exp2i(-my_xe);
     if (MODE == 1) {
         bool mixed = false;
         if (tid < BM) {
@@ -444,7 +443,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
             sx.dn.e[tid] = (int8_t)lo;
             *(u32x4 *)(sx.dn.hx + tid * HEXP_STRIDE) = hw;
             sx.dn.pos[tid] = my_pos;
-            sx.dn.w[tid] = my_w * exp2i(-lo) * winv;
+            sx.dn.w[tid] = my_w * exp2i(-lo);
         }
         // (each wave's flag is read after the K loop's first barrier; the ballot is taken
         // by the whole wave)
@@ -468,7 +467,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         else wait_dma<0>();
     };
     // the scale / bias window of K step k (its first step), as this thread loaded it for
-    // its own row: converted in place to fp16 s 2^p, b 2^p (exact)
+    // its own row: converted in place to fp16 s 2^p, b 2^p (exact) with the wave's p
     auto convert_window = [&](int k) __attribute__((always_inline)) {
         uint8_t *sw = smem + C::NSTAGE * C::STAGE + ((k >> a.wlog) & 1) * 2 * C::S_BYTES;
         const int rs = 64 * wave + lane, bf = L.sb_bf16;
@@ -628,7 +627,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i < msub) {
-                const f32x4 rf = *(const f32x4 *)(sx.xs + i * 16 + 4 * cg);
+                const f32x4 rf = *(const f32x4 *)(sx.xs + i * 16 + 4 * cg) * winv;
                 uint32_t m[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -652,7 +651,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         }
         __syncthreads();
         // the block's scale per row (from the four waves' maxima), then h 2^e staged as fp16
-        const bool exact = __hip_atomic_load(a.err + CTL_HBLOCK_EXACT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i < msub) {
@@ -732,7 +730,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         // routed rows: the (token, slot) row with its routing weight; shared rows:
         // row T*K + t with the shared gate (or 1); both with h's row scale and the
         // weights' prescale taken out
-        const float wv = sx.dn.w[live ? row : 0];
+        const float wv = sx.dn.w[live ? row : 0] * winv;
         const float *src = fs + er * FP + 32 * (lane >> 5);
         f32x4 v[8];
         float mx = 0.0f;
@@ -773,9 +771,8 @@ template <int BITS>
 __global__ __launch_bounds__(NT, 2) void k_gemm(GemmArgs a0, GemmArgs a1, int g0) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg<BITS>::LDS];
     __shared__ TileRows sx;
-    __shared__ uint32_t s_wb[8];
-    if ((int)blockIdx.x < g0) gemm_body<BITS, 0>(a0, (int)blockIdx.x, smem, sx, s_wb);
-    else gemm_body<BITS, 1>(a1, (int)blockIdx.x - g0, smem, sx, s_wb);
+    if ((int)blockIdx.x < g0) gemm_body<BITS, 0>(a0, (int)blockIdx.x, smem, sx);
+    else gemm_body<BITS, 1>(a1, (int)blockIdx.x - g0, smem, sx);
 }
 
 // The combine: y[t] = sum of the token's k slot rows in ascending expert id, then its
