@@ -11,16 +11,18 @@
 // same time, and a phase waits only for the results it consumes.
 //
 // One launch (a dependent launch costs ~1.5 us on this part, as much as streaming
-// 12 MB), five roles chosen by workgroup index:
+// 12 MB), roles chosen by workgroup index:
 //   R  router logits (fp32), one wave per expert
-//   P  selectors: one wave each waits for all logits, takes the top-k and publishes it
-//      (several selectors write disjoint sets of copies)
 //   S  shared expert gate/up + SwiGLU (needs nothing)
-//   G  routed expert gate/up + SwiGLU, one [gate; up] row pair per row group (waits
-//      for the top-k)
+//   G  routed expert gate/up + SwiGLU, one [gate; up] row pair per row group; one wave
+//      waits for all logits and takes the top-k itself
 //   D  down projections of the k routed + shared experts for a block of output rows,
-//      weighted and combined in a fixed order; issues its weight loads as soon as the
-//      top-k is known, then waits for all of h.
+//      weighted and combined in a fixed order; takes the top-k like G, issues its weight
+//      loads at once, then waits for all of h
+//   P  (routing-only calls) one selector that writes the routing out.
+// Each hand-off between workgroups costs ~0.6 us (a device-scope store seen by a poll on
+// another XCD), so the consumers repeat the selection rather than wait for a published
+// one.
 // Roles only wait for workgroups of lower index (dispatched first), and the grid is
 // sized to be resident all at once; every wait is bounded (an error flag is raised if
 // a bound is ever exceeded) so the kernel always ends.
@@ -33,9 +35,13 @@
 // of different waves becomes visible far later).
 // The D workgroups count themselves in, in two levels (NGRP group counters, then one top
 // counter, so that no single line absorbs one atomic per workgroup), as soon as they
-// hold all of h: by then every workgroup of the call has read the generation.  The last
-// to arrive puts the counters back to zero and advances the generation.  Hand-off words
-// are replicated so that no single line absorbs all the polling.
+// have the selection, behind their first weight loads; the last of a group counts the
+// group in at the top while it waits for h, so both replies are back long before the
+// end.  The workgroup that completes the top count, at its end, puts the counters back
+// to zero and advances the generation: by then every D workgroup has counted in, and it
+// has seen all of h and all logits, so every workgroup of the call has read the
+// generation.  Hand-off words are replicated so that no single line absorbs all the
+// polling.
 //
 // Dequantization in registers: codes become fp16 (1024+q) by bit operations and meet
 // fp16 activations in v_dot2_f32_f16 with fp32 accumulation; per 16-byte chunk of codes
@@ -59,7 +65,8 @@ struct DecArgs {
     void *y;
     int y_dtype;
     int shared;
-    int nR, nP, nS, nG, nD;     // workgroups per role (route only: nP = 1, nS = nG = nD = 0)
+    int nR, nP, nS, nG, nD;     // workgroups per role (nP = 1 and nS = nG = nD = 0 for routing
+                                // only, else nP = 0)
     int route_only;
     int lprg;                   // gate/up: lanes per row (row groups per wave = 64 / lprg)
     int lprd;                   // down: lanes per row (rows per wave = 64 / lprd)
@@ -164,30 +171,20 @@ __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K, int ga
                             tag, E, K, gated, gate);
 }
 
-// Consumer: wave 0 waits (bounded) for the published selection, one poll in flight;
-// the workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights (and,
-// gated, entry K: the shared expert's gate in s_w[K]).
+// Consumer: wave 0 waits (bounded) for every logit of the call and takes the top-k
+// itself (a selection published by other workgroups would cost one more hand-off); the
+// workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights (and, gated,
+// entry K: the shared expert's gate in s_w[K]).  Ends with a barrier.
 __device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, int *s_idx, float *s_w) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        const uint64_t *tp = (const uint64_t *)(ctl + TOPK_BASE + (blockIdx.x % TOPK_COPIES) * TOPK_STRIDE);
-        const bool act = lane < 2 * (K + gated);
-        const uint64_t none = (uint64_t)tag << 32;
-        uint64_t w;
-        const uint32_t lim = wait_bound(ctl);
-        for (uint32_t n = 0;; ++n) {
-            w = act ? ld_dev64(tp + lane) : none;
-            if (__ballot(tag_of(w) != tag) == 0ull) break;
-            if (n > lim) {
-                if (lane == 0) raise_error(ctl);
-                break;
-            }
-            poll_pause(n);
+        float gate;
+        const TopkOut tk = select_topk(ctl, tag, E, K, gated, &gate);
+        if (lane < K) {
+            s_idx[lane] = tk.idx;
+            s_w[lane] = tk.w;
         }
-        if (act) {
-            if (lane & 1) s_w[lane >> 1] = __uint_as_float((uint32_t)w);
-            else s_idx[lane >> 1] = min(max((int)(uint32_t)w, 0), E - 1);
-        }
+        if (gated && lane == K) s_w[K] = gate;
     }
     __syncthreads();
 }
@@ -259,27 +256,18 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     }
     const uint32_t tag = call_tag(ctl);
     if (b < nR + a.nP) {
-        // ------------------------------------------- P: selectors (wave 0 works)
+        // ------------------------------------------- P (routing only): the selector
         if (wave != 0) return;
-        const int sel = b - nR;
         float gate;
-        const TopkOut tk = select_topk(ctl, tag, E, K, gated && !a.route_only, &gate);
-        if (a.route_only) {
-            if (lane < K) {
-                if (a.out_idx) a.out_idx[lane] = tk.idx;
-                if (a.out_w) a.out_w[lane] = tk.w;
-            }
-            if (lane == 0) st_dev(ctl + CTL_GEN, tag);       // the only reader of this call's logits
-            return;
+        const TopkOut tk = select_topk(ctl, tag, E, K, 0, &gate);
+        if (lane < K) {
+            if (a.out_idx) a.out_idx[lane] = tk.idx;
+            if (a.out_w) a.out_w[lane] = tk.w;
         }
-        if (lane < K + gated)                                // entry K: the shared expert's gate
-            for (int c = sel; c < TOPK_COPIES; c += a.nP)
-                st_dev128(ctl + TOPK_BASE + c * TOPK_STRIDE + 4 * lane,
-                          lane < K ? (u32x4){(uint32_t)tk.idx, tag, __float_as_uint(tk.w), tag}
-                                   : (u32x4){(uint32_t)E, tag, __float_as_uint(gate), tag});
+        if (lane == 0) st_dev(ctl + CTL_GEN, tag);           // the only reader of this call's logits
         return;
     }
-    nR += a.nP;                                              // the roles below follow the selectors
+    nR += a.nP;                                              // the roles below follow it
     if (b < nR + nS + nG) {
         // ------------------------------------------- S / G: gate/up + SwiGLU -> h
         uint32_t *xs = dsm;
@@ -304,19 +292,24 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // the workgroup's pb values (two per row group, consecutive in j: one slice of h)
         // are gathered in LDS; fp16 pairs under the slice's range scale 2^es go to every
         // copy in 16-byte pieces, and es itself to the slice's word
+        // (each wave's largest magnitude goes with them; a storing thread takes the
+        // slice's from those NW words.  Row groups past the end repeat the last pair.)
         __shared__ float s_hv[2 * NW * 64];
+        __shared__ uint32_t s_hm[NW];
         const int wi = wave * rpw + lane / a.lprg;           // word within the workgroup
         if (lane % a.lprg == 0) {
             s_hv[2 * wi] = hv[0];
             s_hv[2 * wi + 1] = hv[1];
         }
+        const uint32_t wm = wave_max_u32(max(__float_as_uint(hv[0]) & 0x7fffffffu, __float_as_uint(hv[1]) & 0x7fffffffu));
+        if (lane == 0) s_hm[wave] = wm;
         __syncthreads();
         const int jb = j0 - 2 * wi;                          // first j of the workgroup
         const int nw = min(pb, I - jb) / 2;                  // valid words
         if (tid >= H_COPIES * ((nw + 1) / 2) && tid >= H_COPIES) return;   // no store to make
-        // (each storing thread finds the slice's largest magnitude itself: no barrier)
-        uint32_t mb = 0u;
-        for (int i = 0; i < 2 * nw; ++i) mb = max(mb, __float_as_uint(s_hv[i]) & 0x7fffffffu);
+        uint32_t mb = s_hm[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mb = max(mb, s_hm[w]);
         const int es = range_exp(__uint_as_float(mb));
         const float f = exp2i(es);
         auto word = [&](int i) { return pack_f16x2(f32_to_f16_ftz(s_hv[2 * i] * f), f32_to_f16_ftz(s_hv[2 * i + 1] * f)); };
@@ -338,6 +331,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // ------------------------------------------ D: down + weighted combine
         const int d = b - nR - nS - nG;
         get_topk(ctl, tag, E, K, gated, s_idx, s_w);
+        uint32_t arrived = 0, top = 0;                      // replies of the two counters
         if (d == 0 && tid < K) {
             if (a.out_idx) a.out_idx[tid] = s_idx[tid];
             if (a.out_w) a.out_w[tid] = s_w[tid];
@@ -364,17 +358,17 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // ascending id, then the shared one) and its combine weight
         uint64_t pc = 0, ps = 0, pbi = 0;
         float wl = 1.0f;
+        // (the matrix fields are read as uniform values and selected per lane: a per-lane
+        // choice between the two descriptors would read them with vector loads and wait)
         if (lane < nvec) {
             const bool routed = lane < K;
-            const QMat &mm = routed ? L.down : L.s_down;
-            const int64_t R0 = routed ? (int64_t)s_idx[lane] * mm.stride : 0;
-            pc = (uint64_t)(mm.codes + R0 * rb);
-            ps = (uint64_t)(mm.scales + R0 * ng);
-            pbi = (uint64_t)(mm.biases + R0 * ng);
+            const int64_t R0 = routed ? (int64_t)s_idx[lane] * L.down.stride : 0;
+            pc = routed ? (uint64_t)(L.down.codes + R0 * rb) : (uint64_t)L.s_down.codes;
+            ps = routed ? (uint64_t)(L.down.scales + R0 * ng) : (uint64_t)L.s_down.scales;
+            pbi = routed ? (uint64_t)(L.down.biases + R0 * ng) : (uint64_t)L.s_down.biases;
             if (routed || gated) wl = s_w[lane];             // lane K, gated: the shared gate
         }
         float yv = 0.0f;
-        uint32_t arrived = 0;
         // items (vector v, chunk lr + k*lpr), NB per step, loaded unconditionally (clamped
         // to a valid chunk and discarded) so that all of a step's loads are in flight
         constexpr int NB = 5;
@@ -399,35 +393,71 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             }
             __builtin_amdgcn_sched_barrier(0);
             if (base == 0) {
-                // all of h (S and G) as it arrives.  Thread t takes groups of 8
-                // consecutive values (4 words) and the word of the slice they belong to:
-                // the chunk's slices are brought to their smallest range scale (exact: a
-                // power of two), fp16 into LDS in code order with one 16-byte write, and
-                // the chunk sums by a DPP sum over the chunk's groups
+                // this workgroup has read the generation: count it in now, behind the
+                // first weight loads (the polls below wait for the reply with them; its
+                // value is needed only at the end)
+                if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
+                // all of h (S and G).  Wave 0 first waits for the slice words of the copy
+                // (one small word per slice: light polling while the producers work); the
+                // data words, stored along with them, are then read once.  Thread t takes
+                // groups of 8 consecutive values (4 words) and the word of their slice, two
+                // groups at a time with every load in flight: the chunk's slices are brought
+                // to their smallest range scale (exact: a power of two), fp16 into LDS in
+                // code order with one 16-byte write, and the chunk sums by a DPP sum over
+                // the chunk's groups.  A word not yet visible is polled for on its own.
                 const uint64_t *hw = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE);
                 const uint64_t *he = (const uint64_t *)(ctl + H_BASE + (d % H_COPIES) * H_STRIDE + H_EXP);
                 const int ngrp = nvec * I / 8;
                 const int pbg = 2 * NW * (64 / a.lprg);               // values per slice
                 const int nsl = (I + pbg - 1) / pbg;                  // slices per vector
                 const uint32_t lim = wait_bound(ctl);
-                for (int g0 = 0; g0 < ngrp; g0 += DT) {
-                    const int g = g0 + tid;
-                    const bool live = g < ngrp;
-                    const int gg = live ? g : ngrp - 1;
-                    const int sv = (8 * gg) / I, sj = (8 * gg) % I;
-                    const uint64_t *ep = he + sv * nsl + sj / pbg;
-                    u32x4 w0, w1;                                // words (value pair, tag) x 4
-                    uint64_t we;
+                // the last of a group to count in counts the group in at the top (this
+                // waits for the first reply; both are back long before the end)
+                if (tid == 0) {
+                    const int grp = d % NGRP;
+                    const int gsize = nD / NGRP + (grp < nD % NGRP ? 1 : 0);
+                    if (arrived == (uint32_t)(gsize - 1)) top = add_dev(ctl + CNT_TOP) + 1u;
+                }
+                if (wave == 0) {
+                    const int nslt = nvec * nsl;
                     for (uint32_t t = 0;; ++t) {
-                        we = ld_dev64(ep);
-                        ld_dev256(hw + 4 * gg, w0, w1);
-                        if (w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag && tag_of(we) == tag) break;
+                        bool miss = false;
+                        for (int i0 = 0; i0 < nslt; i0 += 8 * 64) {
+                            uint64_t ew[8];
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) {
+                                const int i = i0 + 64 * u + lane;
+                                ew[u] = i < nslt ? ld_dev64(he + i) : (uint64_t)tag << 32;
+                            }
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) miss |= tag_of(ew[u]) != tag;
+                        }
+                        if (__ballot(miss) == 0ull) break;
                         if (t > lim) {
-                            raise_error(ctl);
+                            if (lane == 0) raise_error(ctl);
                             break;
                         }
                         poll_pause(t);
                     }
+                }
+                __syncthreads();
+                auto fresh = [&](uint64_t e, const u32x4 &w0, const u32x4 &w1) {
+                    return w0[1] == tag && w0[3] == tag && w1[1] == tag && w1[3] == tag && tag_of(e) == tag;
+                };
+                // (a stale word: this XCD's L2 lines are dropped, as for an acquire, and the
+                // group is polled for at device scope)
+                auto poll_group = [&](const uint64_t *ep, int gg, uint64_t &e, u32x4 &w0, u32x4 &w1) {
+                    for (uint32_t t = 0; !fresh(e, w0, w1); ++t) {
+                        if (t > lim) {
+                            raise_error(ctl);
+                            break;
+                        }
+                        if (t == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                        else poll_pause(t);
+                        ld_dev_group(ep, hw + 4 * gg, e, w0, w1);
+                    }
+                };
+                auto put_group = [&](int g, bool live, uint64_t we, const u32x4 &w0, const u32x4 &w1) {
                     const int es = (int)(uint32_t)we;
                     int ec = es;                                 // the chunk's smallest slice scale
                     if (CPC / 8 >= 2) ec = min(ec, (int)dpp_u32<0xB1>((uint32_t)ec + 128u) - 128);
@@ -455,11 +485,28 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                         hsum[g / (CPC / 8)] = make_float2(se, so);
                         hinv[g / (CPC / 8)] = exp2i(-ec);
                     }
+                };
+                for (int g0 = 0; g0 < ngrp; g0 += 2 * DT) {
+                    const int ga = g0 + tid, gb = ga + DT;
+                    const int gga = min(ga, ngrp - 1), ggb = min(gb, ngrp - 1);
+                    const uint64_t *epa = he + (8 * gga) / I * nsl + (8 * gga) % I / pbg;
+                    const uint64_t *epb = he + (8 * ggb) / I * nsl + (8 * ggb) % I / pbg;
+                    uint64_t ea, eb = 0;
+                    u32x4 a0, a1, b0, b1;
+                    const bool two = g0 + DT + 64 * wave < ngrp;     // (uniform) a live second group
+                    if (two)
+                        ld_cached_group2(epa, hw + 4 * gga, epb, hw + 4 * ggb, ea, a0, a1, eb, b0, b1);
+                    else
+                        ld_cached_group(epa, hw + 4 * gga, ea, a0, a1);
+                    poll_group(epa, gga, ea, a0, a1);
+                    put_group(ga, ga < ngrp, ea, a0, a1);
+                    if (g0 + DT < ngrp) {                          // (uniform over the workgroup)
+                        if (two) poll_group(epb, ggb, eb, b0, b1);
+                        else b0 = b1 = (u32x4){0u, tag, 0u, tag};
+                        put_group(gb, gb < ngrp && two, eb, b0, b1);
+                    }
                 }
                 __syncthreads();
-                // this workgroup has all it reads of the call's state: count it in now
-                // (the reply is needed only at the end)
-                if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
             }
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
@@ -484,16 +531,11 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
             if (a.y_dtype == MOE_F32) ((float *)a.y)[n] = y;
             else ((uint16_t *)a.y)[n] = f32_to_bf16(y);
         }
-        // the last of the D workgroups to have arrived (every other workgroup of the call
-        // has read the generation before any D workgroup could arrive) resets the state
-        if (tid == 0) {
-            const int g = d % NGRP;
-            const int gsize = nD / NGRP + (g < nD % NGRP ? 1 : 0);
-            const int ngroups = nD < NGRP ? nD : NGRP;
-            uint32_t last = 0;
-            if (arrived == (uint32_t)(gsize - 1)) last = add_dev(ctl + CNT_TOP) == (uint32_t)(ngroups - 1);
-            s_flag = last;
-        }
+        // the workgroup that completed the top count resets the state, here at its end:
+        // every D workgroup read the generation before counting in, and this one has
+        // seen all of h and all logits, which every S, G and R workgroup produced after
+        // reading it
+        if (tid == 0) s_flag = top == (uint32_t)(nD < NGRP ? nD : NGRP);
         __syncthreads();
         if (s_flag) finish_call(ctl, tag);
     }
@@ -526,7 +568,7 @@ hipError_t launch(DecArgs a, hipStream_t s) {
         a.nP = 1;
         a.nS = a.nG = a.nD = 0;
     } else {
-        a.nP = N_SELECT;                               // reduced below to what the consumers need
+        a.nP = 0;                                      // the consumers select for themselves
         a.nS = a.shared ? bpe : 0;
         a.nG = L.K * bpe;
         const int nvec = L.K + (a.shared ? 1 : 0);
@@ -541,10 +583,6 @@ hipError_t launch(DecArgs a, hipStream_t s) {
         }
         const int rows = NW / a.vs * (64 / a.lprd);
         a.nD = (L.H + rows - 1) / rows;
-        // consumer b reads copy b % TOPK_COPIES, written by selector b % nP: with nP a power
-        // of two no larger than the (contiguous) G and D range, every selector is read, so
-        // every selector has started before the call can complete
-        while (a.nP > 1 && a.nP > a.nG + a.nD) a.nP >>= 1;
         const size_t lds_g = (size_t)L.H * 2 + (size_t)(L.H / cpc) * 8;
         const size_t lds_d = (size_t)nvec * (L.I / cpc) * (cpc + 8) * 2 + (size_t)nvec * (L.I / cpc) * 12;
         lds = lds_g > lds_d ? lds_g : lds_d;

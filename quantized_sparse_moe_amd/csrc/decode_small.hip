@@ -607,6 +607,10 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // slots of parity w / 4 (the shared expert is slot |U|)
         const int d = b - nRP - nS - nG;
         small_get_sel(ctl, tag, E, K, T, gated, S);
+        // counted in as soon as the generation has been read, ahead of the weight loads
+        // (their waits cover the reply, which is needed only at the end)
+        uint32_t arrived = 0;
+        if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
         if (d == 0 && tid < T * K) {
             if (a.out_idx) a.out_idx[tid] = S.si[tid];
             if (a.out_w) a.out_w[tid] = S.sw[tid];
@@ -629,7 +633,6 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         float2 *hsum = (float2 *)(dsm + nslot * nch * CPITCH / 2);
         float *hinv = (float *)(hsum + nslot * nch);          // 2^-e of each chunk's h scale
         float *s_part = hinv + nslot * nch;                   // [2][T][4 rpw]: the two parities' sums
-        uint32_t arrived = 0;
         // item it: union slot v = par + 2 (it / cpl), chunk lr + lpr (it % cpl).  Lane j < |U|
         // holds row 0 of routed slot j's down matrix; a slot's bases are read from its lane
         // as scalars (the shared slot's are the layer's)
@@ -754,7 +757,6 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 }
             }
             __syncthreads();
-            if (tid == 0) arrived = add_dev(ctl + CNT_BASE + (d % NGRP) * 64);
         }
         for (int base = 0; base < nit; base += 2 * NB) {
             dcompute(base, wa);

@@ -78,14 +78,59 @@ __device__ __forceinline__ void ld_dev256(const void *p, u32x4 &a, u32x4 &b) {
         : "v"(p)
         : "memory");
 }
+// one h group (the 64-bit word of its slice and its four tagged words), read at device
+// scope, and waited for here
+__device__ __forceinline__ void ld_dev_group(const uint64_t *pe, const void *pd, uint64_t &e, u32x4 &a, u32x4 &b) {
+    asm volatile(
+        "global_load_dwordx2 %0, %3, off sc1\n\t"
+        "global_load_dwordx4 %1, %4, off sc1\n\t"
+        "global_load_dwordx4 %2, %4, off offset:16 sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(e), "=&v"(a), "=&v"(b)
+        : "v"(pe), "v"(pd)
+        : "memory");
+}
+// the same for one group or two through the caches (every load in flight at once):
+// workgroups of one XCD reading one copy then fetch each line from beyond the L2 once.
+// A cached line may predate the producer's write; its tags show it, and such a word is
+// then read again at device scope.
+__device__ __forceinline__ void ld_cached_group(const uint64_t *pe, const void *pd, uint64_t &e, u32x4 &a, u32x4 &b) {
+    asm volatile(
+        "global_load_dwordx2 %0, %3, off\n\t"
+        "global_load_dwordx4 %1, %4, off\n\t"
+        "global_load_dwordx4 %2, %4, off offset:16\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(e), "=&v"(a), "=&v"(b)
+        : "v"(pe), "v"(pd)
+        : "memory");
+}
+__device__ __forceinline__ void ld_cached_group2(const uint64_t *pe0, const void *pd0, const uint64_t *pe1,
+                                                 const void *pd1, uint64_t &e0, u32x4 &a0, u32x4 &b0, uint64_t &e1,
+                                                 u32x4 &a1, u32x4 &b1) {
+    asm volatile(
+        "global_load_dwordx2 %0, %6, off\n\t"
+        "global_load_dwordx4 %1, %7, off\n\t"
+        "global_load_dwordx4 %2, %7, off offset:16\n\t"
+        "global_load_dwordx2 %3, %8, off\n\t"
+        "global_load_dwordx4 %4, %9, off\n\t"
+        "global_load_dwordx4 %5, %9, off offset:16\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(e0), "=&v"(a0), "=&v"(b0), "=&v"(e1), "=&v"(a1), "=&v"(b1)
+        : "v"(pe0), "v"(pd0), "v"(pe1), "v"(pd1)
+        : "memory");
+}
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld_dev64(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// +1 at device scope, returning the old value.  Written as a wrapping increment with
+// bound 2^32 - 1 (the same result as an add of 1): the compiler's wave-level rewrite of
+// atomic adds reads the returned value at once, which would stall the wave for the
+// atomic's full round trip where the value is only needed much later.
 __device__ __forceinline__ uint32_t add_dev(uint32_t *p) {
-    return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_atomic_inc32(p, 0xffffffffu, __ATOMIC_RELAXED, "agent");
 }
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 
