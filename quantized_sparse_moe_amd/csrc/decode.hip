@@ -541,18 +541,6 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     }
 }
 
-int n_compute_units() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, cu = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
-            n = cu;
-        else
-            n = 256;
-    }
-    return n;
-}
 
 hipError_t launch(DecArgs a, hipStream_t s) {
     const Layer &L = a.L;
@@ -606,6 +594,20 @@ DecArgs make_args(const Layer &L, const uint16_t *x, const DecodeBufs &b) {
 }
 
 }  // namespace
+
+// compute units of the current device (queried once)
+int n_compute_units() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+            n = cu;
+        else
+            n = 256;
+    }
+    return n;
+}
 
 namespace {
 __global__ void k_ws_status(uint32_t *ctl, uint32_t *out, int clear) {

@@ -109,6 +109,7 @@ hipError_t launch_prefill_gemms(const Layer &L, int64_t T, const PrefillBufs &b,
                                 int y_dtype, hipStream_t s);
 
 // --------------------------------------------------------------------------- Q8_0
+int n_compute_units();   // of the current device, queried once
 hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint16_t *x,
                           void *y, int y_dtype, hipStream_t s);
 hipError_t launch_q8_quantize_x(const uint16_t *x, int64_t K, int8_t *xq, uint16_t *xd, hipStream_t s);

@@ -126,6 +126,98 @@ __global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv(const uint8_t *__restric
     }
 }
 
+// The same product with 16-byte loads and every tile of the wave in flight at once.
+// A wave reads two consecutive tiles per instruction: lane (t, g, q) = (lane >> 5,
+// (lane >> 2) & 7, lane & 3) takes bytes 64 g + 16 q of tile t -- the 4 columns of
+// group g for rows 4q .. 4q+3 -- and the fp16 scales of those rows.  A wave owns PPW
+// tile pairs (nb = 2 PPW Q8_WAVES) and issues all their loads right behind those of x,
+// so the panel's whole read overlaps the staging.  Each lane keeps four row sums; the
+// 16 lanes of a row quad are reduced across the wave, then the waves across LDS.
+template <int PPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_q8_gemv_wide(const uint8_t *__restrict__ tiles, int64_t K,
+                                                             const uint16_t *__restrict__ x, void *y, int y_dtype) {
+    extern __shared__ float q8s[];
+    constexpr int NT = 64 * WAVES;
+    constexpr int NB = 2 * PPW * WAVES;                 // blocks of 32 columns (K / 32)
+    constexpr int SPT = (NB * 8 + NT - 1) / NT;         // 4-column slots per thread
+    float *xf = q8s;                      // [K]: x in fp32
+    float *xs = q8s + NB * 32;            // [K / 4]: sums of 4 consecutive columns
+    __shared__ float red[WAVES][16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int q = lane & 3, g = (lane >> 2) & 7, tt = lane >> 5;
+    // x is read first, with loads the compiler does not see (it would otherwise move them
+    // behind the tiles', and loads complete in order); they are waited for by count below
+    uint64_t xr[SPT];
+#pragma unroll
+    for (int k = 0; k < SPT; ++k)
+        asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(xr[k]) : "v"(x + 4 * min(tid + k * NT, NB * 8 - 1))
+                     : "memory");
+    const uint8_t *panel = tiles + (int64_t)blockIdx.x * NB * TILE;
+    u32x4 c[PPW];
+    uint64_t sc[PPW];
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const uint8_t *t = panel + (int64_t)(2 * (wave + u * WAVES) + tt) * TILE;
+        c[u] = __builtin_nontemporal_load((const u32x4 *)(t + 64 * g + 16 * q));
+        sc[u] = __builtin_nontemporal_load((const uint64_t *)(t + 512 + 8 * q));
+    }
+    // x's loads are the oldest in flight: wait until no more than the tiles' remain
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PPW) : "memory");
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) asm volatile("" : "+v"(xr[k]));
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+        const int sl = tid + k * NT;
+        if (sl >= NB * 8) break;
+        const uint32_t lo = (uint32_t)xr[k], hi = (uint32_t)(xr[k] >> 32);
+        const float v0 = __uint_as_float(lo << 16), v1 = __uint_as_float(lo & 0xffff0000u);
+        const float v2 = __uint_as_float(hi << 16), v3 = __uint_as_float(hi & 0xffff0000u);
+        *(f32x4 *)(xf + 4 * sl) = (f32x4){v0, v1, v2, v3};
+        xs[sl] = (v0 + v1) + (v2 + v3);
+    }
+    __syncthreads();
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+        const int sl = (2 * (wave + u * WAVES) + tt) * 8 + g;
+        const f32x4 xv = *(const f32x4 *)(xf + 4 * sl);
+        const float x4 = 128.0f * xs[sl];
+        const uint32_t d2[2] = {(uint32_t)sc[u], (uint32_t)(sc[u] >> 32)};
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t p = c[u][rr] ^ 0x80808080u;
+            float s = ubyte<0>(p) * xv[0];
+            s = __builtin_fmaf(ubyte<1>(p), xv[1], s);
+            s = __builtin_fmaf(ubyte<2>(p), xv[2], s);
+            s = __builtin_fmaf(ubyte<3>(p), xv[3], s);
+            const float d = f16_to_f32((uint16_t)(d2[rr >> 1] >> (16 * (rr & 1))));
+            acc[rr] = __builtin_fmaf(d, s - x4, acc[rr]);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+        float a = acc[rr];
+        a += __shfl_xor(a, 4, 64);
+        a += __shfl_xor(a, 8, 64);
+        a += __shfl_xor(a, 16, 64);
+        a += __shfl_xor(a, 32, 64);
+        acc[rr] = a;
+    }
+    if (lane < 4) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) red[wave][4 * lane + rr] = acc[rr];
+    }
+    __syncthreads();
+    if (tid < 16) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) s += red[w][tid];
+        const int64_t n = (int64_t)blockIdx.x * 16 + tid;
+        if (y_dtype == MOE_F32) ((float *)y)[n] = s;
+        else ((uint16_t *)y)[n] = f32_to_bf16(s);
+    }
+}
+
 // the activation quantizer's scale and code (one definition for both kernels below)
 __device__ __forceinline__ float q8x_scale(float amax) { return amax / 127.0f; }
 __device__ __forceinline__ int8_t q8x_code(float v, float d) {
@@ -297,9 +389,22 @@ __global__ __launch_bounds__(256) void k_q8_pack(const uint8_t *__restrict__ row
 
 hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint16_t *x, void *y,
                           int y_dtype, hipStream_t s) {
-    const size_t lds = (size_t)(K / 32) * 32 * 4 + (size_t)(K / 32) * 4 * 4;
-    hipLaunchKernelGGL((k_q8_gemv<4>), dim3((unsigned)(N / 16)), dim3(Q8_THREADS), lds, s, tiles, K, x, y,
-                       y_dtype);
+    const dim3 grid((unsigned)(N / 16)), block(Q8_THREADS), block16(1024);
+    const size_t lds_w = (size_t)K * 4 + (size_t)(K / 4) * 4;
+    // (16 waves pay off for long rows only: 8 tile pairs or more per wave)
+    const bool few = N / 16 < n_compute_units() && K % (64 * 16) == 0 && K >= 8 * 64 * 16;
+    switch (few ? 100 + K / (64 * 16) : K % (64 * Q8_WAVES) == 0 ? K / (64 * Q8_WAVES) : 0) {   // tile pairs per wave
+    case 2: hipLaunchKernelGGL((k_q8_gemv_wide<2, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
+    case 4: hipLaunchKernelGGL((k_q8_gemv_wide<4, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
+    case 8: hipLaunchKernelGGL((k_q8_gemv_wide<8, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
+    case 16: hipLaunchKernelGGL((k_q8_gemv_wide<16, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
+    case 108: hipLaunchKernelGGL((k_q8_gemv_wide<8, 16>), grid, block16, lds_w, s, tiles, K, x, y, y_dtype); break;
+    default: {
+        const size_t lds = (size_t)(K / 32) * 32 * 4 + (size_t)(K / 32) * 4 * 4;
+        hipLaunchKernelGGL((k_q8_gemv<4>), grid, block, lds, s, tiles, K, x, y, y_dtype);
+        break;
+    }
+    }
     return hipGetLastError();
 }
 
