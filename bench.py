@@ -52,12 +52,14 @@ ORDER_SEED = 20261202
 # the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/decode_state.h", "csrc/common.h", "csrc/internal.h")
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/internal.h")
-PREFILL_TRAFFIC = {"sources_sha256": "a1d683c4130b605d777143281266a3820d5ae4e79a84a41909bb194fcc1f9e12", "bytes": 1002660106}
-DECODE_TRAFFIC = {"sources_sha256": "8886823710cf56d48e32cf7a72c37fe7ab5888a9605d6196767a04915e92ef1d", "bytes": 17974594}
+PREFILL_TRAFFIC = {"sources_sha256": "ec5a5af5314a5b762cdd40f6d4c4d0611bd802305e20604fc2c308c4138436fc", "bytes": 1042636140}
+DECODE_TRAFFIC = {"sources_sha256": "0a09a45464c7efd8c897ea1f1b965995824c9b0570a1ea63e234678597583545", "bytes": 18130864}
 # MFMA utilisation of the grouped GEMM from rocprofv3 --pmc (medians per dispatch):
 # busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); keyed like
 # the traffic.
-GEMM_COUNTERS = {"sources_sha256": None}
+GEMM_COUNTERS = {"sources_sha256": "ec5a5af5314a5b762cdd40f6d4c4d0611bd802305e20604fc2c308c4138436fc",
+                 "k_gemm<4>": {"mfma_busy": 0.3684, "profile": "profiles/k_gemm_mfma_busy.md"},
+                 "k_gemm<8>": {"mfma_busy": 0.3778, "profile": "profiles/k_gemm_mfma_busy.md"}}
 
 
 # ----------------------------------------------------------- algorithmic accounting
