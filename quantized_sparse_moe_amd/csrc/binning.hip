@@ -2,7 +2,7 @@
 //
 // [LILY] "Keep expert routing on the GPU": the grouped GEMM needs the activation rows
 // of each expert stored together.  A histogram counts the assignments per expert (done
-// per 32-token block by the router), a prefix scan turns counts into start offsets, a
+// per ROUTER_TOKENS-token block by the router), a prefix scan turns counts into start offsets, a
 // scatter places every (token, slot) assignment into its expert's group, and a block
 // map lists the fixed-size row blocks the grouped GEMM processes.  Everything stays on
 // the device: no count is read back by the host.  [LILY] "Match tile size to expert
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_tiles(const int32_t *__restrict__ count
     if (tid == 0) { ntiles[0] = routed; ntiles[1] = routed + nsh; ntiles[2] = 0; }
 }
 
-// Stable scatter of the assignments of one 32-token block into the expert bins.
+// Stable scatter of the assignments of one ROUTER_TOKENS-token block into the expert bins.
 __global__ __launch_bounds__(256) void k_scatter(const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ blkoff,
                                                  const int32_t *__restrict__ expert_off,
