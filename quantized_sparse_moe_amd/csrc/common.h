@@ -311,12 +311,12 @@ __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_exp
         e[i] = sel[i] ? __expf(val[i] - vmax) : 0.0f;
         part += e[i];
     }
-    const float z = wave_sum(part);
+    const float rz = 1.0f / wave_sum(part);               // (one division, not one per slot)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         if (sel[i]) {
             tk_idx[wv][pos[i]] = lane + 64 * i;
-            tk_w[wv][pos[i]] = e[i] / z;
+            tk_w[wv][pos[i]] = e[i] * rz;
         }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -189,7 +189,9 @@ __device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, i
     __syncthreads();
 }
 
-template <int BITS>
+// SBF: the layer's scales and biases are bf16 (else fp16), fixed per instantiation so that
+// their widening is one instruction
+template <int BITS, int SBF>
 __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_decode(DecArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
     __shared__ uint32_t s_flag;
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     uint32_t *ctl = a.ctl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K;
-    const int sb_bf16 = L.sb_bf16, gated = L.shared_gate_w != nullptr && a.shared;
+    const int sb_bf16 = SBF, gated = L.shared_gate_w != nullptr && a.shared;
     int nR = a.nR;
     const int nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
@@ -576,10 +578,9 @@ hipError_t launch(DecArgs a, hipStream_t s) {
         lds = lds_g > lds_d ? lds_g : lds_d;
     }
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
-    if (L.bits == 4)
-        hipLaunchKernelGGL((k_decode<4>), dim3(grid), dim3(DT), lds, s, a);
-    else
-        hipLaunchKernelGGL((k_decode<8>), dim3(grid), dim3(DT), lds, s, a);
+    void (*kern)(DecArgs) = L.bits == 4 ? (L.sb_bf16 ? k_decode<4, 1> : k_decode<4, 0>)
+                                       : (L.sb_bf16 ? k_decode<8, 1> : k_decode<8, 0>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(DT), lds, s, a);
     return hipGetLastError();
 }
 

@@ -398,7 +398,9 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
     }
 }
 
-template <int BITS>
+// SBF: the layer's scales and biases are bf16 (else fp16), fixed per instantiation so that
+// their widening is one instruction
+template <int BITS, int SBF>
 __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_small(SmallArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t dsm[];
     __shared__ SmallSel S;
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     uint32_t *ctl = a.ctl;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = L.H, I = L.I, E = L.E, K = L.K, T = a.T;
-    const int sb_bf16 = L.sb_bf16, gated = L.shared_gate_w != nullptr && a.shared;
+    const int sb_bf16 = SBF, gated = L.shared_gate_w != nullptr && a.shared;
     const int nR = a.nR, nP = a.nP, nS = a.nS, nG = a.nG, nD = a.nD;
     const int b = blockIdx.x;
     const uint32_t tag = call_tag(ctl);
@@ -834,10 +836,9 @@ hipError_t launch_small(SmallArgs a, hipStream_t s) {
         lds = small_lds_bytes(L, a.T);
     }
     const int grid = a.nR + a.nP + a.nS + a.nG + a.nD;
-    if (L.bits == 4)
-        hipLaunchKernelGGL((k_decode_small<4>), dim3(grid), dim3(DT), lds, s, a);
-    else
-        hipLaunchKernelGGL((k_decode_small<8>), dim3(grid), dim3(DT), lds, s, a);
+    void (*kern)(SmallArgs) = L.bits == 4 ? (L.sb_bf16 ? k_decode_small<4, 1> : k_decode_small<4, 0>)
+                                       : (L.sb_bf16 ? k_decode_small<8, 1> : k_decode_small<8, 0>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(DT), lds, s, a);
     return hipGetLastError();
 }
 
