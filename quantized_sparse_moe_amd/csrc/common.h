@@ -213,7 +213,9 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u); // monotone in v; live keys > 0
 }
 
-// v[i] = value of expert lane + 64 i (ignored for ids >= n_experts)
+// v[i] = value of expert lane + 64 i (ignored for ids >= n_experts).  WEIGHTS = false:
+// the selection only (out.w is 0), for callers that need the experts and not their weights.
+template <bool WEIGHTS = true>
 __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_experts, int top_k) {
     __shared__ int tk_idx[16][16];
     __shared__ float tk_w[16][16];
@@ -303,26 +305,32 @@ __device__ __forceinline__ TopkOut wave_topk_regs(const float (&v)[4], int n_exp
             base += __popcll(sm);
         }
     }
-    // renormalised weights: exp(l - l_max) over the selection, l_max = the key `top`
-    const float vmax = __uint_as_float((top & 0x80000000u) ? (top & 0x7fffffffu) : ~top);
-    float e[4], part = 0.0f;
+    if constexpr (WEIGHTS) {
+        // renormalised weights: exp(l - l_max) over the selection, l_max = the key `top`
+        const float vmax = __uint_as_float((top & 0x80000000u) ? (top & 0x7fffffffu) : ~top);
+        float e[4], part = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        e[i] = sel[i] ? __expf(val[i] - vmax) : 0.0f;
-        part += e[i];
-    }
-    const float rz = 1.0f / wave_sum(part);               // (one division, not one per slot)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        if (sel[i]) {
-            tk_idx[wv][pos[i]] = lane + 64 * i;
-            tk_w[wv][pos[i]] = e[i] * rz;
+        for (int i = 0; i < 4; ++i) {
+            e[i] = sel[i] ? __expf(val[i] - vmax) : 0.0f;
+            part += e[i];
         }
+        const float rz = 1.0f / wave_sum(part);           // (one division, not one per slot)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (sel[i]) {
+                tk_idx[wv][pos[i]] = lane + 64 * i;
+                tk_w[wv][pos[i]] = e[i] * rz;
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (sel[i]) tk_idx[wv][pos[i]] = lane + 64 * i;
+    }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     TopkOut out;
     out.idx = lane < top_k ? tk_idx[wv][lane] : 0;
-    out.w = lane < top_k ? tk_w[wv][lane] : 0.0f;
+    out.w = (WEIGHTS && lane < top_k) ? tk_w[wv][lane] : 0.0f;
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
     return out;

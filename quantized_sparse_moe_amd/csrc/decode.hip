@@ -166,20 +166,23 @@ __device__ void pairs_swiglu(const QMat &mg, const QMat &mu, int e, int j0, int 
     }
 }
 
+template <bool WEIGHTS = true>
 __device__ TopkOut select_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, float *gate) {
-    return select_topk_from(ctl, (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE),
+    return select_topk_from<WEIGHTS>(ctl, (const uint64_t *)(ctl + LOGIT_BASE + (blockIdx.x % LOGIT_COPIES) * LOGIT_STRIDE),
                             tag, E, K, gated, gate);
 }
 
 // Consumer: wave 0 waits (bounded) for every logit of the call and takes the top-k
 // itself (a selection published by other workgroups would cost one more hand-off); the
 // workgroup gets (s_idx, s_w): experts in ascending id, renormalised weights (and, gated,
-// entry K: the shared expert's gate in s_w[K]).  Ends with a barrier.
+// entry K: the shared expert's gate in s_w[K]); WEIGHTS = false leaves the weights 0 (G
+// needs only the experts).  Ends with a barrier.
+template <bool WEIGHTS = true>
 __device__ void get_topk(uint32_t *ctl, uint32_t tag, int E, int K, int gated, int *s_idx, float *s_w) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         float gate;
-        const TopkOut tk = select_topk(ctl, tag, E, K, gated, &gate);
+        const TopkOut tk = select_topk<WEIGHTS>(ctl, tag, E, K, gated, &gate);
         if (lane < K) {
             s_idx[lane] = tk.idx;
             s_w[lane] = tk.w;
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         const int xe = stage_x<BITS>(a.x, H, xs, xsum, s_wm);     // ends with a barrier
         int e = 0;
         if (!sh) {
-            get_topk(ctl, tag, E, K, gated, s_idx, s_w);     // ends with a barrier
+            get_topk<false>(ctl, tag, E, K, gated, s_idx, s_w);   // (experts only); ends with a barrier
             e = __builtin_amdgcn_readfirstlane(s_idx[slot]);
         }
         const int jj = j0 < I ? j0 : I - 2;

@@ -214,7 +214,8 @@ __device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, u
 // id.  One poll is in flight at a time: a read still in flight when the data is found
 // would have to be waited for before its registers are reused, a full extra round trip.
 // gated: logit E is the shared-expert gate's, polled with the others; *gate gets
-// sigmoid of it (every lane).
+// sigmoid of it (every lane).  WEIGHTS = false: the experts only (w = 0).
+template <bool WEIGHTS = true>
 __device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t tag, int E, int K, int gated,
                                     float *gate) {
     const int lane = threadIdx.x & 63;
@@ -238,7 +239,7 @@ __device__ TopkOut select_topk_from(uint32_t *ctl, const uint64_t *lg, uint32_t 
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = no_nan(__uint_as_float((uint32_t)w[i]));
-    TopkOut tk = wave_topk_regs(v, E, K);
+    TopkOut tk = wave_topk_regs<WEIGHTS>(v, E, K);
     tk.idx = min(max(tk.idx, 0), E - 1);
     *gate = sigmoid(__builtin_bit_cast(float, __builtin_amdgcn_readfirstlane((int)(uint32_t)wg)));
     return tk;
