@@ -7,8 +7,10 @@
 //
 // Logits are a dense [T x H] x [H x E] contraction: bf16 activations against bf16
 // router weights on MFMA (v_mfma_f32_16x16x32_bf16, exact products, fp32 accumulation),
-// tiled 64 tokens x 64 experts per workgroup with both operands staged in LDS, so each
-// router row is read once per 64 tokens.  The workgroups of a token block also write
+// tiled LT tokens x 64 experts per workgroup with both operands staged in LDS, so each
+// router row is read once per LT tokens (from L2: the 1 MiB router matrix stays there).
+// LT = 32 when 64-token tiles would leave fewer than two workgroups per CU (T = 4096:
+// four waves per CU did not hide the latency), else 64.  The workgroups of a token block also write
 // the fp16 copy of x (taking K chunks in turn), each group of 8 columns permuted into
 // the code order used by the expert GEMMs, and the largest |x| of each token over the
 // chunks they wrote.  The top-k pass then gives one wave to each token; it also picks
@@ -21,7 +23,6 @@ namespace qs {
 
 namespace {
 
-constexpr int LT = 64;              // tokens per logits tile
 constexpr int LE = 64;              // experts per logits tile
 constexpr int LK = 128;             // K chunk
 constexpr int LPITCH = LK + 8;      // bf16 per LDS row (breaks bank alignment)
@@ -40,8 +41,10 @@ struct LogitArgs {
     int H, E;
 };
 
-template <int BITS>
+template <int BITS, int LT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_logits(LogitArgs a) {
+    constexpr int TW = LT / 16;                     // 16-token blocks of the tile (2 or 4)
+    constexpr int NPW = TW;                         // 16-expert blocks per wave
     __shared__ __attribute__((aligned(16))) uint16_t xa[LT * LPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t wa[LE * LPITCH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -49,43 +52,52 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int64_t t0 = (int64_t)blockIdx.x * LT;
     const int e0 = blockIdx.y * LE;
     const int H = a.H, E = a.E;
-    // staging: thread tid moves chunk (tid % 16) of rows tid / 16 + 16 i (i < 4) of both tiles
+    // staging: thread tid moves chunk (tid % 16) of rows tid / 16 + 16 i of the x tile
+    // (i < TW, LT rows) and of the router tile (i < 4, LE rows)
     const int sr = tid >> 4, sc = (tid & 15) * 8;
-    int64_t xrow[4];
+    int64_t xrow[TW];
     int wrow[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TW; ++i) {
         const int64_t t = t0 + sr + 16 * i;
         xrow[i] = t < a.T ? t : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
         const int e = e0 + sr + 16 * i;
         wrow[i] = e < a.LS ? e : -1;                        // e = E: the shared gate's row
     }
     // (a chunk past the end of a row, when H % 128 == 64, loads zeros)
-    auto load = [&](int kc, u32x4 (&xv)[4], u32x4 (&wv)[4]) {
+    auto load = [&](int kc, u32x4 (&xv)[TW], u32x4 (&wv)[4]) {
         const bool in = kc + sc < H;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TW; ++i)
             xv[i] = in && xrow[i] >= 0 ? *(const u32x4 *)(a.x + xrow[i] * H + kc + sc) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
             wv[i] = in && wrow[i] >= 0
                         ? *(const u32x4 *)((wrow[i] < E ? a.wr + (int64_t)wrow[i] * H : a.gate_w) + kc + sc)
                         : (u32x4){0u, 0u, 0u, 0u};
-        }
     };
-    f32x4 acc[4];
+    // wave w: tokens 16 (w % TW) .. + 16 against the NPW 16-expert blocks from NPW (w / TW)
+    const int tw = wave % TW, eh = wave / TW;
+    f32x4 acc[NPW];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    uint32_t xm[4] = {0u, 0u, 0u, 0u};              // largest |x| written, per staged row
-    // chunk kc: registers -> LDS (and the fp16 copy of x), then 4 x 4 MFMAs; two chunks
-    // are in flight in registers while one is multiplied (one workgroup per CU at the
-    // prefill sizes, so the loads' latency is hidden by this workgroup alone)
-    auto step = [&](int kc, const u32x4 (&xv)[4], const u32x4 (&wv)[4]) __attribute__((always_inline)) {
+    for (int n = 0; n < NPW; ++n) acc[n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    uint32_t xm[TW];                                // largest |x| written, per staged row
+#pragma unroll
+    for (int i = 0; i < TW; ++i) xm[i] = 0u;
+    // chunk kc: registers -> LDS (and the fp16 copy of x), then 4 x NPW MFMAs; two chunks
+    // are in flight in registers while one is multiplied
+    auto step = [&](int kc, const u32x4 (&xv)[TW], const u32x4 (&wv)[4]) __attribute__((always_inline)) {
         // the expert blocks of a token block take turns writing the fp16 copy of x
         const bool write_x16 = a.x16 && (int)((kc / LK) % gridDim.y) == (int)blockIdx.y;
         __syncthreads();                                 // the previous chunk is consumed
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) *(u32x4 *)(wa + (sr + 16 * i) * LPITCH + sc) = wv[i];
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
             *(u32x4 *)(xa + (sr + 16 * i) * LPITCH + sc) = xv[i];
-            *(u32x4 *)(wa + (sr + 16 * i) * LPITCH + sc) = wv[i];
             if (write_x16 && xrow[i] >= 0 && kc + sc < H) {   // this chunk's share of the fp16 copy
                 u32x4 h;
 #pragma unroll
@@ -102,15 +114,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     auto mult = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < LK / 32; ++s) {
-            const bf16x8 A = *(const bf16x8 *)(xa + (wave * 16 + n16) * LPITCH + s * 32 + 8 * cg);
+            const bf16x8 A = *(const bf16x8 *)(xa + (tw * 16 + n16) * LPITCH + s * 32 + 8 * cg);
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const bf16x8 B = *(const bf16x8 *)(wa + (n * 16 + n16) * LPITCH + s * 32 + 8 * cg);
+            for (int n = 0; n < NPW; ++n) {
+                const bf16x8 B = *(const bf16x8 *)(wa + ((NPW * eh + n) * 16 + n16) * LPITCH + s * 32 + 8 * cg);
                 acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[n], 0, 0, 0);
             }
         }
     };
-    u32x4 xv0[4], wv0[4], xv1[4], wv1[4];
+    u32x4 xv0[TW], wv0[4], xv1[TW], wv1[4];
     load(0, xv0, wv0);
     if (LK < H) load(LK, xv1, wv1);
     for (int kc = 0; kc < H; kc += 2 * LK) {
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // the 16 lanes staging a row hold its maxima: one word per (token, expert block)
     if (a.x16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < TW; ++i) {
             uint32_t m = xm[i];
             m = max(m, dpp_u32<0xB1>(m));
             m = max(m, dpp_u32<0x4E>(m));
@@ -135,15 +147,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             if ((tid & 15) == 0 && xrow[i] >= 0) a.xmax[xrow[i] * 8 + blockIdx.y] = m;
         }
     }
-    // acc[n][r]: token 16 * wave + 4 * cg + r, expert e0 + 16 * n + n16
+    // acc[n][r]: token 16 tw + 4 cg + r, expert e0 + 16 (NPW eh + n) + n16
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e = e0 + 16 * n + n16;
+    for (int n = 0; n < NPW; ++n) {
+        const int e = e0 + 16 * (NPW * eh + n) + n16;
         if (e >= a.LS) continue;
         const float b = (a.bias && e < E) ? a.bias[e] : 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + wave * 16 + 4 * cg + r;
+            const int64_t t = t0 + tw * 16 + 4 * cg + r;
             if (t < a.T) a.logits[t * a.LS + e] = acc[n][r] + b;
         }
     }
@@ -242,11 +254,13 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     la.T = T;
     la.H = L.H;
     la.E = L.E;
-    const dim3 lgrid((unsigned)((T + LT - 1) / LT), (unsigned)((la.LS + LE - 1) / LE));
-    if (L.bits == 4)
-        hipLaunchKernelGGL((k_logits<4>), lgrid, dim3(256), 0, s, la);
-    else
-        hipLaunchKernelGGL((k_logits<8>), lgrid, dim3(256), 0, s, la);
+    // 32-token tiles when 64-token ones would not give every CU two workgroups
+    const int eblk = (la.LS + LE - 1) / LE;
+    const bool small = (T + 63) / 64 * eblk < 2 * n_compute_units();
+    const dim3 lgrid((unsigned)(small ? (T + 31) / 32 : (T + 63) / 64), (unsigned)eblk);
+    void (*kern)(LogitArgs) = L.bits == 4 ? (small ? k_logits<4, 32> : k_logits<4, 64>)
+                                          : (small ? k_logits<8, 32> : k_logits<8, 64>);
+    hipLaunchKernelGGL(kern, lgrid, dim3(256), 0, s, la);
     TopkArgs ta;
     ta.logits = b.logits;
     ta.T = T;
