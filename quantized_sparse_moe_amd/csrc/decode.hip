@@ -45,8 +45,9 @@
 //
 // Dequantization in registers: codes become fp16 (1024+q) by bit operations and meet
 // fp16 activations in v_dot2_f32_f16 with fp32 accumulation; per 16-byte chunk of codes
-// the affine map is applied once:  sum_c (s q_c + b) x_c = s A + (b - 1024 s) X  with
-// A = sum_c (1024+q_c) x_c and X = sum_c x_c.
+// the affine map is applied once:  sum_c (s q_c + b) x_c = s (A - Y) + b X  with
+// A = sum_c (1024+q_c) x_c, X = sum_c x_c and Y its magic-value part, X and Y formed once
+// per chunk when x or h is staged (chunk_dot, chunk_sums).
 //
 // Code is kept compact on purpose: a cold kernel fetches its instructions from L2, so
 // long unrolled straight-line code costs microseconds here.
@@ -73,8 +74,8 @@ struct DecArgs {
     int vs;                     // down: wave groups splitting the vectors of a row block
 };
 
-// x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk fp32 sums of
-// the even and of the odd columns, under the row's range scale 2^e (returned; 0 for rows
+// x (bf16) -> LDS fp16 in code order (|v| < 2^-14 flushed) + per-chunk sums (chunk_sums
+// of the even and of the odd columns' fp32 sums), under the row's range scale 2^e (returned; 0 for rows
 // of ordinary magnitude, which are staged in one pass); s_wm holds one word per wave.
 // Ends with a barrier.
 template <int BITS>
@@ -96,7 +97,7 @@ __device__ void stage_x_pass(const uint16_t *x, int nch, float f, uint32_t *xs, 
             }
             *(u32x4 *)(xs + (c * CPC + 8 * g) / 2) = perm8<BITS>(nat);
         }
-        xsum[c] = make_float2(se, so);
+        xsum[c] = chunk_sums<BITS>(se, so);
     }
 }
 template <int BITS>
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
         // of a row, reading 16 different chunks, meet distinct banks
         constexpr int CPITCH = CPC + 8;
         uint16_t *hs16 = (uint16_t *)dsm;                     // nvec * nch chunks
-        float2 *hsum = (float2 *)(dsm + nvec * nch * CPITCH / 2);   // chunk sums (even, odd columns)
+        float2 *hsum = (float2 *)(dsm + nvec * nch * CPITCH / 2);   // chunk sums (chunk_sums)
         float *hinv = (float *)(hsum + nvec * nch);                 // chunk range scales, inverted
         // lane j < nvec holds row 0 of vector j's down matrix (the k routed experts in
         // ascending id, then the shared one) and its combine weight
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                     se = group_sum(se, CPC / 8);                 // groups of a chunk are adjacent lanes
                     so = group_sum(so, CPC / 8);
                     if (live && (g % (CPC / 8)) == 0) {
-                        hsum[g / (CPC / 8)] = make_float2(se, so);
+                        hsum[g / (CPC / 8)] = chunk_sums<BITS>(se, so);
                         hinv[g / (CPC / 8)] = exp2i(-ec);
                     }
                 };

@@ -147,7 +147,7 @@ __device__ __forceinline__ uint32_t stage_x_row(const uint16_t *x, int t, int H,
             }
             *(u32x4 *)(xd + 4 * g) = perm8<BITS>(nat);
         }
-        *(float2 *)(xd + CPC / 2) = make_float2(se, so);
+        *(float2 *)(xd + CPC / 2) = chunk_sums<BITS>(se, so);
     }
     return m;
 }
@@ -345,15 +345,12 @@ __device__ void pairs_swiglu_tokens(const QMat &mg, const QMat &mu, int e, int j
             for (int t = 0; t < SM_TMAX; ++t) {
                 if (t >= T || !((tmask >> t) & 1)) continue;
                 const u32x4 xp = *(const u32x4 *)(xs + (t * nch + cc) * XP + CPC / 2);   // the sums' pad
-                const float2 X = make_float2(__uint_as_float(xp[0]), __uint_as_float(xp[1]));
-                float pg, pu;
-                if constexpr (BITS == 4) {
-                    pg = sg * ag[t][0] + (sg * 0.0625f) * ag[t][1] + (bg - 1024.0f * sg) * X.x + (bg - 64.0f * sg) * X.y;
-                    pu = su * au[t][0] + (su * 0.0625f) * au[t][1] + (bu - 1024.0f * su) * X.x + (bu - 64.0f * su) * X.y;
-                } else {
-                    pg = sg * (ag[t][0] + ag[t][1]) + (bg - 1024.0f * sg) * (X.x + X.y);
-                    pu = su * (au[t][0] + au[t][1]) + (bu - 1024.0f * su) * (X.x + X.y);
-                }
+                const float2 XY = make_float2(__uint_as_float(xp[0]), __uint_as_float(xp[1]));   // chunk_sums
+                // (the affine map of chunk_dot: s (A - Y) + b X)
+                const float Ag = BITS == 4 ? __builtin_fmaf(ag[t][1], 0.0625f, ag[t][0]) : ag[t][0] + ag[t][1];
+                const float Au = BITS == 4 ? __builtin_fmaf(au[t][1], 0.0625f, au[t][0]) : au[t][0] + au[t][1];
+                const float pg = __builtin_fmaf(sg, Ag - XY.y, bg * XY.x);
+                const float pu = __builtin_fmaf(su, Au - XY.y, bu * XY.x);
                 acc[4 * t + 2 * p] += ok ? pg : 0.0f;
                 acc[4 * t + 2 * p + 1] += ok ? pu : 0.0f;
             }
@@ -754,7 +751,7 @@ __global__ __launch_bounds__(DT) __attribute__((amdgpu_waves_per_eu(4))) void k_
                 se = group_sum(se, CPC / 8);
                 so = group_sum(so, CPC / 8);
                 if (live && (g % (CPC / 8)) == 0) {
-                    hsum[g / (CPC / 8)] = make_float2(se, so);
+                    hsum[g / (CPC / 8)] = chunk_sums<BITS>(se, so);
                     hinv[g / (CPC / 8)] = exp2i(-ec);
                 }
             }

@@ -168,45 +168,52 @@ __device__ void finish_call(uint32_t *ctl, uint32_t tag) {
 __device__ __forceinline__ float no_nan(float v) { return (v != v) ? -__builtin_inff() : v; }
 
 
-// sum_c (s q_c + b) x_c over one 16-byte chunk of codes; X = (sum of x over the even
-// columns, over the odd columns).  4-bit: the low nibble of each byte (even columns)
-// becomes 1024 + q, the high nibble (odd columns) is taken in place as 1024 + 16 q, both
-// exact in fp16, so one shift serves 8 codes:
-//   sum (s q + b) x = s A_e + (s / 16) A_o + (b - 1024 s) X_e + (b - 64 s) X_o
-// with A_e, A_o the dot products of the magic values with x.  8-bit: 1024 + q for all.
+// sum_c (s q_c + b) x_c over one 16-byte chunk of codes.  4-bit: the low nibble of each
+// byte (even columns) becomes 1024 + q, the high nibble (odd columns) is taken in place as
+// 1024 + 16 q, both exact in fp16, so one shift serves 8 codes; with A_e, A_o the dot
+// products of those magic values with x over the even and odd columns,
+//   A = A_e + A_o / 16 = sum q x + 1024 X_e + 64 X_o,
+// and  sum (s q + b) x = s (A - Y) + b X  with X = X_e + X_o, Y = 1024 X_e + 64 X_o, the
+// pair chunk_sums forms once per chunk when x or h is staged.  8-bit: 1024 + q for all
+// columns, Y = 1024 X.
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 X,
+__device__ __forceinline__ float2 chunk_sums(float se, float so) {
+    if constexpr (BITS == 4) return make_float2(se + so, __builtin_fmaf(1024.0f, se, 64.0f * so));
+    else return make_float2(se + so, 1024.0f * (se + so));
+}
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const u32x4 &q, const uint32_t *xs, uint32_t s16, uint32_t b16, float2 XY,
                                            int sb_bf16) {
     const u32x4 *xv = (const u32x4 *)xs;
     const uint32_t magic = QS_MAGIC;
     const float s = sb_to_f32(s16, sb_bf16), b = sb_to_f32(b16, sb_bf16);
+    float A;
     if constexpr (BITS == 4) {
         const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u;
-        float ae[2] = {0.0f, 0.0f}, ao[2] = {0.0f, 0.0f};
+        float ae = 0.0f, ao = 0.0f;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t w8 = q[d] >> 8;
             const u32x4 xx = xv[d];
-            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[0]), ae[d & 1], false);
-            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], hi, magic)), as_h2(xx[1]), ao[d & 1], false);
-            ae[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, lo, magic)), as_h2(xx[2]), ae[d & 1], false);
-            ao[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(w8, hi, magic)), as_h2(xx[3]), ao[d & 1], false);
+            ae = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[0]), ae, false);
+            ao = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], hi, magic)), as_h2(xx[1]), ao, false);
+            ae = __builtin_amdgcn_fdot2(as_h2(and_or(w8, lo, magic)), as_h2(xx[2]), ae, false);
+            ao = __builtin_amdgcn_fdot2(as_h2(and_or(w8, hi, magic)), as_h2(xx[3]), ao, false);
         }
-        const float Ae = ae[0] + ae[1], Ao = ao[0] + ao[1];
-        return s * Ae + (s * 0.0625f) * Ao + (b - 1024.0f * s) * X.x + (b - 64.0f * s) * X.y;
+        A = __builtin_fmaf(ao, 0.0625f, ae);
     } else {
         const uint32_t lo = 0x00FF00FFu;
-        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float acc[2] = {0.0f, 0.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const u32x4 xx = xv[d >> 1];
             const int o = 2 * (d & 1);
-            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[o]), acc[d], false);
-            acc[d] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d] >> 8, lo, magic)), as_h2(xx[o + 1]), acc[d], false);
+            acc[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d], lo, magic)), as_h2(xx[o]), acc[d & 1], false);
+            acc[d & 1] = __builtin_amdgcn_fdot2(as_h2(and_or(q[d] >> 8, lo, magic)), as_h2(xx[o + 1]), acc[d & 1], false);
         }
-        const float A = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-        return s * A + (b - 1024.0f * s) * (X.x + X.y);
+        A = acc[0] + acc[1];
     }
+    return __builtin_fmaf(s, A - XY.y, b * XY.x);
 }
 
 // Selector (one wave): waits (bounded) until every logit of this call is in and takes
