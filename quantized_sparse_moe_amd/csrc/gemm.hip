@@ -97,7 +97,7 @@ struct GemmArgs {
     const uint16_t *x16;             // [T][H] fp16 (permuted); row t is x_t 2^xexp[t]
     const int32_t *xexp;             // [T]
     uint16_t *h;                     // [(T*K + T)][I] fp16 (permuted), per-block scaled
-    int8_t *hexp;                    // [(T*K + T)][HEXP_STRIDE] the scale of each 128-column block
+    int8_t *hexp;                    // [HEXP_STRIDE][T*K + T] the scale of each 128-column block
     const int32_t *perm;
     const Tile *tiles;
     int32_t *ntiles;                 // tile counts; [2] = 1 once a down workgroup stored a scaled slot block
@@ -366,10 +366,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         if (p < nk) issue(p);
     u32x4 hw = {0u, 0u, 0u, 0u};         // down pass: the block scales of h row `tid`
     if (MODE == 1 && tid < BM) {
-        // (device scope: written by other workgroups of this launch)
-        const uint32_t *hp = (const uint32_t *)(a.hexp + (int64_t)(tile.row0 + my_row) * HEXP_STRIDE);
+        // (device scope: written by other workgroups of this launch; block-major, so the
+        // rows of a tile are consecutive bytes)
+        const int8_t *hp = a.hexp + tile.row0 + my_row;
+        const int64_t rtot = TK + a.T;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) hw[q] = __hip_atomic_load(hp + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int bk = 0; bk < HEXP_STRIDE; ++bk)
+            if (bk < a.nb_gateup) {
+                const uint32_t v = (uint8_t)__hip_atomic_load(hp + bk * rtot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                hw[bk >> 2] |= v << (8 * (bk & 3));
+            }
     }
     int my_xe = 0;                       // gate/up pass: the scale exponent of x in row `tid`
     if (MODE == 0 && tid < BM) {
@@ -621,6 +627,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         constexpr int HP = 40;                                   // fp16 per staged row
         uint16_t *hs = (uint16_t *)(smem + wave * (BM * HP * 2));
         uint32_t *s_hm = (uint32_t *)(smem + 4 * (BM * HP * 2)); // [4][BM] row maxima per wave
+        int8_t *s_eh = (int8_t *)(s_hm + 4 * BM);                // [BM] the block scale of each row
         const bool cols_live = nbi * 128 + wave * 32 < I;      // this wave's 32 h columns exist
         // h = silu(g) u in fp32 (scales of x and of the weight rows taken out), in place of
         // the gate accumulators; then the largest |h| of each row over this wave's columns
@@ -673,13 +680,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
                         const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
                         hs[row * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(acc[i][j][r] * f));
                     }
-                    if (wave == 0 && n16 == 0 && row < nrows)      // (device scope, as h)
-                        __hip_atomic_store(a.hexp + (int64_t)(tile.row0 + row) * HEXP_STRIDE + nbi, (int8_t)eh,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (wave == 0 && n16 == 0) s_eh[row] = (int8_t)eh;
                 }
             }
         }
         wave_lds_sync();
+        // the block scales of the tile's rows: consecutive bytes of block nbi, stored by
+        // wave 0 at device scope (as h) in runs of 64
+        if (wave == 0) {
+            int8_t *he = a.hexp + (int64_t)nbi * (TK + a.T) + tile.row0;
+#pragma unroll
+            for (int q = 0; q < (BM + 63) / 64; ++q) {
+                const int row = 64 * q + lane;
+                if (row < nrows) __hip_atomic_store(he + row, s_eh[row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
         const int chunk = lane & 3;
         uint16_t *hout = a.h + (int64_t)tile.row0 * I + nbi * 128 + wave * 32 + chunk * 8;
         // h goes out at device scope (sc1, written through), and once every wave's stores

@@ -65,9 +65,9 @@ struct Tile {                      // one row block of one expert bin
 };
 
 // fp16 operands of the grouped path carry power-of-two range scales: x 2^a per token
-// (a in xexp), h 2^e per (row, 128-column block) (e in hexp, HEXP_STRIDE bytes per row,
-// one per block), slot rows 2^e per (row, 64-column block) (sexp, block-major: the
-// exponents of one block for all slot rows together, rows padded to a multiple of 16)
+// (a in xexp), h 2^e per (row, 128-column block) (e in hexp, block-major: the exponents
+// of one block for all T*K + T rows together), slot rows 2^e per (row, 64-column block)
+// (sexp, block-major as well, rows padded to a multiple of 16)
 constexpr int HEXP_STRIDE = 16;    // inter <= 2048: at most 16 blocks of 128 columns
 // a state word read by the grouped GEMM: nonzero gives every h block the scale that puts
 // its largest value in [2^14, 2^15) instead of the shared one (0 for ordinary blocks), so
@@ -91,7 +91,7 @@ struct PrefillBufs {
     int32_t *tile_done;            // [max_tiles] gate/up column blocks finished per tile
     uint32_t *ctl;                 // the workspace's state region (word 0: bounded-wait error flag)
     uint16_t *h;                   // [(T*K + T)][I] fp16, columns permuted per 8-group
-    int8_t *hexp;                  // [(T*K + T)][HEXP_STRIDE]
+    int8_t *hexp;                  // [HEXP_STRIDE][T*K + T]
     uint16_t *slot;                // [T*K + T][H] fp16: w_j * o_j per (token, slot), then shared o
     int8_t *sexp;                  // [H / 64][sexp_rows(T, K)]
     float *sgate;                  // [T] shared-expert gate sigmoid(g . x_t) (gated layers)
