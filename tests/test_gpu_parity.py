@@ -405,7 +405,7 @@ def test_edge_shapes(torch, qs, shape, T):
 
 
 # --------------------------------------------------------------------------- Q8_0
-@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288)])
+@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288), (128, 2048), (256, 4096), (128, 8192)])
 def test_q8_pack_and_gemv(torch, qs, N, K):
     rows = syn.make_q8_rows(N, K, seed=N + K)
     x_np = syn.make_x(1, K, seed=K)[0]
@@ -424,7 +424,7 @@ def test_q8_pack_and_gemv(torch, qs, N, K):
     check_output(y_to_np(yb, torch), ref, True, f"q8 bf16 {N}x{K}")
 
 
-@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288)])
+@pytest.mark.parametrize("N,K", syn.Q8_SHAPES + [(16, 32), (48, 96), (32, 8192), (160, 288), (128, 2048), (256, 4096), (128, 8192)])
 def test_q8_activation_quantized_gemv(torch, qs, N, K):
     """[EMBER] one activation quantization shared by the projections: the activation's
     codes and scales bit for bit against the oracle (an integer decision taken in binary32
