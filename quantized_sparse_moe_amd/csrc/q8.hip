@@ -126,70 +126,47 @@ __global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv(const uint8_t *__restric
     }
 }
 
-// The same product with 16-byte loads and every tile of the wave in flight at once.
-// A wave reads two consecutive tiles per instruction: lane (t, g, q) = (lane >> 5,
-// (lane >> 2) & 7, lane & 3) takes bytes 64 g + 16 q of tile t -- the 4 columns of
-// group g for rows 4q .. 4q+3 -- and the fp16 scales of those rows.  A wave owns PPW
-// tile pairs (nb = 2 PPW Q8_WAVES) and issues all their loads right behind those of x,
-// so the panel's whole read overlaps the staging.  Each lane keeps four row sums; the
-// 16 lanes of a row quad are reduced across the wave, then the waves across LDS.
+// Many panels: one workgroup per 16-row panel, 16-byte loads and every tile of the wave in
+// flight at once.  A wave reads two consecutive tiles per instruction: lane (t, g, q) =
+// (lane >> 5, (lane >> 2) & 7, lane & 3) takes bytes 64 g + 16 q of tile t -- the 4 columns
+// of group g for rows 4q .. 4q+3 -- the fp16 scales of those rows, and the 4 activations
+// the chunk multiplies (8 bytes through the caches: every wave reads the same x, so no
+// staged copy is waited for).  A wave owns PPW tile pairs (nb = 2 PPW WAVES).  Each lane
+// keeps four row sums; the 16 lanes of a row quad are reduced across the wave, then the
+// waves across LDS.
 template <int PPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_q8_gemv_wide(const uint8_t *__restrict__ tiles, int64_t K,
-                                                             const uint16_t *__restrict__ x, void *y, int y_dtype) {
-    extern __shared__ float q8s[];
-    constexpr int NT = 64 * WAVES;
+                                                                const uint16_t *__restrict__ x, void *y, int y_dtype) {
     constexpr int NB = 2 * PPW * WAVES;                 // blocks of 32 columns (K / 32)
-    constexpr int SPT = (NB * 8 + NT - 1) / NT;         // 4-column slots per thread
-    float *xf = q8s;                      // [K]: x in fp32
-    float *xs = q8s + NB * 32;            // [K / 4]: sums of 4 consecutive columns
     __shared__ float red[WAVES][16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int q = lane & 3, g = (lane >> 2) & 7, tt = lane >> 5;
-    // x is read first, with loads the compiler does not see (it would otherwise move them
-    // behind the tiles', and loads complete in order); they are waited for by count below
-    uint64_t xr[SPT];
-#pragma unroll
-    for (int k = 0; k < SPT; ++k)
-        asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(xr[k]) : "v"(x + 4 * min(tid + k * NT, NB * 8 - 1))
-                     : "memory");
     const uint8_t *panel = tiles + (int64_t)blockIdx.x * NB * TILE;
     u32x4 c[PPW];
-    uint64_t sc[PPW];
+    uint64_t sc[PPW], xv[PPW];
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
-        const uint8_t *t = panel + (int64_t)(2 * (wave + u * WAVES) + tt) * TILE;
+        const int b = 2 * (wave + u * WAVES) + tt;
+        const uint8_t *t = panel + (int64_t)b * TILE;
         c[u] = __builtin_nontemporal_load((const u32x4 *)(t + 64 * g + 16 * q));
         sc[u] = __builtin_nontemporal_load((const uint64_t *)(t + 512 + 8 * q));
+        xv[u] = *(const uint64_t *)(x + 32 * b + 4 * g);
     }
-    // x's loads are the oldest in flight: wait until no more than the tiles' remain
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PPW) : "memory");
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) asm volatile("" : "+v"(xr[k]));
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        const int sl = tid + k * NT;
-        if (sl >= NB * 8) break;
-        const uint32_t lo = (uint32_t)xr[k], hi = (uint32_t)(xr[k] >> 32);
-        const float v0 = __uint_as_float(lo << 16), v1 = __uint_as_float(lo & 0xffff0000u);
-        const float v2 = __uint_as_float(hi << 16), v3 = __uint_as_float(hi & 0xffff0000u);
-        *(f32x4 *)(xf + 4 * sl) = (f32x4){v0, v1, v2, v3};
-        xs[sl] = (v0 + v1) + (v2 + v3);
-    }
-    __syncthreads();
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
-        const int sl = (2 * (wave + u * WAVES) + tt) * 8 + g;
-        const f32x4 xv = *(const f32x4 *)(xf + 4 * sl);
-        const float x4 = 128.0f * xs[sl];
+        const uint32_t lo = (uint32_t)xv[u], hi = (uint32_t)(xv[u] >> 32);
+        const float x0 = __uint_as_float(lo << 16), x1 = __uint_as_float(lo & 0xffff0000u);
+        const float x2 = __uint_as_float(hi << 16), x3 = __uint_as_float(hi & 0xffff0000u);
+        const float x4 = 128.0f * ((x0 + x1) + (x2 + x3));
         const uint32_t d2[2] = {(uint32_t)sc[u], (uint32_t)(sc[u] >> 32)};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const uint32_t p = c[u][rr] ^ 0x80808080u;
-            float s = ubyte<0>(p) * xv[0];
-            s = __builtin_fmaf(ubyte<1>(p), xv[1], s);
-            s = __builtin_fmaf(ubyte<2>(p), xv[2], s);
-            s = __builtin_fmaf(ubyte<3>(p), xv[3], s);
+            float s = ubyte<0>(p) * x0;
+            s = __builtin_fmaf(ubyte<1>(p), x1, s);
+            s = __builtin_fmaf(ubyte<2>(p), x2, s);
+            s = __builtin_fmaf(ubyte<3>(p), x3, s);
             const float d = f16_to_f32((uint16_t)(d2[rr >> 1] >> (16 * (rr & 1))));
             acc[rr] = __builtin_fmaf(d, s - x4, acc[rr]);
         }
@@ -218,92 +195,74 @@ __global__ __launch_bounds__(64 * WAVES) void k_q8_gemv_wide(const uint8_t *__re
     }
 }
 
-// Few panels (at most half as many 16-row panels as compute units): two workgroups per panel, each
-// taking 8 of its 16 rows over the whole row length, so that twice the compute units
-// read and no partial sums need combining.  A wave reads four consecutive tiles per
-// 16-byte load: lane (t, g, q) = (lane >> 4, (lane >> 1) & 7, lane & 1) takes bytes
-// 64 g + 16 (2 hf + q) of tile t (rows 8 hf + 4q .. + 3 of group g) and those rows' fp16
-// scales.  The two halves of a panel run on one XCD (workgroups b and b + 8 share b % 8),
-// so each 64-byte group is fetched into that XCD's L2 once for both.  A wave owns QPW
-// tile quads (nb = 4 QPW Q8_WAVES), all in flight behind the activation loads.
-template <int QPW>
-__global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv_half(const uint8_t *__restrict__ tiles, int64_t K,
+// Few panels: PARTS workgroups per panel (two; four measured slower), each taking
+// 16 / PARTS of its 16 rows over the whole row length, so that PARTS times the compute
+// units read and no partial sums need combining.  Row quad rq's 16 bytes of group g are chunk 4 g + rq of a tile;
+// lane (t, g, q) = (lane / LT, (lane / QL) % 8, lane % QL), with QL = 4 / PARTS quads per
+// workgroup and LT = 8 QL lanes per tile, takes chunk 4 g + QL part + q of tile t (TPI =
+// 64 / LT consecutive tiles per 16-byte load), that quad's fp16 scales, and the 4
+// activations the chunk multiplies (8 bytes through the caches: every wave and every part
+// reads the same x, and nothing waits for a staged copy).  The parts of a panel run on one
+// XCD (workgroups b, b + 8, ... share b % 8), so each line is fetched into its L2 once.
+// A wave owns QPW groups of TPI tiles (nb = TPI QPW Q8_WAVES), all loads in flight at once.
+template <int QPW, int PARTS>
+__global__ __launch_bounds__(Q8_THREADS) void k_q8_gemv_part(const uint8_t *__restrict__ tiles, int64_t K,
                                                              const uint16_t *__restrict__ x, void *y, int y_dtype) {
-    extern __shared__ float q8s[];
-    constexpr int NT = Q8_THREADS, NB = 4 * QPW * Q8_WAVES;          // blocks of 32 columns (K / 32)
-    constexpr int SPT = (NB * 8 + NT - 1) / NT;                       // 4-column slots per thread
-    float *xf = q8s;                      // [K]: x in fp32
-    float *xs = q8s + NB * 32;            // [K / 4]: sums of 4 consecutive columns
-    __shared__ float red[Q8_WAVES][8];
+    constexpr int QL = 4 / PARTS, LT = 8 * QL, TPI = 64 / LT, PLOG = PARTS == 4 ? 2 : 1;
+    constexpr int NB = TPI * QPW * Q8_WAVES;                          // blocks of 32 columns (K / 32)
+    __shared__ float red[Q8_WAVES][16 / PARTS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int q = lane & 1, g = (lane >> 1) & 7, tt = lane >> 4;
-    const int bid = blockIdx.x, hf = (bid >> 3) & 1, panel = (bid >> 4) * 8 + (bid & 7);
-    uint64_t xr[SPT];
-#pragma unroll
-    for (int k = 0; k < SPT; ++k)
-        asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(xr[k]) : "v"(x + 4 * min(tid + k * NT, NB * 8 - 1))
-                     : "memory");
+    const int q = lane % QL, g = (lane / QL) & 7, tt = lane / LT;
+    const int bid = blockIdx.x, part = (bid >> 3) & (PARTS - 1), panel = (bid >> (3 + PLOG)) * 8 + (bid & 7);
+    const int rq = QL * part + q;                                     // rows 4 rq .. 4 rq + 3
     const uint8_t *pnl = tiles + (int64_t)panel * NB * TILE;
     u32x4 c[QPW];
-    uint64_t sc[QPW];
+    uint64_t sc[QPW], xv[QPW];
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
-        const uint8_t *t = pnl + (int64_t)(4 * (wave + u * Q8_WAVES) + tt) * TILE;
-        c[u] = __builtin_nontemporal_load((const u32x4 *)(t + 64 * g + 16 * (2 * hf + q)));
-        sc[u] = __builtin_nontemporal_load((const uint64_t *)(t + 512 + 8 * (2 * hf + q)));
+        const int b = TPI * (wave + u * Q8_WAVES) + tt;                // this lane's block of 32 columns
+        const uint8_t *t = pnl + (int64_t)b * TILE;
+        c[u] = __builtin_nontemporal_load((const u32x4 *)(t + 64 * g + 16 * rq));
+        sc[u] = __builtin_nontemporal_load((const uint64_t *)(t + 512 + 8 * rq));
+        xv[u] = *(const uint64_t *)(x + 32 * b + 4 * g);
     }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * QPW) : "memory");
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) asm volatile("" : "+v"(xr[k]));
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-        const int sl = tid + k * NT;
-        if (sl >= NB * 8) break;
-        const uint32_t lo = (uint32_t)xr[k], hi = (uint32_t)(xr[k] >> 32);
-        const float v0 = __uint_as_float(lo << 16), v1 = __uint_as_float(lo & 0xffff0000u);
-        const float v2 = __uint_as_float(hi << 16), v3 = __uint_as_float(hi & 0xffff0000u);
-        *(f32x4 *)(xf + 4 * sl) = (f32x4){v0, v1, v2, v3};
-        xs[sl] = (v0 + v1) + (v2 + v3);
-    }
-    __syncthreads();
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
-        const int sl = (4 * (wave + u * Q8_WAVES) + tt) * 8 + g;
-        const f32x4 xv = *(const f32x4 *)(xf + 4 * sl);
-        const float x4 = 128.0f * xs[sl];
+        const uint32_t lo = (uint32_t)xv[u], hi = (uint32_t)(xv[u] >> 32);
+        const float x0 = __uint_as_float(lo << 16), x1 = __uint_as_float(lo & 0xffff0000u);
+        const float x2 = __uint_as_float(hi << 16), x3 = __uint_as_float(hi & 0xffff0000u);
+        const float x4 = 128.0f * ((x0 + x1) + (x2 + x3));
         const uint32_t d2[2] = {(uint32_t)sc[u], (uint32_t)(sc[u] >> 32)};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const uint32_t p = c[u][rr] ^ 0x80808080u;
-            float s = ubyte<0>(p) * xv[0];
-            s = __builtin_fmaf(ubyte<1>(p), xv[1], s);
-            s = __builtin_fmaf(ubyte<2>(p), xv[2], s);
-            s = __builtin_fmaf(ubyte<3>(p), xv[3], s);
+            float s = ubyte<0>(p) * x0;
+            s = __builtin_fmaf(ubyte<1>(p), x1, s);
+            s = __builtin_fmaf(ubyte<2>(p), x2, s);
+            s = __builtin_fmaf(ubyte<3>(p), x3, s);
             const float d = f16_to_f32((uint16_t)(d2[rr >> 1] >> (16 * (rr & 1))));
             acc[rr] = __builtin_fmaf(d, s - x4, acc[rr]);
         }
     }
+    // the lanes of one quad (all lane bits but q's) in a fixed butterfly, then the waves
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
         float a = acc[rr];
-        a += __shfl_xor(a, 2, 64);
-        a += __shfl_xor(a, 4, 64);
-        a += __shfl_xor(a, 8, 64);
-        a += __shfl_xor(a, 16, 64);
-        a += __shfl_xor(a, 32, 64);
+#pragma unroll
+        for (int m = QL; m < 64; m <<= 1) a += __shfl_xor(a, m, 64);
         acc[rr] = a;
     }
-    if (lane < 2) {
+    if (lane < QL) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) red[wave][4 * lane + rr] = acc[rr];
     }
     __syncthreads();
-    if (tid < 8) {
+    if (tid < 16 / PARTS) {
         float s = 0.0f;
 #pragma unroll
         for (int w = 0; w < Q8_WAVES; ++w) s += red[w][tid];
-        const int64_t n = (int64_t)panel * 16 + 8 * hf + tid;
+        const int64_t n = (int64_t)panel * 16 + (16 / PARTS) * part + tid;
         if (y_dtype == MOE_F32) ((float *)y)[n] = s;
         else ((uint16_t *)y)[n] = f32_to_bf16(s);
     }
@@ -481,26 +440,25 @@ __global__ __launch_bounds__(256) void k_q8_pack(const uint8_t *__restrict__ row
 hipError_t launch_q8_gemv(const uint8_t *tiles, int64_t N, int64_t K, const uint16_t *x, void *y,
                           int y_dtype, hipStream_t s) {
     const dim3 grid((unsigned)(N / 16)), block(Q8_THREADS), block16(1024);
-    const size_t lds_w = (size_t)K * 4 + (size_t)(K / 4) * 4;
-    // few panels (at most one per two compute units): two workgroups per panel (eight
-    // panels at a time, both halves on one XCD)
+    // few panels (at most one per two compute units): two workgroups per panel, eight panels
+    // at a time, both halves on one XCD
     if (2 * (N / 16) <= n_compute_units() && (N / 16) % 8 == 0 && K % (128 * Q8_WAVES) == 0) {
         const dim3 grid2((unsigned)(N / 8));
-        switch (K / (128 * Q8_WAVES)) {                       // tile quads per wave
-        case 2: hipLaunchKernelGGL((k_q8_gemv_half<2>), grid2, block, lds_w, s, tiles, K, x, y, y_dtype); return hipGetLastError();
-        case 4: hipLaunchKernelGGL((k_q8_gemv_half<4>), grid2, block, lds_w, s, tiles, K, x, y, y_dtype); return hipGetLastError();
-        case 8: hipLaunchKernelGGL((k_q8_gemv_half<8>), grid2, block, lds_w, s, tiles, K, x, y, y_dtype); return hipGetLastError();
+        switch (K / (128 * Q8_WAVES)) {                       // groups of 4 tiles per wave
+        case 2: hipLaunchKernelGGL((k_q8_gemv_part<2, 2>), grid2, block, 0, s, tiles, K, x, y, y_dtype); return hipGetLastError();
+        case 4: hipLaunchKernelGGL((k_q8_gemv_part<4, 2>), grid2, block, 0, s, tiles, K, x, y, y_dtype); return hipGetLastError();
+        case 8: hipLaunchKernelGGL((k_q8_gemv_part<8, 2>), grid2, block, 0, s, tiles, K, x, y, y_dtype); return hipGetLastError();
         default: break;
         }
     }
     // (16 waves pay off for long rows only: 8 tile pairs or more per wave)
     const bool few = N / 16 < n_compute_units() && K % (64 * 16) == 0 && K >= 8 * 64 * 16;
     switch (few ? 100 + K / (64 * 16) : K % (64 * Q8_WAVES) == 0 ? K / (64 * Q8_WAVES) : 0) {   // tile pairs per wave
-    case 2: hipLaunchKernelGGL((k_q8_gemv_wide<2, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
-    case 4: hipLaunchKernelGGL((k_q8_gemv_wide<4, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
-    case 8: hipLaunchKernelGGL((k_q8_gemv_wide<8, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
-    case 16: hipLaunchKernelGGL((k_q8_gemv_wide<16, Q8_WAVES>), grid, block, lds_w, s, tiles, K, x, y, y_dtype); break;
-    case 108: hipLaunchKernelGGL((k_q8_gemv_wide<8, 16>), grid, block16, lds_w, s, tiles, K, x, y, y_dtype); break;
+    case 2: hipLaunchKernelGGL((k_q8_gemv_wide<2, Q8_WAVES>), grid, block, 0, s, tiles, K, x, y, y_dtype); break;
+    case 4: hipLaunchKernelGGL((k_q8_gemv_wide<4, Q8_WAVES>), grid, block, 0, s, tiles, K, x, y, y_dtype); break;
+    case 8: hipLaunchKernelGGL((k_q8_gemv_wide<8, Q8_WAVES>), grid, block, 0, s, tiles, K, x, y, y_dtype); break;
+    case 16: hipLaunchKernelGGL((k_q8_gemv_wide<16, Q8_WAVES>), grid, block, 0, s, tiles, K, x, y, y_dtype); break;
+    case 108: hipLaunchKernelGGL((k_q8_gemv_wide<8, 16>), grid, block16, 0, s, tiles, K, x, y, y_dtype); break;
     default: {
         const size_t lds = (size_t)(K / 32) * 32 * 4 + (size_t)(K / 32) * 4 * 4;
         hipLaunchKernelGGL((k_q8_gemv<4>), grid, block, lds, s, tiles, K, x, y, y_dtype);
