@@ -183,26 +183,19 @@ struct TopkArgs {
 // One wave per token (4 tokens per wave), 16 tokens per workgroup: the block's expert
 // histogram is counted in LDS with integer atomics and written once.
 template <int BITS>
-__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+__global__ __launch_bounds__(64 * TK_TOKENS) void k_topk(TopkArgs a) {
     __shared__ int hist[256];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int E = a.E, K = a.K;
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    // the logits of this wave's tokens are all loaded before the first selection
-    constexpr int TPW = TK_TOKENS / 4;
-    float v[TPW][4];
+    // one wave per token: the selection is a chain of dependent single-wave steps, and the
+    // SIMD interleaves the chains of the workgroup's waves
+    const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave;
+    float v[4];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-        const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[q][i] = (t < a.T && lane + 64 * i < E) ? a.logits[t * a.LS + lane + 64 * i] : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-        const int64_t t = (int64_t)blockIdx.x * TK_TOKENS + wave + 4 * q;
-        if (t >= a.T) break;
+    for (int i = 0; i < 4; ++i) v[i] = (t < a.T && lane + 64 * i < E) ? a.logits[t * a.LS + lane + 64 * i] : 0.0f;
+    if (t < a.T) {
         if (a.x16) {
             // the token's range scale; a row outside fp16's range is copied again, scaled
             uint32_t m = 0u;
@@ -222,7 +215,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
                 }
             }
         }
-        const TopkOut tk = wave_topk_regs(v[q], E, K);
+        const TopkOut tk = wave_topk_regs(v, E, K);
         if (a.sgate && lane == 0) a.sgate[t] = sigmoid(a.logits[t * a.LS + E]);
         if (lane < K) {
             a.idx[t * K + lane] = tk.idx;
@@ -281,9 +274,9 @@ hipError_t launch_prefill_router(const Layer &L, const uint16_t *x, int64_t T,
     ta.H = L.H;
     const dim3 tgrid((unsigned)((T + TK_TOKENS - 1) / TK_TOKENS));
     if (L.bits == 4)
-        hipLaunchKernelGGL((k_topk<4>), tgrid, dim3(256), 0, s, ta);
+        hipLaunchKernelGGL((k_topk<4>), tgrid, dim3(64 * TK_TOKENS), 0, s, ta);
     else
-        hipLaunchKernelGGL((k_topk<8>), tgrid, dim3(256), 0, s, ta);
+        hipLaunchKernelGGL((k_topk<8>), tgrid, dim3(64 * TK_TOKENS), 0, s, ta);
     return hipGetLastError();
 }
 
