@@ -4,14 +4,15 @@
 // columns, the bytes of the same 4 columns of the 16 rows sit next to each other
 // (eight 64-byte groups), followed by the 16 fp16 scales -- 544 bytes, the size of 16
 // ordinary Q8_0 blocks.  On x86 this lets one VNNI step broadcast 4 activation bytes
-// against a 64-byte weight group.  On gfx950 the same layout makes a wave's load of
-// 4 consecutive groups one contiguous 256-byte read: lane l takes row l % 16 of group
-// l / 16 (and of group l / 16 + 4), so a whole tile is read by two dword loads per lane
-// and every lane keeps accumulating one row.
+// against a 64-byte weight group.  On gfx950 the same layout makes a wave's 16-byte loads
+// contiguous runs of whole groups: k_q8_gemv_wide (many panels) and k_q8_gemv_part (few
+// panels, two workgroups per panel) read tiles 16 bytes per lane -- 4 columns of 4 rows --
+// and, beside each chunk, the 4 activations it multiplies; k_q8_gemv (any K) reads 4 bytes
+// per lane against a copy of x staged in LDS.
 //
 // Codes are widened exactly: (q ^ 0x80) is q + 128 as an unsigned byte, which the
 // byte-to-float conversion turns into fp32 in one instruction; the +128 is removed per
-// lane with the staged sum of the 8 activations the lane multiplies.
+// lane with the sum of the activations the lane multiplies.
 //
 // [EMBER] also quantizes the activation once (Q8_0 blocks) for all the projections that
 // read it; k_q8_quantize_x and k_q8_gemv_q8x are that variant, with exact int8 dot
