@@ -90,6 +90,10 @@ struct Cfg {
     static constexpr int LDS = NSTAGE * STAGE + 4 * S_BYTES;
 };
 static_assert(Cfg<4>::NSTAGE == 2 && Cfg<8>::NSTAGE == 2, "every stage wait is a full drain (vmcnt 0)");
+// the gate/up epilogue's staging (four waves' h rows, row maxima, block scales and their
+// factors) and the down epilogue's fit in the ring
+static_assert(4 * GEMM_BM * 40 * 2 + 4 * GEMM_BM * 4 + (GEMM_BM + 15) / 16 * 16 + GEMM_BM * 4 <= Cfg<4>::LDS &&
+                  4 * (32 * 68 * 4) <= Cfg<4>::LDS, "epilogue staging");
 
 struct GemmArgs {
     Layer L;
@@ -628,6 +632,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
         uint16_t *hs = (uint16_t *)(smem + wave * (BM * HP * 2));
         uint32_t *s_hm = (uint32_t *)(smem + 4 * (BM * HP * 2)); // [4][BM] row maxima per wave
         int8_t *s_eh = (int8_t *)(s_hm + 4 * BM);                // [BM] the block scale of each row
+        float *s_rf = (float *)(s_eh + (BM + 15) / 16 * 16);     // [BM] 2^e of each row
         const bool cols_live = nbi * 128 + wave * 32 < I;      // this wave's 32 h columns exist
         // h = silu(g) u in fp32 (scales of x and of the weight rows taken out), in place of
         // the gate accumulators; then the largest |h| of each row over this wave's columns
@@ -657,30 +662,34 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &a, const int bid, uint
             }
         }
         __syncthreads();
-        // the block's scale per row (from the four waves' maxima), then h 2^e staged as fp16
+        // the block's scale per row, once per row (thread `row`, from the four waves'
+        // maxima), then h 2^e staged as fp16
+        if (tid < BM) {
+            uint32_t mb = s_hm[tid];
+#pragma unroll
+            for (int w = 1; w < 4; ++w) mb = max(mb, s_hm[w * BM + tid]);
+            const float m = __uint_as_float(mb);
+            const int eh = exact ? (m > 0.0f ? clamp_exp(14 - ilog2f(m)) : 0) : block_exp(m);
+            s_eh[tid] = (int8_t)eh;
+            s_rf[tid] = exp2i(eh);
+        }
+        __syncthreads();
+        int pcol[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = j * 16 + n16;
+            pcol[j] = (col & ~7) | perm_pos<BITS>(col & 7);
+        }
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
             if (i < msub) {
-                u32x4 mb = *(const u32x4 *)(s_hm + i * 16 + 4 * cg);
-#pragma unroll
-                for (int w = 1; w < 4; ++w) {
-                    const u32x4 o = *(const u32x4 *)(s_hm + w * BM + i * 16 + 4 * cg);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mb[r] = max(mb[r], o[r]);
-                }
+                const f32x4 f = *(const f32x4 *)(s_rf + i * 16 + 4 * cg);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float m = __uint_as_float(mb[r]);
-                    const int eh = exact ? (m > 0.0f ? clamp_exp(14 - ilog2f(m)) : 0) : block_exp(m);
-                    const float f = exp2i(eh);
                     const int row = i * 16 + 4 * cg + r;
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int col = j * 16 + n16;
-                        const int pcol = (col & ~7) | perm_pos<BITS>(col & 7);
-                        hs[row * HP + pcol] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(acc[i][j][r] * f));
-                    }
-                    if (wave == 0 && n16 == 0) s_eh[row] = (int8_t)eh;
+                    for (int j = 0; j < 2; ++j)
+                        hs[row * HP + pcol[j]] = __builtin_bit_cast(uint16_t, f32_to_f16_ftz(acc[i][j][r] * f[r]));
                 }
             }
         }
