@@ -52,14 +52,14 @@ ORDER_SEED = 20261202
 # the traffic is reported as null until measured again.
 DECODE_SOURCES = ("csrc/decode.hip", "csrc/decode_state.h", "csrc/common.h", "csrc/internal.h")
 GEMM_SOURCES = ("csrc/gemm.hip", "csrc/common.h", "csrc/internal.h")
-PREFILL_TRAFFIC = {"sources_sha256": "55a29b8f1ef5718d3934721b172c16ae9093677207b32fcc740561035c085f4e", "bytes": 1042226686}
+PREFILL_TRAFFIC = {"sources_sha256": "279c7406c2828432542a77d18847b1e143e9929f7fc32dbc7fa55e0bcac0c139", "bytes": 1045948779}
 DECODE_TRAFFIC = {"sources_sha256": "177650939e42ec1dd0c05f0fed8f9eee0d179577246eafde31da84044b4fd3d2", "bytes": 18129336}
 # MFMA utilisation of the grouped GEMM from rocprofv3 --pmc (medians per dispatch):
 # busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); keyed like
 # the traffic.
-GEMM_COUNTERS = {"sources_sha256": "55a29b8f1ef5718d3934721b172c16ae9093677207b32fcc740561035c085f4e",
-                 "k_gemm<4>": {"mfma_busy": 0.3649, "profile": "profiles/k_gemm_mfma_busy.md"},
-                 "k_gemm<8>": {"mfma_busy": 0.3747, "profile": "profiles/k_gemm_mfma_busy.md"}}
+GEMM_COUNTERS = {"sources_sha256": "279c7406c2828432542a77d18847b1e143e9929f7fc32dbc7fa55e0bcac0c139",
+                 "k_gemm<4>": {"mfma_busy": 0.3741, "profile": "profiles/k_gemm_mfma_busy.md"},
+                 "k_gemm<8>": {"mfma_busy": 0.3864, "profile": "profiles/k_gemm_mfma_busy.md"}}
 
 
 # ----------------------------------------------------------- algorithmic accounting
